@@ -1,0 +1,20 @@
+"""fp64 CPU oracle of the basic-RNN forward recurrence.
+
+TEST INFRASTRUCTURE: imported only by ``tests/``, by ``__graft_entry__.smoke()``
+and by the benchmark's CPU-baseline leg.  The product library never imports it
+and never falls back to it.
+
+Pins: every function here is checked in ``tests/test_oracle.py`` against
+brute force in exact rational arithmetic, closed forms (W = 0, W = I, cyclic
+permutations, the linear regime's block-triangular solve, diagonal W),
+invariants (batch independence, chunking in time, positive homogeneity) and a
+hand-worked example under ``tests/golden/``.
+"""
+from .rnn import (  # noqa: F401
+    TOL_F16,
+    TOL_F32,
+    forward_dense,
+    forward_sparse,
+    sparse_to_dense,
+    tolerance_ratio,
+)

@@ -1,0 +1,136 @@
+"""Seeded synthetic inputs for the basic-RNN forward recurrence.
+
+This module only draws random numbers and lays them out.  It holds none of the
+recurrence's arithmetic, so both the fp64 CPU oracle (through the tests) and the
+HIP path (through the tests and the benchmark) can be fed from it.
+
+Workloads follow the layer sizes, batch size, densities and sequence length on
+the pages:
+  * "Sparse Persistent RNNs: Squeezing Large Recurrent Networks On-Chip",
+    table "Measured effects reported in the paper": layer sizes 1152, 1792 and
+    5760, batch size 4, densities 10 % and 1 %, 256 timesteps, and
+    load-balanced (row-balanced) pruning, i.e. the same number of nonzeros in
+    every row;
+  * "persistent-rnn" (Fast Recurrent Networks Library), "What This Project
+    Does": small batches, "like 4".
+
+Value distributions (the pages state none):
+  dense W   ~ N(0, 0.8^2 / N)   (circular law: spectral radius ~0.8)
+  sparse W  ~ N(0, 0.8^2 / K)   on K distinct columns per row, drawn uniformly
+                                without replacement and stored sorted
+  X         ~ N(0, 1)           fp32, the pre-activations W_x x_t + b
+  h0        = 0                 (or |N(0,1)| when asked for)
+
+Random streams: ``numpy.random.SeedSequence(seed).spawn(3)`` gives independent
+generators for W, X and h0, in that order.  fp16 weights are produced by
+rounding the fp64 draw to the nearest fp16 (numpy's round-to-nearest-even);
+the oracle and the GPU consume the same stored array, so the rounding is part
+of the input, never part of the error.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+from typing import Dict, Optional
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic recurrence problem (sizes, weight format, seed)."""
+
+    name: str
+    kind: str            # "dense" or "sparse"
+    N: int               # hidden size (rows = columns of W)
+    B: int               # batch
+    T: int               # timesteps
+    w_dtype: str         # "f32" or "f16" (dense W, or sparse values)
+    K: int = 0           # nonzeros per row (sparse only)
+    seed: int = 0
+    h0: str = "zeros"    # "zeros" or "randn" (|N(0,1)|)
+
+    @property
+    def nnz(self) -> int:
+        return self.N * (self.K if self.kind == "sparse" else self.N)
+
+    @property
+    def flop_per_step(self) -> int:
+        """Multiply-adds of W.h_{t-1} counted as 2 flops each, all batch rows."""
+        return 2 * self.B * self.nnz
+
+    @property
+    def weight_bytes(self) -> int:
+        if self.kind == "dense":
+            return self.N * self.N * (4 if self.w_dtype == "f32" else 2)
+        return self.N * self.K * ((4 if self.w_dtype == "f32" else 2) + 2)
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five workload families.  K is the nonzero count per row at the stated
+# density (1152*10% -> 115, 1792*10% -> 179, 1792*1% -> 18, 5760*1% -> 58).
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("dense_f32_n256", "dense", 256, 4, 32, "f32", seed=101),
+        Workload("dense_f16_n1152", "dense", 1152, 4, 256, "f16", seed=102),
+        Workload("sparse10_f16_n1152", "sparse", 1152, 4, 256, "f16", K=115, seed=103),
+        Workload("dense_f16_n1792", "dense", 1792, 4, 256, "f16", seed=104),
+        Workload("sparse10_f16_n1792", "sparse", 1792, 4, 256, "f16", K=179, seed=104),
+        Workload("sparse1_f16_n1792", "sparse", 1792, 4, 256, "f16", K=18, seed=104),
+        Workload("sparse1_f16_n5760", "sparse", 5760, 4, 256, "f16", K=58, seed=105),
+    ]
+}
+
+
+def _np_dtype(w_dtype: str):
+    if w_dtype == "f32":
+        return np.float32
+    if w_dtype == "f16":
+        return np.float16
+    raise ValueError(f"unknown weight dtype {w_dtype!r}")
+
+
+def draw_sparse_pattern(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
+    """K distinct column indices per row, uniform without replacement, sorted.
+
+    Returns int16 [N, K] (so N must be at most 32767)."""
+    if not (1 <= K <= N):
+        raise ValueError("need 1 <= K <= N")
+    if N > 32767:
+        raise ValueError("int16 column indices need N <= 32767")
+    col = np.empty((N, K), dtype=np.int16)
+    for i in range(N):
+        col[i] = np.sort(rng.choice(N, size=K, replace=False))
+    return col
+
+
+def generate(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Draw one problem.
+
+    Returns a dict with host numpy arrays:
+      dense : ``W`` [N, N] (float32 or float16), row i = output neuron i
+      sparse: ``col`` int16 [N, K], ``val`` [N, K] (float32 or float16)
+      both  : ``X`` float32 [T, B, N], ``h0`` float32 [B, N]
+    """
+    seed = w.seed if seed is None else seed
+    s_w, s_x, s_h = np.random.SeedSequence(seed).spawn(3)
+    rng_w, rng_x, rng_h = (np.random.default_rng(s) for s in (s_w, s_x, s_h))
+    out: Dict[str, np.ndarray] = {}
+    wdt = _np_dtype(w.w_dtype)
+    if w.kind == "dense":
+        out["W"] = (rng_w.standard_normal((w.N, w.N)) * (0.8 / np.sqrt(w.N))).astype(wdt)
+    elif w.kind == "sparse":
+        out["col"] = draw_sparse_pattern(rng_w, w.N, w.K)
+        out["val"] = (rng_w.standard_normal((w.N, w.K)) * (0.8 / np.sqrt(w.K))).astype(wdt)
+    else:
+        raise ValueError(f"unknown kind {w.kind!r}")
+    out["X"] = rng_x.standard_normal((w.T, w.B, w.N)).astype(np.float32)
+    if w.h0 == "zeros":
+        out["h0"] = np.zeros((w.B, w.N), dtype=np.float32)
+    elif w.h0 == "randn":
+        out["h0"] = np.abs(rng_h.standard_normal((w.B, w.N))).astype(np.float32)
+    else:
+        raise ValueError(f"unknown h0 mode {w.h0!r}")
+    return out

@@ -1,0 +1,353 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test checks the oracle against something other than itself: a hand-worked
+example, brute force in exact rational arithmetic, closed forms (W = 0,
+W = I, cyclic shifts, the linear regime as one block-triangular linear solve,
+diagonal W) and invariants (batch independence, chunking in time, positive
+homogeneity, sparse == its dense copy).  Together they fail on a dropped term,
+a wrong sign, a transposed W, an off-by-one in time, an ignored h0, a wrong
+activation and a swapped sparse index.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from persistent_rnn_fwd_amd.inputs import WORKLOADS, generate
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# hand-worked example
+# ---------------------------------------------------------------------------
+def _golden():
+    with open(os.path.join(GOLDEN, "hand_worked_n2_b2_t3.json")) as f:
+        return json.load(f)
+
+
+def test_golden_dense():
+    g = _golden()
+    H = oracle.forward_dense(np.array(g["W"]), np.array(g["X"]), np.array(g["h0"]))
+    np.testing.assert_array_equal(H, np.array(g["H"]))
+
+
+def test_golden_sparse():
+    g = _golden()
+    H = oracle.forward_sparse(np.array(g["col"]), np.array(g["val"]), np.array(g["X"]), np.array(g["h0"]))
+    np.testing.assert_array_equal(H, np.array(g["H"]))
+
+
+def test_golden_catches_transpose():
+    g = _golden()
+    H = oracle.forward_dense(np.array(g["W"]).T, np.array(g["X"]), np.array(g["h0"]))
+    assert not np.array_equal(H, np.array(g["H"]))
+
+
+# ---------------------------------------------------------------------------
+# brute force in exact rationals
+# ---------------------------------------------------------------------------
+def _brute_dense(W, X, h0):
+    """Element-by-element loops over Fractions: exact, no floating point."""
+    T, B, N = len(X), len(X[0]), len(W)
+    h = [[Fraction(v) for v in row] for row in h0]
+    out = []
+    for t in range(T):
+        new = []
+        for b in range(B):
+            row = []
+            for i in range(N):
+                s = Fraction(X[t][b][i])
+                for j in range(N):
+                    s += Fraction(W[i][j]) * h[b][j]
+                row.append(s if s > 0 else Fraction(0))
+            new.append(row)
+        out.append(new)
+        h = new
+    return out
+
+
+def _brute_sparse(col, val, X, h0):
+    T, B, N, K = len(X), len(X[0]), len(col), len(col[0])
+    h = [[Fraction(v) for v in row] for row in h0]
+    out = []
+    for t in range(T):
+        new = []
+        for b in range(B):
+            row = []
+            for i in range(N):
+                s = Fraction(X[t][b][i])
+                for k in range(K):
+                    s += Fraction(val[i][k]) * h[b][col[i][k]]
+                row.append(s if s > 0 else Fraction(0))
+            new.append(row)
+        out.append(new)
+        h = new
+    return out
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_brute_force_dense_exact(seed):
+    rng = np.random.default_rng(seed)
+    N = int(rng.integers(1, 5))
+    B = int(rng.integers(1, 3))
+    T = int(rng.integers(1, 4))
+    # dyadic values: every partial sum is exact in fp64
+    W = rng.integers(-3, 4, size=(N, N)) / 2.0
+    X = rng.integers(-3, 4, size=(T, B, N)) / 4.0
+    h0 = rng.integers(0, 4, size=(B, N)) / 2.0
+    ref = _brute_dense(W.tolist(), X.tolist(), h0.tolist())
+    H = oracle.forward_dense(W, X, h0)
+    np.testing.assert_array_equal(H, np.array(ref, dtype=np.float64))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_brute_force_sparse_exact(seed):
+    rng = np.random.default_rng(100 + seed)
+    N = int(rng.integers(1, 5))
+    K = int(rng.integers(1, N + 1))
+    B = int(rng.integers(1, 3))
+    T = int(rng.integers(1, 4))
+    col = np.stack([np.sort(rng.choice(N, K, replace=False)) for _ in range(N)])
+    val = rng.integers(-3, 4, size=(N, K)) / 2.0
+    X = rng.integers(-3, 4, size=(T, B, N)) / 4.0
+    h0 = rng.integers(0, 4, size=(B, N)) / 2.0
+    ref = _brute_sparse(col.tolist(), val.tolist(), X.tolist(), h0.tolist())
+    H = oracle.forward_sparse(col, val, X, h0)
+    np.testing.assert_array_equal(H, np.array(ref, dtype=np.float64))
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+def test_zero_weights_give_relu_of_x():
+    rng = np.random.default_rng(1)
+    T, B, N = 5, 3, 17
+    X = rng.standard_normal((T, B, N))
+    h0 = np.abs(rng.standard_normal((B, N)))
+    H = oracle.forward_dense(np.zeros((N, N)), X, h0)
+    np.testing.assert_array_equal(H, np.where(X > 0, X, 0.0))
+    col = np.arange(N).reshape(N, 1)
+    Hs = oracle.forward_sparse(col, np.zeros((N, 1)), X, h0)
+    np.testing.assert_array_equal(Hs, np.where(X > 0, X, 0.0))
+
+
+def test_identity_weights_give_prefix_sums():
+    rng = np.random.default_rng(2)
+    T, B, N = 9, 2, 13
+    X = rng.integers(0, 50, size=(T, B, N)).astype(np.float64)
+    h0 = rng.integers(0, 50, size=(B, N)).astype(np.float64)
+    expect = h0[None] + np.cumsum(X, axis=0)
+    np.testing.assert_array_equal(oracle.forward_dense(np.eye(N), X, h0), expect)
+    col = np.arange(N).reshape(N, 1)
+    np.testing.assert_array_equal(oracle.forward_sparse(col, np.ones((N, 1)), X, h0), expect)
+
+
+def test_cyclic_shift_closed_form():
+    """W[i, (i+1) % N] = 1 shifts the state by one place per step.
+
+    With X >= 0 nothing is clipped, so H[t] = sum_{s<=t} roll(X[s], -(t-s))
+    + roll(h0, -(t+1)); using W^T instead would roll the other way."""
+    rng = np.random.default_rng(3)
+    T, B, N = 7, 2, 11
+    X = rng.integers(0, 9, size=(T, B, N)).astype(np.float64)
+    h0 = rng.integers(0, 9, size=(B, N)).astype(np.float64)
+    W = np.zeros((N, N))
+    W[np.arange(N), (np.arange(N) + 1) % N] = 1.0
+    expect = np.empty((T, B, N))
+    for t in range(T):
+        acc = np.roll(h0, -(t + 1), axis=1)
+        for s in range(t + 1):
+            acc = acc + np.roll(X[s], -(t - s), axis=1)
+        expect[t] = acc
+    np.testing.assert_array_equal(oracle.forward_dense(W, X, h0), expect)
+    col = ((np.arange(N) + 1) % N).reshape(N, 1)
+    np.testing.assert_array_equal(oracle.forward_sparse(col, np.ones((N, 1)), X, h0), expect)
+
+
+def test_linear_regime_block_triangular_solve():
+    """With W >= 0, X > 0, h0 >= 0 no ReLU clips, so the T steps are one linear
+    system: h_0 - 0 = x_0 + W h0, h_t - W h_{t-1} = x_t, solved by LU."""
+    rng = np.random.default_rng(4)
+    T, B, N = 6, 3, 8
+    W = rng.uniform(0, 0.2, size=(N, N))
+    X = rng.uniform(0.1, 1.0, size=(T, B, N))
+    h0 = rng.uniform(0, 1.0, size=(B, N))
+    M = np.eye(T * N)
+    for t in range(1, T):
+        M[t * N:(t + 1) * N, (t - 1) * N:t * N] = -W
+    expect = np.empty((T, B, N))
+    for b in range(B):
+        rhs = X[:, b, :].copy()
+        rhs[0] += W @ h0[b]
+        expect[:, b, :] = np.linalg.solve(M, rhs.reshape(-1)).reshape(T, N)
+    H = oracle.forward_dense(W, X, h0)
+    np.testing.assert_allclose(H, expect, rtol=1e-12, atol=1e-12)
+    # the same system through the sparse route (K = N, every column listed)
+    col = np.tile(np.arange(N), (N, 1))
+    np.testing.assert_allclose(oracle.forward_sparse(col, W, X, h0), expect, rtol=1e-12, atol=1e-12)
+
+
+def test_diagonal_weights_scalar_recurrences():
+    rng = np.random.default_rng(5)
+    T, B, N = 10, 2, 6
+    a = rng.uniform(-1.5, 1.5, size=N)
+    X = rng.standard_normal((T, B, N))
+    h0 = np.abs(rng.standard_normal((B, N)))
+    H = oracle.forward_dense(np.diag(a), X, h0)
+    for b in range(B):
+        for i in range(N):
+            h = h0[b, i]
+            for t in range(T):
+                h = max(a[i] * h + X[t, b, i], 0.0)
+                assert H[t, b, i] == pytest.approx(h, rel=1e-14, abs=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+def _small_problem(seed, T=12, B=4, N=24):
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((N, N)) * 0.8 / np.sqrt(N)
+    X = rng.standard_normal((T, B, N))
+    h0 = np.abs(rng.standard_normal((B, N)))
+    return W, X, h0
+
+
+def test_batch_rows_are_independent():
+    W, X, h0 = _small_problem(6)
+    H = oracle.forward_dense(W, X, h0)
+    for b in range(X.shape[1]):
+        Hb = oracle.forward_dense(W, X[:, b:b + 1], h0[b:b + 1])
+        np.testing.assert_allclose(H[:, b:b + 1], Hb, rtol=1e-13, atol=1e-13)
+    # identical batch rows give identical outputs
+    X2 = np.repeat(X[:, :1], 3, axis=1)
+    H2 = oracle.forward_dense(W, X2, np.repeat(h0[:1], 3, axis=0))
+    assert np.array_equal(H2[:, 0], H2[:, 1]) and np.array_equal(H2[:, 0], H2[:, 2])
+
+
+def test_chunking_in_time_is_exact():
+    W, X, h0 = _small_problem(7)
+    H = oracle.forward_dense(W, X, h0)
+    for T1 in (1, 5, 11):
+        Ha = oracle.forward_dense(W, X[:T1], h0)
+        Hb = oracle.forward_dense(W, X[T1:], Ha[-1])
+        np.testing.assert_array_equal(np.concatenate([Ha, Hb]), H)
+
+
+def test_positive_homogeneity_is_exact():
+    W, X, h0 = _small_problem(8)
+    H = oracle.forward_dense(W, X, h0)
+    for k in (-3, 1, 7):
+        np.testing.assert_array_equal(oracle.forward_dense(W, X * 2.0 ** k, h0 * 2.0 ** k), H * 2.0 ** k)
+
+
+def test_sparse_equals_dense_copy():
+    rng = np.random.default_rng(9)
+    T, B, N, K = 10, 4, 40, 7
+    col = np.stack([np.sort(rng.choice(N, K, replace=False)) for _ in range(N)])
+    val = rng.standard_normal((N, K)) * 0.8 / np.sqrt(K)
+    X = rng.standard_normal((T, B, N))
+    h0 = np.abs(rng.standard_normal((B, N)))
+    Wd = oracle.sparse_to_dense(col, val, N)
+    # the dense copy has exactly the listed entries
+    assert np.count_nonzero(Wd) == np.count_nonzero(val)
+    for i in range(N):
+        for k in range(K):
+            assert Wd[i, col[i, k]] == val[i, k]
+    np.testing.assert_allclose(oracle.forward_sparse(col, val, X, h0),
+                               oracle.forward_dense(Wd, X, h0), rtol=1e-13, atol=1e-13)
+    # the order of the (col, val) pairs inside a row does not matter
+    perm = np.stack([rng.permutation(K) for _ in range(N)])
+    col_p = np.take_along_axis(col, perm, axis=1)
+    val_p = np.take_along_axis(val, perm, axis=1)
+    np.testing.assert_allclose(oracle.forward_sparse(col_p, val_p, X, h0),
+                               oracle.forward_sparse(col, val, X, h0), rtol=1e-13, atol=1e-13)
+
+
+def test_nan_propagates_and_empty_sequence():
+    W, X, h0 = _small_problem(10, T=4, B=2, N=5)
+    X = X.copy()
+    X[1, 0, 2] = np.nan
+    H = oracle.forward_dense(W, X, h0)
+    assert np.isnan(H[1, 0, 2]) and np.isnan(H[2, 0]).all()   # spreads through W
+    assert not np.isnan(H[:, 1]).any()                          # not across batch rows
+    assert oracle.forward_dense(W, X[:0], h0).shape == (0, 2, 5)
+
+
+def test_tolerance_ratio():
+    ref = np.array([0.0, 1.0, 10.0])
+    assert oracle.tolerance_ratio(ref, ref, 1e-4) == 0.0
+    assert oracle.tolerance_ratio(ref + np.array([1e-4, 0, 0]), ref, 1e-4) == pytest.approx(1.0)
+    assert oracle.tolerance_ratio(ref + np.array([0, 0, 11e-4]), ref, 1e-4) == pytest.approx(1.0)
+    assert oracle.tolerance_ratio(np.array([np.nan, 1, 10]), ref, 1e-4) == float("inf")
+    both = np.array([np.nan, 1.0])
+    assert oracle.tolerance_ratio(both, both, 1e-4) == 0.0
+
+
+# ---------------------------------------------------------------------------
+# generators and tolerance sanity
+# ---------------------------------------------------------------------------
+def test_generator_sparse_pattern_and_values():
+    w = WORKLOADS["sparse10_f16_n1152"]
+    d = generate(w)
+    col, val = d["col"], d["val"]
+    assert col.dtype == np.int16 and col.shape == (1152, 115)
+    assert val.dtype == np.float16 and val.shape == (1152, 115)
+    assert (np.diff(col.astype(np.int64), axis=1) > 0).all()      # sorted, distinct
+    assert col.min() >= 0 and col.max() < 1152
+    std = float(np.std(val.astype(np.float64)))
+    assert abs(std - 0.8 / np.sqrt(115)) < 0.02 * 0.8 / np.sqrt(115) * 5
+    assert d["X"].dtype == np.float32 and d["X"].shape == (256, 4, 1152)
+    assert not d["h0"].any()
+    # deterministic per seed, different across seeds
+    d2 = generate(w)
+    assert np.array_equal(d2["col"], col) and np.array_equal(d2["X"], d["X"])
+    d3 = generate(w, seed=w.seed + 1000)
+    assert not np.array_equal(d3["col"], col)
+
+
+@pytest.mark.parametrize("name", ["dense_f32_n256", "sparse10_f16_n1152"])
+def test_generator_spectral_radius_near_0p8(name):
+    w = WORKLOADS[name]
+    d = generate(w)
+    if w.kind == "dense":
+        Wd = d["W"].astype(np.float64)
+    else:
+        Wd = oracle.sparse_to_dense(d["col"], d["val"], w.N)
+    rho = np.max(np.abs(np.linalg.eigvals(Wd)))
+    assert 0.65 < rho < 0.95
+
+
+def test_fp32_arithmetic_meets_fp32_bar():
+    """An fp32 evaluation of the recurrence passes 1e-4 (1 + |h|) with margin,
+    so the bar is reachable by any fp32 summation order."""
+    w = WORKLOADS["dense_f32_n256"]
+    d = generate(w, seed=w.seed + 1000)
+    H = oracle.forward_dense(d["W"], d["X"], d["h0"])
+    W32 = d["W"].astype(np.float32)
+    h = d["h0"].astype(np.float32)
+    H32 = np.empty_like(d["X"])
+    for t in range(w.T):
+        h = np.maximum(d["X"][t] + h @ W32.T, np.float32(0))
+        H32[t] = h
+    assert oracle.tolerance_ratio(H32, H, oracle.TOL_F32) < 0.2
+
+
+def test_fp16_hidden_state_model_meets_fp16_bar():
+    """fp16 weights with fp32 accumulation pass 2e-2 (1 + |h|) by a wide margin,
+    even if h were rounded to fp16 at every step."""
+    w = WORKLOADS["dense_f16_n1152"].with_(T=64)
+    d = generate(w)
+    H = oracle.forward_dense(d["W"], d["X"], d["h0"])
+    W32 = d["W"].astype(np.float32)
+    h = d["h0"]
+    H16 = np.empty_like(d["X"])
+    for t in range(w.T):
+        hq = h.astype(np.float16).astype(np.float32)
+        h = np.maximum(d["X"][t] + hq @ W32.T, np.float32(0))
+        H16[t] = h
+    assert oracle.tolerance_ratio(H16, H, oracle.TOL_F16) < 0.2
