@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the persistent basic-RNN forward on one MI355X.
+
+Workload (one bench step = one pass of the whole recurrence for each weight
+format of the headline layer): N = 1792 neurons, batch B = 4, T = 256
+timesteps,
+  * one call with dense fp16 W        (nnz = N^2),
+  * one call with 10 % row-balanced sparse fp16 W (K = 179 nonzeros per row),
+both with fp32 X / H and fp32 accumulation, inputs resident in HBM.
+
+Prints ONE JSON line:
+  value        RNN timesteps/s over the step (2 * T timesteps per step)
+  roofline     the dominant kernel's algorithmic flops per launch over its
+               mean launch time (HIP events on the launch stream) against the
+               fp32 vector peak; traffic from a committed counter run if it
+               still matches the kernel sources, else null
+  cpu_baseline the fp64 oracle on the host, on a bounded sample of the same
+               workload (timesteps/s, threads it used)
+  detail       per-format timesteps/s, GFLOP/s, per-step time by the slope
+               between T = 256 and T = 128, the measured sync floor per step,
+               equivalent weight bytes/s, and the max error ratio vs the oracle
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP32_VECTOR_PEAK = 157.3e12   # MI355X published fp32 vector peak, FLOP/s
+HBM_PEAK = 8.0e12             # MI355X HBM3E, bytes/s
+COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_dense_f16_n1792.json")
+KERNEL_SOURCES = ["device_common.h", "kernels.h", "dense_kernel.h", "sparse_kernel.h",
+                  "dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "persistent_rnn_fwd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle leg (profiling runs)")
+    ap.add_argument("--no-check", action="store_true", help="skip the oracle check of the GPU output")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the host oracle sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from persistent_rnn_fwd_amd import Handle
+    from persistent_rnn_fwd_amd.inputs import WORKLOADS, generate
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    wd = WORKLOADS["dense_f16_n1792"]
+    ws = WORKLOADS["sparse10_f16_n1792"]
+    w1 = WORKLOADS["sparse1_f16_n1792"]
+    N, B, T = wd.N, wd.B, wd.T
+    host = {w.name: generate(w) for w in (wd, ws, w1)}
+    g = {name: {k: torch.from_numpy(v).to(dev) for k, v in d.items()} for name, d in host.items()}
+    out = {name: torch.empty((T, B, N), dtype=torch.float32, device=dev) for name in host}
+
+    h = Handle()
+    stream = torch.cuda.current_stream()
+
+    def call(name, t=T):
+        d, o = g[name], out[name]
+        if "W" in d:
+            h.forward_dense(d["W"], d["X"][:t], d["h0"], out=o[:t])
+        else:
+            h.forward_sparse(d["col"], d["val"], d["X"][:t], d["h0"], out=o[:t])
+
+    # correctness of the timed configuration (not timed)
+    err = {}
+    if not args.no_check:
+        import oracle
+        for w in (wd, ws, w1):
+            call(w.name)
+            h.synchronize()
+            d = host[w.name]
+            ref = (oracle.forward_dense(d["W"], d["X"], d["h0"]) if w.kind == "dense"
+                   else oracle.forward_sparse(d["col"], d["val"], d["X"], d["h0"]))
+            err[w.name] = oracle.tolerance_ratio(out[w.name].cpu().numpy(), ref, oracle.TOL_F16)
+            if err[w.name] > 1.0:
+                print(f"bench.py: {w.name} fails the oracle tolerance (ratio {err[w.name]:.3g})", file=sys.stderr)
+                sys.exit(1)
+
+    # warmup
+    for _ in range(args.warmup):
+        call(wd.name)
+        call(ws.name)
+    h.synchronize()
+
+    # timed region: K steps, each one dense call and one sparse call, with an
+    # event pair around every launch on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        call(wd.name)
+        ev[k][1].record(stream)
+        ev[k][2].record(stream)
+        call(ws.name)
+        ev[k][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    h.synchronize()
+    dense_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    sparse_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+
+    def timed(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in es:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in es]))
+
+    # per-step time by the slope between T and T/2, and the sync floor
+    detail = {}
+    floor_out = torch.empty((T, B, N), dtype=torch.float32, device=dev)
+    f_full = timed(lambda: h.sync_floor(N, B, T, out=floor_out))
+    f_half = timed(lambda: h.sync_floor(N, B, T // 2, out=floor_out[: T // 2]))
+    floor_us = (f_full - f_half) * 1e3 / (T - T // 2)
+    h.synchronize()
+    for w in (wd, ws, w1):
+        full = timed(lambda: call(w.name))
+        half = timed(lambda: call(w.name, T // 2))
+        step_us = (full - half) * 1e3 / (T - T // 2)
+        flop = w.flop_per_step
+        detail[w.name] = {
+            "ms_per_call": round(full, 4),
+            "timesteps_per_s": round(T / (full * 1e-3), 1),
+            "us_per_step_slope": round(step_us, 3),
+            "vs_sync_floor": round(step_us / floor_us, 3) if floor_us > 0 else None,
+            "gflop_per_s": round(flop * T / (full * 1e-3) / 1e9, 2),
+            "pct_fp32_vector_peak": round(100 * flop * T / (full * 1e-3) / FP32_VECTOR_PEAK, 3),
+            "weight_bytes": w.weight_bytes,
+            "equiv_weight_TB_per_s": round(w.weight_bytes * T / (full * 1e-3) / 1e12, 3),
+            "max_err_ratio": round(err[w.name], 5) if w.name in err else None,
+            "plan": None,
+        }
+        h.synchronize()
+        detail[w.name]["plan"] = {k: v for k, v in h.last_plan().items() if k != "first_step"}
+    detail["sync_floor_us_per_step"] = round(floor_us, 3)
+    detail["sync_floor_ms_per_call"] = round(f_full, 4)
+
+    # roofline of the dominant kernel (larger mean launch time)
+    dom, dom_ms = (wd, dense_ms) if dense_ms >= sparse_ms else (ws, sparse_ms)
+    flop_per_launch = dom.flop_per_step * T
+    achieved = flop_per_launch / (dom_ms * 1e-3)
+    traffic = None
+    if os.path.exists(COUNTER_FILE):
+        try:
+            c = json.load(open(COUNTER_FILE))
+            if c.get("kernel_source_hash") == kernel_source_hash() and c.get("workload") == dom.name:
+                traffic = c.get("hbm_bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    roofline = {
+        "bound": "alu",
+        "kernel": f"dense_kernel ({dom.name})" if dom is wd else f"sparse_kernel ({dom.name})",
+        "achieved": round(achieved / 1e12, 4),
+        "peak": FP32_VECTOR_PEAK / 1e12,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / FP32_VECTOR_PEAK, 5),
+        "traffic": traffic,
+        "mean_launch_ms": round(dom_ms, 4),
+        "flop_per_launch": flop_per_launch,
+    }
+
+    # host baseline: the oracle as it stands, on a bounded sample
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        Ts, spent, steps_done = 8, 0.0, 0
+        while spent < args.cpu_seconds and Ts <= T:
+            for w in (wd, ws):
+                d = host[w.name]
+                a = time.perf_counter()
+                if w.kind == "dense":
+                    oracle.forward_dense(d["W"], d["X"][:Ts], d["h0"])
+                else:
+                    oracle.forward_sparse(d["col"], d["val"], d["X"][:Ts], d["h0"])
+                spent += time.perf_counter() - a
+                steps_done += Ts
+            Ts = min(2 * Ts, T) if Ts < T else Ts
+        cpu = {
+            "value": round(steps_done / spent, 1),
+            "unit": "timesteps/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle, dense + 10% sparse N=1792 B=4, {steps_done} timesteps "
+                      f"in {spent:.1f} s ({os.cpu_count()} host CPUs visible)",
+        }
+
+    h.close()
+    line = {
+        "metric": "RNN timesteps/s & eff. GFLOP/s, N=1792 B=4 dense+10% sparse; % roofline",
+        "value": round(2 * T / (ms_per_step * 1e-3), 1),
+        "unit": "timesteps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "basic-RNN forward N=1792 B=4 T=256: one dense fp16-W call + one 10% "
+                        "row-balanced sparse fp16-W call (K=179) per step, fp32 X/H/accumulate",
+            "N": N, "B": B, "T": T, "K_sparse": ws.K, "weights": "f16",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * prnn.h - persistent basic-RNN forward recurrence for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (a basic RNN layer; "persistent-rnn", section "Important
+ * Constraints": basic RNN layers only):
+ *
+ *     H[t][b][i] = max(0, X[t][b][i] + sum_j W[i][j] * H[t-1][b][j]),   H[-1] = h0
+ *
+ * for t = 0 .. T-1, b = 0 .. B-1, i = 0 .. N-1.  X already holds the input
+ * projection (and bias) of every timestep, computed before the recurrence
+ * ("Optimizing Performance of Recurrent Neural Networks on GPUs", Abstract:
+ * the single-layer stage takes the input-side product out of the sequential
+ * loop).  The activation is ReLU.
+ *
+ * The recurrence runs as ONE persistent kernel per call: every workgroup loads
+ * its rows of W once into registers and keeps them there for all T steps, so W
+ * is never re-read from memory inside the time loop ("persistent-rnn", "What
+ * This Project Does": weights cached in the register files instead of being
+ * reloaded every step).  Workgroups exchange h_{t-1} once per step through a
+ * small ring buffer whose words carry their own step tag, so no separate
+ * barrier pass and no reset pass are needed between steps ("Sparse Persistent
+ * RNNs: Squeezing Large Recurrent Networks On-Chip", table "Measured effects
+ * reported in the paper": Lamport timestamps row).  W may be dense, or sparse
+ * with the same number K of nonzeros in every row (same table: load-balanced
+ * pruning row).
+ *
+ * API style follows a cuDNN-like library ("persistent-rnn", "Who Would Use
+ * This"): an opaque handle, a status code from every call, caller-owned device
+ * buffers, and asynchronous execution on a caller-provided stream.
+ *
+ * Conventions shared by every call below
+ * --------------------------------------
+ *  - All array arguments are DEVICE pointers owned by the caller.  The library
+ *    reads W / col / val / X / h0, writes only H, and keeps no pointer after
+ *    the work it enqueued has finished.  Buffers must stay valid until then.
+ *  - All arrays are dense, row-major, with the last index fastest:
+ *      W   [N][N]   W[i*N + j] = weight from input neuron j to output neuron i
+ *      col [N][K]   int16 column indices of row i's nonzeros, each in [0, N)
+ *      val [N][K]   values belonging to col
+ *      X   [T][B][N] fp32 pre-activations
+ *      h0  [B][N]   fp32 initial state, or NULL for zeros
+ *      H   [T][B][N] fp32 output: H[t] is the state after consuming X[t]
+ *    X, h0 and H need 4-byte alignment; W, col and val need 4-byte alignment.
+ *  - Calls are asynchronous: a SUCCESS return means the work was enqueued on
+ *    `stream` (NULL = the default stream).  An error found while the kernel
+ *    runs (a step that never completes within the watchdog limit) is reported
+ *    as PRNN_STATUS_EXECUTION_FAILED by prnn_synchronize() or prnn_destroy();
+ *    until it has been reported, later forward calls on the handle are
+ *    enqueued but do nothing (H is left as it was).
+ *  - One forward call may be in flight per handle at a time (the handle owns
+ *    the exchange ring).  Use one handle per concurrently used stream.  A
+ *    handle is not thread-safe.  Every call must be made with the handle's
+ *    device current.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef PRNN_H_
+#define PRNN_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct prnnContext* prnnHandle_t;
+
+typedef enum {
+  PRNN_STATUS_SUCCESS = 0,
+  PRNN_STATUS_BAD_PARAM = 1,        /* invalid argument; nothing was enqueued            */
+  PRNN_STATUS_NOT_SUPPORTED = 2,    /* valid, but outside what fits on chip / this GPU   */
+  PRNN_STATUS_ALLOC_FAILED = 3,     /* device or pinned allocation failed                */
+  PRNN_STATUS_EXECUTION_FAILED = 4, /* a launched step never completed (watchdog)        */
+  PRNN_STATUS_INTERNAL_ERROR = 5    /* a HIP runtime call failed                         */
+} prnnStatus_t;
+
+typedef enum {
+  PRNN_DATA_FLOAT = 0, /* fp32 */
+  PRNN_DATA_HALF = 1   /* fp16 (IEEE binary16); products and sums are taken in fp32 */
+} prnnDataType_t;
+
+/* Launch plan of the last forward call on a handle (for tests and reports). */
+typedef struct {
+  int grid;          /* workgroups launched (one per compute unit at most)   */
+  int waves_per_wg;  /* = B: one wavefront of 64 lanes per batch row          */
+  int rows_per_wg;   /* largest number of W rows owned by one workgroup       */
+  int rmax;          /* compiled row capacity of the kernel instance          */
+  int chunks;        /* dense: 256-column chunks per lane; sparse: K slots    */
+  int lds_bytes;     /* dynamic LDS per workgroup                             */
+  uint64_t first_step; /* ring step counter of the call's first timestep      */
+} prnnPlanInfo_t;
+
+/* Creates a handle bound to the current HIP device.
+ * Returns NOT_SUPPORTED if the device is not gfx950, ALLOC_FAILED if the small
+ * internal buffers (status word, exchange ring) cannot be allocated,
+ * BAD_PARAM if handle is NULL. */
+prnnStatus_t prnn_create(prnnHandle_t* handle);
+
+/* Waits for all work the handle enqueued, frees its buffers and the handle.
+ * NULL is accepted (SUCCESS).  Returns EXECUTION_FAILED if a run on this handle
+ * failed and that was not yet reported, else SUCCESS. */
+prnnStatus_t prnn_destroy(prnnHandle_t handle);
+
+/* Dense W.  w_type selects fp32 or fp16 W; X, h0, H are fp32.
+ * BAD_PARAM: NULL handle/W/X/H (h0 may be NULL), N < 1, B not in [1, 8],
+ *            T < 0, bad w_type, misaligned pointer, X and H overlapping.
+ * NOT_SUPPORTED: W does not fit in the register files of the grid, or the
+ *            cooperative grid cannot be resident.
+ * T == 0 enqueues nothing and returns SUCCESS. */
+prnnStatus_t prnn_forward_dense(prnnHandle_t handle, int N, int B, int T,
+                                prnnDataType_t w_type, const void* W,
+                                const float* X, const float* h0, float* H,
+                                hipStream_t stream);
+
+/* Row-balanced sparse W: row i has exactly K nonzeros, at columns col[i][k]
+ * with values val[i][k].  Columns within a row must be distinct (a repeated
+ * column is summed, like the dense equivalent with the values added).
+ * BAD_PARAM: as for dense, plus K not in [1, N]; N > 32767 (int16 columns).
+ * NOT_SUPPORTED: the nonzeros or the staged h do not fit on chip.
+ * Column indices outside [0, N) are not checked on the device; they read
+ * zeros (buffer bounds checking), never memory outside the staging area. */
+prnnStatus_t prnn_forward_sparse(prnnHandle_t handle, int N, int B, int T, int K,
+                                 const int16_t* col, prnnDataType_t val_type, const void* val,
+                                 const float* X, const float* h0, float* H,
+                                 hipStream_t stream);
+
+/* The exchange and step protocol of a dense call with the same N, B and T and
+ * the same grid, without weights or arithmetic: the per-step floor that
+ * synchronisation alone costs.  Writes H (values are step numbers, not a
+ * recurrence).  Same errors as prnn_forward_dense. */
+prnnStatus_t prnn_sync_floor(prnnHandle_t handle, int N, int B, int T, float* H,
+                             hipStream_t stream);
+
+/* Waits for `stream`, then reports whether any run on the handle hit the
+ * watchdog (EXECUTION_FAILED, sticky until reported here or by destroy). */
+prnnStatus_t prnn_synchronize(prnnHandle_t handle, hipStream_t stream);
+/* (After a reported failure the handle is usable again: its exchange ring is
+ * reset before the next forward call.) */
+
+/* Number of workgroups for later calls (0 = automatic: up to one per compute
+ * unit).  BAD_PARAM if negative. */
+prnnStatus_t prnn_set_grid(prnnHandle_t handle, int workgroups);
+
+/* Upper bound, in microseconds, on one wait for h_{t-1} (default 200000).
+ * A wait that exceeds it stops the run and reports EXECUTION_FAILED. */
+prnnStatus_t prnn_set_watchdog_us(prnnHandle_t handle, uint32_t microseconds);
+
+/* Copies the plan of the last successful forward call into *info. */
+prnnStatus_t prnn_get_last_plan(prnnHandle_t handle, prnnPlanInfo_t* info);
+
+/* TEST ONLY: in the next forward call, workgroup `wg` does not publish its
+ * rows at timestep `step`, so the consumers' bounded waits expire and the
+ * run reports EXECUTION_FAILED (every kernel still exits normally).
+ * wg < 0 disables. */
+prnnStatus_t prnn_debug_skip_publish(prnnHandle_t handle, int wg, int step);
+
+/* Static description of a status code; never NULL, never allocates. */
+const char* prnn_status_string(prnnStatus_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRNN_H_ */

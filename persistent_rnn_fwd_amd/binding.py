@@ -1,0 +1,227 @@
+"""ctypes binding of libprnn.so (the C ABI declared in include/prnn.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+stream; every step of the recurrence runs in the library's HIP kernels.  If the
+library has not been built, every entry point raises; nothing falls back to
+another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libprnn.so")
+
+STATUS_NAMES = {
+    0: "PRNN_STATUS_SUCCESS",
+    1: "PRNN_STATUS_BAD_PARAM",
+    2: "PRNN_STATUS_NOT_SUPPORTED",
+    3: "PRNN_STATUS_ALLOC_FAILED",
+    4: "PRNN_STATUS_EXECUTION_FAILED",
+    5: "PRNN_STATUS_INTERNAL_ERROR",
+}
+SUCCESS, BAD_PARAM, NOT_SUPPORTED, ALLOC_FAILED, EXECUTION_FAILED, INTERNAL_ERROR = range(6)
+DATA_FLOAT, DATA_HALF = 0, 1
+
+# Every function include/prnn.h declares, with its ctypes signature.
+_H = ctypes.c_void_p
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+SIGNATURES = {
+    "prnn_create": (_I, [ctypes.POINTER(_H)]),
+    "prnn_destroy": (_I, [_H]),
+    "prnn_forward_dense": (_I, [_H, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "prnn_forward_sparse": (_I, [_H, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
+    "prnn_sync_floor": (_I, [_H, _I, _I, _I, _P, _P]),
+    "prnn_synchronize": (_I, [_H, _P]),
+    "prnn_set_grid": (_I, [_H, _I]),
+    "prnn_set_watchdog_us": (_I, [_H, ctypes.c_uint32]),
+    "prnn_get_last_plan": (_I, [_H, _P]),
+    "prnn_debug_skip_publish": (_I, [_H, _I, _I]),
+    "prnn_status_string": (ctypes.c_char_p, [_I]),
+}
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("grid", ctypes.c_int),
+        ("waves_per_wg", ctypes.c_int),
+        ("rows_per_wg", ctypes.c_int),
+        ("rmax", ctypes.c_int),
+        ("chunks", ctypes.c_int),
+        ("lds_bytes", ctypes.c_int),
+        ("first_step", ctypes.c_uint64),
+    ]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class PrnnError(RuntimeError):
+    def __init__(self, where: str, status: int):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}")
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Loads libprnn.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m persistent_rnn_fwd_amd.build` "
+                "(the HIP library is required; there is no fallback)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(where: str, status: int):
+    if status != SUCCESS:
+        raise PrnnError(where, status)
+
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtypes, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Handle:
+    """A library handle (prnn_create) bound to the current GPU."""
+
+    def __init__(self):
+        self._lib = load_library()
+        h = _H()
+        _check("prnn_create", self._lib.prnn_create(ctypes.byref(h)))
+        self._h = h
+        self.device = torch.device("cuda", torch.cuda.current_device())
+
+    # -- lifetime ---------------------------------------------------------
+    def close(self):
+        if getattr(self, "_h", None):
+            st = self._lib.prnn_destroy(self._h)
+            self._h = None
+            _check("prnn_destroy", st)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            if getattr(self, "_h", None):
+                self._lib.prnn_destroy(self._h)
+                self._h = None
+        except Exception:
+            pass
+
+    # -- options ------------------------------------------------------------
+    def set_grid(self, workgroups: int):
+        _check("prnn_set_grid", self._lib.prnn_set_grid(self._h, int(workgroups)))
+
+    def set_watchdog_us(self, us: int):
+        _check("prnn_set_watchdog_us", self._lib.prnn_set_watchdog_us(self._h, int(us)))
+
+    def debug_skip_publish(self, wg: int, step: int):
+        _check("prnn_debug_skip_publish", self._lib.prnn_debug_skip_publish(self._h, int(wg), int(step)))
+
+    def last_plan(self) -> dict:
+        info = PlanInfo()
+        _check("prnn_get_last_plan", self._lib.prnn_get_last_plan(self._h, ctypes.byref(info)))
+        return info.as_dict()
+
+    def synchronize(self, stream: Optional[torch.cuda.Stream] = None):
+        _check("prnn_synchronize", self._lib.prnn_synchronize(self._h, _stream_ptr(stream)))
+
+    # -- the recurrence -----------------------------------------------------
+    def forward_dense(self, W: torch.Tensor, X: torch.Tensor, h0: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """H[t] = relu(X[t] + H[t-1] W^T); W [N, N] fp32/fp16, X [T, B, N] fp32."""
+        T, B, N = X.shape
+        _need(W, "W", (torch.float32, torch.float16), (N, N))
+        _need(X, "X", (torch.float32,), (T, B, N))
+        if h0 is not None:
+            _need(h0, "h0", (torch.float32,), (B, N))
+        if out is None:
+            out = torch.empty((T, B, N), dtype=torch.float32, device=X.device)
+        _need(out, "out", (torch.float32,), (T, B, N))
+        wt = DATA_FLOAT if W.dtype == torch.float32 else DATA_HALF
+        st = self._lib.prnn_forward_dense(self._h, N, B, T, wt, W.data_ptr(), X.data_ptr(),
+                                          h0.data_ptr() if h0 is not None else None, out.data_ptr(),
+                                          _stream_ptr(stream))
+        _check("prnn_forward_dense", st)
+        return out
+
+    def forward_sparse(self, col: torch.Tensor, val: torch.Tensor, X: torch.Tensor,
+                       h0: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+        """Row-balanced sparse W: col int16 [N, K], val fp16/fp32 [N, K]."""
+        T, B, N = X.shape
+        K = col.shape[1] if col.dim() == 2 else -1
+        _need(col, "col", (torch.int16,), (N, K))
+        _need(val, "val", (torch.float32, torch.float16), (N, K))
+        _need(X, "X", (torch.float32,), (T, B, N))
+        if h0 is not None:
+            _need(h0, "h0", (torch.float32,), (B, N))
+        if out is None:
+            out = torch.empty((T, B, N), dtype=torch.float32, device=X.device)
+        _need(out, "out", (torch.float32,), (T, B, N))
+        vt = DATA_FLOAT if val.dtype == torch.float32 else DATA_HALF
+        st = self._lib.prnn_forward_sparse(self._h, N, B, T, K, col.data_ptr(), vt, val.data_ptr(),
+                                           X.data_ptr(), h0.data_ptr() if h0 is not None else None,
+                                           out.data_ptr(), _stream_ptr(stream))
+        _check("prnn_forward_sparse", st)
+        return out
+
+    def sync_floor(self, N: int, B: int, T: int, out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+        """The exchange/step protocol of a dense call without arithmetic."""
+        if out is None:
+            out = torch.empty((T, B, N), dtype=torch.float32, device=self.device)
+        _need(out, "out", (torch.float32,), (T, B, N))
+        _check("prnn_sync_floor", self._lib.prnn_sync_floor(self._h, N, B, T, out.data_ptr(), _stream_ptr(stream)))
+        return out
+
+
+_default_handles = {}
+
+
+def default_handle() -> Handle:
+    dev = torch.cuda.current_device()
+    h = _default_handles.get(dev)
+    if h is None:
+        h = _default_handles[dev] = Handle()
+    return h
+
+
+def forward_dense(W, X, h0=None, out=None, stream=None):
+    return default_handle().forward_dense(W, X, h0, out, stream)
+
+
+def forward_sparse(col, val, X, h0=None, out=None, stream=None):
+    return default_handle().forward_sparse(col, val, X, h0, out, stream)

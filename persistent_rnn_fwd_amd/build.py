@@ -1,0 +1,62 @@
+"""Builds libprnn.so (the C-ABI library) for gfx950 with hipcc, in-tree.
+
+    python -m persistent_rnn_fwd_amd.build        # or __graft_entry__.build()
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libprnn.so")
+SOURCES = ["dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip", "prnn.cpp"]
+
+# -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.
+FLAGS = [
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build libprnn.so)")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError("build failed: " + " ".join(cmd) + "\n" + err)
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        jobs.append((obj, [cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        for out in ex.map(lambda j: _run(j[1]), jobs):
+            if verbose and out.strip():
+                print(out)
+    tmp = LIB + ".tmp"
+    _run([cc, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *[o for o, _ in jobs]])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,52 @@
+// Kernel arguments and launch tables shared by the host library and the
+// kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace prnn {
+
+// Arguments of every persistent launch (passed by value).
+struct StepArgs {
+  const void* W;        // dense: W [N][N]; sparse: col int16 [N][K]
+  const void* V;        // sparse: val [N][K]; dense: unused
+  const float* X;       // [T][B][N]
+  const float* h0;      // [B][N] or nullptr (zeros)
+  float* H;             // [T][B][N]
+  uint32_t* ring;       // [2][B][Npad] tagged words
+  uint32_t* status;     // device status word (0 = ok)
+  int N, B, T, K, Npad;
+  int lds_stride;       // sparse: words per LDS row of h, multiple of 4, >= N + 1
+  int G;                // workgroups per batch group
+  int base_rows;        // rows per workgroup: base_rows, +1 for g < extra_rows
+  int extra_rows;
+  int chunks;           // 256-column chunks of a row: ceil(N / 256)
+  int spr;              // sparse: 64-pair slots per row, ceil(K / 64)
+  uint32_t step0;       // ring step counter at t = 0
+  uint32_t ring_bytes;
+  uint32_t x_bytes;     // bytes of X (= bytes of H)
+  uint64_t deadline;    // bound on one wait, in ticks of the 100 MHz clock
+  int skip_wg, skip_step;  // test-only publish skip (skip_wg < 0: off)
+};
+
+enum WType { kF32 = 0, kF16 = 1 };
+
+struct KernelEntry {
+  int wtype;   // WType
+  int rmax;    // compiled row capacity per workgroup
+  int cap;     // dense: compiled chunk capacity J; sparse: slots per row SPR
+  const void* fn;
+};
+
+// Instance tables (each terminated by fn == nullptr).
+extern const KernelEntry kDenseF16Kernels[];
+extern const KernelEntry kDenseF32Kernels[];
+extern const KernelEntry kSparseF16Kernels[];
+extern const KernelEntry kSparseF32Kernels[];
+extern const KernelEntry kFloorKernels[];   // wtype unused, rmax = 64 rows max
+
+// Fills n words with v (grid-stride).
+void launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t stream);
+
+}  // namespace prnn

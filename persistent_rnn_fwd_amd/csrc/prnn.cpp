@@ -1,0 +1,371 @@
+// Host side of the C ABI declared in include/prnn.h: handle, argument
+// checks, launch plan, exchange-ring bookkeeping and cooperative launches.
+#include "prnn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "kernels.h"
+
+using prnn::KernelEntry;
+using prnn::StepArgs;
+
+struct prnnContext {
+  int device = 0;
+  int num_cu = 0;
+  size_t lds_per_block = 0;
+  uint32_t* d_status = nullptr;
+  uint32_t* d_ring = nullptr;
+  size_t ring_cap_words = 0;
+  int ring_B = -1;
+  int ring_Npad = -1;
+  bool ring_valid = false;
+  uint64_t step = 0;  // ring step counter of the next timestep
+  int forced_grid = 0;
+  uint32_t watchdog_us = 200000;
+  int skip_wg = -1;
+  int skip_step = -1;
+  prnnPlanInfo_t last_plan{};
+  bool have_plan = false;
+};
+
+namespace {
+
+constexpr uint32_t kRingResetWord = 0xFFFFFFFFu;  // tag 1 = "written at step -2 / -1"
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + bn && pb < pa + an;
+}
+
+struct Plan {
+  int G = 0;           // workgroups per batch group
+  int groups = 0;      // batch groups of up to 4 waves
+  int waves = 0;       // waves per workgroup
+  int base_rows = 0, extra_rows = 0, max_rows = 0;
+  int chunks = 0;
+  const KernelEntry* k = nullptr;
+  int lds_bytes = 0;
+};
+
+// Row split and grid: up to one workgroup per compute unit, each batch group
+// of four batch rows on its own set of workgroups.
+bool split_rows(const prnnContext* h, int N, int B, Plan* p) {
+  p->groups = (B + 3) / 4;
+  p->waves = std::min(B, 4);
+  int G = h->forced_grid > 0 ? h->forced_grid : std::max(1, h->num_cu / p->groups);
+  G = std::min(G, N);
+  if (G < 1) return false;
+  p->G = G;
+  p->base_rows = N / G;
+  p->extra_rows = N % G;
+  p->max_rows = (N + G - 1) / G;
+  p->chunks = (N + 255) / 256;
+  return true;
+}
+
+// Smallest kernel instance that covers (rows, cap) for the weight type.
+const KernelEntry* pick(const KernelEntry* table, int wtype, int rows, int cap, bool match_wtype) {
+  const KernelEntry* best = nullptr;
+  for (const KernelEntry* e = table; e->fn != nullptr; ++e) {
+    if (match_wtype && e->wtype != wtype) continue;
+    if (e->rmax < rows || e->cap < cap) continue;
+    if (best == nullptr || e->rmax < best->rmax || (e->rmax == best->rmax && e->cap < best->cap)) best = e;
+  }
+  return best;
+}
+
+prnnStatus_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return PRNN_STATUS_SUCCESS;
+  if (e == hipErrorCooperativeLaunchTooLarge || e == hipErrorInvalidConfiguration ||
+      e == hipErrorOutOfMemory)
+    return PRNN_STATUS_NOT_SUPPORTED;
+  return PRNN_STATUS_INTERNAL_ERROR;
+}
+
+// Makes the exchange ring fit [2][B][Npad] and, when its layout changed or a
+// run failed, resets it on `stream` and restarts the step counter.
+prnnStatus_t ensure_ring(prnnContext* h, int B, int Npad, hipStream_t stream) {
+  const size_t words = 2ull * (size_t)B * (size_t)Npad;
+  if (words * 4ull > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
+  if (words > h->ring_cap_words) {
+    if (h->d_ring != nullptr) {
+      if (hipDeviceSynchronize() != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+      (void)hipFree(h->d_ring);
+      h->d_ring = nullptr;
+      h->ring_cap_words = 0;
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, words * 4) != hipSuccess) return PRNN_STATUS_ALLOC_FAILED;
+    h->d_ring = static_cast<uint32_t*>(p);
+    h->ring_cap_words = words;
+    h->ring_valid = false;
+  }
+  if (!h->ring_valid || h->ring_B != B || h->ring_Npad != Npad) {
+    prnn::launch_fill(h->d_ring, words, kRingResetWord, stream);
+    if (hipGetLastError() != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+    h->ring_B = B;
+    h->ring_Npad = Npad;
+    h->ring_valid = true;
+    h->step = 0;
+  }
+  return PRNN_STATUS_SUCCESS;
+}
+
+// Shape checks, then (for T > 0) pointer checks.  *empty is set when there is
+// nothing to do (T == 0): the call then succeeds without touching any buffer.
+prnnStatus_t check_common(prnnHandle_t h, int N, int B, int T, const float* X, const float* h0, float* H,
+                          bool* empty) {
+  *empty = false;
+  if (h == nullptr) return PRNN_STATUS_BAD_PARAM;
+  if (N < 1 || B < 1 || B > 8 || T < 0) return PRNN_STATUS_BAD_PARAM;
+  if (T == 0) {
+    *empty = true;
+    return PRNN_STATUS_SUCCESS;
+  }
+  if (X == nullptr || H == nullptr) return PRNN_STATUS_BAD_PARAM;
+  if (!aligned(X, 4) || !aligned(H, 4) || (h0 != nullptr && !aligned(h0, 4))) return PRNN_STATUS_BAD_PARAM;
+  const size_t xb = (size_t)T * B * N * 4;
+  if (overlap(X, xb, H, xb)) return PRNN_STATUS_BAD_PARAM;
+  if (h0 != nullptr && overlap(h0, (size_t)B * N * 4, H, xb)) return PRNN_STATUS_BAD_PARAM;
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream_t stream) {
+  a.step0 = static_cast<uint32_t>(h->step);
+  a.deadline = static_cast<uint64_t>(h->watchdog_us) * 100ull;  // 100 MHz constant clock
+  a.skip_wg = h->skip_wg;
+  a.skip_step = h->skip_step;
+  void* args[] = {&a};
+  hipError_t e = hipLaunchCooperativeKernel(p.k->fn, dim3(p.G * p.groups), dim3(64 * p.waves), args,
+                                            static_cast<unsigned>(p.lds_bytes), stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return hip_status(e);
+  }
+  prnnPlanInfo_t& info = h->last_plan;
+  info.grid = p.G * p.groups;
+  info.waves_per_wg = p.waves;
+  info.rows_per_wg = p.max_rows;
+  info.rmax = p.k->rmax;
+  info.chunks = p.k->cap;
+  info.lds_bytes = p.lds_bytes;
+  info.first_step = h->step;
+  h->have_plan = true;
+  h->step += static_cast<uint64_t>(T);
+  h->skip_wg = -1;
+  h->skip_step = -1;
+  return PRNN_STATUS_SUCCESS;
+}
+
+StepArgs base_args(prnnContext* h, int N, int B, int T, const float* X, const float* h0, float* H,
+                   const Plan& p, int Npad) {
+  StepArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.X = X;
+  a.h0 = h0;
+  a.H = H;
+  a.ring = h->d_ring;
+  a.status = h->d_status;
+  a.N = N;
+  a.B = B;
+  a.T = T;
+  a.Npad = Npad;
+  a.G = p.G;
+  a.base_rows = p.base_rows;
+  a.extra_rows = p.extra_rows;
+  a.chunks = p.chunks;
+  a.ring_bytes = static_cast<uint32_t>(2ull * B * Npad * 4);
+  a.x_bytes = static_cast<uint32_t>((size_t)T * B * N * 4);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* prnn_status_string(prnnStatus_t s) {
+  switch (s) {
+    case PRNN_STATUS_SUCCESS: return "PRNN_STATUS_SUCCESS";
+    case PRNN_STATUS_BAD_PARAM: return "PRNN_STATUS_BAD_PARAM";
+    case PRNN_STATUS_NOT_SUPPORTED: return "PRNN_STATUS_NOT_SUPPORTED";
+    case PRNN_STATUS_ALLOC_FAILED: return "PRNN_STATUS_ALLOC_FAILED";
+    case PRNN_STATUS_EXECUTION_FAILED: return "PRNN_STATUS_EXECUTION_FAILED";
+    case PRNN_STATUS_INTERNAL_ERROR: return "PRNN_STATUS_INTERNAL_ERROR";
+  }
+  return "PRNN_STATUS_UNKNOWN";
+}
+
+prnnStatus_t prnn_create(prnnHandle_t* handle) {
+  if (handle == nullptr) return PRNN_STATUS_BAD_PARAM;
+  *handle = nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+  hipDeviceProp_t props;
+  if (hipGetDeviceProperties(&props, dev) != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+  if (std::strncmp(props.gcnArchName, "gfx950", 6) != 0) return PRNN_STATUS_NOT_SUPPORTED;
+  if (!props.cooperativeLaunch) return PRNN_STATUS_NOT_SUPPORTED;
+  prnnContext* h = new (std::nothrow) prnnContext();
+  if (h == nullptr) return PRNN_STATUS_ALLOC_FAILED;
+  h->device = dev;
+  h->num_cu = props.multiProcessorCount;
+  h->lds_per_block = props.sharedMemPerBlock;
+  void* p = nullptr;
+  if (hipMalloc(&p, 256) != hipSuccess) {
+    delete h;
+    return PRNN_STATUS_ALLOC_FAILED;
+  }
+  h->d_status = static_cast<uint32_t*>(p);
+  prnn::launch_fill(h->d_status, 64, 0u, nullptr);
+  if (hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(p);
+    delete h;
+    return PRNN_STATUS_INTERNAL_ERROR;
+  }
+  *handle = h;
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t prnn_destroy(prnnHandle_t h) {
+  if (h == nullptr) return PRNN_STATUS_SUCCESS;
+  prnnStatus_t st = PRNN_STATUS_SUCCESS;
+  if (hipDeviceSynchronize() != hipSuccess) st = PRNN_STATUS_INTERNAL_ERROR;
+  uint32_t s = 0;
+  if (h->d_status != nullptr && hipMemcpy(&s, h->d_status, 4, hipMemcpyDeviceToHost) == hipSuccess && s != 0)
+    st = PRNN_STATUS_EXECUTION_FAILED;
+  if (h->d_ring != nullptr) (void)hipFree(h->d_ring);
+  if (h->d_status != nullptr) (void)hipFree(h->d_status);
+  delete h;
+  return st;
+}
+
+prnnStatus_t prnn_set_grid(prnnHandle_t h, int workgroups) {
+  if (h == nullptr || workgroups < 0) return PRNN_STATUS_BAD_PARAM;
+  h->forced_grid = workgroups;
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t prnn_set_watchdog_us(prnnHandle_t h, uint32_t us) {
+  if (h == nullptr || us == 0) return PRNN_STATUS_BAD_PARAM;
+  h->watchdog_us = us;
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t prnn_get_last_plan(prnnHandle_t h, prnnPlanInfo_t* info) {
+  if (h == nullptr || info == nullptr || !h->have_plan) return PRNN_STATUS_BAD_PARAM;
+  *info = h->last_plan;
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t prnn_debug_skip_publish(prnnHandle_t h, int wg, int step) {
+  if (h == nullptr) return PRNN_STATUS_BAD_PARAM;
+  h->skip_wg = wg < 0 ? -1 : wg;
+  h->skip_step = wg < 0 ? -1 : step;
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t prnn_synchronize(prnnHandle_t h, hipStream_t stream) {
+  if (h == nullptr) return PRNN_STATUS_BAD_PARAM;
+  if (hipStreamSynchronize(stream) != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+  uint32_t s = 0;
+  if (hipMemcpy(&s, h->d_status, 4, hipMemcpyDeviceToHost) != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+  if (s != 0) {
+    // Report once; clear the status and force a ring reset before the next run.
+    prnn::launch_fill(h->d_status, 64, 0u, stream);
+    if (hipStreamSynchronize(stream) != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+    h->ring_valid = false;
+    return PRNN_STATUS_EXECUTION_FAILED;
+  }
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t prnn_forward_dense(prnnHandle_t h, int N, int B, int T, prnnDataType_t w_type, const void* W,
+                                const float* X, const float* h0, float* H, hipStream_t stream) {
+  bool empty = false;
+  prnnStatus_t st = check_common(h, N, B, T, X, h0, H, &empty);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  if (w_type != PRNN_DATA_FLOAT && w_type != PRNN_DATA_HALF) return PRNN_STATUS_BAD_PARAM;
+  if (empty) return PRNN_STATUS_SUCCESS;
+  if (W == nullptr) return PRNN_STATUS_BAD_PARAM;
+  if (!aligned(W, 4)) return PRNN_STATUS_BAD_PARAM;
+  const size_t wb = (size_t)N * N * (w_type == PRNN_DATA_FLOAT ? 4 : 2);
+  if (overlap(W, wb, H, (size_t)T * B * N * 4)) return PRNN_STATUS_BAD_PARAM;
+  if ((size_t)T * B * N * 4 > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
+  Plan p;
+  if (!split_rows(h, N, B, &p)) return PRNN_STATUS_NOT_SUPPORTED;
+  const int wt = w_type == PRNN_DATA_FLOAT ? prnn::kF32 : prnn::kF16;
+  p.k = pick(wt == prnn::kF32 ? prnn::kDenseF32Kernels : prnn::kDenseF16Kernels, wt, p.max_rows, p.chunks, true);
+  if (p.k == nullptr) return PRNN_STATUS_NOT_SUPPORTED;
+  const int Npad = (N + 3) & ~3;
+  st = ensure_ring(h, B, Npad, stream);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  StepArgs a = base_args(h, N, B, T, X, h0, H, p, Npad);
+  a.W = W;
+  return launch(h, p, a, T, stream);
+}
+
+prnnStatus_t prnn_forward_sparse(prnnHandle_t h, int N, int B, int T, int K, const int16_t* col,
+                                 prnnDataType_t val_type, const void* val, const float* X, const float* h0,
+                                 float* H, hipStream_t stream) {
+  bool empty = false;
+  prnnStatus_t st = check_common(h, N, B, T, X, h0, H, &empty);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  if (val_type != PRNN_DATA_FLOAT && val_type != PRNN_DATA_HALF) return PRNN_STATUS_BAD_PARAM;
+  if (K < 1 || K > N || N > 32767) return PRNN_STATUS_BAD_PARAM;
+  if (empty) return PRNN_STATUS_SUCCESS;
+  if (col == nullptr || val == nullptr) return PRNN_STATUS_BAD_PARAM;
+  if (!aligned(col, 2) || !aligned(val, val_type == PRNN_DATA_FLOAT ? 4 : 2)) return PRNN_STATUS_BAD_PARAM;
+  const size_t hb = (size_t)T * B * N * 4;
+  if (overlap(col, (size_t)N * K * 2, H, hb) ||
+      overlap(val, (size_t)N * K * (val_type == PRNN_DATA_FLOAT ? 4 : 2), H, hb))
+    return PRNN_STATUS_BAD_PARAM;
+  if (hb > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
+  Plan p;
+  if (!split_rows(h, N, B, &p)) return PRNN_STATUS_NOT_SUPPORTED;
+  const int spr = (K + 63) / 64;
+  const int wt = val_type == PRNN_DATA_FLOAT ? prnn::kF32 : prnn::kF16;
+  p.k = pick(wt == prnn::kF32 ? prnn::kSparseF32Kernels : prnn::kSparseF16Kernels, wt, p.max_rows, spr, true);
+  if (p.k == nullptr) return PRNN_STATUS_NOT_SUPPORTED;
+  const int lds_stride = (N + 1 + 3) & ~3;
+  p.lds_bytes = p.waves * lds_stride * 4;
+  if ((size_t)p.lds_bytes > h->lds_per_block) return PRNN_STATUS_NOT_SUPPORTED;
+  if (p.lds_bytes > 65536 &&
+      hipFuncSetAttribute(p.k->fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes) != hipSuccess)
+    return PRNN_STATUS_NOT_SUPPORTED;
+  const int Npad = (N + 3) & ~3;
+  st = ensure_ring(h, B, Npad, stream);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  StepArgs a = base_args(h, N, B, T, X, h0, H, p, Npad);
+  a.W = col;
+  a.V = val;
+  a.K = K;
+  a.spr = spr;
+  a.lds_stride = lds_stride;
+  return launch(h, p, a, T, stream);
+}
+
+prnnStatus_t prnn_sync_floor(prnnHandle_t h, int N, int B, int T, float* H, hipStream_t stream) {
+  if (h == nullptr || N < 1 || B < 1 || B > 8 || T < 0) return PRNN_STATUS_BAD_PARAM;
+  if (T == 0) return PRNN_STATUS_SUCCESS;
+  if (H == nullptr || !aligned(H, 4)) return PRNN_STATUS_BAD_PARAM;
+  if ((size_t)T * B * N * 4 > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
+  Plan p;
+  if (!split_rows(h, N, B, &p)) return PRNN_STATUS_NOT_SUPPORTED;
+  if (p.max_rows > 64) return PRNN_STATUS_NOT_SUPPORTED;
+  p.k = pick(prnn::kFloorKernels, 0, p.max_rows, p.chunks, false);
+  if (p.k == nullptr) return PRNN_STATUS_NOT_SUPPORTED;
+  const int Npad = (N + 3) & ~3;
+  prnnStatus_t st = ensure_ring(h, B, Npad, stream);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  StepArgs a = base_args(h, N, B, T, nullptr, nullptr, H, p, Npad);
+  return launch(h, p, a, T, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+// Row-balanced sparse persistent kernel: every row of W has exactly K
+// nonzeros ("Sparse Persistent RNNs: Squeezing Large Recurrent Networks
+// On-Chip", table "Measured effects reported in the paper": load-balanced
+// pruning row), so every workgroup gets the same work per row and the
+// nonzeros of its rows stay in registers for all T steps.
+//
+// Decomposition: as the dense kernel (workgroup = rows, wave = batch row).
+// Per owned row r, its K (value, column) pairs are spread over the 64 lanes:
+// lane l, slot s holds pair k = 64 s + l (zero value beyond K).  fp16 values
+// and int16 columns are packed into one 32-bit register per pair.
+// Per step each wave copies h_{t-1}[b] from the exchange ring into its own LDS
+// row with 16-byte coherent loads ("wide memory loads" row of the same
+// table) and 16-byte LDS writes, then every pair reads h[col] from LDS.
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace prnn {
+
+
+template <typename VT>
+struct Pair;
+
+template <>
+struct Pair<_Float16> {
+  uint32_t p;  // value bits | column << 16
+  // Padding slots and columns outside [0, n) point at the zero word n.
+  __device__ __forceinline__ void load(const int16_t* col, const void* val, size_t idx, bool live, int n) {
+    uint32_t c = live ? (uint32_t)(uint16_t)col[idx] : (uint32_t)n;
+    uint32_t v = live ? (uint32_t)reinterpret_cast<const uint16_t*>(val)[idx] : 0u;
+    if (c >= (uint32_t)n) { c = (uint32_t)n; v = 0u; }
+    p = v | (c << 16);
+  }
+  __device__ __forceinline__ int column() const { return (int)(p >> 16); }
+  __device__ __forceinline__ void fma(float& acc, float h) const { fma_mix_lo(acc, p, h); }
+};
+
+template <>
+struct Pair<float> {
+  float v;
+  int c;
+  __device__ __forceinline__ void load(const int16_t* col, const void* val, size_t idx, bool live, int n) {
+    c = live ? (int)(uint16_t)col[idx] : n;
+    v = live ? reinterpret_cast<const float*>(val)[idx] : 0.f;
+    if (c >= n) { c = n; v = 0.f; }
+  }
+  __device__ __forceinline__ int column() const { return c; }
+  __device__ __forceinline__ void fma(float& acc, float h) const { acc = fmaf(v, h, acc); }
+};
+
+constexpr int kStageChunks = 8;  // 16-byte loads in flight per lane while staging h
+
+// RMAX rows per workgroup are computed (padding rows carry zero values and
+// are never stored); the cross-lane sum runs over M = RMAX rounded up to a
+// power of two.
+template <typename VT, int RMAX, int SPR>
+__global__ void __launch_bounds__(256) sparse_kernel(StepArgs a) {
+  constexpr int M = pow2_at_least(RMAX);
+  extern __shared__ float lds[];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.x % a.G;
+  const int b = (blockIdx.x / a.G) * 4 + wave;
+  if (b >= a.B) return;
+  if (__builtin_nontemporal_load(a.status) != 0u) return;
+
+  const int N = a.N;
+  const int K = a.K;
+  const int nr = a.base_rows + (g < a.extra_rows ? 1 : 0);
+  const int row0 = g * a.base_rows + min(g, a.extra_rows);
+  const int spr = a.spr;
+  // This wave's copy of h_{t-1}[b].  The row is lds_stride >= N + 1 words
+  // long; word N stays 0 and absorbs the pairs that carry no nonzero.
+  float* hb = lds + wave * a.lds_stride;
+  if (N + lane < a.lds_stride) hb[N + lane] = 0.f;
+
+  // Prologue: the nonzeros of the owned rows into registers, once per call.
+  Pair<VT> pr[RMAX][SPR];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r)
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) {
+      const int k = 64 * s + lane;
+      const bool live = r < nr && s < spr && k < K;
+      pr[r][s].load(reinterpret_cast<const int16_t*>(a.W), a.V, live ? (size_t)(row0 + r) * K + k : 0, live, N);
+    }
+
+  const __amdgpu_buffer_rsrc_t ring = make_rsrc(a.ring, a.ring_bytes);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
+  const int my_row = RowReduce<M>::owner_row(lane);
+  const bool owner = my_row >= 0 && my_row < nr;
+  const bool skipper = (g == a.skip_wg);
+  const int jn = a.chunks;
+
+  for (int t = 0; t < a.T; ++t) {
+    const uint32_t S = a.step0 + (uint32_t)t;
+    const uint32_t xoff = (uint32_t)(((size_t)t * a.B + b) * N + row0 + (owner ? my_row : 0)) * 4u;
+    const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
+
+    // All lanes finished the previous step's LDS reads before hb is rewritten.
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+
+    if (t == 0) {
+      for (int j = 0; j < jn; ++j) {
+        const int c = 256 * j + 4 * lane;
+        if (c < N) {
+          float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (a.h0 != nullptr) {
+            const float* p = a.h0 + (size_t)b * N;
+            f.x = (c + 0 < N) ? p[c + 0] : 0.f;
+            f.y = (c + 1 < N) ? p[c + 1] : 0.f;
+            f.z = (c + 2 < N) ? p[c + 2] : 0.f;
+            f.w = (c + 3 < N) ? p[c + 3] : 0.f;
+          }
+          *reinterpret_cast<float4*>(hb + c) = f;
+        }
+      }
+    } else {
+      const uint32_t prev = S - 1u;
+      const uint32_t tag = tag_bit(prev);
+      for (int j0 = 0; j0 < jn; j0 += kStageChunks) {
+        // chunks j0 .. j0 + 7 of the row, 256 words each
+        const uint32_t row_bytes = (uint32_t)(((prev & 1u) * a.B + b) * a.Npad + 256 * j0) * 4u;
+        const int n = N - 256 * j0;
+        u32x4 v[kStageChunks];
+        if (!gather_row<kStageChunks>(v, ring, row_bytes, lane, jn - j0, n, tag, a.deadline)) {
+          if (lane == 0) atomicOr(a.status, kStatusTimeout);
+          return;
+        }
+#pragma unroll
+        for (int q = 0; q < kStageChunks; ++q) {
+          const int c = 256 * q + 4 * lane;
+          if (q < jn - j0 && c < n) *reinterpret_cast<float4*>(hb + 256 * j0 + c) = chunk_values(v[q], c, n);
+        }
+      }
+    }
+
+    // h_{t-1}[b] is complete in this wave's LDS row before any lane gathers.
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+
+    float acc[M];
+#pragma unroll
+    for (int r = 0; r < M; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) {
+      if (s < spr) {
+#pragma unroll
+        for (int r = 0; r < RMAX; ++r) pr[r][s].fma(acc[r], hb[pr[r][s].column()]);
+      }
+    }
+
+    const float sum = RowReduce<M>::reduce(acc, lane);
+    if (owner && !(skipper && t == a.skip_step)) {
+      const uint32_t hbits = relu_bits(sum + x);
+      const int row = row0 + my_row;
+      a.H[((size_t)t * a.B + b) * N + row] = __uint_as_float(hbits);
+      const uint32_t roff = (uint32_t)(((S & 1u) * a.B + b) * a.Npad + row) * 4u;
+      __builtin_amdgcn_raw_buffer_store_b32(hbits | tag_bit(S), ring, roff, 0, kCoherent);
+    }
+  }
+}
+
+#define PRNN_SPARSE(VT, VTAG, R, S) {VTAG, R, S, reinterpret_cast<const void*>(&sparse_kernel<VT, R, S>)}
+
+}  // namespace prnn

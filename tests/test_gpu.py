@@ -1,0 +1,334 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Every test here runs the persistent kernels on an MI355X and compares with
+``oracle`` element by element on the same seeded inputs:
+  * the five workload families at their full sizes (N up to 5760, T = 256);
+  * ragged and degenerate shapes: N not a multiple of 4, N = 1, several grid
+    sizes (forcing uneven row splits), B = 1..8, T = 1..3 and T = 0, K = 1,
+    K = N, K just above a 64-pair slot;
+  * closed forms that must hold bitwise on the GPU (W = 0, W = I and cyclic
+    shifts with small-integer inputs, positive homogeneity, identical batch
+    rows, chunking in time, run-to-run determinism);
+  * error paths: argument checks, oversize layers, and a forced watchdog expiry
+    (a workgroup skips one publish; every wave still exits normally).
+Tolerance per element: |H - H_ref| <= tol (1 + |H_ref|), tol = 1e-4 for fp32
+weights and 2e-2 for fp16 weights with fp32 accumulation.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from persistent_rnn_fwd_amd import Handle, PrnnError, binding
+from persistent_rnn_fwd_amd.inputs import WORKLOADS, Workload, generate
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def handle(gpu):
+    h = Handle()
+    yield h
+    h.close()
+
+
+def to_dev(d):
+    return {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in d.items()}
+
+
+def run(handle, kind, d, grid=0, h0=True):
+    g = to_dev(d)
+    handle.set_grid(grid)
+    hh = g["h0"] if h0 else None
+    if kind == "dense":
+        H = handle.forward_dense(g["W"], g["X"], hh)
+    else:
+        H = handle.forward_sparse(g["col"], g["val"], g["X"], hh)
+    handle.synchronize()
+    return H.cpu().numpy()
+
+
+def reference(kind, d, h0=True):
+    hh = d["h0"] if h0 else None
+    if kind == "dense":
+        return oracle.forward_dense(d["W"], d["X"], hh)
+    return oracle.forward_sparse(d["col"], d["val"], d["X"], hh)
+
+
+def tol_of(d):
+    w = d["W"] if "W" in d else d["val"]
+    return oracle.TOL_F32 if w.dtype == np.float32 else oracle.TOL_F16
+
+
+def assert_parity(H, ref, tol, what=""):
+    r = oracle.tolerance_ratio(H, ref, tol)
+    assert r <= 1.0, f"{what}: max error ratio {r:.3g} > 1 (tol {tol})"
+    return r
+
+
+# ---------------------------------------------------------------------------
+# the workloads at full size
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed_off", [0, 1000])
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_parity(handle, name, seed_off):
+    w = WORKLOADS[name]
+    d = generate(w, seed=w.seed + seed_off)
+    H = run(handle, w.kind, d)
+    assert np.isfinite(H).all()
+    assert_parity(H, reference(w.kind, d), tol_of(d), name)
+
+
+@pytest.mark.parametrize("name", ["dense_f16_n1792", "sparse10_f16_n1792"])
+def test_workload_parity_random_h0(handle, name):
+    w = WORKLOADS[name].with_(h0="randn", T=64)
+    d = generate(w, seed=w.seed + 2000)
+    assert_parity(run(handle, w.kind, d), reference(w.kind, d), tol_of(d), name)
+
+
+# ---------------------------------------------------------------------------
+# ragged and degenerate shapes, several grids
+# ---------------------------------------------------------------------------
+DENSE_SHAPES = [
+    # N, B, T, wdtype, grid
+    (1, 1, 3, "f32", 0),
+    (3, 2, 5, "f32", 0),
+    (7, 3, 4, "f16", 0),
+    (100, 4, 9, "f32", 0),
+    (100, 4, 9, "f16", 7),
+    (257, 1, 6, "f32", 0),
+    (257, 5, 6, "f16", 13),
+    (256, 8, 8, "f32", 32),
+    (511, 4, 3, "f16", 64),
+    (1000, 2, 5, "f16", 0),
+    (1152, 4, 2, "f16", 192),
+    (1152, 4, 7, "f16", 128),
+    (1792, 4, 5, "f16", 224),
+    (2048, 4, 4, "f16", 0),
+    (1024, 4, 4, "f32", 0),
+]
+
+
+@pytest.mark.parametrize("N,B,T,wdt,grid", DENSE_SHAPES)
+def test_dense_shapes(handle, N, B, T, wdt, grid):
+    w = Workload(f"dense_{N}", "dense", N, B, T, wdt, seed=N * 7 + B, h0="randn")
+    d = generate(w)
+    H = run(handle, "dense", d, grid=grid)
+    assert_parity(H, reference("dense", d), tol_of(d), f"N={N} B={B} T={T} {wdt} grid={grid}")
+
+
+SPARSE_SHAPES = [
+    # N, B, T, K, vdtype, grid
+    (1, 1, 3, 1, "f32", 0),
+    (5, 2, 4, 5, "f16", 0),
+    (64, 4, 6, 64, "f32", 0),
+    (100, 3, 5, 65, "f16", 0),
+    (100, 4, 5, 1, "f16", 9),
+    (257, 4, 7, 26, "f32", 0),
+    (1000, 8, 4, 100, "f16", 0),
+    (1152, 4, 5, 115, "f16", 192),
+    (1792, 4, 5, 179, "f16", 200),
+    (2051, 2, 3, 20, "f16", 0),
+    (5760, 4, 3, 58, "f16", 240),
+    (8000, 2, 3, 80, "f16", 0),
+]
+
+
+@pytest.mark.parametrize("N,B,T,K,vdt,grid", SPARSE_SHAPES)
+def test_sparse_shapes(handle, N, B, T, K, vdt, grid):
+    w = Workload(f"sparse_{N}", "sparse", N, B, T, vdt, K=K, seed=N * 11 + K, h0="randn")
+    d = generate(w)
+    H = run(handle, "sparse", d, grid=grid)
+    assert_parity(H, reference("sparse", d), tol_of(d), f"N={N} B={B} T={T} K={K} {vdt} grid={grid}")
+
+
+def test_zero_timesteps_leave_output_untouched(handle):
+    W = torch.zeros(8, 8, device="cuda")
+    X = torch.zeros(0, 2, 8, device="cuda")
+    out = torch.empty(0, 2, 8, device="cuda")
+    handle.forward_dense(W, X, out=out)
+    handle.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# closed forms, bitwise on the GPU
+# ---------------------------------------------------------------------------
+def test_zero_weights_give_relu_x_bitwise(handle):
+    rng = np.random.default_rng(1)
+    T, B, N = 6, 4, 300
+    X = rng.standard_normal((T, B, N)).astype(np.float32)
+    h0 = np.abs(rng.standard_normal((B, N))).astype(np.float32)
+    for wdt in (np.float32, np.float16):
+        H = run(handle, "dense", {"W": np.zeros((N, N), wdt), "X": X, "h0": h0})
+        np.testing.assert_array_equal(H, np.maximum(X, 0))
+    H = run(handle, "sparse", {"col": np.arange(N, dtype=np.int16).reshape(N, 1),
+                               "val": np.zeros((N, 1), np.float16), "X": X, "h0": h0})
+    np.testing.assert_array_equal(H, np.maximum(X, 0))
+
+
+def test_identity_weights_give_prefix_sums_bitwise(handle):
+    rng = np.random.default_rng(2)
+    T, B, N = 40, 4, 1792
+    X = rng.integers(0, 100, size=(T, B, N)).astype(np.float32)
+    h0 = rng.integers(0, 100, size=(B, N)).astype(np.float32)
+    expect = h0[None].astype(np.float64) + np.cumsum(X.astype(np.float64), axis=0)
+    H = run(handle, "dense", {"W": np.eye(N, dtype=np.float16), "X": X, "h0": h0})
+    np.testing.assert_array_equal(H, expect)
+    H = run(handle, "sparse", {"col": np.arange(N, dtype=np.int16).reshape(N, 1),
+                               "val": np.ones((N, 1), np.float16), "X": X, "h0": h0})
+    np.testing.assert_array_equal(H, expect)
+
+
+def test_cyclic_shift_bitwise(handle):
+    """W[i, (i+1) % N] = 1: catches a transposed W or a misplaced row."""
+    rng = np.random.default_rng(3)
+    T, B, N = 12, 2, 1152
+    X = rng.integers(0, 9, size=(T, B, N)).astype(np.float32)
+    h0 = rng.integers(0, 9, size=(B, N)).astype(np.float32)
+    Wd = np.zeros((N, N), np.float16)
+    Wd[np.arange(N), (np.arange(N) + 1) % N] = 1
+    ref = oracle.forward_dense(Wd, X, h0)
+    np.testing.assert_array_equal(run(handle, "dense", {"W": Wd, "X": X, "h0": h0}), ref)
+    col = ((np.arange(N) + 1) % N).astype(np.int16).reshape(N, 1)
+    np.testing.assert_array_equal(
+        run(handle, "sparse", {"col": col, "val": np.ones((N, 1), np.float32), "X": X, "h0": h0}), ref)
+
+
+def test_sparse_matches_dense_copy(handle):
+    w = WORKLOADS["sparse10_f16_n1152"].with_(T=32, h0="randn")
+    d = generate(w, seed=5)
+    Hs = run(handle, "sparse", d)
+    Wd = oracle.sparse_to_dense(d["col"], d["val"], w.N).astype(np.float16)
+    Hd = run(handle, "dense", {"W": Wd, "X": d["X"], "h0": d["h0"]})
+    assert_parity(Hs, Hd.astype(np.float64), oracle.TOL_F16, "sparse vs dense copy")
+    assert_parity(Hs, reference("sparse", d), oracle.TOL_F16)
+
+
+def test_positive_homogeneity_bitwise(handle):
+    w = WORKLOADS["dense_f16_n1792"].with_(T=20, h0="randn")
+    d = generate(w, seed=9)
+    H1 = run(handle, "dense", d)
+    d2 = dict(d, X=d["X"] * 4, h0=d["h0"] * 4)
+    np.testing.assert_array_equal(run(handle, "dense", d2), H1 * 4)
+
+
+def test_identical_batch_rows_bitwise(handle):
+    w = WORKLOADS["sparse10_f16_n1792"].with_(T=16, h0="randn")
+    d = generate(w, seed=10)
+    X = np.repeat(d["X"][:, :1], 4, axis=1)
+    h0 = np.repeat(d["h0"][:1], 4, axis=0)
+    H = run(handle, "sparse", dict(d, X=X, h0=h0))
+    for b in range(1, 4):
+        np.testing.assert_array_equal(H[:, b], H[:, 0])
+
+
+@pytest.mark.parametrize("name", ["dense_f16_n1792", "sparse10_f16_n1792", "dense_f32_n256"])
+def test_deterministic_and_chunkable(handle, name):
+    w = WORKLOADS[name].with_(T=30, h0="randn")
+    d = generate(w, seed=11)
+    H1 = run(handle, w.kind, d)
+    H2 = run(handle, w.kind, d)
+    np.testing.assert_array_equal(H1, H2)
+    T1 = 13
+    Ha = run(handle, w.kind, dict(d, X=d["X"][:T1]))
+    Hb = run(handle, w.kind, dict(d, X=d["X"][T1:], h0=Ha[-1]))
+    np.testing.assert_array_equal(np.concatenate([Ha, Hb]), H1)
+
+
+def test_nan_propagates_within_its_batch_row(handle):
+    w = WORKLOADS["dense_f32_n256"].with_(T=6)
+    d = generate(w, seed=12)
+    d["X"] = d["X"].copy()
+    d["X"][2, 1, 5] = np.nan
+    H = run(handle, "dense", d)
+    ref = reference("dense", d)
+    np.testing.assert_array_equal(np.isnan(H), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert oracle.tolerance_ratio(H[ok], ref[ok], oracle.TOL_F32) <= 1.0
+
+
+def test_plan_of_headline_layer(handle):
+    d = generate(WORKLOADS["dense_f16_n1792"].with_(T=2))
+    run(handle, "dense", d)
+    p = handle.last_plan()
+    assert p["grid"] == 256 and p["rows_per_wg"] == 7 and p["waves_per_wg"] == 4
+
+
+def test_sync_floor_protocol(handle):
+    T, B, N = 16, 4, 1792
+    handle.set_grid(0)
+    H = handle.sync_floor(N, B, T)
+    handle.synchronize()
+    expect = np.broadcast_to(np.arange(1, T + 1, dtype=np.float32)[:, None, None], (T, B, N))
+    np.testing.assert_array_equal(H.cpu().numpy(), expect)
+
+
+# ---------------------------------------------------------------------------
+# errors
+# ---------------------------------------------------------------------------
+def test_bad_params(handle):
+    lib = binding.load_library()
+    h = handle._h
+    X = torch.zeros(4, 2, 64, device="cuda")
+    H = torch.zeros(4, 2, 64, device="cuda")
+    W = torch.zeros(64, 64, device="cuda")
+    col = torch.zeros(64, 4, dtype=torch.int16, device="cuda")
+    val = torch.zeros(64, 4, dtype=torch.float16, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    bp = binding.BAD_PARAM
+    dense = lambda N, B, T, wt, w, x, h0, out: lib.prnn_forward_dense(h, N, B, T, wt, w, x, h0, out, s)
+    assert dense(64, 2, 4, 0, W.data_ptr(), X.data_ptr(), None, H.data_ptr()) == binding.SUCCESS
+    assert dense(0, 2, 4, 0, W.data_ptr(), X.data_ptr(), None, H.data_ptr()) == bp
+    assert dense(64, 9, 4, 0, W.data_ptr(), X.data_ptr(), None, H.data_ptr()) == bp
+    assert dense(64, 2, -1, 0, W.data_ptr(), X.data_ptr(), None, H.data_ptr()) == bp
+    assert dense(64, 2, 4, 7, W.data_ptr(), X.data_ptr(), None, H.data_ptr()) == bp
+    assert dense(64, 2, 4, 0, None, X.data_ptr(), None, H.data_ptr()) == bp
+    assert dense(64, 2, 4, 0, W.data_ptr(), X.data_ptr() + 2, None, H.data_ptr()) == bp
+    assert dense(64, 2, 4, 0, W.data_ptr(), X.data_ptr(), None, X.data_ptr() + 256) == bp   # X and H overlap
+    sparse = lambda N, K: lib.prnn_forward_sparse(h, N, 2, 4, K, col.data_ptr(), 1, val.data_ptr(),
+                                                  X.data_ptr(), None, H.data_ptr(), s)
+    assert sparse(64, 4) == binding.SUCCESS
+    assert sparse(64, 0) == bp
+    assert sparse(64, 65) == bp
+    assert sparse(40000, 4) == bp
+    handle.synchronize()
+
+
+def test_not_supported(handle):
+    N = 6000
+    W = torch.zeros(N, N, dtype=torch.float16, device="cuda")
+    X = torch.zeros(2, 4, N, device="cuda")
+    with pytest.raises(PrnnError) as e:
+        handle.forward_dense(W, X)
+    assert e.value.status == binding.NOT_SUPPORTED
+    handle.set_grid(1)
+    W = torch.zeros(1792, 1792, dtype=torch.float16, device="cuda")
+    with pytest.raises(PrnnError) as e:
+        handle.forward_dense(W, torch.zeros(2, 4, 1792, device="cuda"))
+    assert e.value.status == binding.NOT_SUPPORTED
+    handle.set_grid(0)
+
+
+@pytest.mark.parametrize("kind", ["dense", "sparse"])
+def test_watchdog_reports_and_recovers(gpu, kind):
+    """A workgroup that never publishes step 5 makes the consumers' bounded
+    waits expire: the run reports EXECUTION_FAILED and the handle recovers."""
+    name = "dense_f16_n1792" if kind == "dense" else "sparse10_f16_n1792"
+    w = WORKLOADS[name].with_(T=12)
+    d = generate(w, seed=13)
+    with Handle() as h:
+        h.set_watchdog_us(2000)
+        h.debug_skip_publish(3, 5)
+        g = to_dev(d)
+        fwd = (lambda: h.forward_dense(g["W"], g["X"], g["h0"])) if kind == "dense" else \
+              (lambda: h.forward_sparse(g["col"], g["val"], g["X"], g["h0"]))
+        fwd()
+        with pytest.raises(PrnnError) as e:
+            h.synchronize()
+        assert e.value.status == binding.EXECUTION_FAILED
+        h.synchronize()           # reported once
+        H = fwd()                 # the ring was reset: a clean run works again
+        h.synchronize()
+        assert_parity(H.cpu().numpy(), reference(kind, d), oracle.TOL_F16)
