@@ -35,7 +35,7 @@ if ROOT not in sys.path:
 
 FP32_VECTOR_PEAK = 157.3e12   # MI355X published fp32 vector peak, FLOP/s
 HBM_PEAK = 8.0e12             # MI355X HBM3E, bytes/s
-COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_dense_f16_n1792.json")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_rnn_fwd_n1792.json")
 KERNEL_SOURCES = ["device_common.h", "kernels.h", "dense_kernel.h", "sparse_kernel.h",
                   "dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip"]
 
@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle leg (profiling runs)")
     ap.add_argument("--no-check", action="store_true", help="skip the oracle check of the GPU output")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the host oracle sample")
+    ap.add_argument("--only-timed", action="store_true",
+                    help="run only warmup + the timed region (every launch is a T=256 call; for profiles)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain copy kernel of this many MiB first (counter calibration)")
     return ap.parse_args()
 
 
@@ -86,6 +90,14 @@ def main():
     host = {w.name: generate(w) for w in (wd, ws, w1)}
     g = {name: {k: torch.from_numpy(v).to(dev) for k, v in d.items()} for name, d in host.items()}
     out = {name: torch.empty((T, B, N), dtype=torch.float32, device=dev) for name in host}
+
+    if args.copy_mib > 0:
+        # a plain elementwise copy of known size: reads and writes copy_mib MiB
+        src = torch.ones(args.copy_mib * 2**18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     h = Handle()
     stream = torch.cuda.current_stream()
@@ -148,8 +160,17 @@ def main():
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in es]))
 
-    # per-step time by the slope between T and T/2, and the sync floor
     detail = {}
+    if args.only_timed:
+        h.close()
+        print(json.dumps({"metric": "RNN timesteps/s & eff. GFLOP/s, N=1792 B=4 dense+10% sparse; % roofline",
+                          "value": round(2 * T / (ms_per_step * 1e-3), 1), "unit": "timesteps/s",
+                          "ms_per_step": round(ms_per_step, 4), "steps": args.steps, "warmup": args.warmup,
+                          "dense_mean_launch_ms": round(dense_ms, 4),
+                          "sparse_mean_launch_ms": round(sparse_ms, 4), "profile_mode": True}), flush=True)
+        return
+
+    # per-step time by the slope between T and T/2, and the sync floor
     floor_out = torch.empty((T, B, N), dtype=torch.float32, device=dev)
     f_full = timed(lambda: h.sync_floor(N, B, T, out=floor_out))
     f_half = timed(lambda: h.sync_floor(N, B, T // 2, out=floor_out[: T // 2]))
@@ -185,8 +206,8 @@ def main():
     if os.path.exists(COUNTER_FILE):
         try:
             c = json.load(open(COUNTER_FILE))
-            if c.get("kernel_source_hash") == kernel_source_hash() and c.get("workload") == dom.name:
-                traffic = c.get("hbm_bytes_per_launch")
+            if c.get("kernel_source_hash") == kernel_source_hash():
+                traffic = c.get("kernels", {}).get(dom.name, {}).get("hbm_bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
     roofline = {

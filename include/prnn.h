@@ -79,6 +79,22 @@ typedef enum {
   PRNN_DATA_HALF = 1   /* fp16 (IEEE binary16); products and sums are taken in fp32 */
 } prnnDataType_t;
 
+/* How workgroups exchange h_{t-1} each step.
+ *  DIRECT: every workgroup reads the whole of h_{t-1} from a device-coherent
+ *          ring that every producer writes.
+ *  RELAY:  each workgroup first copies one slice of h_{t-1} from that ring
+ *          into a copy of the ring kept per XCD (in that XCD's L2), and then
+ *          reads all of h_{t-1} from its XCD's copy: h crosses between XCDs
+ *          once per XCD instead of once per workgroup.  Needs a grid that is
+ *          a multiple of 8 workgroups dealt round-robin over the 8 XCDs.
+ *  AUTO:   RELAY for grids of 192 or more workgroups when possible, else
+ *          DIRECT (the default). */
+typedef enum {
+  PRNN_EXCHANGE_AUTO = 0,
+  PRNN_EXCHANGE_DIRECT = 1,
+  PRNN_EXCHANGE_RELAY = 2
+} prnnExchange_t;
+
 /* Launch plan of the last forward call on a handle (for tests and reports). */
 typedef struct {
   int grid;          /* workgroups launched (one per compute unit at most)   */
@@ -88,6 +104,7 @@ typedef struct {
   int chunks;        /* dense: 256-column chunks per lane; sparse: K slots    */
   int lds_bytes;     /* dynamic LDS per workgroup                             */
   uint64_t first_step; /* ring step counter of the call's first timestep      */
+  int relay_slice;   /* words of h each workgroup relays per step (0: DIRECT) */
 } prnnPlanInfo_t;
 
 /* Creates a handle bound to the current HIP device.
@@ -140,6 +157,11 @@ prnnStatus_t prnn_synchronize(prnnHandle_t handle, hipStream_t stream);
 /* Number of workgroups for later calls (0 = automatic: up to one per compute
  * unit).  BAD_PARAM if negative. */
 prnnStatus_t prnn_set_grid(prnnHandle_t handle, int workgroups);
+
+/* Exchange mode for later calls (default AUTO).  A forced RELAY that the
+ * plan cannot use makes forward calls return NOT_SUPPORTED.  BAD_PARAM for an
+ * unknown mode. */
+prnnStatus_t prnn_set_exchange(prnnHandle_t handle, prnnExchange_t mode);
 
 /* Upper bound, in microseconds, on one wait for h_{t-1} (default 200000).
  * A wait that exceeds it stops the run and reports EXECUTION_FAILED. */

@@ -25,6 +25,7 @@ STATUS_NAMES = {
 }
 SUCCESS, BAD_PARAM, NOT_SUPPORTED, ALLOC_FAILED, EXECUTION_FAILED, INTERNAL_ERROR = range(6)
 DATA_FLOAT, DATA_HALF = 0, 1
+EXCHANGE_AUTO, EXCHANGE_DIRECT, EXCHANGE_RELAY = 0, 1, 2
 
 # Every function include/prnn.h declares, with its ctypes signature.
 _H = ctypes.c_void_p
@@ -39,6 +40,7 @@ SIGNATURES = {
     "prnn_synchronize": (_I, [_H, _P]),
     "prnn_set_grid": (_I, [_H, _I]),
     "prnn_set_watchdog_us": (_I, [_H, ctypes.c_uint32]),
+    "prnn_set_exchange": (_I, [_H, _I]),
     "prnn_get_last_plan": (_I, [_H, _P]),
     "prnn_debug_skip_publish": (_I, [_H, _I, _I]),
     "prnn_status_string": (ctypes.c_char_p, [_I]),
@@ -54,6 +56,7 @@ class PlanInfo(ctypes.Structure):
         ("chunks", ctypes.c_int),
         ("lds_bytes", ctypes.c_int),
         ("first_step", ctypes.c_uint64),
+        ("relay_slice", ctypes.c_int),
     ]
 
     def as_dict(self):
@@ -143,6 +146,10 @@ class Handle:
     # -- options ------------------------------------------------------------
     def set_grid(self, workgroups: int):
         _check("prnn_set_grid", self._lib.prnn_set_grid(self._h, int(workgroups)))
+
+    def set_exchange(self, mode: int):
+        """EXCHANGE_AUTO, EXCHANGE_DIRECT or EXCHANGE_RELAY for later calls."""
+        _check("prnn_set_exchange", self._lib.prnn_set_exchange(self._h, int(mode)))
 
     def set_watchdog_us(self, us: int):
         _check("prnn_set_watchdog_us", self._lib.prnn_set_watchdog_us(self._h, int(us)))

@@ -27,6 +27,12 @@ __global__ void fill_kernel(uint32_t* p, size_t n, uint32_t v) {
     p[i] = v;
 }
 
+__global__ void placement_kernel(uint32_t* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = __builtin_amdgcn_s_getreg((20) | (31 << 11)) & 0xFu;  // HW_REG_XCC_ID
+}
+
+const void* kPlacementKernel = reinterpret_cast<const void*>(&placement_kernel);
+
 void launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t stream) {
   if (n == 0) return;
   size_t blocks = (n + 255) / 256;

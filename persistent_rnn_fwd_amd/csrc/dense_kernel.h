@@ -120,7 +120,7 @@ __global__ void __launch_bounds__(256) dense_kernel(StepArgs a) {
     for (int j = 0; j < J; ++j)
       w[r][j].load(a.W, (size_t)(row0 + r) * N, 256 * j + 4 * lane, N, r < nr && j < jn, vec);
 
-  const __amdgpu_buffer_rsrc_t ring = make_rsrc(a.ring, a.ring_bytes);
+  const Exchange ex = make_exchange(a.ring, a.relay, a.ring_bytes, a.relay_slice, g, N);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
   const int my_row = RowReduce<M>::owner_row(lane);
   const bool owner = my_row >= 0 && my_row < nr;
@@ -147,17 +147,49 @@ __global__ void __launch_bounds__(256) dense_kernel(StepArgs a) {
     } else {
       const uint32_t prev = S - 1u;
       const uint32_t row_bytes = (uint32_t)(((prev & 1u) * a.B + b) * a.Npad) * 4u;
+      const uint32_t tag = tag_bit(prev);
       u32x4 v[J];
-      if (!gather_row<J>(v, ring, row_bytes, lane, jn, N, tag_bit(prev), a.deadline)) {
-        if (lane == 0) atomicOr(a.status, kStatusTimeout);
-        return;
+      bool done = false;
+      if (a.relay_slice > 0) {
+        // Relay: every slice is in this XCD's copy once its last word is.
+        // Then read the row once and multiply each 1 KiB chunk as it lands.
+        if (!relay_slice(ex, row_bytes, lane, N, tag, a.deadline) ||
+            !wait_slices(ex, a.relay_slice, row_bytes, lane, N, tag, a.deadline)) {
+          if (lane == 0) atomicOr(a.status, kStatusTimeout);
+          return;
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          if (j < jn) v[j] = __builtin_amdgcn_raw_buffer_load_b128(ex.local, row_bytes + 4u * (256 * j + 4 * lane), 0, kCoherent);
+        done = true;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          if (j < jn) {
+            done = done && !wave_any(!chunk_ready(v[j], tag, 256 * j + 4 * lane, N));
+            if (done) {
+              const float4 h = chunk_values(v[j], 256 * j + 4 * lane, N);
+#pragma unroll
+              for (int r = 0; r < RMAX; ++r) w[r][j].fma4(acc[r], h);
+            }
+          }
+        }
       }
+      if (!done) {
+        // Direct exchange, or a relayed row that was not complete yet: wait
+        // for the whole row, then (re)compute the sums from scratch.
+        if (!gather_row<J>(v, ex.local, row_bytes, lane, jn, N, tag, a.deadline)) {
+          if (lane == 0) atomicOr(a.status, kStatusTimeout);
+          return;
+        }
 #pragma unroll
-      for (int j = 0; j < J; ++j) {
-        if (j < jn) {
-          const float4 h = chunk_values(v[j], 256 * j + 4 * lane, N);
+        for (int r = 0; r < M; ++r) acc[r] = 0.f;
 #pragma unroll
-          for (int r = 0; r < RMAX; ++r) w[r][j].fma4(acc[r], h);
+        for (int j = 0; j < J; ++j) {
+          if (j < jn) {
+            const float4 h = chunk_values(v[j], 256 * j + 4 * lane, N);
+#pragma unroll
+            for (int r = 0; r < RMAX; ++r) w[r][j].fma4(acc[r], h);
+          }
         }
       }
     }
@@ -168,7 +200,17 @@ __global__ void __launch_bounds__(256) dense_kernel(StepArgs a) {
       const int row = row0 + my_row;
       a.H[((size_t)t * a.B + b) * N + row] = __uint_as_float(hb);
       const uint32_t roff = (uint32_t)(((S & 1u) * a.B + b) * a.Npad + row) * 4u;
-      __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), ring, roff, 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), ex.ring, roff, 0, kCoherent);
+    }
+  }
+
+  // Relay mode: hand the last step to this XCD's copy as well, so that the
+  // copies hold steps S-1 and S-2 when the next call starts at step S (its
+  // first step reads h0, not the ring).
+  if (a.T > 0) {
+    const uint32_t last = a.step0 + (uint32_t)(a.T - 1);
+    if (!relay_slice(ex, (uint32_t)(((last & 1u) * a.B + b) * a.Npad) * 4u, lane, N, tag_bit(last), a.deadline)) {
+      if (lane == 0) atomicOr(a.status, kStatusTimeout);
     }
   }
 }
@@ -187,7 +229,7 @@ __global__ void __launch_bounds__(256) floor_kernel(StepArgs a) {
   const int nr = a.base_rows + (g < a.extra_rows ? 1 : 0);
   const int row0 = g * a.base_rows + min(g, a.extra_rows);
   const int jn = a.chunks;
-  const __amdgpu_buffer_rsrc_t ring = make_rsrc(a.ring, a.ring_bytes);
+  const Exchange ex = make_exchange(a.ring, a.relay, a.ring_bytes, a.relay_slice, g, N);
   for (int t = 0; t < a.T; ++t) {
     const uint32_t S = a.step0 + (uint32_t)t;
     float acc = 0.f;
@@ -195,7 +237,9 @@ __global__ void __launch_bounds__(256) floor_kernel(StepArgs a) {
       const uint32_t prev = S - 1u;
       const uint32_t row_bytes = (uint32_t)(((prev & 1u) * a.B + b) * a.Npad) * 4u;
       u32x4 v[J];
-      if (!gather_row<J>(v, ring, row_bytes, lane, jn, N, tag_bit(prev), a.deadline)) {
+      if (!relay_slice(ex, row_bytes, lane, N, tag_bit(prev), a.deadline) ||
+          (a.relay_slice > 0 && !wait_slices(ex, a.relay_slice, row_bytes, lane, N, tag_bit(prev), a.deadline)) ||
+          !gather_row<J>(v, ex.local, row_bytes, lane, jn, N, tag_bit(prev), a.deadline)) {
         if (lane == 0) atomicOr(a.status, kStatusTimeout);
         return;
       }
@@ -213,7 +257,17 @@ __global__ void __launch_bounds__(256) floor_kernel(StepArgs a) {
       const int row = row0 + lane;
       a.H[((size_t)t * a.B + b) * N + row] = __uint_as_float(hb);
       const uint32_t roff = (uint32_t)(((S & 1u) * a.B + b) * a.Npad + row) * 4u;
-      __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), ring, roff, 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), ex.ring, roff, 0, kCoherent);
+    }
+  }
+
+  // Relay mode: hand the last step to this XCD's copy as well, so that the
+  // copies hold steps S-1 and S-2 when the next call starts at step S (its
+  // first step reads h0, not the ring).
+  if (a.T > 0) {
+    const uint32_t last = a.step0 + (uint32_t)(a.T - 1);
+    if (!relay_slice(ex, (uint32_t)(((last & 1u) * a.B + b) * a.Npad) * 4u, lane, N, tag_bit(last), a.deadline)) {
+      if (lane == 0) atomicOr(a.status, kStatusTimeout);
     }
   }
 }

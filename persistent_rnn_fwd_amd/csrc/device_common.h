@@ -120,6 +120,78 @@ __device__ __forceinline__ bool gather_row(u32x4 (&v)[J], __amdgpu_buffer_rsrc_t
 }
 
 // ---------------------------------------------------------------------------
+// Two-level exchange ("relay").  Polling the device-coherent ring from every
+// compute unit makes each of the 8 XCDs fetch the same row 32 times per step
+// across the fabric.  In relay mode each workgroup first copies one slice of
+// the row (relay_slice words) from the ring into its own XCD's copy of the
+// ring with ordinary stores, which stay in that XCD's L2; the workgroups of
+// the XCD then read the whole row from there.  The row crosses the fabric
+// once per XCD, and the 32 readers of an XCD hit its L2.  The copy keeps the
+// words' step tags, so readers validate it exactly like the ring itself.
+// Which XCD a workgroup runs on is read from the hardware (XCC_ID); the
+// slices of one XCD are covered because workgroups are dealt to XCDs
+// round-robin (checked once when a handle is created).
+// ---------------------------------------------------------------------------
+struct Exchange {
+  __amdgpu_buffer_rsrc_t ring;   // written by every producer, device-coherent
+  __amdgpu_buffer_rsrc_t local;  // where this wave reads h_{t-1}: the ring, or this XCD's copy
+  int slice_lo;                  // first word of the slice this workgroup relays
+  int slice_len;                 // words it relays (0: direct mode)
+};
+
+__device__ __forceinline__ Exchange make_exchange(uint32_t* ring, uint32_t* relay, uint32_t ring_bytes,
+                                                  int relay_slice, int g, int n) {
+  Exchange e;
+  e.ring = make_rsrc(ring, ring_bytes);
+  e.local = e.ring;
+  e.slice_lo = 0;
+  e.slice_len = 0;
+  if (relay_slice > 0) {
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (31 << 11)) & 7u;  // HW_REG_XCC_ID
+    e.local = make_rsrc(relay + (size_t)xcc * (ring_bytes / 4u), ring_bytes);
+    e.slice_lo = (g >> 3) * relay_slice;
+    e.slice_len = max(0, min(relay_slice, n - e.slice_lo));
+  }
+  return e;
+}
+
+// Relay mode, after relay_slice: wait until every slice of the row has
+// reached this XCD's copy, watching only the last word of each slice (one
+// 4-byte load per slice instead of re-reading the whole row while it is
+// incomplete).  The row is then read once; its step tags still decide.
+__device__ __forceinline__ bool wait_slices(const Exchange& e, int relay_slice, uint32_t row_bytes, int lane, int n,
+                                            uint32_t tag, uint64_t deadline) {
+  const int slices = (n + relay_slice - 1) / relay_slice;  // <= 64
+  const bool mine = lane < slices;
+  const int word = min((lane + 1) * relay_slice, n) - 1;
+  uint32_t f = mine ? __builtin_amdgcn_raw_buffer_load_b32(e.local, row_bytes + 4u * word, 0, kCoherent) : tag;
+  const uint64_t t0 = now_ticks();
+  while (wave_any(((f ^ tag) & 0x80000000u) != 0u)) {
+    if (now_ticks() - t0 > deadline) return false;
+    if ((f ^ tag) & 0x80000000u) f = __builtin_amdgcn_raw_buffer_load_b32(e.local, row_bytes + 4u * word, 0, kCoherent);
+  }
+  return true;
+}
+
+// Relay mode: wait until this workgroup's slice of the ring row carries `tag`
+// and copy it into the XCD-local copy.  Direct mode: nothing to do.
+__device__ __forceinline__ bool relay_slice(const Exchange& e, uint32_t row_bytes, int lane, int n, uint32_t tag,
+                                            uint64_t deadline) {
+  if (e.slice_len == 0) return true;
+  const int c = e.slice_lo + 4 * lane;
+  const bool mine = 4 * lane < e.slice_len;
+  u32x4 q = {0u, 0u, 0u, 0u};
+  if (mine) q = __builtin_amdgcn_raw_buffer_load_b128(e.ring, row_bytes + 4u * c, 0, kCoherent);
+  const uint64_t t0 = now_ticks();
+  while (wave_any(mine && !chunk_ready(q, tag, c, n))) {
+    if (now_ticks() - t0 > deadline) return false;
+    if (mine && !chunk_ready(q, tag, c, n)) q = __builtin_amdgcn_raw_buffer_load_b128(e.ring, row_bytes + 4u * c, 0, kCoherent);
+  }
+  if (mine) __builtin_amdgcn_raw_buffer_store_b128(q, e.local, row_bytes + 4u * c, 0, kPlain);
+  return true;
+}
+
+// ---------------------------------------------------------------------------
 // Cross-lane sum of M per-lane partial values (M = 1, 2, 4, ... 32), one per
 // row.  After the call, lane `owner_row(lane)` (if owner(lane)) holds the sum
 // over all 64 lanes of value owner_row.  The order of additions is fixed, so

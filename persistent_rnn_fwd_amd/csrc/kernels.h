@@ -15,6 +15,7 @@ struct StepArgs {
   const float* h0;      // [B][N] or nullptr (zeros)
   float* H;             // [T][B][N]
   uint32_t* ring;       // [2][B][Npad] tagged words
+  uint32_t* relay;      // [8][2][B][Npad]: one copy of the ring per XCD (relay mode)
   uint32_t* status;     // device status word (0 = ok)
   int N, B, T, K, Npad;
   int lds_stride;       // sparse: words per LDS row of h, multiple of 4, >= N + 1
@@ -23,6 +24,7 @@ struct StepArgs {
   int extra_rows;
   int chunks;           // 256-column chunks of a row: ceil(N / 256)
   int spr;              // sparse: 64-pair slots per row, ceil(K / 64)
+  int relay_slice;      // words of a row each workgroup relays (0 = direct mode)
   uint32_t step0;       // ring step counter at t = 0
   uint32_t ring_bytes;
   uint32_t x_bytes;     // bytes of X (= bytes of H)
@@ -48,5 +50,8 @@ extern const KernelEntry kFloorKernels[];   // wtype unused, rmax = 64 rows max
 
 // Fills n words with v (grid-stride).
 void launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t stream);
+
+// One workgroup per entry: out[i] = the XCD (XCC_ID) that ran workgroup i.
+extern const void* kPlacementKernel;
 
 }  // namespace prnn

@@ -19,12 +19,19 @@ struct prnnContext {
   int num_cu = 0;
   size_t lds_per_block = 0;
   uint32_t* d_status = nullptr;
-  uint32_t* d_ring = nullptr;
-  size_t ring_cap_words = 0;
+  uint32_t* d_ring = nullptr;   // ring words, then 8 XCD-local copies of the ring
+  size_t ring_cap_words = 0;    // words of one ring the allocation holds
+  bool placement_round_robin = false;  // workgroup i runs on XCD (i + c) % 8
+  int exchange = PRNN_EXCHANGE_AUTO;
   int ring_B = -1;
   int ring_Npad = -1;
   bool ring_valid = false;
   uint64_t step = 0;  // ring step counter of the next timestep
+  // The XCD-local copies of the ring hold steps S-1 and S-2 (as a relay-mode
+  // call needs when it starts at step S) only for S == relay_next_step: after
+  // a reset (S = 0) and after a relay-mode call.  A relay-mode call starting
+  // anywhere else resets the ring first.
+  uint64_t relay_next_step = 0;
   int forced_grid = 0;
   uint32_t watchdog_us = 200000;
   int skip_wg = -1;
@@ -46,6 +53,7 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 }
 
 struct Plan {
+  int relay_slice = 0; // words of a row each workgroup relays (0 = direct exchange)
   int G = 0;           // workgroups per batch group
   int groups = 0;      // batch groups of up to 4 waves
   int waves = 0;       // waves per workgroup
@@ -71,6 +79,21 @@ bool split_rows(const prnnContext* h, int N, int B, Plan* p) {
   return true;
 }
 
+// Relay exchange when the grid spreads evenly over the 8 XCDs and is large
+// enough that per-XCD fan-in pays (measured: direct polling from 256
+// workgroups costs about 4 us per step, the relay about 2.9 us; from 128 or
+// fewer workgroups direct polling is as fast).
+void choose_exchange(const prnnContext* h, int Npad, Plan* p) {
+  p->relay_slice = 0;
+  if (h->exchange == PRNN_EXCHANGE_DIRECT || !h->placement_round_robin) return;
+  if (p->G % 8 != 0) return;
+  const int per_xcd = p->G / 8;
+  const int slice = (((Npad / 4) + per_xcd - 1) / per_xcd) * 4;  // words, multiple of 4
+  if (slice > 256) return;                                         // one 16-byte load per lane
+  if (h->exchange == PRNN_EXCHANGE_AUTO && p->G < 192) return;
+  p->relay_slice = slice;
+}
+
 // Smallest kernel instance that covers (rows, cap) for the weight type.
 const KernelEntry* pick(const KernelEntry* table, int wtype, int rows, int cap, bool match_wtype) {
   const KernelEntry* best = nullptr;
@@ -94,7 +117,7 @@ prnnStatus_t hip_status(hipError_t e) {
 // run failed, resets it on `stream` and restarts the step counter.
 prnnStatus_t ensure_ring(prnnContext* h, int B, int Npad, hipStream_t stream) {
   const size_t words = 2ull * (size_t)B * (size_t)Npad;
-  if (words * 4ull > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
+  if (words * 4ull * 9ull > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
   if (words > h->ring_cap_words) {
     if (h->d_ring != nullptr) {
       if (hipDeviceSynchronize() != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
@@ -103,18 +126,20 @@ prnnStatus_t ensure_ring(prnnContext* h, int B, int Npad, hipStream_t stream) {
       h->ring_cap_words = 0;
     }
     void* p = nullptr;
-    if (hipMalloc(&p, words * 4) != hipSuccess) return PRNN_STATUS_ALLOC_FAILED;
+    if (hipMalloc(&p, words * 4 * 9) != hipSuccess) return PRNN_STATUS_ALLOC_FAILED;
     h->d_ring = static_cast<uint32_t*>(p);
     h->ring_cap_words = words;
     h->ring_valid = false;
   }
   if (!h->ring_valid || h->ring_B != B || h->ring_Npad != Npad) {
-    prnn::launch_fill(h->d_ring, words, kRingResetWord, stream);
+    // the ring and its 8 XCD-local copies, contiguous for this layout
+    prnn::launch_fill(h->d_ring, words * 9, kRingResetWord, stream);
     if (hipGetLastError() != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
     h->ring_B = B;
     h->ring_Npad = Npad;
     h->ring_valid = true;
     h->step = 0;
+    h->relay_next_step = 0;
   }
   return PRNN_STATUS_SUCCESS;
 }
@@ -158,8 +183,10 @@ prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream
   info.chunks = p.k->cap;
   info.lds_bytes = p.lds_bytes;
   info.first_step = h->step;
+  info.relay_slice = p.relay_slice;
   h->have_plan = true;
   h->step += static_cast<uint64_t>(T);
+  if (p.relay_slice > 0) h->relay_next_step = h->step;
   h->skip_wg = -1;
   h->skip_step = -1;
   return PRNN_STATUS_SUCCESS;
@@ -173,6 +200,8 @@ StepArgs base_args(prnnContext* h, int N, int B, int T, const float* X, const fl
   a.h0 = h0;
   a.H = H;
   a.ring = h->d_ring;
+  a.relay = h->d_ring + 2ull * B * Npad;
+  a.relay_slice = p.relay_slice;
   a.status = h->d_status;
   a.N = N;
   a.B = B;
@@ -185,6 +214,28 @@ StepArgs base_args(prnnContext* h, int N, int B, int T, const float* X, const fl
   a.ring_bytes = static_cast<uint32_t>(2ull * B * Npad * 4);
   a.x_bytes = static_cast<uint32_t>((size_t)T * B * N * 4);
   return a;
+}
+
+// The relay exchange relies on workgroup i of a cooperative launch running on
+// XCD (i + c) % 8 for one constant c.  Checked once per handle.
+bool check_placement(int num_cu) {
+  const int grid = num_cu;
+  void* p = nullptr;
+  if (grid < 8 || hipMalloc(&p, grid * 4) != hipSuccess) return false;
+  uint32_t* d = static_cast<uint32_t*>(p);
+  void* args[] = {&d};
+  bool ok = hipLaunchCooperativeKernel(prnn::kPlacementKernel, dim3(grid), dim3(64), args, 0, nullptr) == hipSuccess &&
+            hipDeviceSynchronize() == hipSuccess;
+  uint32_t* host = new (std::nothrow) uint32_t[grid];
+  ok = ok && host != nullptr && hipMemcpy(host, d, grid * 4, hipMemcpyDeviceToHost) == hipSuccess;
+  if (ok) {
+    const uint32_t c = (host[0] + 8u) % 8u;
+    for (int i = 0; i < grid && ok; ++i) ok = host[i] < 8u && (host[i] + 8u - (uint32_t)i % 8u) % 8u == c;
+  }
+  delete[] host;
+  (void)hipGetLastError();
+  (void)hipFree(p);
+  return ok;
 }
 
 }  // namespace
@@ -229,6 +280,7 @@ prnnStatus_t prnn_create(prnnHandle_t* handle) {
     delete h;
     return PRNN_STATUS_INTERNAL_ERROR;
   }
+  h->placement_round_robin = check_placement(h->num_cu);
   *handle = h;
   return PRNN_STATUS_SUCCESS;
 }
@@ -249,6 +301,14 @@ prnnStatus_t prnn_destroy(prnnHandle_t h) {
 prnnStatus_t prnn_set_grid(prnnHandle_t h, int workgroups) {
   if (h == nullptr || workgroups < 0) return PRNN_STATUS_BAD_PARAM;
   h->forced_grid = workgroups;
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t prnn_set_exchange(prnnHandle_t h, prnnExchange_t mode) {
+  if (h == nullptr) return PRNN_STATUS_BAD_PARAM;
+  if (mode != PRNN_EXCHANGE_AUTO && mode != PRNN_EXCHANGE_DIRECT && mode != PRNN_EXCHANGE_RELAY)
+    return PRNN_STATUS_BAD_PARAM;
+  h->exchange = mode;
   return PRNN_STATUS_SUCCESS;
 }
 
@@ -300,6 +360,9 @@ prnnStatus_t prnn_forward_dense(prnnHandle_t h, int N, int B, int T, prnnDataTyp
   if ((size_t)T * B * N * 4 > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
   Plan p;
   if (!split_rows(h, N, B, &p)) return PRNN_STATUS_NOT_SUPPORTED;
+  choose_exchange(h, (N + 3) & ~3, &p);
+  if (h->exchange == PRNN_EXCHANGE_RELAY && p.relay_slice == 0) return PRNN_STATUS_NOT_SUPPORTED;
+  if (p.relay_slice > 0 && h->step != h->relay_next_step) h->ring_valid = false;
   const int wt = w_type == PRNN_DATA_FLOAT ? prnn::kF32 : prnn::kF16;
   p.k = pick(wt == prnn::kF32 ? prnn::kDenseF32Kernels : prnn::kDenseF16Kernels, wt, p.max_rows, p.chunks, true);
   if (p.k == nullptr) return PRNN_STATUS_NOT_SUPPORTED;
@@ -329,6 +392,9 @@ prnnStatus_t prnn_forward_sparse(prnnHandle_t h, int N, int B, int T, int K, con
   if (hb > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
   Plan p;
   if (!split_rows(h, N, B, &p)) return PRNN_STATUS_NOT_SUPPORTED;
+  choose_exchange(h, (N + 3) & ~3, &p);
+  if (h->exchange == PRNN_EXCHANGE_RELAY && p.relay_slice == 0) return PRNN_STATUS_NOT_SUPPORTED;
+  if (p.relay_slice > 0 && h->step != h->relay_next_step) h->ring_valid = false;
   const int spr = (K + 63) / 64;
   const int wt = val_type == PRNN_DATA_FLOAT ? prnn::kF32 : prnn::kF16;
   p.k = pick(wt == prnn::kF32 ? prnn::kSparseF32Kernels : prnn::kSparseF16Kernels, wt, p.max_rows, spr, true);
@@ -358,6 +424,9 @@ prnnStatus_t prnn_sync_floor(prnnHandle_t h, int N, int B, int T, float* H, hipS
   if ((size_t)T * B * N * 4 > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
   Plan p;
   if (!split_rows(h, N, B, &p)) return PRNN_STATUS_NOT_SUPPORTED;
+  choose_exchange(h, (N + 3) & ~3, &p);
+  if (h->exchange == PRNN_EXCHANGE_RELAY && p.relay_slice == 0) return PRNN_STATUS_NOT_SUPPORTED;
+  if (p.relay_slice > 0 && h->step != h->relay_next_step) h->ring_valid = false;
   if (p.max_rows > 64) return PRNN_STATUS_NOT_SUPPORTED;
   p.k = pick(prnn::kFloorKernels, 0, p.max_rows, p.chunks, false);
   if (p.k == nullptr) return PRNN_STATUS_NOT_SUPPORTED;

@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(256) sparse_kernel(StepArgs a) {
       pr[r][s].load(reinterpret_cast<const int16_t*>(a.W), a.V, live ? (size_t)(row0 + r) * K + k : 0, live, N);
     }
 
-  const __amdgpu_buffer_rsrc_t ring = make_rsrc(a.ring, a.ring_bytes);
+  const Exchange ex = make_exchange(a.ring, a.relay, a.ring_bytes, a.relay_slice, g, N);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
   const int my_row = RowReduce<M>::owner_row(lane);
   const bool owner = my_row >= 0 && my_row < nr;
@@ -120,12 +120,18 @@ __global__ void __launch_bounds__(256) sparse_kernel(StepArgs a) {
     } else {
       const uint32_t prev = S - 1u;
       const uint32_t tag = tag_bit(prev);
+      const uint32_t row0_bytes = (uint32_t)(((prev & 1u) * a.B + b) * a.Npad) * 4u;
+      if (!relay_slice(ex, row0_bytes, lane, N, tag, a.deadline) ||
+          (a.relay_slice > 0 && !wait_slices(ex, a.relay_slice, row0_bytes, lane, N, tag, a.deadline))) {
+        if (lane == 0) atomicOr(a.status, kStatusTimeout);
+        return;
+      }
       for (int j0 = 0; j0 < jn; j0 += kStageChunks) {
         // chunks j0 .. j0 + 7 of the row, 256 words each
         const uint32_t row_bytes = (uint32_t)(((prev & 1u) * a.B + b) * a.Npad + 256 * j0) * 4u;
         const int n = N - 256 * j0;
         u32x4 v[kStageChunks];
-        if (!gather_row<kStageChunks>(v, ring, row_bytes, lane, jn - j0, n, tag, a.deadline)) {
+        if (!gather_row<kStageChunks>(v, ex.local, row_bytes, lane, jn - j0, n, tag, a.deadline)) {
           if (lane == 0) atomicOr(a.status, kStatusTimeout);
           return;
         }
@@ -158,7 +164,17 @@ __global__ void __launch_bounds__(256) sparse_kernel(StepArgs a) {
       const int row = row0 + my_row;
       a.H[((size_t)t * a.B + b) * N + row] = __uint_as_float(hbits);
       const uint32_t roff = (uint32_t)(((S & 1u) * a.B + b) * a.Npad + row) * 4u;
-      __builtin_amdgcn_raw_buffer_store_b32(hbits | tag_bit(S), ring, roff, 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b32(hbits | tag_bit(S), ex.ring, roff, 0, kCoherent);
+    }
+  }
+
+  // Relay mode: hand the last step to this XCD's copy as well, so that the
+  // copies hold steps S-1 and S-2 when the next call starts at step S (its
+  // first step reads h0, not the ring).
+  if (a.T > 0) {
+    const uint32_t last = a.step0 + (uint32_t)(a.T - 1);
+    if (!relay_slice(ex, (uint32_t)(((last & 1u) * a.B + b) * a.Npad) * 4u, lane, N, tag_bit(last), a.deadline)) {
+      if (lane == 0) atomicOr(a.status, kStatusTimeout);
     }
   }
 }

@@ -254,6 +254,49 @@ def test_plan_of_headline_layer(handle):
     run(handle, "dense", d)
     p = handle.last_plan()
     assert p["grid"] == 256 and p["rows_per_wg"] == 7 and p["waves_per_wg"] == 4
+    assert p["relay_slice"] == 1792 // 32   # auto picks the per-XCD relay at 256 workgroups
+
+
+@pytest.mark.parametrize("name,grid", [("dense_f16_n1792", 0), ("sparse10_f16_n1792", 0),
+                                       ("sparse1_f16_n5760", 0), ("dense_f16_n1152", 128),
+                                       ("sparse10_f16_n1152", 192)])
+def test_relay_and_direct_exchange_agree_bitwise(handle, name, grid):
+    """Both exchanges deliver the same h_{t-1}, so the results are identical."""
+    w = WORKLOADS[name].with_(T=40, h0="randn")
+    d = generate(w, seed=21)
+    out = {}
+    for mode in (binding.EXCHANGE_DIRECT, binding.EXCHANGE_RELAY):
+        handle.set_exchange(mode)
+        out[mode] = run(handle, w.kind, d, grid=grid)
+        assert (handle.last_plan()["relay_slice"] > 0) == (mode == binding.EXCHANGE_RELAY)
+    handle.set_exchange(binding.EXCHANGE_AUTO)
+    np.testing.assert_array_equal(out[binding.EXCHANGE_DIRECT], out[binding.EXCHANGE_RELAY])
+    assert_parity(out[binding.EXCHANGE_RELAY], reference(w.kind, d), tol_of(d), name)
+
+
+def test_mixed_exchange_calls_on_one_handle(handle):
+    """Calls that alternate exchanges, grids and lengths on one handle keep the
+    ring and its XCD-local copies consistent (each call matches the oracle)."""
+    w = WORKLOADS["dense_f32_n256"]
+    seq = [(binding.EXCHANGE_RELAY, 0, 32), (binding.EXCHANGE_RELAY, 0, 1), (binding.EXCHANGE_RELAY, 0, 7),
+           (binding.EXCHANGE_DIRECT, 0, 5), (binding.EXCHANGE_RELAY, 0, 6), (binding.EXCHANGE_RELAY, 128, 9),
+           (binding.EXCHANGE_DIRECT, 64, 3), (binding.EXCHANGE_AUTO, 0, 32)]
+    for i, (mode, grid, T) in enumerate(seq):
+        d = generate(w.with_(T=T, h0="randn"), seed=300 + i)
+        handle.set_exchange(mode)
+        H = run(handle, "dense", d, grid=grid)
+        assert_parity(H, reference("dense", d), oracle.TOL_F32, f"call {i} mode {mode} grid {grid} T {T}")
+    handle.set_exchange(binding.EXCHANGE_AUTO)
+
+
+def test_forced_relay_needs_an_even_grid(handle):
+    d = generate(WORKLOADS["dense_f16_n1152"].with_(T=2))
+    handle.set_exchange(binding.EXCHANGE_RELAY)
+    with pytest.raises(PrnnError) as e:
+        run(handle, "dense", d, grid=100)
+    assert e.value.status == binding.NOT_SUPPORTED
+    handle.set_exchange(binding.EXCHANGE_AUTO)
+    handle.set_grid(0)
 
 
 def test_sync_floor_protocol(handle):
