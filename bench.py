@@ -36,8 +36,8 @@ if ROOT not in sys.path:
 FP32_VECTOR_PEAK = 157.3e12   # MI355X published fp32 vector peak, FLOP/s
 HBM_PEAK = 8.0e12             # MI355X HBM3E, bytes/s
 COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_rnn_fwd_n1792.json")
-KERNEL_SOURCES = ["device_common.h", "kernels.h", "dense_kernel.h", "sparse_kernel.h",
-                  "dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip"]
+KERNEL_SOURCES = ["device_common.h", "kernels.h", "dense_kernel.h", "sparse_kernel.h", "team_kernel.h",
+                  "dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip", "team_f16.hip", "team_f32.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -212,7 +212,7 @@ def main():
             traffic = None
     roofline = {
         "bound": "alu",
-        "kernel": f"dense_kernel ({dom.name})" if dom is wd else f"sparse_kernel ({dom.name})",
+        "kernel": f"dense persistent kernel ({dom.name})" if dom is wd else f"sparse persistent kernel ({dom.name})",
         "achieved": round(achieved / 1e12, 4),
         "peak": FP32_VECTOR_PEAK / 1e12,
         "unit": "TFLOP/s",

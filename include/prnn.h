@@ -95,16 +95,35 @@ typedef enum {
   PRNN_EXCHANGE_RELAY = 2
 } prnnExchange_t;
 
+/* How the recurrence is laid out on the GPU.
+ *  SPREAD: up to one workgroup per compute unit over the whole GPU; each
+ *          workgroup owns some rows of W and runs one wave per batch row
+ *          (all batch rows share the workgroup's resident rows).  h_{t-1}
+ *          crosses between XCDs every step (see prnnExchange_t).
+ *  TEAM:   each of the 8 XCDs runs one batch row's whole recurrence with up
+ *          to 32 workgroups of 8 waves; a wave owns a few rows of W.  h_{t-1}
+ *          is exchanged inside the XCD's L2 only.  With B < 8 the remaining
+ *          XCDs recompute batch rows redundantly (they do not write H), so
+ *          every XCD's exchange memory is updated at every step.  Holds W
+ *          once per XCD: for dense fp16 W up to N = 2048.
+ *  AUTO:   TEAM when an instance fits, else SPREAD (the default). */
+typedef enum {
+  PRNN_LAYOUT_AUTO = 0,
+  PRNN_LAYOUT_SPREAD = 1,
+  PRNN_LAYOUT_TEAM = 2
+} prnnLayout_t;
+
 /* Launch plan of the last forward call on a handle (for tests and reports). */
 typedef struct {
-  int grid;          /* workgroups launched (one per compute unit at most)   */
-  int waves_per_wg;  /* = B: one wavefront of 64 lanes per batch row          */
-  int rows_per_wg;   /* largest number of W rows owned by one workgroup       */
-  int rmax;          /* compiled row capacity of the kernel instance          */
-  int chunks;        /* dense: 256-column chunks per lane; sparse: K slots    */
-  int lds_bytes;     /* dynamic LDS per workgroup                             */
-  uint64_t first_step; /* ring step counter of the call's first timestep      */
-  int relay_slice;   /* words of h each workgroup relays per step (0: DIRECT) */
+  int layout;        /* PRNN_LAYOUT_SPREAD or PRNN_LAYOUT_TEAM                 */
+  int grid;          /* workgroups launched                                    */
+  int waves_per_wg;  /* SPREAD: min(B, 4), one wave per batch row; TEAM: 8     */
+  int rows_per_wave; /* largest number of W rows one wave keeps resident       */
+  int rmax;          /* compiled row capacity of the kernel instance           */
+  int chunks;        /* dense: 256-column chunk capacity; sparse: 64-pair slots */
+  int lds_bytes;     /* dynamic LDS per workgroup                              */
+  int relay_slice;   /* SPREAD: words of h each workgroup relays (0: DIRECT)   */
+  uint64_t first_step; /* ring step counter of the call's first timestep       */
 } prnnPlanInfo_t;
 
 /* Creates a handle bound to the current HIP device.
@@ -155,13 +174,19 @@ prnnStatus_t prnn_synchronize(prnnHandle_t handle, hipStream_t stream);
  * reset before the next forward call.) */
 
 /* Number of workgroups for later calls (0 = automatic: up to one per compute
- * unit).  BAD_PARAM if negative. */
+ * unit).  In the TEAM layout it must be a multiple of 8 (8 XCDs x workgroups
+ * per XCD).  BAD_PARAM if negative. */
 prnnStatus_t prnn_set_grid(prnnHandle_t handle, int workgroups);
 
 /* Exchange mode for later calls (default AUTO).  A forced RELAY that the
  * plan cannot use makes forward calls return NOT_SUPPORTED.  BAD_PARAM for an
  * unknown mode. */
 prnnStatus_t prnn_set_exchange(prnnHandle_t handle, prnnExchange_t mode);
+
+/* Layout for later calls (default AUTO).  A forced layout that the shape
+ * cannot use makes forward calls return NOT_SUPPORTED.  BAD_PARAM for an
+ * unknown layout.  The exchange mode applies to the SPREAD layout only. */
+prnnStatus_t prnn_set_layout(prnnHandle_t handle, prnnLayout_t layout);
 
 /* Upper bound, in microseconds, on one wait for h_{t-1} (default 200000).
  * A wait that exceeds it stops the run and reports EXECUTION_FAILED. */
@@ -170,8 +195,9 @@ prnnStatus_t prnn_set_watchdog_us(prnnHandle_t handle, uint32_t microseconds);
 /* Copies the plan of the last successful forward call into *info. */
 prnnStatus_t prnn_get_last_plan(prnnHandle_t handle, prnnPlanInfo_t* info);
 
-/* TEST ONLY: in the next forward call, workgroup `wg` does not publish its
- * rows at timestep `step`, so the consumers' bounded waits expire and the
+/* TEST ONLY: in the next forward call, workgroup `wg` (TEAM layout: the
+ * workgroups of rank `wg` within every XCD) does not publish its rows at
+ * timestep `step`, so the consumers' bounded waits expire and the
  * run reports EXECUTION_FAILED (every kernel still exits normally).
  * wg < 0 disables. */
 prnnStatus_t prnn_debug_skip_publish(prnnHandle_t handle, int wg, int step);

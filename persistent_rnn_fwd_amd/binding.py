@@ -26,6 +26,7 @@ STATUS_NAMES = {
 SUCCESS, BAD_PARAM, NOT_SUPPORTED, ALLOC_FAILED, EXECUTION_FAILED, INTERNAL_ERROR = range(6)
 DATA_FLOAT, DATA_HALF = 0, 1
 EXCHANGE_AUTO, EXCHANGE_DIRECT, EXCHANGE_RELAY = 0, 1, 2
+LAYOUT_AUTO, LAYOUT_SPREAD, LAYOUT_TEAM = 0, 1, 2
 
 # Every function include/prnn.h declares, with its ctypes signature.
 _H = ctypes.c_void_p
@@ -41,6 +42,7 @@ SIGNATURES = {
     "prnn_set_grid": (_I, [_H, _I]),
     "prnn_set_watchdog_us": (_I, [_H, ctypes.c_uint32]),
     "prnn_set_exchange": (_I, [_H, _I]),
+    "prnn_set_layout": (_I, [_H, _I]),
     "prnn_get_last_plan": (_I, [_H, _P]),
     "prnn_debug_skip_publish": (_I, [_H, _I, _I]),
     "prnn_status_string": (ctypes.c_char_p, [_I]),
@@ -49,14 +51,15 @@ SIGNATURES = {
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [
+        ("layout", ctypes.c_int),
         ("grid", ctypes.c_int),
         ("waves_per_wg", ctypes.c_int),
-        ("rows_per_wg", ctypes.c_int),
+        ("rows_per_wave", ctypes.c_int),
         ("rmax", ctypes.c_int),
         ("chunks", ctypes.c_int),
         ("lds_bytes", ctypes.c_int),
-        ("first_step", ctypes.c_uint64),
         ("relay_slice", ctypes.c_int),
+        ("first_step", ctypes.c_uint64),
     ]
 
     def as_dict(self):
@@ -150,6 +153,10 @@ class Handle:
     def set_exchange(self, mode: int):
         """EXCHANGE_AUTO, EXCHANGE_DIRECT or EXCHANGE_RELAY for later calls."""
         _check("prnn_set_exchange", self._lib.prnn_set_exchange(self._h, int(mode)))
+
+    def set_layout(self, layout: int):
+        """LAYOUT_AUTO, LAYOUT_SPREAD or LAYOUT_TEAM for later calls."""
+        _check("prnn_set_layout", self._lib.prnn_set_layout(self._h, int(layout)))
 
     def set_watchdog_us(self, us: int):
         _check("prnn_set_watchdog_us", self._lib.prnn_set_watchdog_us(self._h, int(us)))

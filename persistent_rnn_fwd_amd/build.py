@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libprnn.so")
-SOURCES = ["dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip", "prnn.cpp"]
+SOURCES = ["dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip", "team_f16.hip", "team_f32.hip",
+           "prnn.cpp"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.
 FLAGS = [

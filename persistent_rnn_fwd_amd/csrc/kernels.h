@@ -14,13 +14,13 @@ struct StepArgs {
   const float* X;       // [T][B][N]
   const float* h0;      // [B][N] or nullptr (zeros)
   float* H;             // [T][B][N]
-  uint32_t* ring;       // [2][B][Npad] tagged words
+  uint32_t* ring;       // spread layout: [2][B][Npad] tagged words; team layout: [8][2][Npad]
   uint32_t* relay;      // [8][2][B][Npad]: one copy of the ring per XCD (relay mode)
   uint32_t* status;     // device status word (0 = ok)
   int N, B, T, K, Npad;
   int lds_stride;       // sparse: words per LDS row of h, multiple of 4, >= N + 1
   int G;                // workgroups per batch group
-  int base_rows;        // rows per workgroup: base_rows, +1 for g < extra_rows
+  int base_rows;        // rows per workgroup (team layout: per wave): base_rows, +1 for the first extra_rows
   int extra_rows;
   int chunks;           // 256-column chunks of a row: ceil(N / 256)
   int spr;              // sparse: 64-pair slots per row, ceil(K / 64)
@@ -47,11 +47,20 @@ extern const KernelEntry kDenseF32Kernels[];
 extern const KernelEntry kSparseF16Kernels[];
 extern const KernelEntry kSparseF32Kernels[];
 extern const KernelEntry kFloorKernels[];   // wtype unused, rmax = 64 rows max
+extern const KernelEntry kDenseTeamF16Kernels[];   // team layout: rmax = rows per wave
+extern const KernelEntry kDenseTeamF32Kernels[];
+extern const KernelEntry kSparseTeamF16Kernels[];
+extern const KernelEntry kSparseTeamF32Kernels[];
 
 // Fills n words with v (grid-stride).
 void launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t stream);
 
 // One workgroup per entry: out[i] = the XCD (XCC_ID) that ran workgroup i.
 extern const void* kPlacementKernel;
+
+// Team layout: the protocol-only kernel, and the ring reset in which every XCD
+// fills its own [2][npad] region of the [8][2][npad] ring.
+extern const void* kFloorTeamKernel;
+void launch_team_fill(uint32_t* ring, int npad, uint32_t v, hipStream_t stream);
 
 }  // namespace prnn

@@ -1,5 +1,6 @@
 // Host side of the C ABI declared in include/prnn.h: handle, argument
-// checks, launch plan, exchange-ring bookkeeping and cooperative launches.
+// checks, launch plan (layout, grid, kernel instance, exchange), exchange-ring
+// bookkeeping and cooperative launches.
 #include "prnn.h"
 
 #include <hip/hip_runtime.h>
@@ -19,18 +20,21 @@ struct prnnContext {
   int num_cu = 0;
   size_t lds_per_block = 0;
   uint32_t* d_status = nullptr;
-  uint32_t* d_ring = nullptr;   // ring words, then 8 XCD-local copies of the ring
-  size_t ring_cap_words = 0;    // words of one ring the allocation holds
+  // Exchange memory.  Spread layout: [2][B][Npad] ring followed by 8
+  // XCD-local copies of it.  Team layout: [8][2][Npad], one region per XCD.
+  uint32_t* d_ring = nullptr;
+  size_t ring_cap_words = 0;
   bool placement_round_robin = false;  // workgroup i runs on XCD (i + c) % 8
   int exchange = PRNN_EXCHANGE_AUTO;
+  int layout = PRNN_LAYOUT_AUTO;
+  int ring_layout = -1;  // layout the ring was last reset for
   int ring_B = -1;
   int ring_Npad = -1;
   bool ring_valid = false;
   uint64_t step = 0;  // ring step counter of the next timestep
-  // The XCD-local copies of the ring hold steps S-1 and S-2 (as a relay-mode
-  // call needs when it starts at step S) only for S == relay_next_step: after
-  // a reset (S = 0) and after a relay-mode call.  A relay-mode call starting
-  // anywhere else resets the ring first.
+  // Spread layout, relay exchange: the XCD-local copies hold steps S-1 and S-2
+  // (as a relay call starting at step S needs) only for S == relay_next_step:
+  // after a reset and after a relay call.  Elsewhere the ring is reset first.
   uint64_t relay_next_step = 0;
   int forced_grid = 0;
   uint32_t watchdog_us = 200000;
@@ -43,6 +47,9 @@ struct prnnContext {
 namespace {
 
 constexpr uint32_t kRingResetWord = 0xFFFFFFFFu;  // tag 1 = "written at step -2 / -1"
+constexpr int kTeamMaxWgPerXcd = 32;
+
+enum Kind { kDense, kSparse, kFloor };
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -53,56 +60,122 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 }
 
 struct Plan {
-  int relay_slice = 0; // words of a row each workgroup relays (0 = direct exchange)
-  int G = 0;           // workgroups per batch group
-  int groups = 0;      // batch groups of up to 4 waves
-  int waves = 0;       // waves per workgroup
-  int base_rows = 0, extra_rows = 0, max_rows = 0;
-  int chunks = 0;
+  int layout = PRNN_LAYOUT_SPREAD;
+  int grid = 0, block = 0;
+  int G = 0;                 // spread: workgroups per batch group; team: workgroups per XCD
+  int waves = 0;             // waves per workgroup
+  int base_rows = 0, extra_rows = 0, max_rows = 0;  // spread: per workgroup; team: per wave
+  int chunks = 0;            // 256-column chunks of a row
+  int spr = 0;               // sparse: 64-pair slots per row
+  int relay_slice = 0;       // spread: words each workgroup relays (0 = direct)
+  int lds_stride = 0;        // sparse: words per LDS row
   const KernelEntry* k = nullptr;
   int lds_bytes = 0;
 };
 
-// Row split and grid: up to one workgroup per compute unit, each batch group
-// of four batch rows on its own set of workgroups.
-bool split_rows(const prnnContext* h, int N, int B, Plan* p) {
-  p->groups = (B + 3) / 4;
-  p->waves = std::min(B, 4);
-  int G = h->forced_grid > 0 ? h->forced_grid : std::max(1, h->num_cu / p->groups);
-  G = std::min(G, N);
-  if (G < 1) return false;
-  p->G = G;
-  p->base_rows = N / G;
-  p->extra_rows = N % G;
-  p->max_rows = (N + G - 1) / G;
-  p->chunks = (N + 255) / 256;
-  return true;
-}
-
-// Relay exchange when the grid spreads evenly over the 8 XCDs and is large
-// enough that per-XCD fan-in pays (measured: direct polling from 256
-// workgroups costs about 4 us per step, the relay about 2.9 us; from 128 or
-// fewer workgroups direct polling is as fast).
-void choose_exchange(const prnnContext* h, int Npad, Plan* p) {
-  p->relay_slice = 0;
-  if (h->exchange == PRNN_EXCHANGE_DIRECT || !h->placement_round_robin) return;
-  if (p->G % 8 != 0) return;
-  const int per_xcd = p->G / 8;
-  const int slice = (((Npad / 4) + per_xcd - 1) / per_xcd) * 4;  // words, multiple of 4
-  if (slice > 256) return;                                         // one 16-byte load per lane
-  if (h->exchange == PRNN_EXCHANGE_AUTO && p->G < 192) return;
-  p->relay_slice = slice;
-}
-
-// Smallest kernel instance that covers (rows, cap) for the weight type.
-const KernelEntry* pick(const KernelEntry* table, int wtype, int rows, int cap, bool match_wtype) {
+// Smallest kernel instance that covers (rows, cap).
+const KernelEntry* pick(const KernelEntry* table, int rows, int cap) {
   const KernelEntry* best = nullptr;
   for (const KernelEntry* e = table; e->fn != nullptr; ++e) {
-    if (match_wtype && e->wtype != wtype) continue;
     if (e->rmax < rows || e->cap < cap) continue;
     if (best == nullptr || e->rmax < best->rmax || (e->rmax == best->rmax && e->cap < best->cap)) best = e;
   }
   return best;
+}
+
+int sparse_lds_stride(int N) { return (N + 1 + 3) & ~3; }
+
+// Spread layout: up to one workgroup per compute unit, each batch group of
+// four batch rows on its own set of workgroups, one wave per batch row.
+bool plan_spread(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Plan* p) {
+  p->layout = PRNN_LAYOUT_SPREAD;
+  const int groups = (B + 3) / 4;
+  p->waves = std::min(B, 4);
+  int G = h->forced_grid > 0 ? h->forced_grid : std::max(1, h->num_cu / groups);
+  G = std::min(G, N);
+  if (G < 1) return false;
+  p->G = G;
+  p->grid = G * groups;
+  p->block = 64 * p->waves;
+  p->base_rows = N / G;
+  p->extra_rows = N % G;
+  p->max_rows = (N + G - 1) / G;
+  p->chunks = (N + 255) / 256;
+  if (kind == kDense) {
+    p->k = pick(wt == prnn::kF32 ? prnn::kDenseF32Kernels : prnn::kDenseF16Kernels, p->max_rows, p->chunks);
+  } else if (kind == kSparse) {
+    p->spr = (K + 63) / 64;
+    p->k = pick(wt == prnn::kF32 ? prnn::kSparseF32Kernels : prnn::kSparseF16Kernels, p->max_rows, p->spr);
+    p->lds_stride = sparse_lds_stride(N);
+    p->lds_bytes = p->waves * p->lds_stride * 4;
+  } else {
+    if (p->max_rows > 64) return false;
+    p->k = pick(prnn::kFloorKernels, p->max_rows, p->chunks);
+  }
+  if (p->k == nullptr || (size_t)p->lds_bytes > h->lds_per_block) return false;
+  // Relay exchange when the grid spreads evenly over the 8 XCDs and is large
+  // enough that per-XCD fan-in pays (measured: direct polling from 256
+  // workgroups about 4 us per step; relay with slice sentinels about 3.2 us).
+  p->relay_slice = 0;
+  if (h->exchange != PRNN_EXCHANGE_DIRECT && h->placement_round_robin && G % 8 == 0) {
+    const int Npad = (N + 3) & ~3;
+    const int per_xcd = G / 8;
+    const int slice = (((Npad / 4) + per_xcd - 1) / per_xcd) * 4;  // words, multiple of 4
+    if (slice <= 256 && (h->exchange == PRNN_EXCHANGE_RELAY || G >= 192)) p->relay_slice = slice;
+  }
+  return !(h->exchange == PRNN_EXCHANGE_RELAY && p->relay_slice == 0);
+}
+
+// Team layout: each XCD runs one batch row with P workgroups of 8 waves.
+bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Plan* p) {
+  p->layout = PRNN_LAYOUT_TEAM;
+  if (!h->placement_round_robin || B > 8 || h->num_cu < 8) return false;
+  int P;
+  if (h->forced_grid > 0) {
+    if (h->forced_grid % 8 != 0) return false;
+    P = h->forced_grid / 8;
+  } else {
+    P = std::min(kTeamMaxWgPerXcd, h->num_cu / 8);
+  }
+  P = std::min(P, (N + 7) / 8);  // at least one row per workgroup on average
+  if (P < 1 || 8 * P > h->num_cu) return false;
+  const int Q = P * 8;  // waves per team
+  p->G = P;
+  p->grid = 8 * P;
+  p->waves = 8;
+  p->block = 512;
+  p->base_rows = N / Q;
+  p->extra_rows = N % Q;
+  p->max_rows = (N + Q - 1) / Q;
+  p->chunks = (N + 255) / 256;
+  const int Npad = (N + 3) & ~3;
+  if (kind == kDense) {
+    p->k = pick(wt == prnn::kF32 ? prnn::kDenseTeamF32Kernels : prnn::kDenseTeamF16Kernels, p->max_rows, p->chunks);
+    p->lds_bytes = 2 * Npad * 4;
+  } else if (kind == kSparse) {
+    p->spr = (K + 63) / 64;
+    p->k = pick(wt == prnn::kF32 ? prnn::kSparseTeamF32Kernels : prnn::kSparseTeamF16Kernels, p->max_rows, p->spr);
+    p->lds_stride = sparse_lds_stride(N);
+    p->lds_bytes = 2 * p->lds_stride * 4;
+  } else {
+    static const KernelEntry floor_team = {0, 64, 1 << 30, nullptr};
+    if (p->max_rows > 64) return false;
+    p->k = &floor_team;  // the caller substitutes the team floor kernel
+    p->lds_bytes = 2 * Npad * 4;
+  }
+  return p->k != nullptr && (size_t)p->lds_bytes <= h->lds_per_block;
+}
+
+bool plan(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Plan* p) {
+  if (h->layout != PRNN_LAYOUT_SPREAD) {
+    Plan t;
+    if (plan_team(h, kind, N, B, K, wt, &t)) {
+      *p = t;
+      return true;
+    }
+    if (h->layout == PRNN_LAYOUT_TEAM) return false;
+  }
+  return plan_spread(h, kind, N, B, K, wt, p);
 }
 
 prnnStatus_t hip_status(hipError_t e) {
@@ -113,11 +186,13 @@ prnnStatus_t hip_status(hipError_t e) {
   return PRNN_STATUS_INTERNAL_ERROR;
 }
 
-// Makes the exchange ring fit [2][B][Npad] and, when its layout changed or a
-// run failed, resets it on `stream` and restarts the step counter.
-prnnStatus_t ensure_ring(prnnContext* h, int B, int Npad, hipStream_t stream) {
-  const size_t words = 2ull * (size_t)B * (size_t)Npad;
-  if (words * 4ull * 9ull > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
+// Makes the exchange memory fit the plan's layout and, when the layout or its
+// shape changed, a run failed, or relay continuity was broken, resets it on
+// `stream` and restarts the step counter.
+prnnStatus_t ensure_ring(prnnContext* h, const Plan& p, int B, int Npad, hipStream_t stream) {
+  const bool team = p.layout == PRNN_LAYOUT_TEAM;
+  const size_t words = team ? 16ull * (size_t)Npad : 18ull * (size_t)B * (size_t)Npad;
+  if (words * 4ull > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
   if (words > h->ring_cap_words) {
     if (h->d_ring != nullptr) {
       if (hipDeviceSynchronize() != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
@@ -125,16 +200,21 @@ prnnStatus_t ensure_ring(prnnContext* h, int B, int Npad, hipStream_t stream) {
       h->d_ring = nullptr;
       h->ring_cap_words = 0;
     }
-    void* p = nullptr;
-    if (hipMalloc(&p, words * 4 * 9) != hipSuccess) return PRNN_STATUS_ALLOC_FAILED;
-    h->d_ring = static_cast<uint32_t*>(p);
+    void* mem = nullptr;
+    if (hipMalloc(&mem, words * 4) != hipSuccess) return PRNN_STATUS_ALLOC_FAILED;
+    h->d_ring = static_cast<uint32_t*>(mem);
     h->ring_cap_words = words;
     h->ring_valid = false;
   }
-  if (!h->ring_valid || h->ring_B != B || h->ring_Npad != Npad) {
-    // the ring and its 8 XCD-local copies, contiguous for this layout
-    prnn::launch_fill(h->d_ring, words * 9, kRingResetWord, stream);
+  if (!team && p.relay_slice > 0 && h->step != h->relay_next_step) h->ring_valid = false;
+  const bool same = h->ring_layout == p.layout && h->ring_Npad == Npad && (team || h->ring_B == B);
+  if (!h->ring_valid || !same) {
+    if (team)
+      prnn::launch_team_fill(h->d_ring, Npad, kRingResetWord, stream);
+    else
+      prnn::launch_fill(h->d_ring, words, kRingResetWord, stream);
     if (hipGetLastError() != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+    h->ring_layout = p.layout;
     h->ring_B = B;
     h->ring_Npad = Npad;
     h->ring_valid = true;
@@ -163,35 +243,6 @@ prnnStatus_t check_common(prnnHandle_t h, int N, int B, int T, const float* X, c
   return PRNN_STATUS_SUCCESS;
 }
 
-prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream_t stream) {
-  a.step0 = static_cast<uint32_t>(h->step);
-  a.deadline = static_cast<uint64_t>(h->watchdog_us) * 100ull;  // 100 MHz constant clock
-  a.skip_wg = h->skip_wg;
-  a.skip_step = h->skip_step;
-  void* args[] = {&a};
-  hipError_t e = hipLaunchCooperativeKernel(p.k->fn, dim3(p.G * p.groups), dim3(64 * p.waves), args,
-                                            static_cast<unsigned>(p.lds_bytes), stream);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return hip_status(e);
-  }
-  prnnPlanInfo_t& info = h->last_plan;
-  info.grid = p.G * p.groups;
-  info.waves_per_wg = p.waves;
-  info.rows_per_wg = p.max_rows;
-  info.rmax = p.k->rmax;
-  info.chunks = p.k->cap;
-  info.lds_bytes = p.lds_bytes;
-  info.first_step = h->step;
-  info.relay_slice = p.relay_slice;
-  h->have_plan = true;
-  h->step += static_cast<uint64_t>(T);
-  if (p.relay_slice > 0) h->relay_next_step = h->step;
-  h->skip_wg = -1;
-  h->skip_step = -1;
-  return PRNN_STATUS_SUCCESS;
-}
-
 StepArgs base_args(prnnContext* h, int N, int B, int T, const float* X, const float* h0, float* H,
                    const Plan& p, int Npad) {
   StepArgs a;
@@ -211,13 +262,48 @@ StepArgs base_args(prnnContext* h, int N, int B, int T, const float* X, const fl
   a.base_rows = p.base_rows;
   a.extra_rows = p.extra_rows;
   a.chunks = p.chunks;
+  a.spr = p.spr;
+  a.lds_stride = p.lds_stride;
   a.ring_bytes = static_cast<uint32_t>(2ull * B * Npad * 4);
   a.x_bytes = static_cast<uint32_t>((size_t)T * B * N * 4);
   return a;
 }
 
-// The relay exchange relies on workgroup i of a cooperative launch running on
-// XCD (i + c) % 8 for one constant c.  Checked once per handle.
+prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream_t stream) {
+  if (p.lds_bytes > 65536 &&
+      hipFuncSetAttribute(p.k->fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes) != hipSuccess)
+    return PRNN_STATUS_NOT_SUPPORTED;
+  a.step0 = static_cast<uint32_t>(h->step);
+  a.deadline = static_cast<uint64_t>(h->watchdog_us) * 100ull;  // 100 MHz constant clock
+  a.skip_wg = h->skip_wg;
+  a.skip_step = h->skip_step;
+  void* args[] = {&a};
+  hipError_t e = hipLaunchCooperativeKernel(p.k->fn, dim3(p.grid), dim3(p.block), args,
+                                            static_cast<unsigned>(p.lds_bytes), stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return hip_status(e);
+  }
+  prnnPlanInfo_t& info = h->last_plan;
+  info.layout = p.layout;
+  info.grid = p.grid;
+  info.waves_per_wg = p.waves;
+  info.rows_per_wave = p.max_rows;
+  info.rmax = p.k->rmax;
+  info.chunks = p.k->cap;
+  info.lds_bytes = p.lds_bytes;
+  info.relay_slice = p.relay_slice;
+  info.first_step = h->step;
+  h->have_plan = true;
+  h->step += static_cast<uint64_t>(T);
+  if (p.layout == PRNN_LAYOUT_SPREAD && p.relay_slice > 0) h->relay_next_step = h->step;
+  h->skip_wg = -1;
+  h->skip_step = -1;
+  return PRNN_STATUS_SUCCESS;
+}
+
+// The relay and team exchanges rely on workgroup i of a cooperative launch
+// running on XCD (i + c) % 8 for one constant c.  Checked once per handle.
 bool check_placement(int num_cu) {
   const int grid = num_cu;
   void* p = nullptr;
@@ -229,7 +315,7 @@ bool check_placement(int num_cu) {
   uint32_t* host = new (std::nothrow) uint32_t[grid];
   ok = ok && host != nullptr && hipMemcpy(host, d, grid * 4, hipMemcpyDeviceToHost) == hipSuccess;
   if (ok) {
-    const uint32_t c = (host[0] + 8u) % 8u;
+    const uint32_t c = host[0] % 8u;
     for (int i = 0; i < grid && ok; ++i) ok = host[i] < 8u && (host[i] + 8u - (uint32_t)i % 8u) % 8u == c;
   }
   delete[] host;
@@ -312,6 +398,14 @@ prnnStatus_t prnn_set_exchange(prnnHandle_t h, prnnExchange_t mode) {
   return PRNN_STATUS_SUCCESS;
 }
 
+prnnStatus_t prnn_set_layout(prnnHandle_t h, prnnLayout_t layout) {
+  if (h == nullptr) return PRNN_STATUS_BAD_PARAM;
+  if (layout != PRNN_LAYOUT_AUTO && layout != PRNN_LAYOUT_SPREAD && layout != PRNN_LAYOUT_TEAM)
+    return PRNN_STATUS_BAD_PARAM;
+  h->layout = layout;
+  return PRNN_STATUS_SUCCESS;
+}
+
 prnnStatus_t prnn_set_watchdog_us(prnnHandle_t h, uint32_t us) {
   if (h == nullptr || us == 0) return PRNN_STATUS_BAD_PARAM;
   h->watchdog_us = us;
@@ -358,16 +452,11 @@ prnnStatus_t prnn_forward_dense(prnnHandle_t h, int N, int B, int T, prnnDataTyp
   const size_t wb = (size_t)N * N * (w_type == PRNN_DATA_FLOAT ? 4 : 2);
   if (overlap(W, wb, H, (size_t)T * B * N * 4)) return PRNN_STATUS_BAD_PARAM;
   if ((size_t)T * B * N * 4 > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
-  Plan p;
-  if (!split_rows(h, N, B, &p)) return PRNN_STATUS_NOT_SUPPORTED;
-  choose_exchange(h, (N + 3) & ~3, &p);
-  if (h->exchange == PRNN_EXCHANGE_RELAY && p.relay_slice == 0) return PRNN_STATUS_NOT_SUPPORTED;
-  if (p.relay_slice > 0 && h->step != h->relay_next_step) h->ring_valid = false;
   const int wt = w_type == PRNN_DATA_FLOAT ? prnn::kF32 : prnn::kF16;
-  p.k = pick(wt == prnn::kF32 ? prnn::kDenseF32Kernels : prnn::kDenseF16Kernels, wt, p.max_rows, p.chunks, true);
-  if (p.k == nullptr) return PRNN_STATUS_NOT_SUPPORTED;
+  Plan p;
+  if (!plan(h, kDense, N, B, 0, wt, &p)) return PRNN_STATUS_NOT_SUPPORTED;
   const int Npad = (N + 3) & ~3;
-  st = ensure_ring(h, B, Npad, stream);
+  st = ensure_ring(h, p, B, Npad, stream);
   if (st != PRNN_STATUS_SUCCESS) return st;
   StepArgs a = base_args(h, N, B, T, X, h0, H, p, Npad);
   a.W = W;
@@ -390,30 +479,16 @@ prnnStatus_t prnn_forward_sparse(prnnHandle_t h, int N, int B, int T, int K, con
       overlap(val, (size_t)N * K * (val_type == PRNN_DATA_FLOAT ? 4 : 2), H, hb))
     return PRNN_STATUS_BAD_PARAM;
   if (hb > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
-  Plan p;
-  if (!split_rows(h, N, B, &p)) return PRNN_STATUS_NOT_SUPPORTED;
-  choose_exchange(h, (N + 3) & ~3, &p);
-  if (h->exchange == PRNN_EXCHANGE_RELAY && p.relay_slice == 0) return PRNN_STATUS_NOT_SUPPORTED;
-  if (p.relay_slice > 0 && h->step != h->relay_next_step) h->ring_valid = false;
-  const int spr = (K + 63) / 64;
   const int wt = val_type == PRNN_DATA_FLOAT ? prnn::kF32 : prnn::kF16;
-  p.k = pick(wt == prnn::kF32 ? prnn::kSparseF32Kernels : prnn::kSparseF16Kernels, wt, p.max_rows, spr, true);
-  if (p.k == nullptr) return PRNN_STATUS_NOT_SUPPORTED;
-  const int lds_stride = (N + 1 + 3) & ~3;
-  p.lds_bytes = p.waves * lds_stride * 4;
-  if ((size_t)p.lds_bytes > h->lds_per_block) return PRNN_STATUS_NOT_SUPPORTED;
-  if (p.lds_bytes > 65536 &&
-      hipFuncSetAttribute(p.k->fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes) != hipSuccess)
-    return PRNN_STATUS_NOT_SUPPORTED;
+  Plan p;
+  if (!plan(h, kSparse, N, B, K, wt, &p)) return PRNN_STATUS_NOT_SUPPORTED;
   const int Npad = (N + 3) & ~3;
-  st = ensure_ring(h, B, Npad, stream);
+  st = ensure_ring(h, p, B, Npad, stream);
   if (st != PRNN_STATUS_SUCCESS) return st;
   StepArgs a = base_args(h, N, B, T, X, h0, H, p, Npad);
   a.W = col;
   a.V = val;
   a.K = K;
-  a.spr = spr;
-  a.lds_stride = lds_stride;
   return launch(h, p, a, T, stream);
 }
 
@@ -423,15 +498,14 @@ prnnStatus_t prnn_sync_floor(prnnHandle_t h, int N, int B, int T, float* H, hipS
   if (H == nullptr || !aligned(H, 4)) return PRNN_STATUS_BAD_PARAM;
   if ((size_t)T * B * N * 4 > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
   Plan p;
-  if (!split_rows(h, N, B, &p)) return PRNN_STATUS_NOT_SUPPORTED;
-  choose_exchange(h, (N + 3) & ~3, &p);
-  if (h->exchange == PRNN_EXCHANGE_RELAY && p.relay_slice == 0) return PRNN_STATUS_NOT_SUPPORTED;
-  if (p.relay_slice > 0 && h->step != h->relay_next_step) h->ring_valid = false;
-  if (p.max_rows > 64) return PRNN_STATUS_NOT_SUPPORTED;
-  p.k = pick(prnn::kFloorKernels, 0, p.max_rows, p.chunks, false);
-  if (p.k == nullptr) return PRNN_STATUS_NOT_SUPPORTED;
+  if (!plan(h, kFloor, N, B, 0, prnn::kF16, &p)) return PRNN_STATUS_NOT_SUPPORTED;
+  static KernelEntry floor_team = {0, 64, 1 << 30, nullptr};
+  if (p.layout == PRNN_LAYOUT_TEAM) {
+    floor_team.fn = prnn::kFloorTeamKernel;
+    p.k = &floor_team;
+  }
   const int Npad = (N + 3) & ~3;
-  prnnStatus_t st = ensure_ring(h, B, Npad, stream);
+  prnnStatus_t st = ensure_ring(h, p, B, Npad, stream);
   if (st != PRNN_STATUS_SUCCESS) return st;
   StepArgs a = base_args(h, N, B, T, nullptr, nullptr, H, p, Npad);
   return launch(h, p, a, T, stream);

@@ -1,0 +1,29 @@
+// fp16 instances of the team-layout kernels (rows per wave, chunks / pair slots).
+#include "team_kernel.h"
+
+namespace prnn {
+
+const KernelEntry kDenseTeamF16Kernels[] = {
+    // (rows per wave, 256-column chunks)
+    PRNN_DENSE_TEAM(_Float16, kF16, 1, 1), PRNN_DENSE_TEAM(_Float16, kF16, 2, 1), PRNN_DENSE_TEAM(_Float16, kF16, 4, 1),
+    PRNN_DENSE_TEAM(_Float16, kF16, 8, 1), PRNN_DENSE_TEAM(_Float16, kF16, 1, 2), PRNN_DENSE_TEAM(_Float16, kF16, 2, 2),
+    PRNN_DENSE_TEAM(_Float16, kF16, 4, 2), PRNN_DENSE_TEAM(_Float16, kF16, 8, 2), PRNN_DENSE_TEAM(_Float16, kF16, 2, 4),
+    PRNN_DENSE_TEAM(_Float16, kF16, 4, 4), PRNN_DENSE_TEAM(_Float16, kF16, 8, 4), PRNN_DENSE_TEAM(_Float16, kF16, 4, 5),
+    PRNN_DENSE_TEAM(_Float16, kF16, 5, 5), PRNN_DENSE_TEAM(_Float16, kF16, 6, 5), PRNN_DENSE_TEAM(_Float16, kF16, 8, 5),
+    PRNN_DENSE_TEAM(_Float16, kF16, 7, 7), PRNN_DENSE_TEAM(_Float16, kF16, 8, 7), PRNN_DENSE_TEAM(_Float16, kF16, 6, 8),
+    PRNN_DENSE_TEAM(_Float16, kF16, 8, 8),
+    {0, 0, 0, nullptr},
+};
+
+const KernelEntry kSparseTeamF16Kernels[] = {
+    // (rows per wave, 64-pair slots per row)
+    PRNN_SPARSE_TEAM(_Float16, kF16, 1, 1), PRNN_SPARSE_TEAM(_Float16, kF16, 2, 1), PRNN_SPARSE_TEAM(_Float16, kF16, 4, 1),
+    PRNN_SPARSE_TEAM(_Float16, kF16, 8, 1), PRNN_SPARSE_TEAM(_Float16, kF16, 1, 2), PRNN_SPARSE_TEAM(_Float16, kF16, 2, 2),
+    PRNN_SPARSE_TEAM(_Float16, kF16, 4, 2), PRNN_SPARSE_TEAM(_Float16, kF16, 8, 2), PRNN_SPARSE_TEAM(_Float16, kF16, 4, 3),
+    PRNN_SPARSE_TEAM(_Float16, kF16, 5, 2), PRNN_SPARSE_TEAM(_Float16, kF16, 7, 1), PRNN_SPARSE_TEAM(_Float16, kF16, 7, 3),
+    PRNN_SPARSE_TEAM(_Float16, kF16, 8, 3), PRNN_SPARSE_TEAM(_Float16, kF16, 16, 1), PRNN_SPARSE_TEAM(_Float16, kF16, 23, 1),
+    PRNN_SPARSE_TEAM(_Float16, kF16, 24, 1), PRNN_SPARSE_TEAM(_Float16, kF16, 32, 1),
+    {0, 0, 0, nullptr},
+};
+
+}  // namespace prnn

@@ -1,0 +1,236 @@
+// "Team" layout: each XCD runs one batch row's whole recurrence.
+//
+// The grid is 8 teams of P workgroups; the workgroups of one team share
+// blockIdx % 8 and therefore one XCD (workgroups are dealt to the 8 XCDs
+// round-robin; checked once per handle).  Team x serves batch row x % B.
+// With B < 8 the teams x >= B recompute a batch row another team owns and do
+// not write H: every XCD then takes part in every step, so every XCD's
+// exchange region is written at every step (see below).
+//
+// Within a team, the N rows of W are split over its P * 8 waves (balanced to
+// within one row); a wave keeps its rows in registers for all T steps.  Per
+// step the team exchanges h_{t-1} through its own XCD's region of the ring,
+// ring[xcd][2][Npad], with ordinary stores and loads that stay in the XCD's
+// L2: no data crosses between XCDs inside the time loop.  Words carry the
+// same step tag as in the other layout (bit 31 = (S >> 1) & 1, slot S & 1).
+// Region x is indexed by the hardware XCD id, written and read only by the
+// workgroups running on XCD x (and reset by them), and written for every
+// step of every call, so it always holds steps S-1 and S-2 when step S
+// starts, whatever batch row the team on it serves.
+//
+// Per step each of the 8 waves stages its share of h_{t-1} (chunks w, w+8,
+// ...) from the region into a double-buffered LDS row, spinning on the tags;
+// one workgroup barrier later every wave multiplies its rows with the whole
+// row from LDS.  A wave whose wait expires raises a workgroup abort flag but
+// still reaches the barrier; the workgroup then leaves together.
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+#include "dense_kernel.h"
+#include "sparse_kernel.h"
+
+namespace prnn {
+
+constexpr int kTeamWaves = 8;
+
+struct TeamPos {
+  int team, rank, b, wave, lane, q;  // q = global wave index inside the team
+  bool primary;
+  int nr, r0;                        // this wave's rows
+};
+
+__device__ __forceinline__ TeamPos team_pos(const StepArgs& a) {
+  TeamPos p;
+  p.team = blockIdx.x & 7;
+  p.rank = blockIdx.x >> 3;
+  p.b = p.team % a.B;
+  p.primary = p.team < a.B;
+  p.wave = threadIdx.x >> 6;
+  p.lane = threadIdx.x & 63;
+  p.q = p.rank * kTeamWaves + p.wave;
+  p.nr = a.base_rows + (p.q < a.extra_rows ? 1 : 0);
+  p.r0 = p.q * a.base_rows + min(p.q, a.extra_rows);
+  return p;
+}
+
+// This XCD's region of the team ring: [2][Npad] words.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t team_region(const StepArgs& a) {
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (31 << 11)) & 7u;  // HW_REG_XCC_ID
+  return make_rsrc(a.ring + (size_t)xcc * 2 * a.Npad, 2u * a.Npad * 4u);
+}
+
+// Stages chunks w, w + 8, ... of ring slot `slot` into the LDS row `dst`
+// (Npad floats), waiting until every word carries `tag`.  Returns false if the
+// wait expired (the caller must still reach the workgroup barrier).
+__device__ __forceinline__ bool team_stage(__amdgpu_buffer_rsrc_t region, uint32_t slot, int npad, int n, int jn,
+                                           int wave, int lane, uint32_t tag, uint64_t deadline, float* dst) {
+  const uint32_t base = slot * (uint32_t)npad * 4u;
+  bool ok = true;
+  for (int j = wave; j < jn; j += kTeamWaves) {
+    const int c = 256 * j + 4 * lane;
+    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(region, base + 4u * c, 0, kCoherent);
+    const uint64_t t0 = now_ticks();
+    while (wave_any(!chunk_ready(v, tag, c, n))) {
+      if (now_ticks() - t0 > deadline) { ok = false; break; }
+      if (!chunk_ready(v, tag, c, n)) v = __builtin_amdgcn_raw_buffer_load_b128(region, base + 4u * c, 0, kCoherent);
+    }
+    if (!ok) break;
+    if (c < n) *reinterpret_cast<float4*>(dst + c) = chunk_values(v, c, n);
+  }
+  return ok;
+}
+
+// h0 (or zeros) into the LDS row, all threads of the workgroup.
+__device__ __forceinline__ void team_stage_h0(const float* h0, int b, int n, int npad, float* dst) {
+  for (int c = threadIdx.x; c < npad; c += blockDim.x)
+    dst[c] = (h0 != nullptr && c < n) ? h0[(size_t)b * n + c] : 0.f;
+}
+
+// The dense recurrence in the team layout.  RW = rows per wave (capacity),
+// J = 256-column chunks per row (capacity).
+template <typename WT, int RW, int J>
+__global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
+  constexpr int M = pow2_at_least(RW);
+  extern __shared__ float lds[];  // [2][Npad] double-buffered h row
+  __shared__ int abort_flag;
+  const TeamPos p = team_pos(a);
+  // A failed run stays failed until reported.  One thread reads the status
+  // word so that the whole workgroup takes the same decision.
+  if (threadIdx.x == 0) abort_flag = __builtin_nontemporal_load(a.status) != 0u;
+  __syncthreads();
+  if (abort_flag) return;
+
+  const int N = a.N;
+  const int jn = a.chunks;
+  const bool vec = (N & 3) == 0;
+  WChunk<WT> w[RW][J];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      w[r][j].load(a.W, (size_t)(p.r0 + r) * N, 256 * j + 4 * p.lane, N, r < p.nr && j < jn, vec);
+
+  const __amdgpu_buffer_rsrc_t region = team_region(a);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
+  const int my_row = RowReduce<M>::owner_row(p.lane);
+  const bool owner = my_row >= 0 && my_row < p.nr;
+
+  for (int t = 0; t < a.T; ++t) {
+    const uint32_t S = a.step0 + (uint32_t)t;
+    float* hrow = lds + (t & 1) * a.Npad;
+    const uint32_t xoff = (uint32_t)(((size_t)t * a.B + p.b) * N + p.r0 + (owner ? my_row : 0)) * 4u;
+    const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
+    bool ok = true;
+    if (t == 0) {
+      team_stage_h0(a.h0, p.b, N, a.Npad, hrow);
+    } else {
+      const uint32_t prev = S - 1u;
+      ok = team_stage(region, prev & 1u, a.Npad, N, jn, p.wave, p.lane, tag_bit(prev), a.deadline, hrow);
+    }
+    if (!ok && p.lane == 0) {
+      abort_flag = 1;
+      atomicOr(a.status, kStatusTimeout);
+    }
+    __syncthreads();
+    if (abort_flag) return;
+
+    float acc[M];
+#pragma unroll
+    for (int r = 0; r < M; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (j < jn) {
+        const float4 h = *reinterpret_cast<const float4*>(hrow + 256 * j + 4 * p.lane);
+#pragma unroll
+        for (int r = 0; r < RW; ++r) w[r][j].fma4(acc[r], h);
+      }
+    }
+    const float sum = RowReduce<M>::reduce(acc, p.lane);
+    if (owner && !(p.rank == a.skip_wg && t == a.skip_step)) {
+      const uint32_t hb = relu_bits(sum + x);
+      const int row = p.r0 + my_row;
+      if (p.primary) a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
+      __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), region, ((S & 1u) * a.Npad + row) * 4u, 0, kPlain);
+    }
+  }
+}
+
+// The sparse recurrence in the team layout: the h row is staged once per
+// workgroup (all its waves serve the same batch row) and every wave gathers
+// from it for its own rows.  RW = rows per wave, SPR = 64-pair slots per row.
+template <typename VT, int RW, int SPR>
+__global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
+  constexpr int M = pow2_at_least(RW);
+  extern __shared__ float lds[];  // [2][lds_stride]: word N of each row stays 0
+  __shared__ int abort_flag;
+  const TeamPos p = team_pos(a);
+  const int N = a.N;
+  const int K = a.K;
+  const int stride = a.lds_stride;
+  if (threadIdx.x == 0) abort_flag = __builtin_nontemporal_load(a.status) != 0u;
+  for (int c = N + (int)threadIdx.x; c < 2 * stride; c += blockDim.x)
+    if (c % stride >= N) lds[c] = 0.f;
+  __syncthreads();
+  if (abort_flag) return;
+
+  Pair<VT> pr[RW][SPR];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) {
+      const int k = 64 * s + p.lane;
+      const bool live = r < p.nr && s < a.spr && k < K;
+      pr[r][s].load(reinterpret_cast<const int16_t*>(a.W), a.V, live ? (size_t)(p.r0 + r) * K + k : 0, live, N);
+    }
+
+  const __amdgpu_buffer_rsrc_t region = team_region(a);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
+  const int my_row = RowReduce<M>::owner_row(p.lane);
+  const bool owner = my_row >= 0 && my_row < p.nr;
+  const int jn = a.chunks;
+
+  for (int t = 0; t < a.T; ++t) {
+    const uint32_t S = a.step0 + (uint32_t)t;
+    float* hrow = lds + (t & 1) * stride;
+    const uint32_t xoff = (uint32_t)(((size_t)t * a.B + p.b) * N + p.r0 + (owner ? my_row : 0)) * 4u;
+    const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
+    bool ok = true;
+    if (t == 0) {
+      for (int c = threadIdx.x; c < N; c += blockDim.x) hrow[c] = a.h0 != nullptr ? a.h0[(size_t)p.b * N + c] : 0.f;
+    } else {
+      const uint32_t prev = S - 1u;
+      ok = team_stage(region, prev & 1u, a.Npad, N, jn, p.wave, p.lane, tag_bit(prev), a.deadline, hrow);
+    }
+    if (!ok && p.lane == 0) {
+      abort_flag = 1;
+      atomicOr(a.status, kStatusTimeout);
+    }
+    __syncthreads();
+    if (abort_flag) return;
+
+    float acc[M];
+#pragma unroll
+    for (int r = 0; r < M; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) {
+      if (s < a.spr) {
+#pragma unroll
+        for (int r = 0; r < RW; ++r) pr[r][s].fma(acc[r], hrow[pr[r][s].column()]);
+      }
+    }
+    const float sum = RowReduce<M>::reduce(acc, p.lane);
+    if (owner && !(p.rank == a.skip_wg && t == a.skip_step)) {
+      const uint32_t hb = relu_bits(sum + x);
+      const int row = p.r0 + my_row;
+      if (p.primary) a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
+      __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), region, ((S & 1u) * a.Npad + row) * 4u, 0, kPlain);
+    }
+  }
+}
+
+
+#define PRNN_DENSE_TEAM(WT, WTAG, R, JJ) {WTAG, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<WT, R, JJ>)}
+#define PRNN_SPARSE_TEAM(VT, VTAG, R, S) {VTAG, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<VT, R, S>)}
+
+}  // namespace prnn

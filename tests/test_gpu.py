@@ -38,9 +38,10 @@ def to_dev(d):
     return {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in d.items()}
 
 
-def run(handle, kind, d, grid=0, h0=True):
+def run(handle, kind, d, grid=0, h0=True, layout=binding.LAYOUT_AUTO):
     g = to_dev(d)
     handle.set_grid(grid)
+    handle.set_layout(layout)
     hh = g["h0"] if h0 else None
     if kind == "dense":
         H = handle.forward_dense(g["W"], g["X"], hh)
@@ -111,12 +112,16 @@ DENSE_SHAPES = [
 ]
 
 
+LAYOUTS = [binding.LAYOUT_AUTO, binding.LAYOUT_SPREAD]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("N,B,T,wdt,grid", DENSE_SHAPES)
-def test_dense_shapes(handle, N, B, T, wdt, grid):
+def test_dense_shapes(handle, N, B, T, wdt, grid, layout):
     w = Workload(f"dense_{N}", "dense", N, B, T, wdt, seed=N * 7 + B, h0="randn")
     d = generate(w)
-    H = run(handle, "dense", d, grid=grid)
-    assert_parity(H, reference("dense", d), tol_of(d), f"N={N} B={B} T={T} {wdt} grid={grid}")
+    H = run(handle, "dense", d, grid=grid, layout=layout)
+    assert_parity(H, reference("dense", d), tol_of(d), f"N={N} B={B} T={T} {wdt} grid={grid} plan={handle.last_plan()}")
 
 
 SPARSE_SHAPES = [
@@ -136,12 +141,14 @@ SPARSE_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("N,B,T,K,vdt,grid", SPARSE_SHAPES)
-def test_sparse_shapes(handle, N, B, T, K, vdt, grid):
+def test_sparse_shapes(handle, N, B, T, K, vdt, grid, layout):
     w = Workload(f"sparse_{N}", "sparse", N, B, T, vdt, K=K, seed=N * 11 + K, h0="randn")
     d = generate(w)
-    H = run(handle, "sparse", d, grid=grid)
-    assert_parity(H, reference("sparse", d), tol_of(d), f"N={N} B={B} T={T} K={K} {vdt} grid={grid}")
+    H = run(handle, "sparse", d, grid=grid, layout=layout)
+    assert_parity(H, reference("sparse", d), tol_of(d),
+                  f"N={N} B={B} T={T} K={K} {vdt} grid={grid} plan={handle.last_plan()}")
 
 
 def test_zero_timesteps_leave_output_untouched(handle):
@@ -253,8 +260,38 @@ def test_plan_of_headline_layer(handle):
     d = generate(WORKLOADS["dense_f16_n1792"].with_(T=2))
     run(handle, "dense", d)
     p = handle.last_plan()
-    assert p["grid"] == 256 and p["rows_per_wg"] == 7 and p["waves_per_wg"] == 4
+    assert p["layout"] == binding.LAYOUT_TEAM
+    assert p["grid"] == 256 and p["rows_per_wave"] == 7 and p["waves_per_wg"] == 8
+    run(handle, "dense", d, layout=binding.LAYOUT_SPREAD)
+    p = handle.last_plan()
+    assert p["layout"] == binding.LAYOUT_SPREAD
+    assert p["grid"] == 256 and p["rows_per_wave"] == 7 and p["waves_per_wg"] == 4
     assert p["relay_slice"] == 1792 // 32   # auto picks the per-XCD relay at 256 workgroups
+
+
+@pytest.mark.parametrize("name", ["dense_f16_n1792", "sparse10_f16_n1792", "sparse1_f16_n1792"])
+def test_team_and_spread_agree_bitwise(handle, name):
+    """At N = 1792 both layouts give every wave the same 7 rows, the same
+    column-to-lane map and the same summation order: identical results."""
+    w = WORKLOADS[name].with_(T=48, h0="randn")
+    d = generate(w, seed=31)
+    Ht = run(handle, w.kind, d, layout=binding.LAYOUT_TEAM)
+    assert handle.last_plan()["layout"] == binding.LAYOUT_TEAM
+    Hs = run(handle, w.kind, d, layout=binding.LAYOUT_SPREAD)
+    np.testing.assert_array_equal(Ht, Hs)
+    assert_parity(Ht, reference(w.kind, d), tol_of(d), name)
+
+
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_team_layout_batch_rows(handle, B):
+    """B < 8 leaves XCDs that recompute a batch row without writing H; B = 8
+    uses every XCD once."""
+    for name in ("dense_f16_n1152", "sparse10_f16_n1792"):
+        w = WORKLOADS[name].with_(T=20, B=B, h0="randn")
+        d = generate(w, seed=40 + B)
+        H = run(handle, w.kind, d, layout=binding.LAYOUT_TEAM)
+        assert handle.last_plan()["layout"] == binding.LAYOUT_TEAM
+        assert_parity(H, reference(w.kind, d), tol_of(d), f"{name} B={B}")
 
 
 @pytest.mark.parametrize("name,grid", [("dense_f16_n1792", 0), ("sparse10_f16_n1792", 0),
@@ -267,7 +304,7 @@ def test_relay_and_direct_exchange_agree_bitwise(handle, name, grid):
     out = {}
     for mode in (binding.EXCHANGE_DIRECT, binding.EXCHANGE_RELAY):
         handle.set_exchange(mode)
-        out[mode] = run(handle, w.kind, d, grid=grid)
+        out[mode] = run(handle, w.kind, d, grid=grid, layout=binding.LAYOUT_SPREAD)
         assert (handle.last_plan()["relay_slice"] > 0) == (mode == binding.EXCHANGE_RELAY)
     handle.set_exchange(binding.EXCHANGE_AUTO)
     np.testing.assert_array_equal(out[binding.EXCHANGE_DIRECT], out[binding.EXCHANGE_RELAY])
@@ -278,14 +315,18 @@ def test_mixed_exchange_calls_on_one_handle(handle):
     """Calls that alternate exchanges, grids and lengths on one handle keep the
     ring and its XCD-local copies consistent (each call matches the oracle)."""
     w = WORKLOADS["dense_f32_n256"]
-    seq = [(binding.EXCHANGE_RELAY, 0, 32), (binding.EXCHANGE_RELAY, 0, 1), (binding.EXCHANGE_RELAY, 0, 7),
-           (binding.EXCHANGE_DIRECT, 0, 5), (binding.EXCHANGE_RELAY, 0, 6), (binding.EXCHANGE_RELAY, 128, 9),
-           (binding.EXCHANGE_DIRECT, 64, 3), (binding.EXCHANGE_AUTO, 0, 32)]
-    for i, (mode, grid, T) in enumerate(seq):
-        d = generate(w.with_(T=T, h0="randn"), seed=300 + i)
+    S, T_ = binding.LAYOUT_SPREAD, binding.LAYOUT_TEAM
+    seq = [(S, binding.EXCHANGE_RELAY, 0, 32), (S, binding.EXCHANGE_RELAY, 0, 1), (S, binding.EXCHANGE_RELAY, 0, 7),
+           (S, binding.EXCHANGE_DIRECT, 0, 5), (S, binding.EXCHANGE_RELAY, 0, 6), (S, binding.EXCHANGE_RELAY, 128, 9),
+           (S, binding.EXCHANGE_DIRECT, 64, 3), (T_, binding.EXCHANGE_AUTO, 0, 32), (T_, binding.EXCHANGE_AUTO, 0, 1),
+           (T_, binding.EXCHANGE_AUTO, 64, 5), (S, binding.EXCHANGE_AUTO, 0, 4), (T_, binding.EXCHANGE_AUTO, 0, 9),
+           (binding.LAYOUT_AUTO, binding.EXCHANGE_AUTO, 0, 32)]
+    for i, (layout, mode, grid, T) in enumerate(seq):
+        d = generate(w.with_(T=T, h0="randn", B=1 + i % 4), seed=300 + i)
         handle.set_exchange(mode)
-        H = run(handle, "dense", d, grid=grid)
-        assert_parity(H, reference("dense", d), oracle.TOL_F32, f"call {i} mode {mode} grid {grid} T {T}")
+        H = run(handle, "dense", d, grid=grid, layout=layout)
+        assert_parity(H, reference("dense", d), oracle.TOL_F32,
+                      f"call {i} layout {layout} mode {mode} grid {grid} T {T} plan {handle.last_plan()}")
     handle.set_exchange(binding.EXCHANGE_AUTO)
 
 
@@ -293,19 +334,23 @@ def test_forced_relay_needs_an_even_grid(handle):
     d = generate(WORKLOADS["dense_f16_n1152"].with_(T=2))
     handle.set_exchange(binding.EXCHANGE_RELAY)
     with pytest.raises(PrnnError) as e:
-        run(handle, "dense", d, grid=100)
+        run(handle, "dense", d, grid=100, layout=binding.LAYOUT_SPREAD)
     assert e.value.status == binding.NOT_SUPPORTED
     handle.set_exchange(binding.EXCHANGE_AUTO)
     handle.set_grid(0)
 
 
-def test_sync_floor_protocol(handle):
+@pytest.mark.parametrize("layout", [binding.LAYOUT_TEAM, binding.LAYOUT_SPREAD])
+def test_sync_floor_protocol(handle, layout):
     T, B, N = 16, 4, 1792
     handle.set_grid(0)
+    handle.set_layout(layout)
     H = handle.sync_floor(N, B, T)
     handle.synchronize()
+    assert handle.last_plan()["layout"] == layout
     expect = np.broadcast_to(np.arange(1, T + 1, dtype=np.float32)[:, None, None], (T, B, N))
     np.testing.assert_array_equal(H.cpu().numpy(), expect)
+    handle.set_layout(binding.LAYOUT_AUTO)
 
 
 # ---------------------------------------------------------------------------
@@ -354,14 +399,16 @@ def test_not_supported(handle):
     handle.set_grid(0)
 
 
+@pytest.mark.parametrize("layout", [binding.LAYOUT_TEAM, binding.LAYOUT_SPREAD])
 @pytest.mark.parametrize("kind", ["dense", "sparse"])
-def test_watchdog_reports_and_recovers(gpu, kind):
+def test_watchdog_reports_and_recovers(gpu, kind, layout):
     """A workgroup that never publishes step 5 makes the consumers' bounded
     waits expire: the run reports EXECUTION_FAILED and the handle recovers."""
     name = "dense_f16_n1792" if kind == "dense" else "sparse10_f16_n1792"
     w = WORKLOADS[name].with_(T=12)
     d = generate(w, seed=13)
     with Handle() as h:
+        h.set_layout(layout)
         h.set_watchdog_us(2000)
         h.debug_skip_publish(3, 5)
         g = to_dev(d)
