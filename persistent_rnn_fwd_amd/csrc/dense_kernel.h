@@ -25,6 +25,8 @@
 
 namespace prnn {
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 
 template <typename WT>
 struct WChunk;  // four consecutive weights of one row
@@ -77,6 +79,26 @@ struct WChunk<_Float16> {
     fma_mix_hi(acc, lo, h.y);
     fma_mix_lo(acc, hi, h.z);
     fma_mix_hi(acc, hi, h.w);
+  }
+};
+
+// fp16 weights widened once to fp32 in the prologue: twice the registers of
+// the packed form, but the time loop then runs v_fmac_f32, which issues about
+// 1.7x faster than v_fma_mix_f32 on gfx950 (measured).  Widening is exact.
+struct WChunkWide {
+  float4 w;
+  __device__ __forceinline__ void load(const void* W, size_t row_off, int c, int n, bool live, bool vec) {
+    WChunk<_Float16> p;
+    p.load(W, row_off, c, n, live, vec);
+    const f16x2 a = __builtin_bit_cast(f16x2, p.lo);
+    const f16x2 b = __builtin_bit_cast(f16x2, p.hi);
+    w = make_float4((float)a.x, (float)a.y, (float)b.x, (float)b.y);
+  }
+  __device__ __forceinline__ void fma4(float& acc, const float4& h) const {
+    acc = fmaf(w.x, h.x, acc);
+    acc = fmaf(w.y, h.y, acc);
+    acc = fmaf(w.z, h.z, acc);
+    acc = fmaf(w.w, h.w, acc);
   }
 };
 

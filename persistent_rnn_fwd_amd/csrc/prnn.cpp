@@ -151,7 +151,8 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
   const int Npad = (N + 3) & ~3;
   if (kind == kDense) {
     p->k = pick(wt == prnn::kF32 ? prnn::kDenseTeamF32Kernels : prnn::kDenseTeamF16Kernels, p->max_rows, p->chunks);
-    p->lds_bytes = 2 * Npad * 4;
+    if (p->k == nullptr) return false;
+    p->lds_bytes = 2 * 256 * p->k->cap * 4;  // two rows of every chunk the instance holds
   } else if (kind == kSparse) {
     p->spr = (K + 63) / 64;
     p->k = pick(wt == prnn::kF32 ? prnn::kSparseTeamF32Kernels : prnn::kSparseTeamF16Kernels, p->max_rows, p->spr);

@@ -4,13 +4,14 @@
 namespace prnn {
 
 const KernelEntry kDenseTeamF16Kernels[] = {
-    // (rows per wave, 256-column chunks)
-    PRNN_DENSE_TEAM(_Float16, kF16, 1, 1), PRNN_DENSE_TEAM(_Float16, kF16, 2, 1), PRNN_DENSE_TEAM(_Float16, kF16, 4, 1),
-    PRNN_DENSE_TEAM(_Float16, kF16, 8, 1), PRNN_DENSE_TEAM(_Float16, kF16, 1, 2), PRNN_DENSE_TEAM(_Float16, kF16, 2, 2),
-    PRNN_DENSE_TEAM(_Float16, kF16, 4, 2), PRNN_DENSE_TEAM(_Float16, kF16, 8, 2), PRNN_DENSE_TEAM(_Float16, kF16, 2, 4),
-    PRNN_DENSE_TEAM(_Float16, kF16, 4, 4), PRNN_DENSE_TEAM(_Float16, kF16, 8, 4), PRNN_DENSE_TEAM(_Float16, kF16, 4, 5),
-    PRNN_DENSE_TEAM(_Float16, kF16, 5, 5), PRNN_DENSE_TEAM(_Float16, kF16, 6, 5), PRNN_DENSE_TEAM(_Float16, kF16, 8, 5),
-    PRNN_DENSE_TEAM(_Float16, kF16, 7, 7), PRNN_DENSE_TEAM(_Float16, kF16, 8, 7), PRNN_DENSE_TEAM(_Float16, kF16, 6, 8),
+    // (rows per wave, 256-column chunks).  Widened fp16 (fp32 registers, 4 per
+    // weight quad) where rows * chunks <= 50; packed fp16 beyond.
+    PRNN_DENSE_TEAM_WIDE(1, 1), PRNN_DENSE_TEAM_WIDE(2, 1), PRNN_DENSE_TEAM_WIDE(4, 1),
+    PRNN_DENSE_TEAM_WIDE(8, 1), PRNN_DENSE_TEAM_WIDE(1, 2), PRNN_DENSE_TEAM_WIDE(2, 2),
+    PRNN_DENSE_TEAM_WIDE(4, 2), PRNN_DENSE_TEAM_WIDE(8, 2), PRNN_DENSE_TEAM_WIDE(2, 4),
+    PRNN_DENSE_TEAM_WIDE(4, 4), PRNN_DENSE_TEAM_WIDE(8, 4), PRNN_DENSE_TEAM_WIDE(4, 5),
+    PRNN_DENSE_TEAM_WIDE(5, 5), PRNN_DENSE_TEAM_WIDE(6, 5), PRNN_DENSE_TEAM_WIDE(7, 7),
+    PRNN_DENSE_TEAM(_Float16, kF16, 8, 5), PRNN_DENSE_TEAM(_Float16, kF16, 8, 7), PRNN_DENSE_TEAM(_Float16, kF16, 6, 8),
     PRNN_DENSE_TEAM(_Float16, kF16, 8, 8),
     {0, 0, 0, nullptr},
 };

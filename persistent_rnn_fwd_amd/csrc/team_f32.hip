@@ -22,7 +22,7 @@ const KernelEntry kSparseTeamF32Kernels[] = {
 
 // The team layout's exchange and step protocol without weights or arithmetic.
 __global__ void __launch_bounds__(512) floor_team_kernel(StepArgs a) {
-  extern __shared__ float lds[];
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // float4-staged rows
   __shared__ int abort_flag;
   const TeamPos p = team_pos(a);
   if (threadIdx.x == 0) abort_flag = __builtin_nontemporal_load(a.status) != 0u;
@@ -30,6 +30,10 @@ __global__ void __launch_bounds__(512) floor_team_kernel(StepArgs a) {
   if (abort_flag) return;
   const int N = a.N;
   const __amdgpu_buffer_rsrc_t region = team_region(a);
+  if (!p.primary) {
+    team_stamp_tail(a, p, region);
+    return;
+  }
   for (int t = 0; t < a.T; ++t) {
     const uint32_t S = a.step0 + (uint32_t)t;
     float* hrow = lds + (t & 1) * a.Npad;

@@ -89,22 +89,55 @@ __device__ __forceinline__ void team_stage_h0(const float* h0, int b, int n, int
 
 // The dense recurrence in the team layout.  RW = rows per wave (capacity),
 // J = 256-column chunks per row (capacity).
-template <typename WT, int RW, int J>
+// Register form of a 4-weight chunk for each weight type: fp32 as is, fp16
+// either packed (v_fma_mix_f32) or widened to fp32 in the prologue.
+template <typename WT, bool WIDE>
+struct TeamChunk { using type = WChunk<WT>; };
+template <>
+struct TeamChunk<_Float16, true> { using type = WChunkWide; };
+
+// Keeps this XCD's region continuous when the team serves no batch row of its
+// own (B < 8): the next call only needs the tags of this call's last two
+// steps, so the team stamps those on its rows and leaves.  No one reads the
+// region during this call.
+__device__ __forceinline__ void team_stamp_tail(const StepArgs& a, const TeamPos& p,
+                                                __amdgpu_buffer_rsrc_t region) {
+  const uint32_t last = a.step0 + (uint32_t)(a.T - 1);
+  for (int k = 0; k < 2 && k < a.T; ++k) {
+    const uint32_t S = last - (uint32_t)k;
+    for (int r = p.lane; r < p.nr; r += 64)
+      __builtin_amdgcn_raw_buffer_store_b32(tag_bit(S), region, ((S & 1u) * a.Npad + p.r0 + r) * 4u, 0, kPlain);
+  }
+}
+
+template <typename WT, int RW, int J, bool WIDE = false>
 __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
   constexpr int M = pow2_at_least(RW);
-  extern __shared__ float lds[];  // [2][Npad] double-buffered h row
+  constexpr int kRow = 256 * J;   // LDS row: every chunk the instance can hold
+  // 16-byte aligned: the row is read and written as float4, and the static
+  // abort flag would otherwise leave the dynamic block at byte 4.
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // [2][kRow] double-buffered h row
   __shared__ int abort_flag;
   const TeamPos p = team_pos(a);
   // A failed run stays failed until reported.  One thread reads the status
   // word so that the whole workgroup takes the same decision.
   if (threadIdx.x == 0) abort_flag = __builtin_nontemporal_load(a.status) != 0u;
+  // Words past the row stay zero (their weights are zero too), so every chunk
+  // below is read and multiplied without a bounds test and the compiler can
+  // issue all the LDS reads of a step together.
+  for (int c = a.Npad + (int)threadIdx.x; c < 2 * kRow; c += blockDim.x)
+    if (c % kRow >= a.Npad) lds[c] = 0.f;
   __syncthreads();
   if (abort_flag) return;
 
   const int N = a.N;
   const int jn = a.chunks;
   const bool vec = (N & 3) == 0;
-  WChunk<WT> w[RW][J];
+  if (!p.primary) {
+    team_stamp_tail(a, p, team_region(a));
+    return;
+  }
+  typename TeamChunk<WT, WIDE>::type w[RW][J];
 #pragma unroll
   for (int r = 0; r < RW; ++r)
 #pragma unroll
@@ -118,7 +151,7 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
 
   for (int t = 0; t < a.T; ++t) {
     const uint32_t S = a.step0 + (uint32_t)t;
-    float* hrow = lds + (t & 1) * a.Npad;
+    float* hrow = lds + (t & 1) * kRow;
     const uint32_t xoff = (uint32_t)(((size_t)t * a.B + p.b) * N + p.r0 + (owner ? my_row : 0)) * 4u;
     const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
     bool ok = true;
@@ -135,17 +168,16 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
     __syncthreads();
     if (abort_flag) return;
 
+    float4 h[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) h[j] = *reinterpret_cast<const float4*>(hrow + 256 * j + 4 * p.lane);
     float acc[M];
 #pragma unroll
     for (int r = 0; r < M; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      if (j < jn) {
-        const float4 h = *reinterpret_cast<const float4*>(hrow + 256 * j + 4 * p.lane);
+    for (int j = 0; j < J; ++j)
 #pragma unroll
-        for (int r = 0; r < RW; ++r) w[r][j].fma4(acc[r], h);
-      }
-    }
+      for (int r = 0; r < RW; ++r) w[r][j].fma4(acc[r], h[j]);
     const float sum = RowReduce<M>::reduce(acc, p.lane);
     if (owner && !(p.rank == a.skip_wg && t == a.skip_step)) {
       const uint32_t hb = relu_bits(sum + x);
@@ -162,7 +194,7 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
 template <typename VT, int RW, int SPR>
 __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
   constexpr int M = pow2_at_least(RW);
-  extern __shared__ float lds[];  // [2][lds_stride]: word N of each row stays 0
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // [2][lds_stride]: word N of each row stays 0
   __shared__ int abort_flag;
   const TeamPos p = team_pos(a);
   const int N = a.N;
@@ -173,6 +205,10 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
     if (c % stride >= N) lds[c] = 0.f;
   __syncthreads();
   if (abort_flag) return;
+  if (!p.primary) {
+    team_stamp_tail(a, p, team_region(a));
+    return;
+  }
 
   Pair<VT> pr[RW][SPR];
 #pragma unroll
@@ -231,6 +267,7 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
 
 
 #define PRNN_DENSE_TEAM(WT, WTAG, R, JJ) {WTAG, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<WT, R, JJ>)}
+#define PRNN_DENSE_TEAM_WIDE(R, JJ) {kF16, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<_Float16, R, JJ, true>)}
 #define PRNN_SPARSE_TEAM(VT, VTAG, R, S) {VTAG, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<VT, R, S>)}
 
 }  // namespace prnn
