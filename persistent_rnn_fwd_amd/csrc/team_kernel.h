@@ -46,7 +46,7 @@ __device__ __forceinline__ TeamPos team_pos(const StepArgs& a) {
   p.rank = blockIdx.x >> 3;
   p.b = p.team % a.B;
   p.primary = p.team < a.B;
-  p.wave = threadIdx.x >> 6;
+  p.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform for the compiler
   p.lane = threadIdx.x & 63;
   p.q = p.rank * kTeamWaves + p.wave;
   p.nr = a.base_rows + (p.q < a.extra_rows ? 1 : 0);
@@ -71,9 +71,13 @@ __device__ __forceinline__ bool team_stage(__amdgpu_buffer_rsrc_t region, uint32
     const int c = 256 * j + 4 * lane;
     u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(region, base + 4u * c, 0, kCoherent);
     const uint64_t t0 = now_ticks();
-    while (wave_any(!chunk_ready(v, tag, c, n))) {
+    while (true) {
+      const bool mine = chunk_ready(v, tag, c, n);
+      if (!wave_any(!mine)) break;
+      // Re-issue before reading the clock: the clock read then overlaps the
+      // load instead of adding its latency to every poll.
+      if (!mine) v = __builtin_amdgcn_raw_buffer_load_b128(region, base + 4u * c, 0, kCoherent);
       if (now_ticks() - t0 > deadline) { ok = false; break; }
-      if (!chunk_ready(v, tag, c, n)) v = __builtin_amdgcn_raw_buffer_load_b128(region, base + 4u * c, 0, kCoherent);
     }
     if (!ok) break;
     if (c < n) *reinterpret_cast<float4*>(dst + c) = chunk_values(v, c, n);
@@ -149,11 +153,16 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
   const int my_row = RowReduce<M>::owner_row(p.lane);
   const bool owner = my_row >= 0 && my_row < p.nr;
 
+  // x of the row this lane owns.  The load for step t + 1 is issued right
+  // after step t's staging: the next step's polls, whose waits also drain
+  // every earlier load of the wave, then find it long finished.
+  const uint32_t xstep = (uint32_t)a.B * (uint32_t)N * 4u;
+  uint32_t xoff = ((uint32_t)p.b * (uint32_t)N + (uint32_t)(p.r0 + (owner ? my_row : 0))) * 4u;
+  float x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
+
   for (int t = 0; t < a.T; ++t) {
     const uint32_t S = a.step0 + (uint32_t)t;
     float* hrow = lds + (t & 1) * kRow;
-    const uint32_t xoff = (uint32_t)(((size_t)t * a.B + p.b) * N + p.r0 + (owner ? my_row : 0)) * 4u;
-    const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
     bool ok = true;
     if (t == 0) {
       team_stage_h0(a.h0, p.b, N, a.Npad, hrow);
@@ -167,6 +176,9 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
     }
     __syncthreads();
     if (abort_flag) return;
+    const float x = x_next;
+    xoff += xstep;
+    if (t + 1 < a.T) x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
 
     float4 h[J];
 #pragma unroll
@@ -226,11 +238,16 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
   const bool owner = my_row >= 0 && my_row < p.nr;
   const int jn = a.chunks;
 
+  // x of the row this lane owns.  The load for step t + 1 is issued right
+  // after step t's staging: the next step's polls, whose waits also drain
+  // every earlier load of the wave, then find it long finished.
+  const uint32_t xstep = (uint32_t)a.B * (uint32_t)N * 4u;
+  uint32_t xoff = ((uint32_t)p.b * (uint32_t)N + (uint32_t)(p.r0 + (owner ? my_row : 0))) * 4u;
+  float x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
+
   for (int t = 0; t < a.T; ++t) {
     const uint32_t S = a.step0 + (uint32_t)t;
     float* hrow = lds + (t & 1) * stride;
-    const uint32_t xoff = (uint32_t)(((size_t)t * a.B + p.b) * N + p.r0 + (owner ? my_row : 0)) * 4u;
-    const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
     bool ok = true;
     if (t == 0) {
       for (int c = threadIdx.x; c < N; c += blockDim.x) hrow[c] = a.h0 != nullptr ? a.h0[(size_t)p.b * N + c] : 0.f;
@@ -244,6 +261,9 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
     }
     __syncthreads();
     if (abort_flag) return;
+    const float x = x_next;
+    xoff += xstep;
+    if (t + 1 < a.T) x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
 
     float acc[M];
 #pragma unroll
