@@ -18,7 +18,13 @@ Prints ONE JSON line:
                workload (timesteps/s, threads it used)
   detail       per-format timesteps/s, GFLOP/s, per-step time by the slope
                between T = 256 and T = 128, the measured sync floor per step,
-               equivalent weight bytes/s, and the max error ratio vs the oracle
+               equivalent weight bytes/s, the max error ratio vs the oracle,
+               p10/p50/p90 of the timed launches and the dense/sparse ratio
+  baselines    the same recurrence as a per-step library loop on the GPU
+               (hipBLAS fp32 GEMM + add + ReLU per step, eager and captured in
+               a HIP graph; a per-step CSR SpMM for the sparse layer) and as a
+               torch-CPU fp32 loop on the host's threads, with the speedups of
+               the persistent kernels over them (context, not the target)
 """
 from __future__ import annotations
 
@@ -58,9 +64,172 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the host oracle sample")
     ap.add_argument("--only-timed", action="store_true",
                     help="run only warmup + the timed region (every launch is a T=256 call; for profiles)")
+    ap.add_argument("--no-baselines", action="store_true", help="skip the library and torch-CPU loop baselines")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain copy kernel of this many MiB first (counter calibration)")
     return ap.parse_args()
+
+
+def percentiles(xs):
+    import numpy as np
+    p10, p50, p90 = np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])
+    return {"p10": round(float(p10), 4), "p50": round(float(p50), 4), "p90": round(float(p90), 4)}
+
+
+def gpu_clock_report():
+    """Shader clock as amd-smi reports it after the run (a child process; text kept short)."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except (OSError, subprocess.SubprocessError) as e:
+            last = f"{cmd[0]}: {type(e).__name__}"
+            continue
+        text = (r.stdout or "") + (r.stderr or "")
+        try:
+            data = json.loads(r.stdout)
+        except ValueError:
+            last = f"{cmd[0]}: " + " ".join(text.split())[:200]
+            continue
+        found = {}
+
+        def walk(o, path):
+            if isinstance(o, dict):
+                for k, v in o.items():
+                    walk(v, path + [str(k)])
+            elif isinstance(o, list):
+                for i, v in enumerate(o):
+                    walk(v, path + [str(i)])
+            else:
+                key = "/".join(path).lower()
+                if ("gfx" in key or "sclk" in key) and len(found) < 12:
+                    found["/".join(path)] = o
+        walk(data, [])
+        return {"tool": cmd[0], "values": found}
+    return {"tool": None, "error": last}
+
+
+def library_baselines(torch, dev, host, wd, ws, T, persistent_ms):
+    """The recurrence as a per-step library loop on the GPU, and as a torch-CPU
+    loop: h = relu(X[t] + h W^T) one step at a time (the plain formulation the
+    persistent kernels replace).  fp32 throughout (the fp16 weights widened
+    exactly), inputs already on the device.  Returns timesteps/s per variant and
+    the persistent kernels' speedups over them."""
+    import warnings
+    import numpy as np
+    warnings.filterwarnings("ignore", message="Sparse CSR tensor support")
+    stream = torch.cuda.current_stream()
+    N, B = wd.N, wd.B
+    W32 = torch.from_numpy(host[wd.name]["W"].astype(np.float32)).to(dev)
+    Wt = W32.t().contiguous()
+    X = torch.from_numpy(host[wd.name]["X"]).to(dev)
+    h0 = torch.zeros((B, N), dtype=torch.float32, device=dev)
+    Hb = torch.empty((T, B, N), dtype=torch.float32, device=dev)
+
+    def gemm_loop(Wt_, X_, H_):
+        h = h0
+        for t in range(T):
+            torch.addmm(X_[t], h, Wt_, out=H_[t])
+            H_[t].relu_()
+            h = H_[t]
+
+    def time_ms(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in es:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in es]))
+
+    out = {}
+    eager_ms = time_ms(lambda: gemm_loop(Wt, X, Hb))
+    out["hipblas_eager"] = {"timesteps_per_s": round(T / (eager_ms * 1e-3), 1), "ms_per_call": round(eager_ms, 4),
+                            "what": "per step: torch.addmm (hipBLAS fp32 GEMM, [4,1792]x[1792,1792]) + relu_, eager"}
+    ref = Hb.clone()
+
+    # the same loop captured once in a HIP graph; every replay is checked
+    # against the eager result, with eager work and syncs between replays
+    try:
+        Hg = torch.empty_like(Hb)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            gemm_loop(Wt, X, Hg)  # warm the library outside the capture
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            gemm_loop(Wt, X, Hg)
+        bad = 0
+        for _ in range(3):
+            Hg.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            bad += int(not torch.equal(Hg, ref))
+            gemm_loop(Wt, X, Hb)   # eager work between the replays
+            torch.cuda.synchronize()
+        if bad:
+            out["hipblas_graph"] = {"timesteps_per_s": None, "error": f"{bad} of 3 replays differ from eager"}
+        else:
+            g_ms = time_ms(graph.replay)
+            out["hipblas_graph"] = {"timesteps_per_s": round(T / (g_ms * 1e-3), 1), "ms_per_call": round(g_ms, 4),
+                                    "what": "the eager loop captured in one HIP graph, replayed"}
+        del graph
+    except Exception as e:  # the baseline is context: report, do not fail the bench
+        out["hipblas_graph"] = {"timesteps_per_s": None, "error": f"{type(e).__name__}: {str(e)[:160]}"}
+
+    # sparse layer as a per-step CSR SpMM (fp32 values)
+    try:
+        d = host[ws.name]
+        K = ws.K
+        crow = torch.arange(0, (N + 1) * K, K, dtype=torch.int64, device=dev)[: N + 1]
+        col = torch.from_numpy(d["col"].astype(np.int64).reshape(-1)).to(dev)
+        val = torch.from_numpy(d["val"].astype(np.float32).reshape(-1)).to(dev)
+        Wcsr = torch.sparse_csr_tensor(crow, col, val, size=(N, N))
+        Xs = torch.from_numpy(d["X"]).to(dev)
+        Hs = torch.empty((T, B, N), dtype=torch.float32, device=dev)
+
+        def spmm_loop():
+            h = h0
+            for t in range(T):
+                y = torch.sparse.mm(Wcsr, h.t().contiguous())   # [N, B]
+                torch.add(Xs[t], y.t(), out=Hs[t])
+                Hs[t].relu_()
+                h = Hs[t]
+        s_ms = time_ms(spmm_loop, reps=5)
+        out["hipsparse_eager"] = {"timesteps_per_s": round(T / (s_ms * 1e-3), 1), "ms_per_call": round(s_ms, 4),
+                                  "what": "per step: torch.sparse.mm (CSR fp32, K=179 per row) + add + relu_, eager"}
+    except Exception as e:
+        out["hipsparse_eager"] = {"timesteps_per_s": None, "error": f"{type(e).__name__}: {str(e)[:160]}"}
+
+    # torch-CPU fp32 loop on the host threads, bounded sample
+    Wc = torch.from_numpy(host[wd.name]["W"].astype(np.float32)).t().contiguous()
+    Xc = torch.from_numpy(host[wd.name]["X"])
+    h = torch.zeros((B, N), dtype=torch.float32)
+    steps, a = 0, time.perf_counter()
+    while time.perf_counter() - a < 3.0 and steps < 100 * T:
+        for t in range(T):
+            h = torch.relu(torch.addmm(Xc[t], h, Wc))
+        steps += T
+    spent = time.perf_counter() - a
+    out["cpu_torch_loop"] = {"timesteps_per_s": round(steps / spent, 1), "threads": torch.get_num_threads(),
+                             "what": f"torch CPU fp32 addmm + relu per step, dense N=1792 B=4, {steps} steps"}
+
+    def speedup(persistent, base):
+        v = out[base].get("timesteps_per_s")
+        return round(T / (persistent * 1e-3) / v, 2) if v else None
+    # persistent_ms: {"dense": ms per call, "sparse10": ms per call}
+    out["speedups"] = {
+        "dense_persistent_vs_hipblas_eager": speedup(persistent_ms["dense"], "hipblas_eager"),
+        "dense_persistent_vs_hipblas_graph": speedup(persistent_ms["dense"], "hipblas_graph"),
+        "sparse10_persistent_vs_hipblas_eager": speedup(persistent_ms["sparse10"], "hipblas_eager"),
+        "sparse10_persistent_vs_hipblas_graph": speedup(persistent_ms["sparse10"], "hipblas_graph"),
+        "sparse10_persistent_vs_hipsparse_eager": speedup(persistent_ms["sparse10"], "hipsparse_eager"),
+    }
+    return out
 
 
 def main():
@@ -145,8 +314,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     h.synchronize()
-    dense_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    sparse_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    dense_list = [e[0].elapsed_time(e[1]) for e in ev]
+    sparse_list = [e[2].elapsed_time(e[3]) for e in ev]
+    dense_ms = float(np.mean(dense_list))
+    sparse_ms = float(np.mean(sparse_list))
     ms_per_step = wall * 1e3 / args.steps
 
     def timed(fn, reps=20):
@@ -197,6 +368,15 @@ def main():
         detail[w.name]["plan"] = {k: v for k, v in h.last_plan().items() if k != "first_step"}
     detail["sync_floor_us_per_step"] = round(floor_us, 3)
     detail["sync_floor_ms_per_call"] = round(f_full, 4)
+    detail["timed_launch_ms"] = {"dense_f16_n1792": percentiles(dense_list), "sparse10_f16_n1792": percentiles(sparse_list)}
+    sd, ss = detail[wd.name]["us_per_step_slope"], detail[ws.name]["us_per_step_slope"]
+    detail["dense_over_sparse10_step_time"] = round(sd / ss, 3) if ss > 0 else None
+
+    baselines = None
+    if not args.no_baselines:
+        baselines = library_baselines(torch, dev, host, wd, ws, T,
+                                      {"dense": detail[wd.name]["ms_per_call"], "sparse10": detail[ws.name]["ms_per_call"]})
+    detail["gpu_clock_after_run"] = gpu_clock_report()
 
     # roofline of the dominant kernel (larger mean launch time)
     dom, dom_ms = (wd, dense_ms) if dense_ms >= sparse_ms else (ws, sparse_ms)
@@ -270,6 +450,7 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "baselines": baselines,
         "detail": detail,
     }
     print(json.dumps(line), flush=True)
