@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--only-timed", action="store_true",
                     help="run only warmup + the timed region (every launch is a T=256 call; for profiles)")
     ap.add_argument("--no-baselines", action="store_true", help="skip the library and torch-CPU loop baselines")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config table (every workload, not timed "
+                    "in the headline step)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain copy kernel of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -232,6 +234,90 @@ def library_baselines(torch, dev, host, wd, ws, T, persistent_ms):
     return out
 
 
+def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=False):
+    """Per workload: timesteps/s of a full call, per-step time by the slope
+    between T and T/2, the sync floor at the same N, B, T, and the error ratio
+    of the timed output against the oracle."""
+    import numpy as np
+    rows = {}
+    h = Handle()
+    for name, w in WORKLOADS.items():
+        d = generate(w)
+        g = {k: torch.from_numpy(v).to(dev) for k, v in d.items()}
+        T, B, N = w.T, w.B, w.N
+        o = torch.empty((T, B, N), dtype=torch.float32, device=dev)
+
+        def call(t=T):
+            if w.kind == "dense":
+                h.forward_dense(g["W"], g["X"][:t], g["h0"], out=o[:t])
+            else:
+                h.forward_sparse(g["col"], g["val"], g["X"][:t], g["h0"], out=o[:t])
+        full = timed(call)
+        half = timed(lambda: call(T // 2))
+        step_us = (full - half) * 1e3 / (T - T // 2)
+        h.synchronize()
+        plan = {k: v for k, v in h.last_plan().items() if k != "first_step"}
+        fo = torch.empty((T, B, N), dtype=torch.float32, device=dev)
+        f_full = timed(lambda: h.sync_floor(N, B, T, out=fo))
+        f_half = timed(lambda: h.sync_floor(N, B, T // 2, out=fo[: T // 2]))
+        floor_us = (f_full - f_half) * 1e3 / (T - T // 2)
+        err = None
+        if not no_check:
+            import oracle
+            call()
+            h.synchronize()
+            ref = (oracle.forward_dense(d["W"], d["X"], d["h0"]) if w.kind == "dense"
+                   else oracle.forward_sparse(d["col"], d["val"], d["X"], d["h0"]))
+            tol = oracle.TOL_F32 if w.w_dtype == "f32" else oracle.TOL_F16
+            err = round(float(oracle.tolerance_ratio(o.cpu().numpy(), ref, tol)), 5)
+        rows[name] = {
+            "N": N, "K": w.K if w.kind == "sparse" else N, "T": T, "w": w.w_dtype,
+            "timesteps_per_s": round(T / (full * 1e-3), 1),
+            "us_per_step_slope": round(step_us, 3),
+            "floor_us_per_step": round(floor_us, 3),
+            "vs_floor": round(step_us / floor_us, 3) if floor_us > 0 else None,
+            "gflop_per_s": round(w.flop_per_step * T / (full * 1e-3) / 1e9, 2),
+            "max_err_ratio": err,
+            "plan": plan,
+        }
+        del g, o, fo
+    h.close()
+    return rows
+
+
+def trace_breakdown(torch, dev, Handle, g, wd, ws, T):
+    """Per-phase time per step from one traced call of each headline kernel
+    and of the floor (team layout): mean over the waves that serve a batch
+    row, and the largest wave mean.  Traced calls run a little slower than
+    untraced ones (every phase mark reads the clock)."""
+    import numpy as np
+    names = ["stage", "barrier", "compute", "reduce", "epilogue"]
+    out = {}
+    h = Handle()
+    h.set_trace(True)
+    N, B = wd.N, wd.B
+    o = torch.empty((T, B, N), dtype=torch.float32, device=dev)
+    runs = {
+        wd.name: lambda: h.forward_dense(g[wd.name]["W"], g[wd.name]["X"], g[wd.name]["h0"], out=o),
+        ws.name: lambda: h.forward_sparse(g[ws.name]["col"], g[ws.name]["val"], g[ws.name]["X"], g[ws.name]["h0"], out=o),
+        "sync_floor": lambda: h.sync_floor(N, B, T, out=o),
+    }
+    for name, fn in runs.items():
+        fn()
+        fn()
+        rec = h.get_trace().astype(np.float64)
+        live = rec[rec[:, 7] == T]
+        ghz = float(np.mean(live[:, 5] / (live[:, 6] * 10.0)))
+        us = live[:, :6] / (ghz * 1e3) / T
+        out[name] = {"clock_ghz": round(ghz, 3), "waves": int(live.shape[0]),
+                     "loop_us_per_step": round(float(us[:, 5].mean()), 3)}
+        for i, n in enumerate(names):
+            out[name][n] = {"mean_us": round(float(us[:, i].mean()), 3), "max_wave_us": round(float(us[:, i].max()), 3)}
+    h.set_trace(False)
+    h.close()
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -372,6 +458,14 @@ def main():
     sd, ss = detail[wd.name]["us_per_step_slope"], detail[ws.name]["us_per_step_slope"]
     detail["dense_over_sparse10_step_time"] = round(sd / ss, 3) if ss > 0 else None
 
+    # every workload at its own size: per-step slope, floor at the same
+    # size, error ratio against the oracle (not part of the headline step)
+    configs = None
+    if not args.no_configs:
+        configs = per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=args.no_check)
+
+    detail["trace_us_per_step"] = trace_breakdown(torch, dev, Handle, g, wd, ws, T)
+
     baselines = None
     if not args.no_baselines:
         baselines = library_baselines(torch, dev, host, wd, ws, T,
@@ -451,6 +545,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "baselines": baselines,
+        "configs": configs,
         "detail": detail,
     }
     print(json.dumps(line), flush=True)

@@ -195,6 +195,30 @@ prnnStatus_t prnn_set_watchdog_us(prnnHandle_t handle, uint32_t microseconds);
 /* Copies the plan of the last successful forward call into *info. */
 prnnStatus_t prnn_get_last_plan(prnnHandle_t handle, prnnPlanInfo_t* info);
 
+/* Phase tracing (TEAM layout only).  With enable != 0, later forward and
+ * floor calls run trace instances of the team kernels: each wave of each
+ * workgroup that serves a batch row records, per call, the shader-clock
+ * cycles it spent in staging h_{t-1} (polling the exchange and writing LDS),
+ * waiting at the workgroup barrier, reading LDS and multiplying, reducing
+ * across lanes, and in the epilogue (x, ReLU, stores), then the whole time
+ * loop in cycles and in ticks of the 100 MHz constant clock, and the number
+ * of steps (8 uint64 words per wave, in that order).  Tracing slows each step
+ * a little (each mark reads the clock).  The first enable allocates the
+ * handle-owned trace buffer (ALLOC_FAILED if that fails).  While tracing is
+ * on, shapes without a trace instance and the SPREAD layout return
+ * NOT_SUPPORTED.  enable = 0 returns to the untraced kernels. */
+prnnStatus_t prnn_set_trace(prnnHandle_t handle, int enable);
+
+/* Copies the trace of the last traced call into `out` (host memory,
+ * `capacity` uint64 words), after synchronizing `stream`.  Record w (words
+ * [8 w, 8 w + 8)) belongs to wave w % 8 of workgroup w / 8; records of
+ * workgroups that serve no batch row of their own are zero.  *records
+ * receives the number of records (grid * 8).  BAD_PARAM if no traced call
+ * was made, or if out is NULL or capacity < 8 * records (then *records is
+ * still set, so out = NULL, capacity = 0 asks for the size). */
+prnnStatus_t prnn_get_trace(prnnHandle_t handle, uint64_t* out, size_t capacity, int* records,
+                            hipStream_t stream);
+
 /* TEST ONLY: in the next forward call, workgroup `wg` (TEAM layout: the
  * workgroups of rank `wg` within every XCD) does not publish its rows at
  * timestep `step`, so the consumers' bounded waits expire and the

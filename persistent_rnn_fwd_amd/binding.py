@@ -27,6 +27,7 @@ SUCCESS, BAD_PARAM, NOT_SUPPORTED, ALLOC_FAILED, EXECUTION_FAILED, INTERNAL_ERRO
 DATA_FLOAT, DATA_HALF = 0, 1
 EXCHANGE_AUTO, EXCHANGE_DIRECT, EXCHANGE_RELAY = 0, 1, 2
 LAYOUT_AUTO, LAYOUT_SPREAD, LAYOUT_TEAM = 0, 1, 2
+TRACE_WORDS = 8  # per-wave trace record: see Handle.get_trace
 
 # Every function include/prnn.h declares, with its ctypes signature.
 _H = ctypes.c_void_p
@@ -45,6 +46,8 @@ SIGNATURES = {
     "prnn_set_layout": (_I, [_H, _I]),
     "prnn_get_last_plan": (_I, [_H, _P]),
     "prnn_debug_skip_publish": (_I, [_H, _I, _I]),
+    "prnn_set_trace": (_I, [_H, _I]),
+    "prnn_get_trace": (_I, [_H, _P, ctypes.c_size_t, ctypes.POINTER(_I), _P]),
     "prnn_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -171,6 +174,23 @@ class Handle:
 
     def synchronize(self, stream: Optional[torch.cuda.Stream] = None):
         _check("prnn_synchronize", self._lib.prnn_synchronize(self._h, _stream_ptr(stream)))
+
+    def set_trace(self, enable: bool):
+        _check("prnn_set_trace", self._lib.prnn_set_trace(self._h, 1 if enable else 0))
+
+    def get_trace(self, stream: Optional[torch.cuda.Stream] = None):
+        """Phase records of the last traced call: uint64 array [grid * 8, 8]
+        (stage, barrier, compute, reduce, epilogue cycles; loop cycles; loop
+        ticks of the 100 MHz clock; steps), one row per wave."""
+        import numpy as np
+        records = ctypes.c_int(0)
+        st = self._lib.prnn_get_trace(self._h, None, 0, ctypes.byref(records), _stream_ptr(stream))
+        if records.value <= 0:
+            _check("prnn_get_trace", st)
+        buf = np.zeros((records.value, TRACE_WORDS), dtype=np.uint64)
+        _check("prnn_get_trace", self._lib.prnn_get_trace(self._h, buf.ctypes.data, buf.size, ctypes.byref(records),
+                                                          _stream_ptr(stream)))
+        return buf
 
     # -- the recurrence -----------------------------------------------------
     def forward_dense(self, W: torch.Tensor, X: torch.Tensor, h0: Optional[torch.Tensor] = None,

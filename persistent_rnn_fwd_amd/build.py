@@ -4,7 +4,9 @@
 """
 from __future__ import annotations
 
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -15,6 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libprnn.so")
+RESOURCES = os.path.join(BUILD, "kernel_resources.json")  # per-kernel registers, scratch, LDS, occupancy
 SOURCES = ["dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip", "team_f16.hip", "team_f32.hip",
            "prnn.cpp"]
 
@@ -42,17 +45,39 @@ def _run(cmd):
     return err
 
 
+_REMARK = re.compile(r"remark:\s+(Function Name|TotalSGPRs|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Dynamic Stack|"
+                     r"Occupancy \[waves/SIMD\]|SGPRs Spill|VGPRs Spill|LDS Size \[bytes/block\]): (\S+)")
+
+
+def parse_resource_remarks(text: str) -> dict:
+    """The compiler's kernel-resource-usage remarks, per kernel symbol."""
+    out, cur = {}, None
+    for m in _REMARK.finditer(text):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key.split(" [")[0]] = int(val) if val.isdigit() else val
+    return out
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
     jobs = []
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        jobs.append((obj, [cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+        extra = ["-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
+        jobs.append((obj, [cc, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]))
+    resources = {}
     with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
         for out in ex.map(lambda j: _run(j[1]), jobs):
-            if verbose and out.strip():
-                print(out)
+            resources.update(parse_resource_remarks(out))
+            rest = "\n".join(l for l in out.splitlines() if "remark:" not in l and l.strip())
+            if verbose and rest:
+                print(rest)
+    with open(RESOURCES, "w") as fh:
+        json.dump(resources, fh, indent=0, sort_keys=True)
     tmp = LIB + ".tmp"
     _run([cc, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *[o for o, _ in jobs]])
     os.replace(tmp, LIB)

@@ -30,7 +30,16 @@ struct StepArgs {
   uint32_t x_bytes;     // bytes of X (= bytes of H)
   uint64_t deadline;    // bound on one wait, in ticks of the 100 MHz clock
   int skip_wg, skip_step;  // test-only publish skip (skip_wg < 0: off)
+  uint64_t* trace;      // trace instances: kTraceWords per wave, [grid][8 waves][kTraceWords]
 };
+
+// Per-wave phase record written by the trace instances of the team kernels:
+// shader-clock cycles spent in staging (poll + LDS write), at the workgroup
+// barrier, in the LDS reads and multiply-adds, in the cross-lane reduction
+// and in the epilogue, then the whole time loop in cycles and in ticks of the
+// 100 MHz clock, and the number of steps.
+constexpr int kTraceWords = 8;
+enum TraceWord { kTrStage = 0, kTrBarrier, kTrCompute, kTrReduce, kTrEpilogue, kTrLoopCycles, kTrLoopTicks, kTrSteps };
 
 enum WType { kF32 = 0, kF16 = 1 };
 
@@ -61,6 +70,12 @@ extern const void* kPlacementKernel;
 // Team layout: the protocol-only kernel, and the ring reset in which every XCD
 // fills its own [2][npad] region of the [8][2][npad] ring.
 extern const void* kFloorTeamKernel;
+// Trace instances (team layout only): the same kernels with phase timing.
+extern const KernelEntry kDenseTeamF16TraceKernels[];
+extern const KernelEntry kDenseTeamF32TraceKernels[];
+extern const KernelEntry kSparseTeamF16TraceKernels[];
+extern const KernelEntry kSparseTeamF32TraceKernels[];
+extern const void* kFloorTeamTraceKernel;
 void launch_team_fill(uint32_t* ring, int npad, uint32_t v, hipStream_t stream);
 
 }  // namespace prnn

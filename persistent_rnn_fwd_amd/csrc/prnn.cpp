@@ -42,6 +42,10 @@ struct prnnContext {
   int skip_step = -1;
   prnnPlanInfo_t last_plan{};
   bool have_plan = false;
+  // Phase tracing: [num_cu][8 waves][kTraceWords] of the last traced call.
+  bool trace = false;
+  uint64_t* d_trace = nullptr;
+  int trace_records = 0;  // records written by the last traced call (0: none)
 };
 
 namespace {
@@ -112,7 +116,10 @@ bool plan_spread(const prnnContext* h, Kind kind, int N, int B, int K, int wt, P
     if (p->max_rows > 64) return false;
     p->k = pick(prnn::kFloorKernels, p->max_rows, p->chunks);
   }
-  if (p->k == nullptr || (size_t)p->lds_bytes > h->lds_per_block) return false;
+  if (p->k == nullptr) return false;
+  // static LDS: the sparse kernel's per-wave pair placement scratch
+  const size_t static_lds = kind == kSparse ? (size_t)4 * 64 * p->k->cap * 8 : 0;
+  if ((size_t)p->lds_bytes + static_lds > h->lds_per_block) return false;
   // Relay exchange when the grid spreads evenly over the 8 XCDs and is large
   // enough that per-XCD fan-in pays (measured: direct polling from 256
   // workgroups about 4 us per step; relay with slice sentinels about 3.2 us).
@@ -150,12 +157,16 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
   p->chunks = (N + 255) / 256;
   const int Npad = (N + 3) & ~3;
   if (kind == kDense) {
-    p->k = pick(wt == prnn::kF32 ? prnn::kDenseTeamF32Kernels : prnn::kDenseTeamF16Kernels, p->max_rows, p->chunks);
+    const KernelEntry* table = h->trace ? (wt == prnn::kF32 ? prnn::kDenseTeamF32TraceKernels : prnn::kDenseTeamF16TraceKernels)
+                                        : (wt == prnn::kF32 ? prnn::kDenseTeamF32Kernels : prnn::kDenseTeamF16Kernels);
+    p->k = pick(table, p->max_rows, p->chunks);
     if (p->k == nullptr) return false;
     p->lds_bytes = 2 * 256 * p->k->cap * 4;  // two rows of every chunk the instance holds
   } else if (kind == kSparse) {
     p->spr = (K + 63) / 64;
-    p->k = pick(wt == prnn::kF32 ? prnn::kSparseTeamF32Kernels : prnn::kSparseTeamF16Kernels, p->max_rows, p->spr);
+    const KernelEntry* table = h->trace ? (wt == prnn::kF32 ? prnn::kSparseTeamF32TraceKernels : prnn::kSparseTeamF16TraceKernels)
+                                        : (wt == prnn::kF32 ? prnn::kSparseTeamF32Kernels : prnn::kSparseTeamF16Kernels);
+    p->k = pick(table, p->max_rows, p->spr);
     p->lds_stride = sparse_lds_stride(N);
     p->lds_bytes = 2 * p->lds_stride * 4;
   } else {
@@ -164,7 +175,11 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
     p->k = &floor_team;  // the caller substitutes the team floor kernel
     p->lds_bytes = 2 * Npad * 4;
   }
-  return p->k != nullptr && (size_t)p->lds_bytes <= h->lds_per_block;
+  if (p->k == nullptr) return false;
+  // static LDS of the team kernels: flags, and for sparse the per-wave pair
+  // placement scratch (8 waves x 64 x slots x 8 bytes)
+  const size_t static_lds = 256 + (kind == kSparse ? (size_t)8 * 64 * p->k->cap * 8 : 0);
+  return (size_t)p->lds_bytes + static_lds <= h->lds_per_block;
 }
 
 bool plan(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Plan* p) {
@@ -176,6 +191,7 @@ bool plan(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Plan* p)
     }
     if (h->layout == PRNN_LAYOUT_TEAM) return false;
   }
+  if (h->trace) return false;  // trace instances exist for the team layout only
   return plan_spread(h, kind, N, B, K, wt, p);
 }
 
@@ -278,6 +294,12 @@ prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream
   a.deadline = static_cast<uint64_t>(h->watchdog_us) * 100ull;  // 100 MHz constant clock
   a.skip_wg = h->skip_wg;
   a.skip_step = h->skip_step;
+  a.trace = nullptr;
+  if (h->trace) {
+    // records of workgroups without a batch row of their own stay zero
+    prnn::launch_fill(reinterpret_cast<uint32_t*>(h->d_trace), (size_t)p.grid * 8 * prnn::kTraceWords * 2, 0u, stream);
+    a.trace = h->d_trace;
+  }
   void* args[] = {&a};
   hipError_t e = hipLaunchCooperativeKernel(p.k->fn, dim3(p.grid), dim3(p.block), args,
                                             static_cast<unsigned>(p.lds_bytes), stream);
@@ -296,6 +318,7 @@ prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream
   info.relay_slice = p.relay_slice;
   info.first_step = h->step;
   h->have_plan = true;
+  h->trace_records = h->trace ? p.grid * 8 : 0;
   h->step += static_cast<uint64_t>(T);
   if (p.layout == PRNN_LAYOUT_SPREAD && p.relay_slice > 0) h->relay_next_step = h->step;
   h->skip_wg = -1;
@@ -380,9 +403,36 @@ prnnStatus_t prnn_destroy(prnnHandle_t h) {
   if (h->d_status != nullptr && hipMemcpy(&s, h->d_status, 4, hipMemcpyDeviceToHost) == hipSuccess && s != 0)
     st = PRNN_STATUS_EXECUTION_FAILED;
   if (h->d_ring != nullptr) (void)hipFree(h->d_ring);
+  if (h->d_trace != nullptr) (void)hipFree(h->d_trace);
   if (h->d_status != nullptr) (void)hipFree(h->d_status);
   delete h;
   return st;
+}
+
+prnnStatus_t prnn_set_trace(prnnHandle_t h, int enable) {
+  if (h == nullptr) return PRNN_STATUS_BAD_PARAM;
+  if (enable != 0 && h->d_trace == nullptr) {
+    void* p = nullptr;
+    if (hipMalloc(&p, (size_t)h->num_cu * 8 * prnn::kTraceWords * sizeof(uint64_t)) != hipSuccess) {
+      (void)hipGetLastError();
+      return PRNN_STATUS_ALLOC_FAILED;
+    }
+    h->d_trace = static_cast<uint64_t*>(p);
+  }
+  h->trace = enable != 0;
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t prnn_get_trace(prnnHandle_t h, uint64_t* out, size_t capacity, int* records, hipStream_t stream) {
+  if (h == nullptr || records == nullptr) return PRNN_STATUS_BAD_PARAM;
+  *records = h->trace_records;
+  if (h->trace_records == 0) return PRNN_STATUS_BAD_PARAM;
+  const size_t words = (size_t)h->trace_records * prnn::kTraceWords;
+  if (out == nullptr || capacity < words) return PRNN_STATUS_BAD_PARAM;
+  if (hipStreamSynchronize(stream) != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+  if (hipMemcpy(out, h->d_trace, words * sizeof(uint64_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return PRNN_STATUS_INTERNAL_ERROR;
+  return PRNN_STATUS_SUCCESS;
 }
 
 prnnStatus_t prnn_set_grid(prnnHandle_t h, int workgroups) {
@@ -501,9 +551,11 @@ prnnStatus_t prnn_sync_floor(prnnHandle_t h, int N, int B, int T, float* H, hipS
   Plan p;
   if (!plan(h, kFloor, N, B, 0, prnn::kF16, &p)) return PRNN_STATUS_NOT_SUPPORTED;
   static KernelEntry floor_team = {0, 64, 1 << 30, nullptr};
+  static KernelEntry floor_team_trace = {0, 64, 1 << 30, nullptr};
   if (p.layout == PRNN_LAYOUT_TEAM) {
     floor_team.fn = prnn::kFloorTeamKernel;
-    p.k = &floor_team;
+    floor_team_trace.fn = prnn::kFloorTeamTraceKernel;
+    p.k = h->trace ? &floor_team_trace : &floor_team;
   }
   const int Npad = (N + 3) & ~3;
   prnnStatus_t st = ensure_ring(h, p, B, Npad, stream);

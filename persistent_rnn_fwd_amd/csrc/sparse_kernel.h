@@ -34,6 +34,8 @@ struct Pair<_Float16> {
   }
   __device__ __forceinline__ int column() const { return (int)(p >> 16); }
   __device__ __forceinline__ void fma(float& acc, float h) const { fma_mix_lo(acc, p, h); }
+  __device__ __forceinline__ uint2 raw() const { return make_uint2(p, 0u); }
+  __device__ __forceinline__ void set_raw(uint2 r) { p = r.x; }
 };
 
 template <>
@@ -47,7 +49,79 @@ struct Pair<float> {
   }
   __device__ __forceinline__ int column() const { return c; }
   __device__ __forceinline__ void fma(float& acc, float h) const { acc = fmaf(v, h, acc); }
+  __device__ __forceinline__ uint2 raw() const { return make_uint2(__float_as_uint(v), (uint32_t)c); }
+  __device__ __forceinline__ void set_raw(uint2 r) {
+    v = __uint_as_float(r.x);
+    c = (int)r.y;
+  }
 };
+
+// LDS: 32 banks of 4-byte words; each half of a wave (lanes 0-31, 32-63) is
+// served on its own, one word per bank per cycle, all lanes that read the
+// same word at once.  A gather whose 32 lanes hit b distinct words in one
+// bank takes b cycles for that half (measured on gfx950).
+constexpr int kLdsBanks = 32;
+
+// Bank-aware placement of one row's pairs (the pages' bank-aware layout,
+// our reading: every gather instruction should touch each LDS bank once).
+// On entry lane l of slot s holds pair 64 s + l (s < spr, pairs >= K are
+// padding that points at the zero word).  On exit the same K pairs sit so
+// that each group (slot, half-wave) holds at most one pair per bank whenever
+// no bank holds more than 2 * spr of the row's pairs: the pairs are ranked by
+// bank (ties in their original order, so the placement and hence the
+// summation order are deterministic) and dealt round-robin over the 2 * spr
+// groups.  The sum is order-free, so any placement computes the same row.
+// `scratch` is this wave's LDS area of SPR * 64 entries.
+template <typename P, int SPR>
+__device__ __forceinline__ void place_row_bank_aware(P (&row)[SPR], int spr, int K, int n, int lane, uint2* scratch) {
+  P pad;
+  pad.load(nullptr, nullptr, 0, false, n);
+  int rank[SPR];
+#pragma unroll
+  for (int s = 0; s < SPR; ++s) {
+    rank[s] = 0;
+    if (s < spr) scratch[64 * s + lane] = pad.raw();
+  }
+  // rank = number of pairs in lower banks + earlier pairs of the same bank
+  uint32_t base = 0;
+  for (int bank = 0; bank < kLdsBanks; ++bank) {
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) {
+      if (s < spr) {
+        const bool mine = 64 * s + lane < K && (row[s].column() & (kLdsBanks - 1)) == bank;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(mine);
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (mine) rank[s] = (int)(base + below);
+        base += (uint32_t)__builtin_popcountll(m);
+      }
+    }
+  }
+  const int groups = 2 * spr;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // padding written before the pairs
+#pragma unroll
+  for (int s = 0; s < SPR; ++s) {
+    if (s < spr && 64 * s + lane < K) {
+      const int g = rank[s] % groups, q = rank[s] / groups;  // q < 32: K <= 32 * groups
+      scratch[64 * (g >> 1) + 32 * (g & 1) + q] = row[s].raw();
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // all lanes' writes before the reads
+#pragma unroll
+  for (int s = 0; s < SPR; ++s)
+    if (s < spr) row[s].set_raw(scratch[64 * s + lane]);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // scratch free for the next row
+}
+
+// Rows [R, RW) of a register-resident pair block, unrolled at compile time
+// (a runtime row index would force the block out of registers).
+template <int R, int RW, typename P, int SPR>
+__device__ __forceinline__ void place_rows_bank_aware(P (&pr)[RW][SPR], int nr, int spr, int K, int n, int lane,
+                                                      uint2* scratch) {
+  if constexpr (R < RW) {
+    if (R < nr) place_row_bank_aware<P, SPR>(pr[R], spr, K, n, lane, scratch);
+    place_rows_bank_aware<R + 1, RW, P, SPR>(pr, nr, spr, K, n, lane, scratch);
+  }
+}
 
 constexpr int kStageChunks = 8;  // 16-byte loads in flight per lane while staging h
 
@@ -85,6 +159,10 @@ __global__ void __launch_bounds__(256) sparse_kernel(StepArgs a) {
       const bool live = r < nr && s < spr && k < K;
       pr[r][s].load(reinterpret_cast<const int16_t*>(a.W), a.V, live ? (size_t)(row0 + r) * K + k : 0, live, N);
     }
+  // Bank-aware order of each row's pairs (the same placement as the team
+  // layout, so both layouts sum in the same order).
+  __shared__ uint2 place_scratch[4][64 * SPR];
+  place_rows_bank_aware<0, RMAX, Pair<VT>, SPR>(pr, nr, spr, K, N, lane, place_scratch[wave]);
 
   const Exchange ex = make_exchange(a.ring, a.relay, a.ring_bytes, a.relay_slice, g, N);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);

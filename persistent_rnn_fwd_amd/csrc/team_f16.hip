@@ -27,4 +27,16 @@ const KernelEntry kSparseTeamF16Kernels[] = {
     {0, 0, 0, nullptr},
 };
 
+// Trace instances: the shapes of the configured layers (N = 1152 and 1792
+// dense; 10 % and 1 % sparse at N = 1152, 1792 and 5760).
+const KernelEntry kDenseTeamF16TraceKernels[] = {
+    PRNN_DENSE_TEAM_WIDE_TRACE(5, 5), PRNN_DENSE_TEAM_WIDE_TRACE(7, 7),
+    {0, 0, 0, nullptr},
+};
+const KernelEntry kSparseTeamF16TraceKernels[] = {
+    PRNN_SPARSE_TEAM_TRACE(_Float16, kF16, 5, 2), PRNN_SPARSE_TEAM_TRACE(_Float16, kF16, 7, 1),
+    PRNN_SPARSE_TEAM_TRACE(_Float16, kF16, 7, 3), PRNN_SPARSE_TEAM_TRACE(_Float16, kF16, 23, 1),
+    {0, 0, 0, nullptr},
+};
+
 }  // namespace prnn

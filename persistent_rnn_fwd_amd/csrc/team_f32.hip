@@ -21,6 +21,7 @@ const KernelEntry kSparseTeamF32Kernels[] = {
 };
 
 // The team layout's exchange and step protocol without weights or arithmetic.
+template <bool TRACE>
 __global__ void __launch_bounds__(512) floor_team_kernel(StepArgs a) {
   extern __shared__ __attribute__((aligned(16))) float lds[];  // float4-staged rows
   __shared__ int abort_flag;
@@ -34,6 +35,8 @@ __global__ void __launch_bounds__(512) floor_team_kernel(StepArgs a) {
     team_stamp_tail(a, p, region);
     return;
   }
+  PhaseClock<TRACE> clk;
+  clk.start();
   for (int t = 0; t < a.T; ++t) {
     const uint32_t S = a.step0 + (uint32_t)t;
     float* hrow = lds + (t & 1) * a.Npad;
@@ -46,16 +49,21 @@ __global__ void __launch_bounds__(512) floor_team_kernel(StepArgs a) {
       abort_flag = 1;
       atomicOr(a.status, kStatusTimeout);
     }
+    clk.mark(kTrStage);
     __syncthreads();
+    clk.mark(kTrBarrier);
     if (abort_flag) return;
     const float seen = t > 0 ? hrow[p.lane] : 0.f;
+    clk.mark(kTrCompute);
     if (p.lane < p.nr) {
       const uint32_t hb = relu_bits((float)(t + 1) + seen * 0.f);
       const int row = p.r0 + p.lane;
-      if (p.primary) a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
+      a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
       __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), region, ((S & 1u) * a.Npad + row) * 4u, 0, kPlain);
     }
+    clk.mark(kTrEpilogue);
   }
+  if (TRACE) clk.finish(trace_record(a, p), a.T);
 }
 
 // Resets the team ring: every XCD fills its own region (so its L2 never holds
@@ -68,7 +76,17 @@ __global__ void team_fill_kernel(uint32_t* ring, int npad, uint32_t v) {
     region[i] = v;
 }
 
-const void* kFloorTeamKernel = reinterpret_cast<const void*>(&floor_team_kernel);
+const void* kFloorTeamKernel = reinterpret_cast<const void*>(&floor_team_kernel<false>);
+const void* kFloorTeamTraceKernel = reinterpret_cast<const void*>(&floor_team_kernel<true>);
+
+// Trace instances (the N = 256 fp32 layer).
+const KernelEntry kDenseTeamF32TraceKernels[] = {
+    PRNN_DENSE_TEAM_TRACE(float, kF32, 1, 1),
+    {0, 0, 0, nullptr},
+};
+const KernelEntry kSparseTeamF32TraceKernels[] = {
+    {0, 0, 0, nullptr},
+};
 
 void launch_team_fill(uint32_t* ring, int npad, uint32_t v, hipStream_t stream) {
   hipLaunchKernelGGL(team_fill_kernel, dim3(64), dim3(256), 0, stream, ring, npad, v);

@@ -91,6 +91,45 @@ __device__ __forceinline__ void team_stage_h0(const float* h0, int b, int n, int
     dst[c] = (h0 != nullptr && c < n) ? h0[(size_t)b * n + c] : 0.f;
 }
 
+// Phase timing for the trace instances; compiles to nothing otherwise.  The
+// shader clock is read with s_memtime, whose result the next use waits for,
+// so a traced run is a little slower than an untraced one.
+template <bool ON>
+struct PhaseClock {
+  __device__ __forceinline__ void start() {}
+  __device__ __forceinline__ void mark(int) {}
+  __device__ __forceinline__ void finish(uint64_t*, int) {}
+};
+template <>
+struct PhaseClock<true> {
+  uint64_t acc[5], last, c0, r0;
+  __device__ __forceinline__ void start() {
+    for (int k = 0; k < 5; ++k) acc[k] = 0;
+    r0 = __builtin_amdgcn_s_memrealtime();
+    c0 = last = __builtin_amdgcn_s_memtime();
+  }
+  __device__ __forceinline__ void mark(int k) {
+    const uint64_t now = __builtin_amdgcn_s_memtime();
+    acc[k] += now - last;
+    last = now;
+  }
+  // out = this wave's record; lane 0 writes it.
+  __device__ __forceinline__ void finish(uint64_t* out, int steps) {
+    const uint64_t c1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    if ((threadIdx.x & 63) == 0) {
+      for (int k = 0; k < 5; ++k) out[k] = acc[k];
+      out[kTrLoopCycles] = c1 - c0;
+      out[kTrLoopTicks] = r1 - r0;
+      out[kTrSteps] = (uint64_t)steps;
+    }
+  }
+};
+
+__device__ __forceinline__ uint64_t* trace_record(const StepArgs& a, const TeamPos& p) {
+  return a.trace + ((size_t)blockIdx.x * kTeamWaves + (size_t)p.wave) * kTraceWords;
+}
+
 // The dense recurrence in the team layout.  RW = rows per wave (capacity),
 // J = 256-column chunks per row (capacity).
 // Register form of a 4-weight chunk for each weight type: fp32 as is, fp16
@@ -114,7 +153,7 @@ __device__ __forceinline__ void team_stamp_tail(const StepArgs& a, const TeamPos
   }
 }
 
-template <typename WT, int RW, int J, bool WIDE = false>
+template <typename WT, int RW, int J, bool WIDE = false, bool TRACE = false>
 __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
   constexpr int M = pow2_at_least(RW);
   constexpr int kRow = 256 * J;   // LDS row: every chunk the instance can hold
@@ -159,6 +198,8 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
   const uint32_t xstep = (uint32_t)a.B * (uint32_t)N * 4u;
   uint32_t xoff = ((uint32_t)p.b * (uint32_t)N + (uint32_t)(p.r0 + (owner ? my_row : 0))) * 4u;
   float x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
+  PhaseClock<TRACE> clk;
+  clk.start();
 
   for (int t = 0; t < a.T; ++t) {
     const uint32_t S = a.step0 + (uint32_t)t;
@@ -174,7 +215,9 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
       abort_flag = 1;
       atomicOr(a.status, kStatusTimeout);
     }
+    clk.mark(kTrStage);
     __syncthreads();
+    clk.mark(kTrBarrier);
     if (abort_flag) return;
     const float x = x_next;
     xoff += xstep;
@@ -190,24 +233,29 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
     for (int j = 0; j < J; ++j)
 #pragma unroll
       for (int r = 0; r < RW; ++r) w[r][j].fma4(acc[r], h[j]);
+    clk.mark(kTrCompute);
     const float sum = RowReduce<M>::reduce(acc, p.lane);
+    clk.mark(kTrReduce);
     if (owner && !(p.rank == a.skip_wg && t == a.skip_step)) {
       const uint32_t hb = relu_bits(sum + x);
       const int row = p.r0 + my_row;
-      if (p.primary) a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
+      a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
       __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), region, ((S & 1u) * a.Npad + row) * 4u, 0, kPlain);
     }
+    clk.mark(kTrEpilogue);
   }
+  if (TRACE) clk.finish(trace_record(a, p), a.T);
 }
 
 // The sparse recurrence in the team layout: the h row is staged once per
 // workgroup (all its waves serve the same batch row) and every wave gathers
 // from it for its own rows.  RW = rows per wave, SPR = 64-pair slots per row.
-template <typename VT, int RW, int SPR>
+template <typename VT, int RW, int SPR, bool TRACE = false>
 __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
   constexpr int M = pow2_at_least(RW);
   extern __shared__ __attribute__((aligned(16))) float lds[];  // [2][lds_stride]: word N of each row stays 0
   __shared__ int abort_flag;
+  __shared__ uint2 place_scratch[kTeamWaves][64 * SPR];  // prologue only: pair placement
   const TeamPos p = team_pos(a);
   const int N = a.N;
   const int K = a.K;
@@ -231,6 +279,9 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
       const bool live = r < p.nr && s < a.spr && k < K;
       pr[r][s].load(reinterpret_cast<const int16_t*>(a.W), a.V, live ? (size_t)(p.r0 + r) * K + k : 0, live, N);
     }
+  // Bank-aware order of each row's pairs, so the gathers below hit distinct
+  // LDS banks.
+  place_rows_bank_aware<0, RW, Pair<VT>, SPR>(pr, p.nr, a.spr, K, N, p.lane, place_scratch[p.wave]);
 
   const __amdgpu_buffer_rsrc_t region = team_region(a);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
@@ -244,6 +295,8 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
   const uint32_t xstep = (uint32_t)a.B * (uint32_t)N * 4u;
   uint32_t xoff = ((uint32_t)p.b * (uint32_t)N + (uint32_t)(p.r0 + (owner ? my_row : 0))) * 4u;
   float x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
+  PhaseClock<TRACE> clk;
+  clk.start();
 
   for (int t = 0; t < a.T; ++t) {
     const uint32_t S = a.step0 + (uint32_t)t;
@@ -259,7 +312,9 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
       abort_flag = 1;
       atomicOr(a.status, kStatusTimeout);
     }
+    clk.mark(kTrStage);
     __syncthreads();
+    clk.mark(kTrBarrier);
     if (abort_flag) return;
     const float x = x_next;
     xoff += xstep;
@@ -275,19 +330,29 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
         for (int r = 0; r < RW; ++r) pr[r][s].fma(acc[r], hrow[pr[r][s].column()]);
       }
     }
+    clk.mark(kTrCompute);
     const float sum = RowReduce<M>::reduce(acc, p.lane);
+    clk.mark(kTrReduce);
     if (owner && !(p.rank == a.skip_wg && t == a.skip_step)) {
       const uint32_t hb = relu_bits(sum + x);
       const int row = p.r0 + my_row;
-      if (p.primary) a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
+      a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
       __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), region, ((S & 1u) * a.Npad + row) * 4u, 0, kPlain);
     }
+    clk.mark(kTrEpilogue);
   }
+  if (TRACE) clk.finish(trace_record(a, p), a.T);
 }
 
 
 #define PRNN_DENSE_TEAM(WT, WTAG, R, JJ) {WTAG, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<WT, R, JJ>)}
 #define PRNN_DENSE_TEAM_WIDE(R, JJ) {kF16, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<_Float16, R, JJ, true>)}
 #define PRNN_SPARSE_TEAM(VT, VTAG, R, S) {VTAG, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<VT, R, S>)}
+#define PRNN_DENSE_TEAM_TRACE(WT, WTAG, R, JJ) \
+  {WTAG, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<WT, R, JJ, false, true>)}
+#define PRNN_DENSE_TEAM_WIDE_TRACE(R, JJ) \
+  {kF16, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<_Float16, R, JJ, true, true>)}
+#define PRNN_SPARSE_TEAM_TRACE(VT, VTAG, R, S) \
+  {VTAG, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<VT, R, S, true>)}
 
 }  // namespace prnn

@@ -399,6 +399,63 @@ def test_not_supported(handle):
     handle.set_grid(0)
 
 
+# ---------------------------------------------------------------------------
+# phase tracing
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["dense_f16_n1792", "sparse10_f16_n1792", "dense_f32_n256", "sparse1_f16_n5760",
+                                  "dense_f16_n1152", "sparse10_f16_n1152"])
+def test_trace_records_phases(gpu, name):
+    """A traced run gives the untraced result bitwise; every wave of a team
+    that serves a batch row records T steps whose phase cycles add up to its
+    time loop; the other records stay zero."""
+    w = WORKLOADS[name].with_(T=48)
+    d = generate(w, seed=w.seed + 21)
+    with Handle() as h:
+        H0 = run(h, w.kind, d)
+        h.set_trace(True)
+        H1 = run(h, w.kind, d)
+        tr = h.get_trace()
+        plan = h.last_plan()
+        h.set_trace(False)
+        H2 = run(h, w.kind, d)
+    assert np.array_equal(H0, H1) and np.array_equal(H0, H2)
+    assert plan["layout"] == binding.LAYOUT_TEAM
+    grid = plan["grid"]
+    assert tr.shape == (grid * 8, binding.TRACE_WORDS)
+    rec = tr.reshape(grid, 8, binding.TRACE_WORDS).astype(np.float64)
+    serving = (np.arange(grid) % 8) < w.B
+    live = rec[serving]
+    assert np.all(live[..., 7] == w.T)
+    phases, loop = live[..., :5].sum(-1), live[..., 5]
+    assert np.all(phases <= loop) and np.all(phases >= 0.9 * loop)
+    assert np.all(rec[~serving] == 0)
+    cycles_per_tick = loop / live[..., 6]
+    assert np.all((cycles_per_tick > 5) & (cycles_per_tick < 40)), cycles_per_tick.min()
+
+
+def test_trace_floor_and_errors(gpu):
+    N, B, T = 1792, 4, 16
+    with Handle() as h:
+        with pytest.raises(PrnnError) as e:
+            h.get_trace()                       # no traced call yet
+        assert e.value.status == binding.BAD_PARAM
+        h.set_trace(True)
+        out = torch.empty((T, B, N), device="cuda")
+        h.sync_floor(N, B, T, out=out)
+        tr = h.get_trace()
+        assert int((tr[:, 7] == T).sum()) == B * (h.last_plan()["grid"] // 8) * 8
+        h.set_layout(binding.LAYOUT_SPREAD)     # trace instances are team-layout only
+        w = WORKLOADS["dense_f16_n1792"].with_(T=4)
+        g = to_dev(generate(w))
+        with pytest.raises(PrnnError) as e:
+            h.forward_dense(g["W"], g["X"], g["h0"])
+        assert e.value.status == binding.NOT_SUPPORTED
+        h.set_layout(binding.LAYOUT_AUTO)
+        h.set_trace(False)
+        h.forward_dense(g["W"], g["X"], g["h0"])
+        h.synchronize()
+
+
 @pytest.mark.parametrize("layout", [binding.LAYOUT_TEAM, binding.LAYOUT_SPREAD])
 @pytest.mark.parametrize("kind", ["dense", "sparse"])
 def test_watchdog_reports_and_recovers(gpu, kind, layout):
