@@ -52,14 +52,16 @@ __global__ void __launch_bounds__(512) floor_team_kernel(StepArgs a) {
     clk.mark(kTrStage);
     __syncthreads();
     clk.mark(kTrBarrier);
-    if (abort_flag) return;
+    int aborted_now = abort_flag;  // read with the row and tested before the stores, as in the kernels
     const float seen = t > 0 ? hrow[p.lane] : 0.f;
     clk.mark(kTrCompute);
+    asm volatile("" : "+v"(aborted_now) : "v"(seen));
+    if (aborted_now) return;
     if (p.lane < p.nr) {
       const uint32_t hb = relu_bits((float)(t + 1) + seen * 0.f);
       const int row = p.r0 + p.lane;
-      a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
       __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), region, ((S & 1u) * a.Npad + row) * 4u, 0, kPlain);
+      a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
     }
     clk.mark(kTrEpilogue);
   }

@@ -218,7 +218,9 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
     clk.mark(kTrStage);
     __syncthreads();
     clk.mark(kTrBarrier);
-    if (abort_flag) return;
+    // The abort flag is read together with the row and tested only before
+    // the stores, so it adds no LDS round trip to the step's path.
+    int aborted_now = abort_flag;
     const float x = x_next;
     xoff += xstep;
     if (t + 1 < a.T) x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
@@ -236,11 +238,14 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
     clk.mark(kTrCompute);
     const float sum = RowReduce<M>::reduce(acc, p.lane);
     clk.mark(kTrReduce);
+    asm volatile("" : "+v"(aborted_now) : "v"(sum));  // keep the test after the arithmetic
+    if (aborted_now) return;
     if (owner && !(p.rank == a.skip_wg && t == a.skip_step)) {
       const uint32_t hb = relu_bits(sum + x);
       const int row = p.r0 + my_row;
-      a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
+      // the exchange store first: the next step waits for it, not for H
       __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), region, ((S & 1u) * a.Npad + row) * 4u, 0, kPlain);
+      a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
     }
     clk.mark(kTrEpilogue);
   }
@@ -315,7 +320,9 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
     clk.mark(kTrStage);
     __syncthreads();
     clk.mark(kTrBarrier);
-    if (abort_flag) return;
+    // The abort flag is read together with the row and tested only before
+    // the stores, so it adds no LDS round trip to the step's path.
+    int aborted_now = abort_flag;
     const float x = x_next;
     xoff += xstep;
     if (t + 1 < a.T) x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
@@ -333,11 +340,14 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
     clk.mark(kTrCompute);
     const float sum = RowReduce<M>::reduce(acc, p.lane);
     clk.mark(kTrReduce);
+    asm volatile("" : "+v"(aborted_now) : "v"(sum));  // keep the test after the arithmetic
+    if (aborted_now) return;
     if (owner && !(p.rank == a.skip_wg && t == a.skip_step)) {
       const uint32_t hb = relu_bits(sum + x);
       const int row = p.r0 + my_row;
-      a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
+      // the exchange store first: the next step waits for it, not for H
       __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), region, ((S & 1u) * a.Npad + row) * 4u, 0, kPlain);
+      a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
     }
     clk.mark(kTrEpilogue);
   }
