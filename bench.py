@@ -454,6 +454,27 @@ def main():
         detail[w.name]["plan"] = {k: v for k, v in h.last_plan().items() if k != "first_step"}
     detail["sync_floor_us_per_step"] = round(floor_us, 3)
     detail["sync_floor_ms_per_call"] = round(f_full, 4)
+
+    # the dense layer on the matrix cores (h as fp16 hi + lo), not in the headline step
+    from persistent_rnn_fwd_amd import binding as _b
+    h.set_math(_b.MATH_SPLIT)
+    full = timed(lambda: call(wd.name))
+    half = timed(lambda: call(wd.name, T // 2))
+    step_us = (full - half) * 1e3 / (T - T // 2)
+    h.synchronize()
+    split = {"ms_per_call": round(full, 4), "us_per_step_slope": round(step_us, 3),
+             "vs_sync_floor": round(step_us / floor_us, 3) if floor_us > 0 else None,
+             "plan": {k: v for k, v in h.last_plan().items() if k != "first_step"}}
+    if not args.no_check:
+        import oracle
+        call(wd.name)
+        h.synchronize()
+        d = host[wd.name]
+        split["max_err_ratio"] = round(float(oracle.tolerance_ratio(out[wd.name].cpu().numpy(),
+                                                                    oracle.forward_dense(d["W"], d["X"], d["h0"]),
+                                                                    oracle.TOL_F16)), 5)
+    h.set_math(_b.MATH_AUTO)
+    detail["dense_f16_n1792_split_math"] = split
     detail["timed_launch_ms"] = {"dense_f16_n1792": percentiles(dense_list), "sparse10_f16_n1792": percentiles(sparse_list)}
     sd, ss = detail[wd.name]["us_per_step_slope"], detail[ws.name]["us_per_step_slope"]
     detail["dense_over_sparse10_step_time"] = round(sd / ss, 3) if ss > 0 else None

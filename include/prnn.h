@@ -113,6 +113,20 @@ typedef enum {
   PRNN_LAYOUT_TEAM = 2
 } prnnLayout_t;
 
+/* How the dense fp16 recurrence forms W h_{t-1}.
+ * EXACT: fp32 h times the exactly widened fp16 weights, fp32 sums (VALU).
+ * SPLIT: h enters as two fp16 values, hi = fp16(h) and lo = fp16(h - hi), and
+ *   the matrix cores form W hi + W lo with exact products and fp32 sums: the
+ *   product sees h to about 2^-22 of |h| (fp32 h carries 2^-24).  Needs
+ *   |h| < 65504; a larger value makes the call report EXECUTION_FAILED.
+ *   TEAM layout, fp16 W, N <= 2048 only (else NOT_SUPPORTED).
+ * AUTO: EXACT.  fp32 weights and sparse layers always use EXACT. */
+typedef enum {
+  PRNN_MATH_AUTO = 0,
+  PRNN_MATH_EXACT = 1,
+  PRNN_MATH_SPLIT = 2
+} prnnMath_t;
+
 /* Launch plan of the last forward call on a handle (for tests and reports). */
 typedef struct {
   int layout;        /* PRNN_LAYOUT_SPREAD or PRNN_LAYOUT_TEAM                 */
@@ -124,6 +138,8 @@ typedef struct {
   int lds_bytes;     /* dynamic LDS per workgroup                              */
   int relay_slice;   /* SPREAD: words of h each workgroup relays (0: DIRECT)   */
   uint64_t first_step; /* ring step counter of the call's first timestep       */
+  int math;          /* PRNN_MATH_EXACT or PRNN_MATH_SPLIT (rows_per_wave and
+                        rmax then count rows per workgroup)                   */
 } prnnPlanInfo_t;
 
 /* Creates a handle bound to the current HIP device.
@@ -187,6 +203,10 @@ prnnStatus_t prnn_set_exchange(prnnHandle_t handle, prnnExchange_t mode);
  * cannot use makes forward calls return NOT_SUPPORTED.  BAD_PARAM for an
  * unknown layout.  The exchange mode applies to the SPREAD layout only. */
 prnnStatus_t prnn_set_layout(prnnHandle_t handle, prnnLayout_t layout);
+
+/* Math of the dense fp16 path for later calls (default AUTO; see
+ * prnnMath_t).  BAD_PARAM for an unknown mode. */
+prnnStatus_t prnn_set_math(prnnHandle_t handle, prnnMath_t mode);
 
 /* Upper bound, in microseconds, on one wait for h_{t-1} (default 200000).
  * A wait that exceeds it stops the run and reports EXECUTION_FAILED. */

@@ -27,6 +27,7 @@ SUCCESS, BAD_PARAM, NOT_SUPPORTED, ALLOC_FAILED, EXECUTION_FAILED, INTERNAL_ERRO
 DATA_FLOAT, DATA_HALF = 0, 1
 EXCHANGE_AUTO, EXCHANGE_DIRECT, EXCHANGE_RELAY = 0, 1, 2
 LAYOUT_AUTO, LAYOUT_SPREAD, LAYOUT_TEAM = 0, 1, 2
+MATH_AUTO, MATH_EXACT, MATH_SPLIT = 0, 1, 2
 TRACE_WORDS = 8  # per-wave trace record: see Handle.get_trace
 
 # Every function include/prnn.h declares, with its ctypes signature.
@@ -44,6 +45,7 @@ SIGNATURES = {
     "prnn_set_watchdog_us": (_I, [_H, ctypes.c_uint32]),
     "prnn_set_exchange": (_I, [_H, _I]),
     "prnn_set_layout": (_I, [_H, _I]),
+    "prnn_set_math": (_I, [_H, _I]),
     "prnn_get_last_plan": (_I, [_H, _P]),
     "prnn_debug_skip_publish": (_I, [_H, _I, _I]),
     "prnn_set_trace": (_I, [_H, _I]),
@@ -63,6 +65,7 @@ class PlanInfo(ctypes.Structure):
         ("lds_bytes", ctypes.c_int),
         ("relay_slice", ctypes.c_int),
         ("first_step", ctypes.c_uint64),
+        ("math", ctypes.c_int),
     ]
 
     def as_dict(self):
@@ -160,6 +163,10 @@ class Handle:
     def set_layout(self, layout: int):
         """LAYOUT_AUTO, LAYOUT_SPREAD or LAYOUT_TEAM for later calls."""
         _check("prnn_set_layout", self._lib.prnn_set_layout(self._h, int(layout)))
+
+    def set_math(self, mode: int):
+        """MATH_AUTO, MATH_EXACT or MATH_SPLIT (dense fp16) for later calls."""
+        _check("prnn_set_math", self._lib.prnn_set_math(self._h, int(mode)))
 
     def set_watchdog_us(self, us: int):
         _check("prnn_set_watchdog_us", self._lib.prnn_set_watchdog_us(self._h, int(us)))

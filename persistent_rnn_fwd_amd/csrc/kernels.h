@@ -70,6 +70,10 @@ extern const void* kPlacementKernel;
 // Team layout: the protocol-only kernel, and the ring reset in which every XCD
 // fills its own [2][npad] region of the [8][2][npad] ring.
 extern const void* kFloorTeamKernel;
+// Dense fp16 team layout on the matrix cores (rmax = rows per workgroup,
+// cap = 8 chunks of 256 columns, one per wave).
+extern const KernelEntry kDenseTeamMfmaKernels[];
+extern const KernelEntry kDenseTeamMfmaTraceKernels[];
 // Trace instances (team layout only): the same kernels with phase timing.
 extern const KernelEntry kDenseTeamF16TraceKernels[];
 extern const KernelEntry kDenseTeamF32TraceKernels[];

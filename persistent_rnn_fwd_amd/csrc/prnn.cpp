@@ -38,6 +38,7 @@ struct prnnContext {
   uint64_t relay_next_step = 0;
   int forced_grid = 0;
   uint32_t watchdog_us = 200000;
+  int math = PRNN_MATH_AUTO;
   int skip_wg = -1;
   int skip_step = -1;
   prnnPlanInfo_t last_plan{};
@@ -65,6 +66,7 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 
 struct Plan {
   int layout = PRNN_LAYOUT_SPREAD;
+  int math = PRNN_MATH_EXACT;
   int grid = 0, block = 0;
   int G = 0;                 // spread: workgroups per batch group; team: workgroups per XCD
   int waves = 0;             // waves per workgroup
@@ -156,6 +158,23 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
   p->max_rows = (N + Q - 1) / Q;
   p->chunks = (N + 255) / 256;
   const int Npad = (N + 3) & ~3;
+  if (kind == kDense && wt == prnn::kF16 && h->math == PRNN_MATH_SPLIT) {
+    // Matrix cores: 16 TR rows per workgroup, one 256-column chunk per wave.
+    if (p->chunks > 8) return false;
+    const int cap = h->forced_grid > 0 ? h->forced_grid / 8 : std::min(kTeamMaxWgPerXcd, h->num_cu / 8);
+    int TR = 1;
+    while (TR <= 4 && (N + 16 * TR - 1) / (16 * TR) > cap) ++TR;
+    if (TR > 4) return false;
+    const int Pm = h->forced_grid > 0 ? cap : (N + 16 * TR - 1) / (16 * TR);
+    p->math = PRNN_MATH_SPLIT;
+    p->G = Pm;
+    p->grid = 8 * Pm;
+    p->max_rows = 16 * TR;
+    p->k = pick(h->trace ? prnn::kDenseTeamMfmaTraceKernels : prnn::kDenseTeamMfmaKernels, 16 * TR, 8);
+    if (p->k == nullptr) return false;
+    p->lds_bytes = 8 * 520 * 2 + 2 * 8 * p->k->rmax * 4;  // per-wave fp16 hi/lo/zero slots + partials
+    return (size_t)p->lds_bytes + 256 <= h->lds_per_block;
+  }
   if (kind == kDense) {
     const KernelEntry* table = h->trace ? (wt == prnn::kF32 ? prnn::kDenseTeamF32TraceKernels : prnn::kDenseTeamF16TraceKernels)
                                         : (wt == prnn::kF32 ? prnn::kDenseTeamF32Kernels : prnn::kDenseTeamF16Kernels);
@@ -316,6 +335,7 @@ prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream
   info.chunks = p.k->cap;
   info.lds_bytes = p.lds_bytes;
   info.relay_slice = p.relay_slice;
+  info.math = p.math;
   info.first_step = h->step;
   h->have_plan = true;
   h->trace_records = h->trace ? p.grid * 8 : 0;
@@ -454,6 +474,13 @@ prnnStatus_t prnn_set_layout(prnnHandle_t h, prnnLayout_t layout) {
   if (layout != PRNN_LAYOUT_AUTO && layout != PRNN_LAYOUT_SPREAD && layout != PRNN_LAYOUT_TEAM)
     return PRNN_STATUS_BAD_PARAM;
   h->layout = layout;
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t prnn_set_math(prnnHandle_t h, prnnMath_t mode) {
+  if (h == nullptr) return PRNN_STATUS_BAD_PARAM;
+  if (mode != PRNN_MATH_AUTO && mode != PRNN_MATH_EXACT && mode != PRNN_MATH_SPLIT) return PRNN_STATUS_BAD_PARAM;
+  h->math = mode;
   return PRNN_STATUS_SUCCESS;
 }
 

@@ -1,5 +1,6 @@
 // fp16 instances of the team-layout kernels (rows per wave, chunks / pair slots).
 #include "team_kernel.h"
+#include "team_mfma.h"
 
 namespace prnn {
 
@@ -36,6 +37,16 @@ const KernelEntry kDenseTeamF16TraceKernels[] = {
 const KernelEntry kSparseTeamF16TraceKernels[] = {
     PRNN_SPARSE_TEAM_TRACE(_Float16, kF16, 5, 2), PRNN_SPARSE_TEAM_TRACE(_Float16, kF16, 7, 1),
     PRNN_SPARSE_TEAM_TRACE(_Float16, kF16, 7, 3), PRNN_SPARSE_TEAM_TRACE(_Float16, kF16, 23, 1),
+    {0, 0, 0, nullptr},
+};
+
+// Matrix-core dense instances: 16, 32, 48, 64 rows per workgroup.
+const KernelEntry kDenseTeamMfmaKernels[] = {
+    PRNN_DENSE_TEAM_MFMA(1), PRNN_DENSE_TEAM_MFMA(2), PRNN_DENSE_TEAM_MFMA(3), PRNN_DENSE_TEAM_MFMA(4),
+    {0, 0, 0, nullptr},
+};
+const KernelEntry kDenseTeamMfmaTraceKernels[] = {
+    PRNN_DENSE_TEAM_MFMA_TRACE(3), PRNN_DENSE_TEAM_MFMA_TRACE(4),
     {0, 0, 0, nullptr},
 };
 

@@ -479,3 +479,111 @@ def test_watchdog_reports_and_recovers(gpu, kind, layout):
         H = fwd()                 # the ring was reset: a clean run works again
         h.synchronize()
         assert_parity(H.cpu().numpy(), reference(kind, d), oracle.TOL_F16)
+
+
+# ---------------------------------------------------------------------------
+# dense fp16 on the matrix cores (MATH_SPLIT: h as fp16 hi + lo)
+# ---------------------------------------------------------------------------
+def run_split(handle, d, grid=0, h0=True):
+    handle.set_math(binding.MATH_SPLIT)
+    try:
+        H = run(handle, "dense", d, grid=grid, h0=h0)
+        assert handle.last_plan()["math"] == binding.MATH_SPLIT
+    finally:
+        handle.set_math(binding.MATH_AUTO)
+    return H
+
+
+@pytest.mark.parametrize("name", ["dense_f16_n1152", "dense_f16_n1792"])
+def test_split_parity_workloads(handle, name):
+    w = WORKLOADS[name]
+    d = generate(w, seed=w.seed + 3000)
+    H = run_split(handle, d)
+    assert_parity(H, reference("dense", d), oracle.TOL_F16, name)
+    p = handle.last_plan()
+    assert p["layout"] == binding.LAYOUT_TEAM and p["waves_per_wg"] == 8
+
+
+@pytest.mark.parametrize("N,B,T,grid", [(1, 1, 3, 0), (3, 2, 4, 0), (7, 3, 5, 0), (100, 4, 6, 0), (257, 5, 4, 0),
+                                        (1000, 8, 3, 0), (2048, 4, 3, 0), (1792, 4, 5, 240), (1152, 2, 6, 256)])
+def test_split_shapes(handle, N, B, T, grid):
+    w = Workload(f"dense_{N}", "dense", N, B, T, "f16", seed=N * 13 + B, h0="randn")
+    d = generate(w)
+    H = run_split(handle, d, grid=grid)
+    assert_parity(H, reference("dense", d), oracle.TOL_F16, f"N={N} B={B} grid={grid} {handle.last_plan()}")
+
+
+def test_split_closed_forms_bitwise(handle):
+    """hi + lo holds small integers exactly, so the closed forms stay exact."""
+    rng = np.random.default_rng(41)
+    T, B, N = 30, 4, 1792
+    X = rng.integers(0, 100, size=(T, B, N)).astype(np.float32)
+    h0 = rng.integers(0, 100, size=(B, N)).astype(np.float32)
+    expect = h0[None].astype(np.float64) + np.cumsum(X.astype(np.float64), axis=0)
+    np.testing.assert_array_equal(run_split(handle, {"W": np.eye(N, dtype=np.float16), "X": X, "h0": h0}), expect)
+    Xr = rng.standard_normal((T, B, N)).astype(np.float32)
+    np.testing.assert_array_equal(run_split(handle, {"W": np.zeros((N, N), np.float16), "X": Xr, "h0": h0}),
+                                  np.maximum(Xr, 0))
+    N = 1152
+    Xs = rng.integers(0, 9, size=(12, 2, N)).astype(np.float32)
+    hs = rng.integers(0, 9, size=(2, N)).astype(np.float32)
+    Wd = np.zeros((N, N), np.float16)
+    Wd[np.arange(N), (np.arange(N) + 1) % N] = 1
+    np.testing.assert_array_equal(run_split(handle, {"W": Wd, "X": Xs, "h0": hs}), oracle.forward_dense(Wd, Xs, hs))
+
+
+def test_split_close_to_exact_deterministic_and_chunkable(handle):
+    w = WORKLOADS["dense_f16_n1792"].with_(T=40, h0="randn")
+    d = generate(w, seed=43)
+    He = run(handle, "dense", d)
+    Hs = run_split(handle, d)
+    assert np.all(np.abs(Hs - He) <= 2e-5 * (1 + np.abs(He)))
+    np.testing.assert_array_equal(run_split(handle, d), Hs)
+    Ha = run_split(handle, dict(d, X=d["X"][:17]))
+    Hb = run_split(handle, dict(d, X=d["X"][17:], h0=Ha[-1]))
+    np.testing.assert_array_equal(np.concatenate([Ha, Hb]), Hs)
+
+
+def test_split_range_reported(gpu):
+    """|h| beyond the fp16 range of the split is reported, then the handle recovers."""
+    w = WORKLOADS["dense_f16_n1792"].with_(T=6)
+    d = generate(w, seed=44)
+    d["X"] = d["X"].copy()
+    d["X"][2, 1, 7] = 1e6
+    with Handle() as h:
+        h.set_math(binding.MATH_SPLIT)
+        g = to_dev(d)
+        h.forward_dense(g["W"], g["X"], g["h0"])
+        with pytest.raises(PrnnError) as e:
+            h.synchronize()
+        assert e.value.status == binding.EXECUTION_FAILED
+        h.set_math(binding.MATH_EXACT)
+        H = h.forward_dense(g["W"], g["X"], g["h0"])
+        h.synchronize()
+        assert_parity(H.cpu().numpy(), reference("dense", d), oracle.TOL_F16)
+
+
+def test_split_trace_and_watchdog(gpu):
+    w = WORKLOADS["dense_f16_n1792"].with_(T=24)
+    d = generate(w, seed=45)
+    with Handle() as h:
+        h.set_math(binding.MATH_SPLIT)
+        H0 = run(h, "dense", d)
+        h.set_trace(True)
+        H1 = run(h, "dense", d)
+        tr = h.get_trace()
+        h.set_trace(False)
+        np.testing.assert_array_equal(H0, H1)
+        live = tr[tr[:, 7] == w.T].astype(np.float64)
+        assert live.shape[0] == 4 * (h.last_plan()["grid"] // 8) * 8
+        assert np.all(live[:, :5].sum(1) <= live[:, 5])
+        h.set_watchdog_us(2000)
+        h.debug_skip_publish(3, 5)
+        g = to_dev(d)
+        h.forward_dense(g["W"], g["X"], g["h0"])
+        with pytest.raises(PrnnError) as e:
+            h.synchronize()
+        assert e.value.status == binding.EXECUTION_FAILED
+        H2 = h.forward_dense(g["W"], g["X"], g["h0"])
+        h.synchronize()
+        np.testing.assert_array_equal(H2.cpu().numpy(), H0)
