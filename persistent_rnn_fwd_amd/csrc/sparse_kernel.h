@@ -123,6 +123,25 @@ __device__ __forceinline__ void place_rows_bank_aware(P (&pr)[RW][SPR], int nr, 
   }
 }
 
+// Loads rows [R, RW) of a register-resident pair block and places each one
+// before the next row's loads are issued: with every row's loads in flight
+// at once the largest blocks would not fit the registers.
+template <int R, int RW, typename P, int SPR>
+__device__ __forceinline__ void load_place_rows(P (&pr)[RW][SPR], const int16_t* col, const void* val, int r0, int nr,
+                                                int spr, int K, int n, int lane, uint2* scratch) {
+  if constexpr (R < RW) {
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) {
+      const int k = 64 * s + lane;
+      const bool live = R < nr && s < spr && k < K;
+      pr[R][s].load(col, val, live ? (size_t)(r0 + R) * K + k : 0, live, n);
+    }
+    if (R < nr) place_row_bank_aware<P, SPR>(pr[R], spr, K, n, lane, scratch);
+    asm volatile("" ::: "memory");
+    load_place_rows<R + 1, RW, P, SPR>(pr, col, val, r0, nr, spr, K, n, lane, scratch);
+  }
+}
+
 constexpr int kStageChunks = 8;  // 16-byte loads in flight per lane while staging h
 
 // RMAX rows per workgroup are computed (padding rows carry zero values and
@@ -231,8 +250,13 @@ __global__ void __launch_bounds__(256) sparse_kernel(StepArgs a) {
 #pragma unroll
     for (int s = 0; s < SPR; ++s) {
       if (s < spr) {
+        // The slot's gathers all go out before its first FMA (inline asm,
+        // which the compiler does not move loads across).
+        float hv[RMAX];
 #pragma unroll
-        for (int r = 0; r < RMAX; ++r) pr[r][s].fma(acc[r], hb[pr[r][s].column()]);
+        for (int r = 0; r < RMAX; ++r) hv[r] = hb[pr[r][s].column()];
+#pragma unroll
+        for (int r = 0; r < RMAX; ++r) pr[r][s].fma(acc[r], hv[r]);
       }
     }
 

@@ -25,6 +25,9 @@ const KernelEntry kSparseTeamF16Kernels[] = {
     PRNN_SPARSE_TEAM(_Float16, kF16, 5, 2), PRNN_SPARSE_TEAM(_Float16, kF16, 7, 1), PRNN_SPARSE_TEAM(_Float16, kF16, 7, 3),
     PRNN_SPARSE_TEAM(_Float16, kF16, 8, 3), PRNN_SPARSE_TEAM(_Float16, kF16, 16, 1), PRNN_SPARSE_TEAM(_Float16, kF16, 23, 1),
     PRNN_SPARSE_TEAM(_Float16, kF16, 24, 1), PRNN_SPARSE_TEAM(_Float16, kF16, 32, 1),
+    // 2304-neuron layers at 10 % / 25 % (padded unbalanced rows up to 1024 pairs); 5760 at 5 %
+    PRNN_SPARSE_TEAM(_Float16, kF16, 9, 4), PRNN_SPARSE_TEAM(_Float16, kF16, 9, 9), PRNN_SPARSE_TEAM(_Float16, kF16, 9, 10),
+    PRNN_SPARSE_TEAM(_Float16, kF16, 23, 5),
     {0, 0, 0, nullptr},
 };
 

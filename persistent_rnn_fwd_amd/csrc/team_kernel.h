@@ -275,18 +275,11 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
     return;
   }
 
+  // The owned rows' pairs into registers, each row in bank-aware order so
+  // that the gathers below hit distinct LDS banks.
   Pair<VT> pr[RW][SPR];
-#pragma unroll
-  for (int r = 0; r < RW; ++r)
-#pragma unroll
-    for (int s = 0; s < SPR; ++s) {
-      const int k = 64 * s + p.lane;
-      const bool live = r < p.nr && s < a.spr && k < K;
-      pr[r][s].load(reinterpret_cast<const int16_t*>(a.W), a.V, live ? (size_t)(p.r0 + r) * K + k : 0, live, N);
-    }
-  // Bank-aware order of each row's pairs, so the gathers below hit distinct
-  // LDS banks.
-  place_rows_bank_aware<0, RW, Pair<VT>, SPR>(pr, p.nr, a.spr, K, N, p.lane, place_scratch[p.wave]);
+  load_place_rows<0, RW, Pair<VT>, SPR>(pr, reinterpret_cast<const int16_t*>(a.W), a.V, p.r0, p.nr, a.spr, K, N,
+                                        p.lane, place_scratch[p.wave]);
 
   const __amdgpu_buffer_rsrc_t region = team_region(a);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
@@ -333,8 +326,14 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
 #pragma unroll
     for (int s = 0; s < SPR; ++s) {
       if (s < a.spr) {
+        // All of the slot's gathers are issued before its first FMA, so
+        // their LDS latencies overlap (the FMA is inline asm, which the
+        // compiler does not move loads across).
+        float hv[RW];
 #pragma unroll
-        for (int r = 0; r < RW; ++r) pr[r][s].fma(acc[r], hrow[pr[r][s].column()]);
+        for (int r = 0; r < RW; ++r) hv[r] = hrow[pr[r][s].column()];
+#pragma unroll
+        for (int r = 0; r < RW; ++r) pr[r][s].fma(acc[r], hv[r]);
       }
     }
     clk.mark(kTrCompute);

@@ -21,6 +21,14 @@ Value distributions (the pages state none):
   X         ~ N(0, 1)           fp32, the pre-activations W_x x_t + b
   h0        = 0                 (or |N(0,1)| when asked for)
 
+Unbalanced rows ("magnitude" pruning), for the pages' load-balanced vs
+unbalanced pruning comparison: a dense Gaussian matrix whose rows carry
+log-normal scales exp(N(0, 0.1^2)) is pruned by keeping the N K largest
+magnitudes of the whole matrix, so rows keep different numbers of entries
+(K on average); each row's kept values are rescaled to L2 norm 0.8 and the
+rows are stored in the row-balanced format at the width of the longest row,
+padded with distinct unused columns of value 0.
+
 Random streams: ``numpy.random.SeedSequence(seed).spawn(3)`` gives independent
 generators for W, X and h0, in that order.  fp16 weights are produced by
 rounding the fp64 draw to the nearest fp16 (numpy's round-to-nearest-even);
@@ -48,6 +56,7 @@ class Workload:
     K: int = 0           # nonzeros per row (sparse only)
     seed: int = 0
     h0: str = "zeros"    # "zeros" or "randn" (|N(0,1)|)
+    rows: str = "balanced"  # sparse: "balanced" (K per row) or "magnitude" (K on average, padded)
 
     @property
     def nnz(self) -> int:
@@ -80,6 +89,10 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("sparse10_f16_n1792", "sparse", 1792, 4, 256, "f16", K=179, seed=104),
         Workload("sparse1_f16_n1792", "sparse", 1792, 4, 256, "f16", K=18, seed=104),
         Workload("sparse1_f16_n5760", "sparse", 5760, 4, 256, "f16", K=58, seed=105),
+        Workload("sparse10_f16_n2304", "sparse", 2304, 4, 256, "f16", K=230, seed=106),
+        Workload("sparse25_f16_n2304", "sparse", 2304, 4, 256, "f16", K=576, seed=107),
+        Workload("sparse10u_f16_n2304", "sparse", 2304, 4, 256, "f16", K=230, seed=106, rows="magnitude"),
+        Workload("sparse5_f16_n5760", "sparse", 5760, 4, 256, "f16", K=288, seed=108),
     ]
 }
 
@@ -106,6 +119,33 @@ def draw_sparse_pattern(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
     return col
 
 
+def draw_magnitude_pruned(rng: np.random.Generator, N: int, K: int, wdt, sigma: float = 0.1):
+    """Unbalanced sparse W (see the module docstring), stored row-balanced at
+    the width of the longest row: returns (col int16 [N, Kmax], val [N, Kmax])."""
+    if not 1 <= K <= N or N > 32767:
+        raise ValueError("need 1 <= K <= N <= 32767")
+    scale = np.exp(rng.normal(0.0, sigma, size=N))
+    g = rng.standard_normal((N, N)) * scale[:, None]
+    mag = np.abs(g)
+    thr = np.partition(mag.ravel(), mag.size - N * K)[mag.size - N * K]
+    keep = mag >= thr
+    empty = ~keep.any(axis=1)                    # every row keeps at least its largest entry
+    keep[empty, np.argmax(mag[empty], axis=1)] = True
+    kmax = int(keep.sum(axis=1).max())
+    col = np.empty((N, kmax), dtype=np.int16)
+    val = np.zeros((N, kmax), dtype=np.float64)
+    for i in range(N):
+        real = np.flatnonzero(keep[i])
+        v = g[i, real]
+        v = v * (0.8 / np.sqrt(np.sum(v * v)))
+        pad = np.flatnonzero(~keep[i])[: kmax - real.size]   # distinct unused columns, value 0
+        c = np.concatenate([real, pad])
+        order = np.argsort(c)
+        col[i] = c[order]
+        val[i] = np.concatenate([v, np.zeros(pad.size)])[order]
+    return col, val.astype(wdt)
+
+
 def generate(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Draw one problem.
 
@@ -121,6 +161,8 @@ def generate(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
     wdt = _np_dtype(w.w_dtype)
     if w.kind == "dense":
         out["W"] = (rng_w.standard_normal((w.N, w.N)) * (0.8 / np.sqrt(w.N))).astype(wdt)
+    elif w.kind == "sparse" and w.rows == "magnitude":
+        out["col"], out["val"] = draw_magnitude_pruned(rng_w, w.N, w.K, wdt)
     elif w.kind == "sparse":
         out["col"] = draw_sparse_pattern(rng_w, w.N, w.K)
         out["val"] = (rng_w.standard_normal((w.N, w.K)) * (0.8 / np.sqrt(w.K))).astype(wdt)

@@ -310,6 +310,29 @@ def test_generator_sparse_pattern_and_values():
     assert not np.array_equal(d3["col"], col)
 
 
+def test_generator_magnitude_pruned_rows():
+    """Unbalanced rows: K kept entries per row on average, stored at the longest
+    row's width with zero-valued padding on distinct unused columns; kept
+    values have row norm 0.8."""
+    w = WORKLOADS["sparse10u_f16_n2304"]
+    d = generate(w)
+    col, val = d["col"].astype(np.int64), d["val"].astype(np.float64)
+    N = w.N
+    assert col.shape == val.shape and col.shape[0] == N and col.shape[1] > w.K
+    assert (np.diff(col, axis=1) > 0).all() and col.min() >= 0 and col.max() < N
+    kept = (val != 0).sum(axis=1)
+    assert abs(kept.mean() - w.K) < 0.01 * w.K          # fp16 zeros of tiny values aside
+    assert kept.max() == col.shape[1] or kept.max() >= 0.98 * col.shape[1]
+    assert kept.max() > 1.3 * w.K                        # rows really are unbalanced
+    norms = np.sqrt((val * val).sum(axis=1))
+    assert np.allclose(norms, 0.8, rtol=2e-3)
+    # the padded form is the same matrix as the unpadded one: sparse == dense copy
+    X = generate(w.with_(T=3))["X"]
+    Wd = oracle.sparse_to_dense(d["col"], d["val"], N)
+    np.testing.assert_allclose(oracle.forward_sparse(d["col"], d["val"], X, None),
+                               oracle.forward_dense(Wd, X, None), rtol=1e-12, atol=1e-12)
+
+
 @pytest.mark.parametrize("name", ["dense_f32_n256", "sparse10_f16_n1152"])
 def test_generator_spectral_radius_near_0p8(name):
     w = WORKLOADS[name]
