@@ -103,9 +103,9 @@ typedef enum {
  *  TEAM:   each of the 8 XCDs runs one batch row's whole recurrence with up
  *          to 32 workgroups of 8 waves; a wave owns a few rows of W.  h_{t-1}
  *          is exchanged inside the XCD's L2 only.  With B < 8 the remaining
- *          XCDs recompute batch rows redundantly (they do not write H), so
- *          every XCD's exchange memory is updated at every step.  Holds W
- *          once per XCD: for dense fp16 W up to N = 2048.
+ *          XCDs compute nothing; they only mark their exchange memory as
+ *          written for the call's last steps.  Holds W once per XCD: for
+ *          dense fp16 W up to N = 2048.
  *  AUTO:   TEAM when an instance fits, else SPREAD (the default). */
 typedef enum {
   PRNN_LAYOUT_AUTO = 0,

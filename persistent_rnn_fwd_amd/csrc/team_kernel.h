@@ -3,9 +3,8 @@
 // The grid is 8 teams of P workgroups; the workgroups of one team share
 // blockIdx % 8 and therefore one XCD (workgroups are dealt to the 8 XCDs
 // round-robin; checked once per handle).  Team x serves batch row x % B.
-// With B < 8 the teams x >= B recompute a batch row another team owns and do
-// not write H: every XCD then takes part in every step, so every XCD's
-// exchange region is written at every step (see below).
+// With B < 8 the teams x >= B compute nothing: they stamp their region with
+// the tags of the call's last two steps and leave (team_stamp_tail).
 //
 // Within a team, the N rows of W are split over its P * 8 waves (balanced to
 // within one row); a wave keeps its rows in registers for all T steps.  Per
