@@ -8,7 +8,8 @@ Pins: every function here is checked in ``tests/test_oracle.py`` against
 brute force in exact rational arithmetic, closed forms (W = 0, W = I, cyclic
 permutations, the linear regime's block-triangular solve, diagonal W),
 invariants (batch independence, chunking in time, positive homogeneity) and a
-hand-worked example under ``tests/golden/``.
+hand-worked example under ``tests/golden/``.  The projection, layer and stack
+functions (``oracle.layer``) are pinned in ``tests/test_oracle_layer.py``.
 """
 from .rnn import (  # noqa: F401
     TOL_F16,
@@ -17,4 +18,10 @@ from .rnn import (  # noqa: F401
     forward_sparse,
     sparse_to_dense,
     tolerance_ratio,
+)
+from .layer import (  # noqa: F401
+    forward_layer_dense,
+    forward_layer_sparse,
+    forward_stack_dense,
+    project,
 )

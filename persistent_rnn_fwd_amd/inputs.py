@@ -29,6 +29,16 @@ magnitudes of the whole matrix, so rows keep different numbers of entries
 rows are stored in the row-balanced format at the width of the longest row,
 padded with distinct unused columns of value 0.
 
+Layers (input projection + recurrence, "Optimizing Performance of Recurrent
+Neural Networks on GPUs", Abstract): on top of a recurrence workload, the
+layer input x ~ N(0, 1) fp32 [T, B, I], U ~ N(0, 1 / I) rounded to fp16 [N, I]
+and bias ~ N(0, 0.1^2) fp32 [N], so that U x has the N(0, 1) scale of the
+recurrence workloads' X.  The pages give no input width; I = N (a layer of a
+stack, whose input is the layer below's output) is the plain reading.  These
+arrays come from their own streams, ``SeedSequence([seed, 1, I]).spawn(3)``.
+A stack of L layers draws layer l's U, bias and W from
+``SeedSequence([seed, 2, l]).spawn(3)``.
+
 Random streams: ``numpy.random.SeedSequence(seed).spawn(3)`` gives independent
 generators for W, X and h0, in that order.  fp16 weights are produced by
 rounding the fp64 draw to the nearest fp16 (numpy's round-to-nearest-even);
@@ -176,3 +186,51 @@ def generate(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
     else:
         raise ValueError(f"unknown h0 mode {w.h0!r}")
     return out
+
+
+# Layers: a recurrence workload plus its input width I.
+LAYER_WORKLOADS: Dict[str, tuple] = {
+    "layer_dense_f16_n1792": ("dense_f16_n1792", 1792),
+    "layer_sparse10_f16_n1792": ("sparse10_f16_n1792", 1792),
+}
+
+
+def generate_layer(w: Workload, I: int, seed: Optional[int] = None, x_dtype: str = "f32") -> Dict[str, np.ndarray]:
+    """``generate(w)`` (W or col/val, h0; its X is not used by a layer) plus
+    ``U`` float16 [N, I], ``bias`` float32 [N] and the layer input ``x``
+    [T, B, I] (float32, or float16 with x_dtype="f16")."""
+    seed = w.seed if seed is None else seed
+    out = generate(w, seed)
+    s_u, s_b, s_x = np.random.SeedSequence([seed, 1, I]).spawn(3)
+    rng_u, rng_b, rng_x = (np.random.default_rng(t) for t in (s_u, s_b, s_x))
+    out["U"] = (rng_u.standard_normal((w.N, I)) / np.sqrt(I)).astype(np.float16)
+    out["bias"] = (0.1 * rng_b.standard_normal(w.N)).astype(np.float32)
+    out["x"] = rng_x.standard_normal((w.T, w.B, I)).astype(_np_dtype(x_dtype))
+    return out
+
+
+def generate_stack(w: Workload, L: int, seed: Optional[int] = None) -> Dict[str, object]:
+    """L dense layers of width N = I = w.N: ``layers`` = [{U, bias, W}] (fp16
+    U and W as in ``generate_layer`` and ``generate``), the input ``x`` fp32
+    [T, B, N] and per-layer ``h0s`` (zeros, or |N(0,1)| with w.h0 == "randn")."""
+    if w.kind != "dense":
+        raise ValueError("stacks are dense")
+    seed = w.seed if seed is None else seed
+    base = generate_layer(w, w.N, seed)
+    layers, h0s = [], []
+    for l in range(L):
+        s_u, s_b, s_w = np.random.SeedSequence([seed, 2, l]).spawn(3)
+        rng_u, rng_b, rng_w = (np.random.default_rng(t) for t in (s_u, s_b, s_w))
+        layers.append({
+            "U": (rng_u.standard_normal((w.N, w.N)) / np.sqrt(w.N)).astype(np.float16),
+            "bias": (0.1 * rng_b.standard_normal(w.N)).astype(np.float32),
+            "W": (rng_w.standard_normal((w.N, w.N)) * (0.8 / np.sqrt(w.N))).astype(_np_dtype(w.w_dtype)),
+        })
+        if l == 0:
+            h0 = base["h0"]
+        elif w.h0 == "randn":
+            h0 = np.abs(rng_b.standard_normal((w.B, w.N))).astype(np.float32)
+        else:
+            h0 = np.zeros((w.B, w.N), dtype=np.float32)
+        h0s.append(h0)
+    return {"layers": layers, "x": base["x"], "h0s": h0s}
