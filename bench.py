@@ -65,6 +65,7 @@ def parse():
     ap.add_argument("--only-timed", action="store_true",
                     help="run only warmup + the timed region (every launch is a T=256 call; for profiles)")
     ap.add_argument("--no-baselines", action="store_true", help="skip the library and torch-CPU loop baselines")
+    ap.add_argument("--no-layers", action="store_true", help="skip the whole-layer (projection + recurrence) table")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config table (every workload, not timed "
                     "in the headline step)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -285,6 +286,58 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
     return rows
 
 
+MFMA_F16_PEAK = 2.5e15  # MI355X dense fp16 matrix peak, flop/s
+
+
+def layer_table(torch, dev, Handle, timed, no_check=False):
+    """Whole layers (input projection + recurrence) at the layer sizes: the
+    projection's time and its throughput against the fp16 matrix peak
+    (algorithmic flops 2 M N I; fp32 x issues twice the products, hi and lo),
+    the layer's timesteps/s, and the error ratios against the oracle."""
+    import numpy as np
+    from persistent_rnn_fwd_amd.inputs import LAYER_WORKLOADS, WORKLOADS, generate_layer
+    rows = {}
+    h = Handle()
+    for name, (base, I) in LAYER_WORKLOADS.items():
+        w = WORKLOADS[base]
+        d = generate_layer(w, I)
+        g = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in d.items()}
+        T, B, N = w.T, w.B, w.N
+        Xw = torch.empty((T, B, N), dtype=torch.float32, device=dev)
+        H = torch.empty((T, B, N), dtype=torch.float32, device=dev)
+        proj_ms = timed(lambda: h.project(g["U"], g["x"], g["bias"], out=Xw))
+        if w.kind == "dense":
+            run = lambda: h.forward_layer_dense(g["U"], g["bias"], g["W"], g["x"], g["h0"], out=H, workspace=Xw)
+        else:
+            run = lambda: h.forward_layer_sparse(g["U"], g["bias"], g["col"], g["val"], g["x"], g["h0"], out=H,
+                                                 workspace=Xw)
+        layer_ms = timed(run)
+        flop = 2.0 * T * B * N * I
+        row = {
+            "N": N, "I": I, "T": T, "B": B, "kind": w.kind,
+            "projection_us": round(proj_ms * 1e3, 2),
+            "projection_tflops": round(flop / (proj_ms * 1e-3) / 1e12, 1),
+            "projection_frac_of_fp16_mfma_peak": round(flop / (proj_ms * 1e-3) / MFMA_F16_PEAK, 4),
+            "layer_us": round(layer_ms * 1e3, 1),
+            "layer_timesteps_per_s": round(T / (layer_ms * 1e-3), 1),
+            "projection_share_of_layer": round(proj_ms / layer_ms, 3),
+        }
+        if not no_check:
+            import oracle
+            run()
+            h.synchronize()
+            ref = (oracle.forward_layer_dense(d["U"], d["bias"], d["W"], d["x"], d["h0"]) if w.kind == "dense"
+                   else oracle.forward_layer_sparse(d["U"], d["bias"], d["col"], d["val"], d["x"], d["h0"]))
+            row["layer_max_err_ratio"] = round(float(oracle.tolerance_ratio(H.cpu().numpy(), ref, oracle.TOL_F16)), 6)
+            Xref = oracle.project(d["U"], d["x"], d["bias"])
+            S = np.abs(d["x"].astype(np.float64)) @ np.abs(d["U"].astype(np.float64)).T + np.abs(d["bias"])
+            row["projection_max_err_ratio"] = round(float(np.max(np.abs(Xw.cpu().numpy() - Xref) / (1e-6 * (1 + S)))), 4)
+        rows[name] = row
+        del g, Xw, H
+    h.close()
+    return rows
+
+
 def trace_breakdown(torch, dev, Handle, g, wd, ws, T):
     """Per-phase time per step from one traced call of each headline kernel
     and of the floor (team layout): mean over the waves that serve a batch
@@ -486,6 +539,8 @@ def main():
         configs = per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=args.no_check)
 
     detail["trace_us_per_step"] = trace_breakdown(torch, dev, Handle, g, wd, ws, T)
+    if not args.no_layers:
+        detail["layers"] = layer_table(torch, dev, Handle, timed, no_check=args.no_check)
 
     baselines = None
     if not args.no_baselines:

@@ -176,6 +176,55 @@ prnnStatus_t prnn_forward_sparse(prnnHandle_t handle, int N, int B, int T, int K
                                  const float* X, const float* h0, float* H,
                                  hipStream_t stream);
 
+/* Input projection of a layer ("Optimizing Performance of Recurrent Neural
+ * Networks on GPUs", Abstract, single-layer stage: the input-side product of
+ * every timestep is independent of the state, so a whole sequence's is one
+ * matrix product computed before the recurrence):
+ *
+ *   X[m][n] = bias[n] + sum_i U[n][i] * x[m][i],   0 <= m < M, 0 <= n < N,
+ *
+ * with x [M][I] row-major (M = T * B rows for a sequence [T][B][I]), U [N][I]
+ * row-major (row n feeds output neuron n, like W), bias [N] or NULL (zeros)
+ * and X [M][N] fp32 (the pre-activations the forward calls take).  All are
+ * device pointers owned by the caller; only X is written.
+ * u_type: PRNN_DATA_HALF (PRNN_DATA_FLOAT returns NOT_SUPPORTED).
+ * x_type: PRNN_DATA_FLOAT or PRNN_DATA_HALF.  Runs on the matrix cores with
+ * fp32 accumulation.  An fp32 x enters as fp16 hi = fp16(x) plus
+ * lo = fp16(x - hi), whose products with the fp16 U are exact: x is seen to
+ * about 2^-22 of |x|.  A finite |x| >= 65520 does not fit the split; the
+ * handle then reports EXECUTION_FAILED at prnn_synchronize (X is not valid)
+ * and the next forward call on the handle does nothing until that report.
+ * BAD_PARAM: NULL handle, x, U or X (when M > 0); M < 0, N < 1, I < 1;
+ * unknown types; x, U, bias or X not aligned to their element size; X
+ * overlapping x, U or bias.  NOT_SUPPORTED: fp32 U; x or U over 4 GiB.
+ * M == 0 enqueues nothing and returns SUCCESS.  Asynchronous on `stream`. */
+prnnStatus_t prnn_project(prnnHandle_t handle, int M, int N, int I,
+                          prnnDataType_t x_type, const void* x,
+                          prnnDataType_t u_type, const void* U, const float* bias,
+                          float* X, hipStream_t stream);
+
+/* One whole layer: prnn_project of the input sequence x [T][B][I] into the
+ * caller's workspace Xbuf [T][B][N] (fp32), then the dense recurrence over it
+ * (prnn_forward_dense with X = Xbuf), both on `stream`.  Every argument is
+ * checked, and the recurrence planned, before anything is enqueued; the
+ * errors are those of the two calls, plus BAD_PARAM when Xbuf overlaps h0 or
+ * W.  T == 0 enqueues nothing and returns SUCCESS. */
+prnnStatus_t prnn_forward_layer_dense(prnnHandle_t handle, int N, int I, int B, int T,
+                                      prnnDataType_t x_type, const void* x,
+                                      prnnDataType_t u_type, const void* U, const float* bias,
+                                      prnnDataType_t w_type, const void* W,
+                                      const float* h0, float* Xbuf, float* H,
+                                      hipStream_t stream);
+
+/* The same with a row-balanced sparse recurrent matrix (as in
+ * prnn_forward_sparse); BAD_PARAM also when Xbuf overlaps col or val. */
+prnnStatus_t prnn_forward_layer_sparse(prnnHandle_t handle, int N, int I, int B, int T, int K,
+                                       prnnDataType_t x_type, const void* x,
+                                       prnnDataType_t u_type, const void* U, const float* bias,
+                                       const int16_t* col, prnnDataType_t val_type, const void* val,
+                                       const float* h0, float* Xbuf, float* H,
+                                       hipStream_t stream);
+
 /* The exchange and step protocol of a dense call with the same N, B and T and
  * the same grid, without weights or arithmetic: the per-step floor that
  * synchronisation alone costs.  Writes H (values are step numbers, not a

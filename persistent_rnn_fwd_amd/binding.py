@@ -51,6 +51,9 @@ SIGNATURES = {
     "prnn_set_trace": (_I, [_H, _I]),
     "prnn_get_trace": (_I, [_H, _P, ctypes.c_size_t, ctypes.POINTER(_I), _P]),
     "prnn_status_string": (ctypes.c_char_p, [_I]),
+    "prnn_project": (_I, [_H, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P]),
+    "prnn_forward_layer_dense": (_I, [_H, _I, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P]),
+    "prnn_forward_layer_sparse": (_I, [_H, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
 }
 
 
@@ -237,6 +240,80 @@ class Handle:
                                            X.data_ptr(), h0.data_ptr() if h0 is not None else None,
                                            out.data_ptr(), _stream_ptr(stream))
         _check("prnn_forward_sparse", st)
+        return out
+
+    # -- the input projection and whole layers ------------------------------
+    def project(self, U: torch.Tensor, x: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """X[..., n] = bias[n] + sum_i U[n, i] x[..., i]; U fp16 [N, I], x fp32/fp16 [..., I]."""
+        N, I = U.shape
+        lead = tuple(x.shape[:-1])
+        M = 1
+        for d in lead:
+            M *= int(d)
+        _need(U, "U", (torch.float16,), (N, I))
+        _need(x, "x", (torch.float32, torch.float16), lead + (I,))
+        if bias is not None:
+            _need(bias, "bias", (torch.float32,), (N,))
+        if out is None:
+            out = torch.empty(lead + (N,), dtype=torch.float32, device=x.device)
+        _need(out, "out", (torch.float32,), lead + (N,))
+        xt = DATA_FLOAT if x.dtype == torch.float32 else DATA_HALF
+        st = self._lib.prnn_project(self._h, M, N, I, xt, x.data_ptr(), DATA_HALF, U.data_ptr(),
+                                    bias.data_ptr() if bias is not None else None, out.data_ptr(),
+                                    _stream_ptr(stream))
+        _check("prnn_project", st)
+        return out
+
+    def _layer_buffers(self, x, U, bias, h0, N, workspace, out):
+        T, B, I = x.shape
+        _need(U, "U", (torch.float16,), (N, I))
+        _need(x, "x", (torch.float32, torch.float16), (T, B, I))
+        if bias is not None:
+            _need(bias, "bias", (torch.float32,), (N,))
+        if h0 is not None:
+            _need(h0, "h0", (torch.float32,), (B, N))
+        if workspace is None:
+            workspace = torch.empty((T, B, N), dtype=torch.float32, device=x.device)
+        _need(workspace, "workspace", (torch.float32,), (T, B, N))
+        if out is None:
+            out = torch.empty((T, B, N), dtype=torch.float32, device=x.device)
+        _need(out, "out", (torch.float32,), (T, B, N))
+        return T, B, I, workspace, out
+
+    def forward_layer_dense(self, U: torch.Tensor, bias: Optional[torch.Tensor], W: torch.Tensor, x: torch.Tensor,
+                            h0: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """One dense layer: X = x U^T + bias into `workspace` [T, B, N], then the recurrence."""
+        N = W.shape[0]
+        _need(W, "W", (torch.float32, torch.float16), (N, N))
+        T, B, I, workspace, out = self._layer_buffers(x, U, bias, h0, N, workspace, out)
+        xt = DATA_FLOAT if x.dtype == torch.float32 else DATA_HALF
+        wt = DATA_FLOAT if W.dtype == torch.float32 else DATA_HALF
+        st = self._lib.prnn_forward_layer_dense(
+            self._h, N, I, B, T, xt, x.data_ptr(), DATA_HALF, U.data_ptr(),
+            bias.data_ptr() if bias is not None else None, wt, W.data_ptr(),
+            h0.data_ptr() if h0 is not None else None, workspace.data_ptr(), out.data_ptr(), _stream_ptr(stream))
+        _check("prnn_forward_layer_dense", st)
+        return out
+
+    def forward_layer_sparse(self, U: torch.Tensor, bias: Optional[torch.Tensor], col: torch.Tensor,
+                             val: torch.Tensor, x: torch.Tensor, h0: Optional[torch.Tensor] = None,
+                             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
+        """One row-balanced sparse layer: the projection, then the sparse recurrence."""
+        N = col.shape[0]
+        K = col.shape[1] if col.dim() == 2 else -1
+        _need(col, "col", (torch.int16,), (N, K))
+        _need(val, "val", (torch.float32, torch.float16), (N, K))
+        T, B, I, workspace, out = self._layer_buffers(x, U, bias, h0, N, workspace, out)
+        xt = DATA_FLOAT if x.dtype == torch.float32 else DATA_HALF
+        vt = DATA_FLOAT if val.dtype == torch.float32 else DATA_HALF
+        st = self._lib.prnn_forward_layer_sparse(
+            self._h, N, I, B, T, K, xt, x.data_ptr(), DATA_HALF, U.data_ptr(),
+            bias.data_ptr() if bias is not None else None, col.data_ptr(), vt, val.data_ptr(),
+            h0.data_ptr() if h0 is not None else None, workspace.data_ptr(), out.data_ptr(), _stream_ptr(stream))
+        _check("prnn_forward_layer_sparse", st)
         return out
 
     def sync_floor(self, N: int, B: int, T: int, out: Optional[torch.Tensor] = None,

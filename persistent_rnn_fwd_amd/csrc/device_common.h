@@ -44,6 +44,7 @@ constexpr int kCoherent = 16 | 1;
 constexpr int kPlain = 0;
 
 constexpr uint32_t kStatusTimeout = 1u;
+constexpr uint32_t kStatusRange = 2u;  // a value reached the fp16 range of an hi + lo split
 
 // Raw buffer resource over [p, p + bytes): out-of-range accesses read 0 and
 // drop writes instead of faulting.

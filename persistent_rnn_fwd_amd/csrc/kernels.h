@@ -82,4 +82,20 @@ extern const KernelEntry kSparseTeamF32TraceKernels[];
 extern const void* kFloorTeamTraceKernel;
 void launch_team_fill(uint32_t* ring, int npad, uint32_t v, hipStream_t stream);
 
+// Input projection X[m][n] = bias[n] + sum_i U[n][i] x[m][i] (project.hip).
+struct ProjArgs {
+  const void* x;      // [M][I], fp32 or fp16
+  const void* U;      // [N][I] fp16
+  const float* bias;  // [N] or nullptr
+  float* X;           // [M][N]
+  uint32_t* status;   // kStatusRange if an fp32 x exceeds the fp16 range of its split
+  int M, N, I;
+  uint32_t x_bytes, u_bytes;
+  int tiles_n;        // 128-column tiles of X
+  int tiles;          // all 64 x 128 tiles
+  int per_xcd;        // tiles per XCD (grid = 8 per_xcd workgroups of 256)
+};
+// vec: I % 8 == 0 and x, U 16-byte aligned.
+hipError_t launch_project(const ProjArgs& a, bool x_f32, bool vec, hipStream_t stream);
+
 }  // namespace prnn

@@ -368,6 +368,117 @@ bool check_placement(int num_cu) {
   return ok;
 }
 
+// Argument checks and launch plan of a dense forward call.  *empty: T == 0
+// (nothing to do).  Nothing is enqueued.
+prnnStatus_t prepare_dense(prnnContext* h, int N, int B, int T, prnnDataType_t w_type, const void* W,
+                           const float* X, const float* h0, float* H, Plan* p, bool* empty) {
+  prnnStatus_t st = check_common(h, N, B, T, X, h0, H, empty);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  if (w_type != PRNN_DATA_FLOAT && w_type != PRNN_DATA_HALF) return PRNN_STATUS_BAD_PARAM;
+  if (*empty) return PRNN_STATUS_SUCCESS;
+  if (W == nullptr) return PRNN_STATUS_BAD_PARAM;
+  if (!aligned(W, 4)) return PRNN_STATUS_BAD_PARAM;
+  const size_t wb = (size_t)N * N * (w_type == PRNN_DATA_FLOAT ? 4 : 2);
+  if (overlap(W, wb, H, (size_t)T * B * N * 4)) return PRNN_STATUS_BAD_PARAM;
+  if ((size_t)T * B * N * 4 > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
+  const int wt = w_type == PRNN_DATA_FLOAT ? prnn::kF32 : prnn::kF16;
+  if (!plan(h, kDense, N, B, 0, wt, p)) return PRNN_STATUS_NOT_SUPPORTED;
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t run_dense(prnnContext* h, const Plan& p, int N, int B, int T, const void* W, const float* X,
+                       const float* h0, float* H, hipStream_t stream) {
+  const int Npad = (N + 3) & ~3;
+  prnnStatus_t st = ensure_ring(h, p, B, Npad, stream);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  StepArgs a = base_args(h, N, B, T, X, h0, H, p, Npad);
+  a.W = W;
+  return launch(h, p, a, T, stream);
+}
+
+prnnStatus_t prepare_sparse(prnnContext* h, int N, int B, int T, int K, const int16_t* col, prnnDataType_t val_type,
+                            const void* val, const float* X, const float* h0, float* H, Plan* p, bool* empty) {
+  prnnStatus_t st = check_common(h, N, B, T, X, h0, H, empty);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  if (val_type != PRNN_DATA_FLOAT && val_type != PRNN_DATA_HALF) return PRNN_STATUS_BAD_PARAM;
+  if (K < 1 || K > N || N > 32767) return PRNN_STATUS_BAD_PARAM;
+  if (*empty) return PRNN_STATUS_SUCCESS;
+  if (col == nullptr || val == nullptr) return PRNN_STATUS_BAD_PARAM;
+  if (!aligned(col, 2) || !aligned(val, val_type == PRNN_DATA_FLOAT ? 4 : 2)) return PRNN_STATUS_BAD_PARAM;
+  const size_t hb = (size_t)T * B * N * 4;
+  if (overlap(col, (size_t)N * K * 2, H, hb) ||
+      overlap(val, (size_t)N * K * (val_type == PRNN_DATA_FLOAT ? 4 : 2), H, hb))
+    return PRNN_STATUS_BAD_PARAM;
+  if (hb > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
+  const int wt = val_type == PRNN_DATA_FLOAT ? prnn::kF32 : prnn::kF16;
+  if (!plan(h, kSparse, N, B, K, wt, p)) return PRNN_STATUS_NOT_SUPPORTED;
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t run_sparse(prnnContext* h, const Plan& p, int N, int B, int T, int K, const int16_t* col,
+                        const void* val, const float* X, const float* h0, float* H, hipStream_t stream) {
+  const int Npad = (N + 3) & ~3;
+  prnnStatus_t st = ensure_ring(h, p, B, Npad, stream);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  StepArgs a = base_args(h, N, B, T, X, h0, H, p, Npad);
+  a.W = col;
+  a.V = val;
+  a.K = K;
+  return launch(h, p, a, T, stream);
+}
+
+// Argument checks of the input projection; fills the kernel arguments.
+prnnStatus_t prepare_project(prnnContext* h, int M, int N, int I, prnnDataType_t x_type, const void* x,
+                             prnnDataType_t u_type, const void* U, const float* bias, float* X, prnn::ProjArgs* a,
+                             bool* vec) {
+  if (h == nullptr || M < 0 || N < 1 || I < 1) return PRNN_STATUS_BAD_PARAM;
+  if (x_type != PRNN_DATA_FLOAT && x_type != PRNN_DATA_HALF) return PRNN_STATUS_BAD_PARAM;
+  if (u_type != PRNN_DATA_FLOAT && u_type != PRNN_DATA_HALF) return PRNN_STATUS_BAD_PARAM;
+  if (u_type != PRNN_DATA_HALF) return PRNN_STATUS_NOT_SUPPORTED;
+  if (M == 0) return PRNN_STATUS_SUCCESS;
+  if (x == nullptr || U == nullptr || X == nullptr) return PRNN_STATUS_BAD_PARAM;
+  const size_t xe = x_type == PRNN_DATA_FLOAT ? 4 : 2;
+  if (!aligned(x, xe) || !aligned(U, 2) || !aligned(X, 4) || (bias != nullptr && !aligned(bias, 4)))
+    return PRNN_STATUS_BAD_PARAM;
+  const size_t xb = (size_t)M * I * xe, ub = (size_t)N * I * 2, ob = (size_t)M * N * 4;
+  if (overlap(X, ob, x, xb) || overlap(X, ob, U, ub) || (bias != nullptr && overlap(X, ob, bias, (size_t)N * 4)))
+    return PRNN_STATUS_BAD_PARAM;
+  const long long tiles = (long long)((M + 63) / 64) * ((N + 127) / 128);  // 64 x 128 tiles of X
+  if (xb > 0xFFFFFF00ull || ub > 0xFFFFFF00ull || tiles > (1ll << 28)) return PRNN_STATUS_NOT_SUPPORTED;
+  a->x = x;
+  a->U = U;
+  a->bias = bias;
+  a->X = X;
+  a->status = h->d_status;
+  a->M = M;
+  a->N = N;
+  a->I = I;
+  a->x_bytes = static_cast<uint32_t>(xb);
+  a->u_bytes = static_cast<uint32_t>(ub);
+  a->tiles_n = (N + 127) / 128;
+  a->tiles = static_cast<int>(tiles);
+  a->per_xcd = static_cast<int>((tiles + 7) / 8);
+  *vec = I % 8 == 0 && aligned(x, 16) && aligned(U, 16);
+  return PRNN_STATUS_SUCCESS;
+}
+
+// The projection of a layer call into its workspace Xbuf ([T][B][N]): besides
+// the projection's own checks, Xbuf must not overlap h0 or the recurrent
+// weights (the projection writes it before the recurrence reads them).
+prnnStatus_t prepare_layer_projection(prnnContext* h, int N, int I, int B, int T, prnnDataType_t x_type,
+                                      const void* x, prnnDataType_t u_type, const void* U, const float* bias,
+                                      float* Xbuf, const float* h0, const void* w0, size_t w0_bytes,
+                                      const void* w1, size_t w1_bytes, prnn::ProjArgs* a, bool* vec) {
+  if (I < 1) return PRNN_STATUS_BAD_PARAM;
+  const long long M = (long long)T * B;
+  if (M > 0x7fffffffll) return PRNN_STATUS_NOT_SUPPORTED;
+  const size_t ob = (size_t)M * N * 4;
+  if ((h0 != nullptr && overlap(Xbuf, ob, h0, (size_t)B * N * 4)) || overlap(Xbuf, ob, w0, w0_bytes) ||
+      (w1 != nullptr && overlap(Xbuf, ob, w1, w1_bytes)))
+    return PRNN_STATUS_BAD_PARAM;
+  return prepare_project(h, static_cast<int>(M), N, I, x_type, x, u_type, U, bias, Xbuf, a, vec);
+}
+
 }  // namespace
 
 extern "C" {
@@ -520,54 +631,66 @@ prnnStatus_t prnn_synchronize(prnnHandle_t h, hipStream_t stream) {
 
 prnnStatus_t prnn_forward_dense(prnnHandle_t h, int N, int B, int T, prnnDataType_t w_type, const void* W,
                                 const float* X, const float* h0, float* H, hipStream_t stream) {
-  bool empty = false;
-  prnnStatus_t st = check_common(h, N, B, T, X, h0, H, &empty);
-  if (st != PRNN_STATUS_SUCCESS) return st;
-  if (w_type != PRNN_DATA_FLOAT && w_type != PRNN_DATA_HALF) return PRNN_STATUS_BAD_PARAM;
-  if (empty) return PRNN_STATUS_SUCCESS;
-  if (W == nullptr) return PRNN_STATUS_BAD_PARAM;
-  if (!aligned(W, 4)) return PRNN_STATUS_BAD_PARAM;
-  const size_t wb = (size_t)N * N * (w_type == PRNN_DATA_FLOAT ? 4 : 2);
-  if (overlap(W, wb, H, (size_t)T * B * N * 4)) return PRNN_STATUS_BAD_PARAM;
-  if ((size_t)T * B * N * 4 > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
-  const int wt = w_type == PRNN_DATA_FLOAT ? prnn::kF32 : prnn::kF16;
   Plan p;
-  if (!plan(h, kDense, N, B, 0, wt, &p)) return PRNN_STATUS_NOT_SUPPORTED;
-  const int Npad = (N + 3) & ~3;
-  st = ensure_ring(h, p, B, Npad, stream);
-  if (st != PRNN_STATUS_SUCCESS) return st;
-  StepArgs a = base_args(h, N, B, T, X, h0, H, p, Npad);
-  a.W = W;
-  return launch(h, p, a, T, stream);
+  bool empty = false;
+  prnnStatus_t st = prepare_dense(h, N, B, T, w_type, W, X, h0, H, &p, &empty);
+  if (st != PRNN_STATUS_SUCCESS || empty) return st;
+  return run_dense(h, p, N, B, T, W, X, h0, H, stream);
 }
 
 prnnStatus_t prnn_forward_sparse(prnnHandle_t h, int N, int B, int T, int K, const int16_t* col,
                                  prnnDataType_t val_type, const void* val, const float* X, const float* h0,
                                  float* H, hipStream_t stream) {
-  bool empty = false;
-  prnnStatus_t st = check_common(h, N, B, T, X, h0, H, &empty);
-  if (st != PRNN_STATUS_SUCCESS) return st;
-  if (val_type != PRNN_DATA_FLOAT && val_type != PRNN_DATA_HALF) return PRNN_STATUS_BAD_PARAM;
-  if (K < 1 || K > N || N > 32767) return PRNN_STATUS_BAD_PARAM;
-  if (empty) return PRNN_STATUS_SUCCESS;
-  if (col == nullptr || val == nullptr) return PRNN_STATUS_BAD_PARAM;
-  if (!aligned(col, 2) || !aligned(val, val_type == PRNN_DATA_FLOAT ? 4 : 2)) return PRNN_STATUS_BAD_PARAM;
-  const size_t hb = (size_t)T * B * N * 4;
-  if (overlap(col, (size_t)N * K * 2, H, hb) ||
-      overlap(val, (size_t)N * K * (val_type == PRNN_DATA_FLOAT ? 4 : 2), H, hb))
-    return PRNN_STATUS_BAD_PARAM;
-  if (hb > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
-  const int wt = val_type == PRNN_DATA_FLOAT ? prnn::kF32 : prnn::kF16;
   Plan p;
-  if (!plan(h, kSparse, N, B, K, wt, &p)) return PRNN_STATUS_NOT_SUPPORTED;
-  const int Npad = (N + 3) & ~3;
-  st = ensure_ring(h, p, B, Npad, stream);
+  bool empty = false;
+  prnnStatus_t st = prepare_sparse(h, N, B, T, K, col, val_type, val, X, h0, H, &p, &empty);
+  if (st != PRNN_STATUS_SUCCESS || empty) return st;
+  return run_sparse(h, p, N, B, T, K, col, val, X, h0, H, stream);
+}
+
+prnnStatus_t prnn_project(prnnHandle_t h, int M, int N, int I, prnnDataType_t x_type, const void* x,
+                          prnnDataType_t u_type, const void* U, const float* bias, float* X, hipStream_t stream) {
+  prnn::ProjArgs a;
+  bool vec = false;
+  prnnStatus_t st = prepare_project(h, M, N, I, x_type, x, u_type, U, bias, X, &a, &vec);
+  if (st != PRNN_STATUS_SUCCESS || M == 0) return st;
+  return hip_status(prnn::launch_project(a, x_type == PRNN_DATA_FLOAT, vec, stream));
+}
+
+prnnStatus_t prnn_forward_layer_dense(prnnHandle_t h, int N, int I, int B, int T, prnnDataType_t x_type,
+                                      const void* x, prnnDataType_t u_type, const void* U, const float* bias,
+                                      prnnDataType_t w_type, const void* W, const float* h0, float* Xbuf, float* H,
+                                      hipStream_t stream) {
+  Plan p;
+  bool empty = false;
+  prnnStatus_t st = prepare_dense(h, N, B, T, w_type, W, Xbuf, h0, H, &p, &empty);
+  if (st != PRNN_STATUS_SUCCESS || empty) return st;
+  prnn::ProjArgs a;
+  bool vec = false;
+  st = prepare_layer_projection(h, N, I, B, T, x_type, x, u_type, U, bias, Xbuf, h0, W,
+                                (size_t)N * N * (w_type == PRNN_DATA_FLOAT ? 4 : 2), nullptr, 0, &a, &vec);
   if (st != PRNN_STATUS_SUCCESS) return st;
-  StepArgs a = base_args(h, N, B, T, X, h0, H, p, Npad);
-  a.W = col;
-  a.V = val;
-  a.K = K;
-  return launch(h, p, a, T, stream);
+  st = hip_status(prnn::launch_project(a, x_type == PRNN_DATA_FLOAT, vec, stream));
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  return run_dense(h, p, N, B, T, W, Xbuf, h0, H, stream);
+}
+
+prnnStatus_t prnn_forward_layer_sparse(prnnHandle_t h, int N, int I, int B, int T, int K, prnnDataType_t x_type,
+                                       const void* x, prnnDataType_t u_type, const void* U, const float* bias,
+                                       const int16_t* col, prnnDataType_t val_type, const void* val,
+                                       const float* h0, float* Xbuf, float* H, hipStream_t stream) {
+  Plan p;
+  bool empty = false;
+  prnnStatus_t st = prepare_sparse(h, N, B, T, K, col, val_type, val, Xbuf, h0, H, &p, &empty);
+  if (st != PRNN_STATUS_SUCCESS || empty) return st;
+  prnn::ProjArgs a;
+  bool vec = false;
+  st = prepare_layer_projection(h, N, I, B, T, x_type, x, u_type, U, bias, Xbuf, h0, col, (size_t)N * K * 2, val,
+                                (size_t)N * K * (val_type == PRNN_DATA_FLOAT ? 4 : 2), &a, &vec);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  st = hip_status(prnn::launch_project(a, x_type == PRNN_DATA_FLOAT, vec, stream));
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  return run_sparse(h, p, N, B, T, K, col, val, Xbuf, h0, H, stream);
 }
 
 prnnStatus_t prnn_sync_floor(prnnHandle_t h, int N, int B, int T, float* H, hipStream_t stream) {

@@ -28,8 +28,6 @@
 
 namespace prnn {
 
-constexpr uint32_t kStatusRange = 2u;  // |h| reached the fp16 range of the split
-
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
