@@ -338,6 +338,50 @@ def layer_table(torch, dev, Handle, timed, no_check=False):
     return rows
 
 
+def stack_table(torch, dev, Handle, timed, no_check=False):
+    """Two-layer stacks (B = 4, T = 256) as one wavefront against the same two
+    layers run one after the other (two layer calls), at N = 1152 and 1792."""
+    import numpy as np
+    from persistent_rnn_fwd_amd.inputs import WORKLOADS, generate_stack
+    rows = {}
+    h = Handle()
+    for base in ("dense_f16_n1152", "dense_f16_n1792"):
+        w = WORKLOADS[base]
+        st = generate_stack(w, 2)
+        layers = [{k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in ly.items()} for ly in st["layers"]]
+        x = torch.from_numpy(st["x"]).to(dev)
+        h0s = [torch.from_numpy(v).to(dev) for v in st["h0s"]]
+        T, B, N = w.T, w.B, w.N
+        outs = [torch.empty((T, B, N), dtype=torch.float32, device=dev) for _ in range(2)]
+        ws = torch.empty((T, B, N), dtype=torch.float32, device=dev)
+        seq = [torch.empty((T, B, N), dtype=torch.float32, device=dev) for _ in range(2)]
+        wave = lambda: h.forward_stack_dense(layers, x, h0s, outs=outs, workspace=ws)
+
+        def sequential():
+            h.forward_layer_dense(layers[0]["U"], layers[0]["bias"], layers[0]["W"], x, h0s[0], out=seq[0], workspace=ws)
+            h.forward_layer_dense(layers[1]["U"], layers[1]["bias"], layers[1]["W"], seq[0], h0s[1], out=seq[1],
+                                  workspace=ws)
+        t_wave = timed(wave)
+        t_seq = timed(sequential)
+        row = {
+            "layers": 2, "N": N, "B": B, "T": T,
+            "wavefront_us": round(t_wave * 1e3, 1),
+            "wavefront_timesteps_per_s": round(T / (t_wave * 1e-3), 1),
+            "sequential_layers_us": round(t_seq * 1e3, 1),
+            "speedup_over_sequential": round(t_seq / t_wave, 3),
+        }
+        if not no_check:
+            import oracle
+            wave()
+            h.synchronize()
+            refs = oracle.forward_stack_dense(st["layers"], st["x"], st["h0s"])
+            row["max_err_ratio"] = round(max(float(oracle.tolerance_ratio(o.cpu().numpy(), r, oracle.TOL_F16))
+                                             for o, r in zip(outs, refs)), 6)
+        rows[f"stack2_{base}"] = row
+    h.close()
+    return rows
+
+
 def trace_breakdown(torch, dev, Handle, g, wd, ws, T):
     """Per-phase time per step from one traced call of each headline kernel
     and of the floor (team layout): mean over the waves that serve a batch
@@ -541,6 +585,7 @@ def main():
     detail["trace_us_per_step"] = trace_breakdown(torch, dev, Handle, g, wd, ws, T)
     if not args.no_layers:
         detail["layers"] = layer_table(torch, dev, Handle, timed, no_check=args.no_check)
+        detail["stacks"] = stack_table(torch, dev, Handle, timed, no_check=args.no_check)
 
     baselines = None
     if not args.no_baselines:

@@ -225,6 +225,38 @@ prnnStatus_t prnn_forward_layer_sparse(prnnHandle_t handle, int N, int I, int B,
                                        const float* h0, float* Xbuf, float* H,
                                        hipStream_t stream);
 
+/* A stack of L dense fp16 layers of width N as one wavefront ("Optimizing
+ * Performance of Recurrent Neural Networks on GPUs", Abstract, entire-network
+ * stage):
+ *
+ *   X_0       = prnn_project(x, U[0], bias[0])           (into Xbuf)
+ *   H[0][t]   = max(0, X_0[t] + W[0] H[0][t-1])
+ *   H[l][t]   = max(0, bias[l] + U[l] H[l-1][t] + W[l] H[l][t-1]),  l >= 1
+ *   H[l][-1]  = h0[l] (zeros if h0 or h0[l] is NULL)
+ *
+ * Layer l + 1's step t needs only layer l's step t and its own step t - 1,
+ * so all layers run at the same time on separate XCDs (layer l, batch row b
+ * on XCD l B + b; hence L B <= 8).  x [T][B][I] (fp32 or fp16); U[0] [N][I],
+ * U[l >= 1] [N][N], W[l] [N][N], all fp16, 16-byte aligned; bias[l] [N] or
+ * NULL; Xbuf [T][B][N] fp32 workspace; H[l] [T][B][N] fp32 outputs.  U, bias,
+ * W, h0 and H are host arrays of L device pointers (bias and h0 may be NULL
+ * arrays).  All device buffers are the caller's.  H[0] .. H[L-2] are also
+ * the hand-over between layers (filled with a marker before the launch and
+ * overwritten by the results).  Not traced.
+ * BAD_PARAM: NULL handle/arrays/pointers, L < 1, N < 1, I < 1, B outside
+ * [1, 8], T < 0, unknown x_type, misalignment, any output overlapping any
+ * input, the workspace or another output, the workspace overlapping an
+ * input.  NOT_SUPPORTED: L B > 8 or L > 8, no instance for N (rows per wave
+ * and 256-column chunks up to 7 x 7: N <= 1792), sizes over 4 GiB, and what
+ * prnn_project does not support.  EXECUTION_FAILED (at prnn_synchronize):
+ * a bounded wait expired, or x exceeded the fp16 range of its split.
+ * T == 0 enqueues nothing and returns SUCCESS. */
+prnnStatus_t prnn_forward_stack_dense(prnnHandle_t handle, int L, int N, int I, int B, int T,
+                                      prnnDataType_t x_type, const void* x,
+                                      const void* const* U, const float* const* bias,
+                                      const void* const* W, const float* const* h0,
+                                      float* Xbuf, float* const* H, hipStream_t stream);
+
 /* The exchange and step protocol of a dense call with the same N, B and T and
  * the same grid, without weights or arithmetic: the per-step floor that
  * synchronisation alone costs.  Writes H (values are step numbers, not a

@@ -54,6 +54,7 @@ SIGNATURES = {
     "prnn_project": (_I, [_H, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P]),
     "prnn_forward_layer_dense": (_I, [_H, _I, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P]),
     "prnn_forward_layer_sparse": (_I, [_H, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
+    "prnn_forward_stack_dense": (_I, [_H, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 
@@ -315,6 +316,40 @@ class Handle:
             h0.data_ptr() if h0 is not None else None, workspace.data_ptr(), out.data_ptr(), _stream_ptr(stream))
         _check("prnn_forward_layer_sparse", st)
         return out
+
+    def forward_stack_dense(self, layers, x: torch.Tensor, h0s=None, outs=None,
+                            workspace: Optional[torch.Tensor] = None, stream=None):
+        """A stack of dense fp16 layers as one wavefront.  layers: list of dicts
+        with U (fp16 [N, I] for the first, [N, N] after), bias (fp32 [N] or
+        None) and W (fp16 [N, N]); x [T, B, I]; h0s: None or one [B, N] (or
+        None) per layer.  Returns the list of every layer's H [T, B, N]."""
+        L = len(layers)
+        T, B, I = x.shape
+        N = layers[0]["W"].shape[0]
+        _need(x, "x", (torch.float32, torch.float16), (T, B, I))
+        for l, ly in enumerate(layers):
+            _need(ly["U"], f"layers[{l}].U", (torch.float16,), (N, I if l == 0 else N))
+            _need(ly["W"], f"layers[{l}].W", (torch.float16,), (N, N))
+            if ly.get("bias") is not None:
+                _need(ly["bias"], f"layers[{l}].bias", (torch.float32,), (N,))
+            if h0s is not None and h0s[l] is not None:
+                _need(h0s[l], f"h0s[{l}]", (torch.float32,), (B, N))
+        if workspace is None:
+            workspace = torch.empty((T, B, N), dtype=torch.float32, device=x.device)
+        _need(workspace, "workspace", (torch.float32,), (T, B, N))
+        if outs is None:
+            outs = [torch.empty((T, B, N), dtype=torch.float32, device=x.device) for _ in range(L)]
+        for l, o in enumerate(outs):
+            _need(o, f"outs[{l}]", (torch.float32,), (T, B, N))
+        ptrs = lambda ts: (ctypes.c_void_p * L)(*[(t.data_ptr() if t is not None else None) for t in ts])
+        Up, Wp, Hp = ptrs([ly["U"] for ly in layers]), ptrs([ly["W"] for ly in layers]), ptrs(outs)
+        bp = ptrs([ly.get("bias") for ly in layers])
+        hp = ptrs(h0s) if h0s is not None else None
+        xt = DATA_FLOAT if x.dtype == torch.float32 else DATA_HALF
+        st = self._lib.prnn_forward_stack_dense(self._h, L, N, I, B, T, xt, x.data_ptr(), Up, bp, Wp, hp,
+                                                workspace.data_ptr(), Hp, _stream_ptr(stream))
+        _check("prnn_forward_stack_dense", st)
+        return outs
 
     def sync_floor(self, N: int, B: int, T: int, out: Optional[torch.Tensor] = None,
                    stream=None) -> torch.Tensor:

@@ -82,6 +82,27 @@ extern const KernelEntry kSparseTeamF32TraceKernels[];
 extern const void* kFloorTeamTraceKernel;
 void launch_team_fill(uint32_t* ring, int npad, uint32_t v, hipStream_t stream);
 
+// A stack of dense fp16 layers as one wavefront (stack.hip).  Team x serves
+// layer x / B, batch row x % B (L B <= 8); the team regions are the team
+// layout's ring.
+constexpr int kMaxStack = 8;
+struct StackArgs {
+  const void* W[kMaxStack];      // fp16 [N][N] recurrent weights
+  const void* U[kMaxStack];      // fp16 [N][N] input weights of layers >= 1 (U[0] unused)
+  const float* bias[kMaxStack];  // [N] or nullptr, layers >= 1 (layer 0's is in X0)
+  const float* h0[kMaxStack];    // [B][N] or nullptr (zeros)
+  float* H[kMaxStack];           // [T][B][N]; H[0 .. L-2] filled with 0xFFFFFFFF before the launch
+  const float* X0;               // [T][B][N] pre-activations of layer 0
+  uint32_t* ring;                // [8][2][Npad]
+  uint32_t* status;
+  int L, N, B, T, Npad, chunks, base_rows, extra_rows;
+  uint32_t step0;
+  uint32_t x_bytes;              // bytes of one [T][B][N] sequence
+  uint64_t deadline;
+};
+// (rmax = rows per wave, cap = chunks of each part)
+extern const KernelEntry kStackKernels[];
+
 // Input projection X[m][n] = bias[n] + sum_i U[n][i] x[m][i] (project.hip).
 struct ProjArgs {
   const void* x;      // [M][I], fp32 or fp16

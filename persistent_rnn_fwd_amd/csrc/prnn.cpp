@@ -693,6 +693,131 @@ prnnStatus_t prnn_forward_layer_sparse(prnnHandle_t h, int N, int I, int B, int 
   return run_sparse(h, p, N, B, T, K, col, val, Xbuf, h0, H, stream);
 }
 
+prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B, int T, prnnDataType_t x_type,
+                                      const void* x, const void* const* U, const float* const* bias,
+                                      const void* const* W, const float* const* h0, float* Xbuf, float* const* H,
+                                      hipStream_t stream) {
+  if (h == nullptr || L < 1 || N < 1 || I < 1 || B < 1 || B > 8 || T < 0) return PRNN_STATUS_BAD_PARAM;
+  if (x_type != PRNN_DATA_FLOAT && x_type != PRNN_DATA_HALF) return PRNN_STATUS_BAD_PARAM;
+  if (L > prnn::kMaxStack || L * B > 8) return PRNN_STATUS_NOT_SUPPORTED;
+  if (T == 0) return PRNN_STATUS_SUCCESS;
+  if (U == nullptr || W == nullptr || H == nullptr || x == nullptr || Xbuf == nullptr) return PRNN_STATUS_BAD_PARAM;
+  const size_t seq = (size_t)T * B * N * 4;
+  if (seq > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
+  if (!aligned(Xbuf, 4)) return PRNN_STATUS_BAD_PARAM;
+  for (int l = 0; l < L; ++l) {
+    const float* hl = h0 != nullptr ? h0[l] : nullptr;
+    const float* bl = bias != nullptr ? bias[l] : nullptr;
+    if (U[l] == nullptr || W[l] == nullptr || H[l] == nullptr) return PRNN_STATUS_BAD_PARAM;
+    if (!aligned(U[l], 16) || !aligned(W[l], 16) || !aligned(H[l], 16) || (hl != nullptr && !aligned(hl, 4)) ||
+        (bl != nullptr && !aligned(bl, 4)))
+      return PRNN_STATUS_BAD_PARAM;
+    // H[l] is written while every weight, bias, h0, the workspace and the
+    // other outputs are read: none of them may overlap it.
+    if (overlap(H[l], seq, Xbuf, seq)) return PRNN_STATUS_BAD_PARAM;
+    for (int m = 0; m < L; ++m) {
+      const float* hm = h0 != nullptr ? h0[m] : nullptr;
+      const float* bm = bias != nullptr ? bias[m] : nullptr;
+      const size_t ub = (size_t)N * (m == 0 ? I : N) * 2;
+      if ((m != l && overlap(H[l], seq, H[m], seq)) || overlap(H[l], seq, W[m], (size_t)N * N * 2) ||
+          overlap(H[l], seq, U[m], ub) || (hm != nullptr && overlap(H[l], seq, hm, (size_t)B * N * 4)) ||
+          (bm != nullptr && overlap(H[l], seq, bm, (size_t)N * 4)))
+        return PRNN_STATUS_BAD_PARAM;
+    }
+  }
+  // The workspace is written (layer 0's projection) before the weights, biases
+  // and initial states are read.
+  for (int m = 0; m < L; ++m) {
+    const float* hm = h0 != nullptr ? h0[m] : nullptr;
+    const float* bm = bias != nullptr ? bias[m] : nullptr;
+    if (overlap(Xbuf, seq, W[m], (size_t)N * N * 2) || overlap(Xbuf, seq, U[m], (size_t)N * (m == 0 ? I : N) * 2) ||
+        (hm != nullptr && overlap(Xbuf, seq, hm, (size_t)B * N * 4)) ||
+        (bm != nullptr && overlap(Xbuf, seq, bm, (size_t)N * 4)))
+      return PRNN_STATUS_BAD_PARAM;
+  }
+  // Plan: the team grid; each wave keeps its rows of [U_l | W_l].
+  if (!h->placement_round_robin || h->num_cu < 8) return PRNN_STATUS_NOT_SUPPORTED;
+  int P = h->forced_grid > 0 ? h->forced_grid / 8 : std::min(kTeamMaxWgPerXcd, h->num_cu / 8);
+  if (h->forced_grid > 0 && h->forced_grid % 8 != 0) return PRNN_STATUS_NOT_SUPPORTED;
+  P = std::min(P, (N + 7) / 8);
+  if (P < 1 || 8 * P > h->num_cu) return PRNN_STATUS_NOT_SUPPORTED;
+  Plan p;
+  p.layout = PRNN_LAYOUT_TEAM;
+  p.G = P;
+  p.grid = 8 * P;
+  p.waves = 8;
+  p.block = 512;
+  const int Q = 8 * P;
+  p.base_rows = N / Q;
+  p.extra_rows = N % Q;
+  p.max_rows = (N + Q - 1) / Q;
+  p.chunks = (N + 255) / 256;
+  p.k = pick(prnn::kStackKernels, p.max_rows, p.chunks);
+  if (p.k == nullptr) return PRNN_STATUS_NOT_SUPPORTED;
+  p.lds_bytes = 2 * 2 * 256 * p.k->cap * 4;  // [2 steps][input, state][chunks x 256]
+  if ((size_t)p.lds_bytes + 256 > h->lds_per_block) return PRNN_STATUS_NOT_SUPPORTED;
+  // Layer 0's input projection, checked before anything is enqueued.
+  prnn::ProjArgs pa;
+  bool vec = false;
+  prnnStatus_t st = prepare_layer_projection(h, N, I, B, T, x_type, x, PRNN_DATA_HALF, U[0],
+                                             bias != nullptr ? bias[0] : nullptr, Xbuf,
+                                             h0 != nullptr ? h0[0] : nullptr, W[0], (size_t)N * N * 2, nullptr, 0,
+                                             &pa, &vec);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  const int Npad = (N + 3) & ~3;
+  st = ensure_ring(h, p, B, Npad, stream);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  st = hip_status(prnn::launch_project(pa, x_type == PRNN_DATA_FLOAT, vec, stream));
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  for (int l = 0; l + 1 < L; ++l)  // "not written yet" marks for the layers that feed another
+    prnn::launch_fill(reinterpret_cast<uint32_t*>(H[l]), (size_t)T * B * N, 0xFFFFFFFFu, stream);
+  prnn::StackArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (int l = 0; l < L; ++l) {
+    a.W[l] = W[l];
+    a.U[l] = U[l];
+    a.bias[l] = bias != nullptr ? bias[l] : nullptr;
+    a.h0[l] = h0 != nullptr ? h0[l] : nullptr;
+    a.H[l] = H[l];
+  }
+  a.X0 = Xbuf;
+  a.ring = h->d_ring;
+  a.status = h->d_status;
+  a.L = L;
+  a.N = N;
+  a.B = B;
+  a.T = T;
+  a.Npad = Npad;
+  a.chunks = p.chunks;
+  a.base_rows = p.base_rows;
+  a.extra_rows = p.extra_rows;
+  a.step0 = static_cast<uint32_t>(h->step);
+  a.x_bytes = static_cast<uint32_t>(seq);
+  a.deadline = static_cast<uint64_t>(h->watchdog_us) * 100ull;
+  void* args[] = {&a};
+  hipError_t e = hipLaunchCooperativeKernel(p.k->fn, dim3(p.grid), dim3(p.block), args,
+                                            static_cast<unsigned>(p.lds_bytes), stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return hip_status(e);
+  }
+  prnnPlanInfo_t& info = h->last_plan;
+  info.layout = p.layout;
+  info.grid = p.grid;
+  info.waves_per_wg = p.waves;
+  info.rows_per_wave = p.max_rows;
+  info.rmax = p.k->rmax;
+  info.chunks = p.k->cap;
+  info.lds_bytes = p.lds_bytes;
+  info.relay_slice = 0;
+  info.math = PRNN_MATH_EXACT;
+  info.first_step = h->step;
+  h->have_plan = true;
+  h->trace_records = 0;
+  h->step += static_cast<uint64_t>(T);
+  return PRNN_STATUS_SUCCESS;
+}
+
 prnnStatus_t prnn_sync_floor(prnnHandle_t h, int N, int B, int T, float* H, hipStream_t stream) {
   if (h == nullptr || N < 1 || B < 1 || B > 8 || T < 0) return PRNN_STATUS_BAD_PARAM;
   if (T == 0) return PRNN_STATUS_SUCCESS;

@@ -1,0 +1,120 @@
+"""GPU parity of a stack of dense layers run as one wavefront (through the C ABI).
+
+``prnn_forward_stack_dense`` runs layer 0's input projection, then every
+layer of the stack at the same time (layer l, batch row b on its own XCD),
+layer l + 1 reading layer l's outputs as they appear.  It is compared with
+``oracle.forward_stack_dense`` element by element on every layer's output, at
+the recurrence's fp16 bar (|H - H_ref| <= 2e-2 (1 + |H_ref|)), for stacks of
+2 to 8 layers, full and ragged sizes, with and without initial states.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from persistent_rnn_fwd_amd import Handle, PrnnError, binding
+from persistent_rnn_fwd_amd.inputs import WORKLOADS, generate_stack
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def handle(gpu):
+    h = Handle()
+    yield h
+    h.close()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_stack(handle, st, h0=True):
+    layers = [{k: dev(v) for k, v in ly.items()} for ly in st["layers"]]
+    h0s = [dev(h) for h in st["h0s"]] if h0 else None
+    outs = handle.forward_stack_dense(layers, dev(st["x"]), h0s)
+    handle.synchronize()
+    return [o.cpu().numpy() for o in outs]
+
+
+def check(st, got, h0=True):
+    refs = oracle.forward_stack_dense(st["layers"], st["x"], st["h0s"] if h0 else None)
+    ratios = [oracle.tolerance_ratio(g, r, oracle.TOL_F16) for g, r in zip(got, refs)]
+    return ratios
+
+
+# (L, B, N, T, h0 mode): full size at N=1152; N=1792 (7 rows x 7 chunks per
+# wave and part); deeper stacks at smaller B; ragged N (not a multiple of 4,
+# of 256, or of the 256 waves of a team).
+CASES = [
+    (2, 4, 1152, 256, "zeros"),
+    (2, 4, 1792, 64, "randn"),
+    (4, 2, 256, 32, "randn"),
+    (8, 1, 200, 16, "randn"),
+    (3, 2, 1000, 20, "zeros"),
+    (2, 3, 777, 12, "randn"),
+]
+
+
+@pytest.mark.parametrize("L,B,N,T,h0", CASES)
+def test_stack_parity(handle, L, B, N, T, h0):
+    w = WORKLOADS["dense_f16_n1152"].with_(N=N, B=B, T=T, h0=h0, seed=300 + L * 10 + B)
+    st = generate_stack(w, L)
+    handle.set_grid(0)
+    got = run_stack(handle, st)
+    ratios = check(st, got)
+    print(f"stack L={L} B={B} N={N} T={T}: error ratios {[f'{r:.3g}' for r in ratios]}")
+    assert max(ratios) <= 1.0
+
+
+def test_stack_deterministic_and_grid_independent_parity(handle):
+    w = WORKLOADS["dense_f16_n1152"].with_(N=512, B=2, T=24, h0="randn", seed=9)
+    st = generate_stack(w, 3)
+    a = run_stack(handle, st)
+    b = run_stack(handle, st)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    handle.set_grid(128)                 # 16 workgroups per team: more rows per wave
+    c = run_stack(handle, st)
+    handle.set_grid(0)
+    assert max(check(st, c)) <= 1.0
+
+
+def test_single_layer_stack_matches_layer_call(handle):
+    """L = 1 is one layer: the same arithmetic as prnn_forward_layer_dense up to
+    the order of the sums."""
+    w = WORKLOADS["dense_f16_n1152"].with_(T=32, h0="randn", seed=21)
+    st = generate_stack(w, 1)
+    got = run_stack(handle, st)[0]
+    ly = {k: dev(v) for k, v in st["layers"][0].items()}
+    H = handle.forward_layer_dense(ly["U"], ly["bias"], ly["W"], dev(st["x"]), dev(st["h0s"][0]))
+    handle.synchronize()
+    ref = oracle.forward_stack_dense(st["layers"], st["x"], st["h0s"])[0]
+    assert oracle.tolerance_ratio(got, ref, oracle.TOL_F16) <= 1.0
+    np.testing.assert_allclose(got, H.cpu().numpy(), rtol=1e-5, atol=1e-5)
+
+
+def test_stack_errors(handle):
+    w = WORKLOADS["dense_f16_n1152"].with_(N=256, B=4, T=4, seed=5)
+    st = generate_stack(w, 3)
+    layers = [{k: dev(v) for k, v in ly.items()} for ly in st["layers"]]
+    with pytest.raises(PrnnError) as e:                       # L B = 12 > 8 XCDs
+        handle.forward_stack_dense(layers, dev(st["x"]))
+    assert e.value.status == binding.NOT_SUPPORTED
+    w2 = WORKLOADS["dense_f16_n1152"].with_(N=2048, B=1, T=2, seed=5)
+    st2 = generate_stack(w2, 2)
+    with pytest.raises(PrnnError) as e:                       # 8 chunks per part: no instance
+        handle.forward_stack_dense([{k: dev(v) for k, v in ly.items()} for ly in st2["layers"]], dev(st2["x"]))
+    assert e.value.status == binding.NOT_SUPPORTED
+    two = layers[:2]
+    x = dev(st["x"])
+    outs = [torch.full((4, 4, 256), 3.0, device="cuda") for _ in range(2)]
+    with pytest.raises(PrnnError) as e:                       # an output doubles as the workspace
+        handle.forward_stack_dense(two, x, outs=outs, workspace=outs[1])
+    assert e.value.status == binding.BAD_PARAM
+    with pytest.raises(PrnnError) as e:                       # two layers share one output
+        handle.forward_stack_dense(two, x, outs=[outs[0], outs[0]])
+    assert e.value.status == binding.BAD_PARAM
+    handle.synchronize()
+    assert all(bool((o == 3.0).all()) for o in outs)           # nothing ran
+    empty = handle.forward_stack_dense(two, x[:0], outs=[o[:0] for o in outs])
+    assert all(o.numel() == 0 for o in empty)
