@@ -66,6 +66,9 @@ def parse():
                     help="run only warmup + the timed region (every launch is a T=256 call; for profiles)")
     ap.add_argument("--no-baselines", action="store_true", help="skip the library and torch-CPU loop baselines")
     ap.add_argument("--no-layers", action="store_true", help="skip the whole-layer (projection + recurrence) table")
+    ap.add_argument("--profile-layers", action="store_true",
+                    help="with --only-timed: also run 5 input projections, one layer call and one 2-layer stack "
+                         "(N=1792, T=256) after the timed loop, for profilers")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config table (every workload, not timed "
                     "in the headline step)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -339,8 +342,9 @@ def layer_table(torch, dev, Handle, timed, no_check=False):
 
 
 def stack_table(torch, dev, Handle, timed, no_check=False):
-    """Two-layer stacks (B = 4, T = 256) as one wavefront against the same two
-    layers run one after the other (two layer calls), at N = 1152 and 1792."""
+    """Two-layer stacks (B = 4, T = 256) through prnn_forward_stack_dense against
+    the same two layers run as two layer calls, at N = 1152 (a wavefront) and
+    1792 (the library runs the layers one after another there)."""
     import numpy as np
     from persistent_rnn_fwd_amd.inputs import WORKLOADS, generate_stack
     rows = {}
@@ -365,6 +369,8 @@ def stack_table(torch, dev, Handle, timed, no_check=False):
         t_seq = timed(sequential)
         row = {
             "layers": 2, "N": N, "B": B, "T": T,
+            # the library runs a wavefront where [U | W] fits the registers widened (N <= 1280)
+            "stack_runs_as": "wavefront" if N <= 1280 else "one layer after another",
             "wavefront_us": round(t_wave * 1e3, 1),
             "wavefront_timesteps_per_s": round(T / (t_wave * 1e-3), 1),
             "sequential_layers_us": round(t_seq * 1e3, 1),
@@ -515,6 +521,18 @@ def main():
         return float(np.median([a.elapsed_time(b) for a, b in es]))
 
     detail = {}
+    if args.only_timed and args.profile_layers:
+        from persistent_rnn_fwd_amd.inputs import generate_layer, generate_stack
+        dl = generate_layer(wd, wd.N)
+        gl = {k: torch.from_numpy(v).to(dev) for k, v in dl.items()}
+        Xw = torch.empty((T, B, N), dtype=torch.float32, device=dev)
+        for _ in range(5):
+            h.project(gl["U"], gl["x"], gl["bias"], out=Xw)
+        h.forward_layer_dense(gl["U"], gl["bias"], gl["W"], gl["x"], gl["h0"], out=out[wd.name], workspace=Xw)
+        st = generate_stack(wd, 2)
+        layers = [{k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in ly.items()} for ly in st["layers"]]
+        h.forward_stack_dense(layers, torch.from_numpy(st["x"]).to(dev), workspace=Xw)
+        h.synchronize()
     if args.only_timed:
         h.close()
         print(json.dumps({"metric": "RNN timesteps/s & eff. GFLOP/s, N=1792 B=4 dense+10% sparse; % roofline",

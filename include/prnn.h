@@ -236,7 +236,11 @@ prnnStatus_t prnn_forward_layer_sparse(prnnHandle_t handle, int N, int I, int B,
  *
  * Layer l + 1's step t needs only layer l's step t and its own step t - 1,
  * so all layers run at the same time on separate XCDs (layer l, batch row b
- * on XCD l B + b; hence L B <= 8).  x [T][B][I] (fp32 or fp16); U[0] [N][I],
+ * on XCD l B + b; hence L B <= 8), each keeping [U_l | W_l] in registers
+ * widened to fp32.  Where that does not fit (N > 1280) the layers run one
+ * after another instead (prnn_forward_layer_dense each, with layer l's
+ * output as layer l + 1's input), which measures faster than a wavefront
+ * with packed fp16 weights.  x [T][B][I] (fp32 or fp16); U[0] [N][I],
  * U[l >= 1] [N][N], W[l] [N][N], all fp16, 16-byte aligned; bias[l] [N] or
  * NULL; Xbuf [T][B][N] fp32 workspace; H[l] [T][B][N] fp32 outputs.  U, bias,
  * W, h0 and H are host arrays of L device pointers (bias and h0 may be NULL
@@ -246,9 +250,9 @@ prnnStatus_t prnn_forward_layer_sparse(prnnHandle_t handle, int N, int I, int B,
  * BAD_PARAM: NULL handle/arrays/pointers, L < 1, N < 1, I < 1, B outside
  * [1, 8], T < 0, unknown x_type, misalignment, any output overlapping any
  * input, the workspace or another output, the workspace overlapping an
- * input.  NOT_SUPPORTED: L B > 8 or L > 8, no instance for N (rows per wave
- * and 256-column chunks up to 7 x 7: N <= 1792), sizes over 4 GiB, and what
- * prnn_project does not support.  EXECUTION_FAILED (at prnn_synchronize):
+ * input.  NOT_SUPPORTED: L B > 8 or L > 8, sizes over 4 GiB, and what
+ * prnn_project or (one layer after another) prnn_forward_dense does not
+ * support.  EXECUTION_FAILED (at prnn_synchronize):
  * a bounded wait expired, or x exceeded the fp16 range of its split.
  * T == 0 enqueues nothing and returns SUCCESS. */
 prnnStatus_t prnn_forward_stack_dense(prnnHandle_t handle, int L, int N, int I, int B, int T,

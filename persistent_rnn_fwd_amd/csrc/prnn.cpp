@@ -753,9 +753,22 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B
   p.max_rows = (N + Q - 1) / Q;
   p.chunks = (N + 255) / 256;
   p.k = pick(prnn::kStackKernels, p.max_rows, p.chunks);
-  if (p.k == nullptr) return PRNN_STATUS_NOT_SUPPORTED;
-  p.lds_bytes = 2 * 2 * 256 * p.k->cap * 4;  // [2 steps][input, state][chunks x 256]
-  if ((size_t)p.lds_bytes + 256 > h->lds_per_block) return PRNN_STATUS_NOT_SUPPORTED;
+  p.lds_bytes = p.k != nullptr ? 2 * 2 * 256 * p.k->cap * 4 : 0;  // [2 steps][input, state][chunks x 256]
+  if (p.k == nullptr || (size_t)p.lds_bytes + 256 > h->lds_per_block) {
+    // No wavefront instance (the weights would not fit the registers
+    // widened): the layers one after another, each a projection and a
+    // recurrence.  Every layer's recurrence must have a plan.
+    Plan lp;
+    if (!plan(h, kDense, N, B, 0, prnn::kF16, &lp)) return PRNN_STATUS_NOT_SUPPORTED;
+    for (int l = 0; l < L; ++l) {
+      prnnStatus_t st = prnn_forward_layer_dense(h, N, l == 0 ? I : N, B, T, l == 0 ? x_type : PRNN_DATA_FLOAT,
+                                                 l == 0 ? x : H[l - 1], PRNN_DATA_HALF, U[l],
+                                                 bias != nullptr ? bias[l] : nullptr, PRNN_DATA_HALF, W[l],
+                                                 h0 != nullptr ? h0[l] : nullptr, Xbuf, H[l], stream);
+      if (st != PRNN_STATUS_SUCCESS) return st;
+    }
+    return PRNN_STATUS_SUCCESS;
+  }
   // Layer 0's input projection, checked before anything is enqueued.
   prnn::ProjArgs pa;
   bool vec = false;

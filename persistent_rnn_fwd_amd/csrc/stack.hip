@@ -8,7 +8,8 @@
 // team x serves layer x / B and batch row x % B, so L B <= 8.  Layer 0 runs
 // the dense team recurrence over its precomputed input X0[t] (the projection
 // of the network input).  A layer l >= 1 keeps the rows of [U_l | W_l] in
-// registers and multiplies them with the staged row [H_{l-1}[t] ; h_l[t-1]]:
+// registers (widened to fp32) and multiplies them with the staged row
+// [H_{l-1}[t] ; h_l[t-1]]:
 //
 //   h_l[t] = max(0, bias_l + U_l H_{l-1}[t] + W_l h_l[t-1]).
 //
@@ -24,7 +25,7 @@
 namespace prnn {
 namespace {
 
-template <int RW, int J>
+template <int RW, int J, bool WIDE>
 __global__ void __launch_bounds__(512) stack_team_kernel(StackArgs a) {
   constexpr int M = pow2_at_least(RW);
   constexpr int kHalf = 256 * J;  // one half of an LDS row: input part, then state part
@@ -65,8 +66,9 @@ __global__ void __launch_bounds__(512) stack_team_kernel(StackArgs a) {
 
   const bool has_input = layer > 0;
   const bool vec = (N & 3) == 0;
-  // w[r][j]: j < J the input part (U_l), j >= J the state part (W_l).
-  WChunk<_Float16> w[RW][2 * J];
+  // w[r][j]: j < J the input part (U_l), j >= J the state part (W_l); fp16
+  // kept packed, or widened to fp32 registers once (WIDE).
+  typename TeamChunk<_Float16, WIDE>::type w[RW][2 * J];
 #pragma unroll
   for (int r = 0; r < RW; ++r)
 #pragma unroll
@@ -167,10 +169,13 @@ __global__ void __launch_bounds__(512) stack_team_kernel(StackArgs a) {
 
 }  // namespace
 
-#define PRNN_STACK(R, JJ) {kF16, R, JJ, reinterpret_cast<const void*>(&stack_team_kernel<R, JJ>)}
+#define PRNN_STACK(R, JJ) {kF16, R, JJ, reinterpret_cast<const void*>(&stack_team_kernel<R, JJ, true>)}
 const KernelEntry kStackKernels[] = {
-    // (rows per wave, 256-column chunks of each part)
-    PRNN_STACK(1, 1), PRNN_STACK(2, 2), PRNN_STACK(4, 4), PRNN_STACK(5, 5), PRNN_STACK(7, 7),
+    // (rows per wave, 256-column chunks of each part), weights widened to
+    // fp32 registers.  Larger layers would have to keep them packed (7 x 7 at
+    // N = 1792): measured slower than running the layers one after another,
+    // which is what the host does for them.
+    PRNN_STACK(1, 1), PRNN_STACK(2, 2), PRNN_STACK(4, 4), PRNN_STACK(5, 5),
     {0, 0, 0, nullptr},
 };
 
