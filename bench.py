@@ -42,8 +42,9 @@ if ROOT not in sys.path:
 FP32_VECTOR_PEAK = 157.3e12   # MI355X published fp32 vector peak, FLOP/s
 HBM_PEAK = 8.0e12             # MI355X HBM3E, bytes/s
 COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_rnn_fwd_n1792.json")
-KERNEL_SOURCES = ["device_common.h", "kernels.h", "dense_kernel.h", "sparse_kernel.h", "team_kernel.h",
-                  "dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip", "team_f16.hip", "team_f32.hip"]
+KERNEL_SOURCES = ["device_common.h", "kernels.h", "dense_kernel.h", "sparse_kernel.h", "team_kernel.h", "team_mfma.h",
+                  "dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip", "team_f16.hip", "team_f32.hip",
+                  "project.hip", "stack.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -67,8 +68,8 @@ def parse():
     ap.add_argument("--no-baselines", action="store_true", help="skip the library and torch-CPU loop baselines")
     ap.add_argument("--no-layers", action="store_true", help="skip the whole-layer (projection + recurrence) table")
     ap.add_argument("--profile-layers", action="store_true",
-                    help="with --only-timed: also run 5 input projections, one layer call and one 2-layer stack "
-                         "(N=1792, T=256) after the timed loop, for profilers")
+                    help="with --only-timed: also run 5 input projections and one layer call (N=1792) and one "
+                         "2-layer stack wavefront (N=1152), T=256, after the timed loop, for profilers")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config table (every workload, not timed "
                     "in the headline step)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -529,9 +530,9 @@ def main():
         for _ in range(5):
             h.project(gl["U"], gl["x"], gl["bias"], out=Xw)
         h.forward_layer_dense(gl["U"], gl["bias"], gl["W"], gl["x"], gl["h0"], out=out[wd.name], workspace=Xw)
-        st = generate_stack(wd, 2)
+        st = generate_stack(WORKLOADS["dense_f16_n1152"], 2)  # the largest wavefront size
         layers = [{k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in ly.items()} for ly in st["layers"]]
-        h.forward_stack_dense(layers, torch.from_numpy(st["x"]).to(dev), workspace=Xw)
+        h.forward_stack_dense(layers, torch.from_numpy(st["x"]).to(dev))
         h.synchronize()
     if args.only_timed:
         h.close()
