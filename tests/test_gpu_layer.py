@@ -217,3 +217,44 @@ def test_layer_rejects_workspace_over_h0_and_enqueues_nothing(handle):
     assert st == binding.BAD_PARAM                          # workspace is H
     handle.synchronize()
     assert bool((H == 9.0).all())
+
+
+def test_project_long_ragged_reduction(handle):
+    """I = 2050 (not a multiple of 8: the element-wise path over 65 k-steps)."""
+    rng = np.random.default_rng(12)
+    U, x, b = draw(rng, 70, 90, 2050)
+    X = handle.project(dev(U), dev(x), dev(b))
+    handle.synchronize()
+    assert proj_ratio(X.cpu().numpy(), U, x, b) <= 1.0
+
+
+@pytest.mark.parametrize("kind", ["dense", "sparse"])
+def test_layer_chunked_in_time(handle, kind):
+    """One layer call over T steps equals two calls over T1 and T - T1 steps with
+    h0 = the first call's last state (within 1e-6; bitwise expected)."""
+    base = "dense_f16_n1152" if kind == "dense" else "sparse10_f16_n1152"
+    w = WORKLOADS[base].with_(N=640 if kind == "dense" else 1152, T=16, h0="randn", seed=41)
+    d = generate_layer(w, 200)
+    g = {k: dev(v) for k, v in d.items()}
+
+    def layer(x, h0):
+        if kind == "dense":
+            return handle.forward_layer_dense(g["U"], g["bias"], g["W"], x, h0)
+        return handle.forward_layer_sparse(g["U"], g["bias"], g["col"], g["val"], x, h0)
+    full = layer(g["x"], g["h0"])
+    a = layer(g["x"][:7].contiguous(), g["h0"])
+    b = layer(g["x"][7:].contiguous(), a[-1].contiguous())
+    handle.synchronize()
+    both = torch.cat([a, b]).cpu().numpy()
+    print(f"layer {kind} chunked: bitwise {np.array_equal(both, full.cpu().numpy())}")
+    np.testing.assert_allclose(both, full.cpu().numpy(), rtol=1e-6, atol=1e-6)
+
+
+def test_layer_sparse_fp32_values(handle):
+    w = WORKLOADS["sparse10_f16_n1152"].with_(N=512, K=40, T=6, w_dtype="f32", h0="randn", seed=44)
+    d = generate_layer(w, 128, x_dtype="f16")
+    g = {k: dev(v) for k, v in d.items()}
+    H = handle.forward_layer_sparse(g["U"], g["bias"], g["col"], g["val"], g["x"], g["h0"])
+    handle.synchronize()
+    ref = oracle.forward_layer_sparse(d["U"], d["bias"], d["col"], d["val"], d["x"], d["h0"])
+    assert oracle.tolerance_ratio(H.cpu().numpy(), ref, oracle.TOL_F32) <= 1.0

@@ -116,3 +116,22 @@ def test_stack_errors(handle):
     assert all(bool((o == 3.0).all()) for o in outs)           # nothing ran
     empty = handle.forward_stack_dense(two, x[:0], outs=[o[:0] for o in outs])
     assert all(o.numel() == 0 for o in empty)
+
+
+@pytest.mark.parametrize("N", [384, 1792])
+def test_stack_chunked_in_time(handle, N):
+    """A stack over T steps equals two stack calls over T1 and T - T1 steps, the
+    second starting from every layer's last state (within 1e-6; wavefront at
+    N=384, layers one after another at N=1792)."""
+    w = WORKLOADS["dense_f16_n1152"].with_(N=N, B=2, T=12, h0="randn", seed=77)
+    st = generate_stack(w, 3)
+    layers = [{k: dev(v) for k, v in ly.items()} for ly in st["layers"]]
+    x = dev(st["x"])
+    h0s = [dev(v) for v in st["h0s"]]
+    full = handle.forward_stack_dense(layers, x, h0s)
+    a = handle.forward_stack_dense(layers, x[:5].contiguous(), h0s)
+    b = handle.forward_stack_dense(layers, x[5:].contiguous(), [o[-1].contiguous() for o in a])
+    handle.synchronize()
+    for l in range(3):
+        both = torch.cat([a[l], b[l]]).cpu().numpy()
+        np.testing.assert_allclose(both, full[l].cpu().numpy(), rtol=1e-6, atol=1e-6)
