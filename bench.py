@@ -343,9 +343,9 @@ def layer_table(torch, dev, Handle, timed, no_check=False):
 
 
 def stack_table(torch, dev, Handle, timed, no_check=False):
-    """Two-layer stacks (B = 4, T = 256) through prnn_forward_stack_dense against
-    the same two layers run as two layer calls, at N = 1152 (a wavefront) and
-    1792 (the library runs the layers one after another there)."""
+    """Two-layer stacks (B = 4, T = 256) through prnn_forward_stack_dense (its
+    default, the blocked wavefront) against the same two layers run as two
+    layer calls, at N = 1152 and 1792."""
     import numpy as np
     from persistent_rnn_fwd_amd.inputs import WORKLOADS, generate_stack
     rows = {}
@@ -370,8 +370,7 @@ def stack_table(torch, dev, Handle, timed, no_check=False):
         t_seq = timed(sequential)
         row = {
             "layers": 2, "N": N, "B": B, "T": T,
-            # the library runs a wavefront where [U | W] fits the registers widened (N <= 1280)
-            "stack_runs_as": "wavefront" if N <= 1280 else "one layer after another",
+            "stack_runs_as": "blocked wavefront (blocks of about 64 steps)",
             "wavefront_us": round(t_wave * 1e3, 1),
             "wavefront_timesteps_per_s": round(T / (t_wave * 1e-3), 1),
             "sequential_layers_us": round(t_seq * 1e3, 1),

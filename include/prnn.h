@@ -235,18 +235,20 @@ prnnStatus_t prnn_forward_layer_sparse(prnnHandle_t handle, int N, int I, int B,
  *   H[l][-1]  = h0[l] (zeros if h0 or h0[l] is NULL)
  *
  * Layer l + 1's step t needs only layer l's step t and its own step t - 1,
- * so all layers run at the same time on separate XCDs (layer l, batch row b
- * on XCD l B + b; hence L B <= 8), each keeping [U_l | W_l] in registers
- * widened to fp32.  Where that does not fit (N > 1280) the layers run one
- * after another instead (prnn_forward_layer_dense each, with layer l's
- * output as layer l + 1's input), which measures faster than a wavefront
- * with packed fp16 weights.  x [T][B][I] (fp32 or fp16); U[0] [N][I],
+ * so the layers run at the same time on separate XCDs (layer l, batch row b
+ * on XCD l B + b; hence L B <= 8), keeping their weights in registers
+ * widened to fp32 (prnnStackMode_t: in blocks of steps, layer l + 1 one block
+ * behind layer l with the input projections between the launches; or fused
+ * per step).  Where the weights do not fit (N > 1792) the layers run one
+ * after another (prnn_forward_layer_dense each, with layer l's output as
+ * layer l + 1's input).  x [T][B][I] (fp32 or fp16); U[0] [N][I],
  * U[l >= 1] [N][N], W[l] [N][N], all fp16, 16-byte aligned; bias[l] [N] or
  * NULL; Xbuf [T][B][N] fp32 workspace; H[l] [T][B][N] fp32 outputs.  U, bias,
  * W, h0 and H are host arrays of L device pointers (bias and h0 may be NULL
- * arrays).  All device buffers are the caller's.  H[0] .. H[L-2] are also
- * the hand-over between layers (filled with a marker before the launch and
- * overwritten by the results).  Not traced.
+ * arrays).  All device buffers are the caller's.  H[1] .. H[L-1] (blocked)
+ * or H[0] .. H[L-2] (fused) also carry intermediate values (the next layer's
+ * projected input, or a not-yet-written marker) before the results
+ * overwrite them.  Not traced.
  * BAD_PARAM: NULL handle/arrays/pointers, L < 1, N < 1, I < 1, B outside
  * [1, 8], T < 0, unknown x_type, misalignment, any output overlapping any
  * input, the workspace or another output, the workspace overlapping an
@@ -255,6 +257,25 @@ prnnStatus_t prnn_forward_layer_sparse(prnnHandle_t handle, int N, int I, int B,
  * support.  EXECUTION_FAILED (at prnn_synchronize):
  * a bounded wait expired, or x exceeded the fp16 range of its split.
  * T == 0 enqueues nothing and returns SUCCESS. */
+/* How prnn_forward_stack_dense runs the layers (see there).
+ * BLOCKED: blocks of about 64 steps, layer l one block behind layer l - 1,
+ *   the input projections of the next blocks between the launches.
+ * FUSED: one launch; each layer l >= 1 forms U_l H_{l-1}[t] itself at every
+ *   step (N <= 1280).
+ * LAYERS: one layer after another (prnn_forward_layer_dense each).
+ * AUTO: BLOCKED where an instance fits (N <= 1792), else LAYERS. */
+typedef enum {
+  PRNN_STACK_AUTO = 0,
+  PRNN_STACK_BLOCKED = 1,
+  PRNN_STACK_FUSED = 2,
+  PRNN_STACK_LAYERS = 3
+} prnnStackMode_t;
+
+/* Stack mode for later calls (default AUTO).  A forced mode the shape
+ * cannot use makes stack calls return NOT_SUPPORTED.  BAD_PARAM for an
+ * unknown mode. */
+prnnStatus_t prnn_set_stack_mode(prnnHandle_t handle, prnnStackMode_t mode);
+
 prnnStatus_t prnn_forward_stack_dense(prnnHandle_t handle, int L, int N, int I, int B, int T,
                                       prnnDataType_t x_type, const void* x,
                                       const void* const* U, const float* const* bias,

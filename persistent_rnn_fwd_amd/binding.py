@@ -28,6 +28,7 @@ DATA_FLOAT, DATA_HALF = 0, 1
 EXCHANGE_AUTO, EXCHANGE_DIRECT, EXCHANGE_RELAY = 0, 1, 2
 LAYOUT_AUTO, LAYOUT_SPREAD, LAYOUT_TEAM = 0, 1, 2
 MATH_AUTO, MATH_EXACT, MATH_SPLIT = 0, 1, 2
+STACK_AUTO, STACK_BLOCKED, STACK_FUSED, STACK_LAYERS = 0, 1, 2, 3
 TRACE_WORDS = 8  # per-wave trace record: see Handle.get_trace
 
 # Every function include/prnn.h declares, with its ctypes signature.
@@ -55,6 +56,7 @@ SIGNATURES = {
     "prnn_forward_layer_dense": (_I, [_H, _I, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P]),
     "prnn_forward_layer_sparse": (_I, [_H, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
     "prnn_forward_stack_dense": (_I, [_H, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "prnn_set_stack_mode": (_I, [_H, _I]),
 }
 
 
@@ -167,6 +169,10 @@ class Handle:
     def set_layout(self, layout: int):
         """LAYOUT_AUTO, LAYOUT_SPREAD or LAYOUT_TEAM for later calls."""
         _check("prnn_set_layout", self._lib.prnn_set_layout(self._h, int(layout)))
+
+    def set_stack_mode(self, mode: int):
+        """STACK_AUTO, STACK_BLOCKED, STACK_FUSED or STACK_LAYERS for later stack calls."""
+        _check("prnn_set_stack_mode", self._lib.prnn_set_stack_mode(self._h, mode))
 
     def set_math(self, mode: int):
         """MATH_AUTO, MATH_EXACT or MATH_SPLIT (dense fp16) for later calls."""

@@ -91,17 +91,19 @@ struct StackArgs {
   const void* U[kMaxStack];      // fp16 [N][N] input weights of layers >= 1 (U[0] unused)
   const float* bias[kMaxStack];  // [N] or nullptr, layers >= 1 (layer 0's is in X0)
   const float* h0[kMaxStack];    // [B][N] or nullptr (zeros)
-  float* H[kMaxStack];           // [T][B][N]; H[0 .. L-2] filled with 0xFFFFFFFF before the launch
-  const float* X0;               // [T][B][N] pre-activations of layer 0
+  float* H[kMaxStack];           // [Tl][B][N] outputs (fused: H[0 .. L-2] filled with 0xFFFFFFFF first)
+  const float* X[kMaxStack];     // [Tl][B][N] pre-activations (fused: layer 0 only; may alias H[l])
+  int Tl[kMaxStack];             // steps of layer l in this launch (<= T; 0: idle)
   uint32_t* ring;                // [8][2][Npad]
   uint32_t* status;
   int L, N, B, T, Npad, chunks, base_rows, extra_rows;
   uint32_t step0;
-  uint32_t x_bytes;              // bytes of one [T][B][N] sequence
+  uint32_t x_bytes;              // bytes of one [T][B][N] sequence (T = the launch's steps)
   uint64_t deadline;
 };
 // (rmax = rows per wave, cap = chunks of each part)
-extern const KernelEntry kStackKernels[];
+extern const KernelEntry kStackFusedKernels[];
+extern const KernelEntry kStackBlockedKernels[];
 
 // Input projection X[m][n] = bias[n] + sum_i U[n][i] x[m][i] (project.hip).
 struct ProjArgs {

@@ -39,6 +39,7 @@ struct prnnContext {
   int forced_grid = 0;
   uint32_t watchdog_us = 200000;
   int math = PRNN_MATH_AUTO;
+  int stack_mode = PRNN_STACK_AUTO;
   int skip_wg = -1;
   int skip_step = -1;
   prnnPlanInfo_t last_plan{};
@@ -752,12 +753,19 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B
   p.extra_rows = N % Q;
   p.max_rows = (N + Q - 1) / Q;
   p.chunks = (N + 255) / 256;
-  p.k = pick(prnn::kStackKernels, p.max_rows, p.chunks);
-  p.lds_bytes = p.k != nullptr ? 2 * 2 * 256 * p.k->cap * 4 : 0;  // [2 steps][input, state][chunks x 256]
-  if (p.k == nullptr || (size_t)p.lds_bytes + 256 > h->lds_per_block) {
-    // No wavefront instance (the weights would not fit the registers
-    // widened): the layers one after another, each a projection and a
-    // recurrence.  Every layer's recurrence must have a plan.
+  const prnn::KernelEntry* kb = pick(prnn::kStackBlockedKernels, p.max_rows, p.chunks);
+  const prnn::KernelEntry* kf = pick(prnn::kStackFusedKernels, p.max_rows, p.chunks);
+  const int lds_b = kb != nullptr ? 2 * 256 * kb->cap * 4 : 0;  // [2 steps][chunks x 256]
+  const int lds_f = kf != nullptr ? 2 * 2 * 256 * kf->cap * 4 : 0;  // [2 steps][input, state][chunks x 256]
+  if (kb != nullptr && (size_t)lds_b + 256 > h->lds_per_block) kb = nullptr;
+  if (kf != nullptr && (size_t)lds_f + 256 > h->lds_per_block) kf = nullptr;
+  int mode = h->stack_mode;
+  if (mode == PRNN_STACK_AUTO) mode = kb != nullptr ? PRNN_STACK_BLOCKED : PRNN_STACK_LAYERS;
+  if ((mode == PRNN_STACK_BLOCKED && kb == nullptr) || (mode == PRNN_STACK_FUSED && kf == nullptr))
+    return PRNN_STATUS_NOT_SUPPORTED;
+  if (mode == PRNN_STACK_LAYERS) {
+    // The layers one after another, each a projection and a recurrence.
+    // Every layer's recurrence must have a plan.
     Plan lp;
     if (!plan(h, kDense, N, B, 0, prnn::kF16, &lp)) return PRNN_STATUS_NOT_SUPPORTED;
     for (int l = 0; l < L; ++l) {
@@ -769,6 +777,8 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B
     }
     return PRNN_STATUS_SUCCESS;
   }
+  p.k = mode == PRNN_STACK_BLOCKED ? kb : kf;
+  p.lds_bytes = mode == PRNN_STACK_BLOCKED ? lds_b : lds_f;
   // Layer 0's input projection, checked before anything is enqueued.
   prnn::ProjArgs pa;
   bool vec = false;
@@ -782,38 +792,81 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B
   if (st != PRNN_STATUS_SUCCESS) return st;
   st = hip_status(prnn::launch_project(pa, x_type == PRNN_DATA_FLOAT, vec, stream));
   if (st != PRNN_STATUS_SUCCESS) return st;
-  for (int l = 0; l + 1 < L; ++l)  // "not written yet" marks for the layers that feed another
-    prnn::launch_fill(reinterpret_cast<uint32_t*>(H[l]), (size_t)T * B * N, 0xFFFFFFFFu, stream);
+
   prnn::StackArgs a;
   std::memset(&a, 0, sizeof(a));
   for (int l = 0; l < L; ++l) {
     a.W[l] = W[l];
     a.U[l] = U[l];
     a.bias[l] = bias != nullptr ? bias[l] : nullptr;
-    a.h0[l] = h0 != nullptr ? h0[l] : nullptr;
-    a.H[l] = H[l];
   }
-  a.X0 = Xbuf;
   a.ring = h->d_ring;
   a.status = h->d_status;
   a.L = L;
   a.N = N;
   a.B = B;
-  a.T = T;
   a.Npad = Npad;
   a.chunks = p.chunks;
   a.base_rows = p.base_rows;
   a.extra_rows = p.extra_rows;
-  a.step0 = static_cast<uint32_t>(h->step);
-  a.x_bytes = static_cast<uint32_t>(seq);
   a.deadline = static_cast<uint64_t>(h->watchdog_us) * 100ull;
-  void* args[] = {&a};
-  hipError_t e = hipLaunchCooperativeKernel(p.k->fn, dim3(p.grid), dim3(p.block), args,
-                                            static_cast<unsigned>(p.lds_bytes), stream);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return hip_status(e);
+  auto launch_stack = [&](int Tlaunch) -> prnnStatus_t {
+    a.T = Tlaunch;
+    a.step0 = static_cast<uint32_t>(h->step);
+    a.x_bytes = static_cast<uint32_t>((size_t)Tlaunch * B * N * 4);
+    void* args[] = {&a};
+    hipError_t e = hipLaunchCooperativeKernel(p.k->fn, dim3(p.grid), dim3(p.block), args,
+                                              static_cast<unsigned>(p.lds_bytes), stream);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return hip_status(e);
+    }
+    h->step += static_cast<uint64_t>(Tlaunch);
+    return PRNN_STATUS_SUCCESS;
+  };
+
+  if (mode == PRNN_STACK_FUSED) {
+    for (int l = 0; l + 1 < L; ++l)  // "not written yet" marks for the layers that feed another
+      prnn::launch_fill(reinterpret_cast<uint32_t*>(H[l]), (size_t)T * B * N, 0xFFFFFFFFu, stream);
+    for (int l = 0; l < L; ++l) {
+      a.h0[l] = h0 != nullptr ? h0[l] : nullptr;
+      a.H[l] = H[l];
+      a.Tl[l] = T;
+    }
+    a.X[0] = Xbuf;
+    st = launch_stack(T);
+  } else {
+    // Blocks of about 64 steps; launch i runs layer l on block i - l.  Before
+    // launch i, the input projection of every layer l >= 1 that enters block
+    // i - l is written into that block of H[l] (the recurrence reads it there
+    // and overwrites it with the outputs).
+    const int nb = std::max(1, (T + 32) / 64);
+    const int tau = (T + nb - 1) / nb;
+    const size_t blk = (size_t)tau * B * N;  // floats per full block
+    for (int i = 0; i < nb + L - 1 && st == PRNN_STATUS_SUCCESS; ++i) {
+      int Tlaunch = 0;
+      for (int l = 0; l < L; ++l) {
+        const int k = i - l;
+        const int len = (k >= 0 && k < nb) ? std::min(tau, T - k * tau) : 0;
+        a.Tl[l] = std::max(len, 0);
+        if (a.Tl[l] == 0) continue;
+        Tlaunch = std::max(Tlaunch, a.Tl[l]);
+        a.H[l] = H[l] + (size_t)k * blk;
+        a.X[l] = l == 0 ? Xbuf + (size_t)k * blk : H[l] + (size_t)k * blk;
+        a.h0[l] = k == 0 ? (h0 != nullptr ? h0[l] : nullptr) : H[l] + (size_t)k * blk - (size_t)B * N;
+        if (l > 0) {
+          prnn::ProjArgs pl;
+          bool vl = false;
+          st = prepare_project(h, a.Tl[l] * B, N, N, PRNN_DATA_FLOAT, H[l - 1] + (size_t)k * blk, PRNN_DATA_HALF,
+                               U[l], bias != nullptr ? bias[l] : nullptr, H[l] + (size_t)k * blk, &pl, &vl);
+          if (st == PRNN_STATUS_SUCCESS) st = hip_status(prnn::launch_project(pl, true, vl, stream));
+          if (st != PRNN_STATUS_SUCCESS) break;
+        }
+      }
+      if (st == PRNN_STATUS_SUCCESS && Tlaunch > 0) st = launch_stack(Tlaunch);
+    }
   }
+  if (st != PRNN_STATUS_SUCCESS) return st;
   prnnPlanInfo_t& info = h->last_plan;
   info.layout = p.layout;
   info.grid = p.grid;
@@ -827,7 +880,14 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B
   info.first_step = h->step;
   h->have_plan = true;
   h->trace_records = 0;
-  h->step += static_cast<uint64_t>(T);
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t prnn_set_stack_mode(prnnHandle_t h, prnnStackMode_t mode) {
+  if (h == nullptr) return PRNN_STATUS_BAD_PARAM;
+  if (mode != PRNN_STACK_AUTO && mode != PRNN_STACK_BLOCKED && mode != PRNN_STACK_FUSED && mode != PRNN_STACK_LAYERS)
+    return PRNN_STATUS_BAD_PARAM;
+  h->stack_mode = mode;
   return PRNN_STATUS_SUCCESS;
 }
 

@@ -1,13 +1,23 @@
-// A stack of L dense fp16 layers as one wavefront ("Optimizing Performance of
+// A stack of L dense fp16 layers as a wavefront ("Optimizing Performance of
 // Recurrent Neural Networks on GPUs", Abstract, entire-network stage: layer
 // l + 1's step t depends only on layer l's step t and on its own step t - 1,
-// so the layers run at the same time, each a step or more behind the one
-// below, on their own compute units).
+// so the layers run at the same time, each behind the one below, on their
+// own compute units).
 //
 // The grid is the team layout's (8 teams of P workgroups, team x on XCD x);
-// team x serves layer x / B and batch row x % B, so L B <= 8.  Layer 0 runs
-// the dense team recurrence over its precomputed input X0[t] (the projection
-// of the network input).  A layer l >= 1 keeps the rows of [U_l | W_l] in
+// team x serves layer x / B and batch row x % B, so L B <= 8.  Team (l, b)
+// runs Tl[l] steps of its layer from its own pre-activations X[l] (0 steps:
+// it only keeps its region current).  Two ways to feed the layers:
+//
+// Blocked (FUSED = false): every layer adds X[l][t], computed before the
+// launch.  The host cuts the sequence into blocks and launch i runs layer l
+// on block i - l: layer l + 1 runs one block behind layer l, and between
+// launches the input projection of the next blocks (U_l H_{l-1} + bias_l,
+// on the matrix cores) is written in place into H_l, which the recurrence
+// then reads (each element by the lane that later overwrites it).
+//
+// Fused (FUSED = true): layer 0 adds X[0][t]; a layer l >= 1 keeps the rows
+// of [U_l | W_l] in
 // registers (widened to fp32) and multiplies them with the staged row
 // [H_{l-1}[t] ; h_l[t-1]]:
 //
@@ -25,11 +35,12 @@
 namespace prnn {
 namespace {
 
-template <int RW, int J, bool WIDE>
+template <int RW, int J, bool FUSED>
 __global__ void __launch_bounds__(512) stack_team_kernel(StackArgs a) {
   constexpr int M = pow2_at_least(RW);
   constexpr int kHalf = 256 * J;  // one half of an LDS row: input part, then state part
-  extern __shared__ __attribute__((aligned(16))) float lds[];  // [2 steps][2 halves][kHalf]
+  constexpr int kParts = FUSED ? 2 : 1;
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // [2 steps][kParts][kHalf]
   __shared__ int abort_flag;
   const int team = blockIdx.x & 7;
   const int rank = blockIdx.x >> 3;
@@ -37,7 +48,7 @@ __global__ void __launch_bounds__(512) stack_team_kernel(StackArgs a) {
   const int lane = threadIdx.x & 63;
   const int layer = team / a.B;
   const int b = team % a.B;
-  const bool primary = team < a.L * a.B;
+  const bool primary = team < a.L * a.B && a.Tl[team / a.B] > 0;
   const int q = rank * kTeamWaves + wave;
   const int nr = a.base_rows + (q < a.extra_rows ? 1 : 0);
   const int r0 = q * a.base_rows + min(q, a.extra_rows);
@@ -46,46 +57,51 @@ __global__ void __launch_bounds__(512) stack_team_kernel(StackArgs a) {
 
   if (threadIdx.x == 0) abort_flag = __builtin_nontemporal_load(a.status) != 0u;
   // Words past N in each half stay zero (their weights are zero too).
-  for (int c = threadIdx.x; c < 4 * kHalf; c += blockDim.x)
+  for (int c = threadIdx.x; c < 2 * kParts * kHalf; c += blockDim.x)
     if (c % kHalf >= N) lds[c] = 0.f;
   __syncthreads();
   if (abort_flag) return;
   const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (31 << 11)) & 7u;  // HW_REG_XCC_ID
   const __amdgpu_buffer_rsrc_t region = make_rsrc(a.ring + (size_t)xcc * 2 * a.Npad, 2u * a.Npad * 4u);
-  if (!primary) {
-    // No (layer, batch row) of its own: keep the region continuous for the
-    // next call (the tags of this call's last two steps on its rows).
+  // Keeps the region continuous for the next launch: the tags of this
+  // launch's last two steps on this wave's rows (teams that run no step, or
+  // fewer steps than the launch).
+  auto stamp_tail = [&]() {
     const uint32_t last = a.step0 + (uint32_t)(a.T - 1);
     for (int k = 0; k < 2 && k < a.T; ++k) {
       const uint32_t S = last - (uint32_t)k;
       for (int r = lane; r < nr; r += 64)
         __builtin_amdgcn_raw_buffer_store_b32(tag_bit(S), region, ((S & 1u) * a.Npad + r0 + r) * 4u, 0, kPlain);
     }
+  };
+  if (!primary) {
+    stamp_tail();
     return;
   }
 
-  const bool has_input = layer > 0;
+  const int Tl = a.Tl[layer];
+  const bool has_input = FUSED && layer > 0;
   const bool vec = (N & 3) == 0;
-  // w[r][j]: j < J the input part (U_l), j >= J the state part (W_l); fp16
-  // kept packed, or widened to fp32 registers once (WIDE).
-  typename TeamChunk<_Float16, WIDE>::type w[RW][2 * J];
+  // w[r][j]: (fused) j < J the input part (U_l), then the state part (W_l);
+  // fp16 widened to fp32 registers once.
+  WChunkWide w[RW][kParts * J];
 #pragma unroll
   for (int r = 0; r < RW; ++r)
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const size_t off = (size_t)(r0 + r) * N;
       const bool live = r < nr && j < jn;
-      w[r][j].load(a.U[layer], off, 256 * j + 4 * lane, N, live && has_input, vec);
-      w[r][J + j].load(a.W[layer], off, 256 * j + 4 * lane, N, live, vec);
+      if (FUSED) w[r][j].load(a.U[layer], off, 256 * j + 4 * lane, N, live && has_input, vec);
+      w[r][(kParts - 1) * J + j].load(a.W[layer], off, 256 * j + 4 * lane, N, live, vec);
     }
 
   const int my_row = RowReduce<M>::owner_row(lane);
   const bool owner = my_row >= 0 && my_row < nr;
   const int row = r0 + (owner ? my_row : 0);
   const uint32_t hbytes = a.x_bytes;  // every [T][B][N] sequence has this size
-  const __amdgpu_buffer_rsrc_t in = make_rsrc(has_input ? a.H[layer - 1] : a.X0, hbytes);
+  const __amdgpu_buffer_rsrc_t in = make_rsrc(has_input ? a.H[layer - 1] : a.X[layer], hbytes);
   const __amdgpu_buffer_rsrc_t out = make_rsrc(a.H[layer], hbytes);
-  const bool feeds_next = layer + 1 < a.L;
+  const bool feeds_next = FUSED && layer + 1 < a.L;
   // Layer 0 adds X0[t] (loaded a step ahead); the others add their bias.
   const float bias = (has_input && owner && a.bias[layer] != nullptr) ? a.bias[layer][row] : 0.f;
   const uint32_t xstep = (uint32_t)a.B * (uint32_t)N * 4u;
@@ -93,10 +109,10 @@ __global__ void __launch_bounds__(512) stack_team_kernel(StackArgs a) {
   float x_next = has_input ? 0.f : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in, xoff, 0, kPlain));
   const float* h0 = a.h0[layer];
 
-  for (int t = 0; t < a.T; ++t) {
+  for (int t = 0; t < Tl; ++t) {
     const uint32_t S = a.step0 + (uint32_t)t;
-    float* inrow = lds + (t & 1) * 2 * kHalf;
-    float* strow = inrow + kHalf;
+    float* inrow = lds + (t & 1) * kParts * kHalf;
+    float* strow = inrow + (kParts - 1) * kHalf;
     bool ok = true;
     // Staging tasks: the state part's chunks, then (layers >= 1) the input
     // part's, dealt over the 8 waves.
@@ -140,14 +156,14 @@ __global__ void __launch_bounds__(512) stack_team_kernel(StackArgs a) {
     int aborted_now = abort_flag;
     const float x = has_input ? bias : x_next;
     xoff += xstep;
-    if (!has_input && t + 1 < a.T) x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in, xoff, 0, kPlain));
+    if (!has_input && t + 1 < Tl) x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in, xoff, 0, kPlain));
 
     float acc[M];
 #pragma unroll
     for (int r = 0; r < M; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 2 * J; ++j) {
-      if (j < J && !has_input) continue;  // layer 0 has no input part
+    for (int j = 0; j < kParts * J; ++j) {
+      if (FUSED && j < J && !has_input) continue;  // layer 0 has no input part
       const float4 h = *reinterpret_cast<const float4*>(inrow + 256 * j + 4 * lane);
 #pragma unroll
       for (int r = 0; r < RW; ++r) w[r][j].fma4(acc[r], h);
@@ -165,17 +181,20 @@ __global__ void __launch_bounds__(512) stack_team_kernel(StackArgs a) {
         __builtin_amdgcn_raw_buffer_store_b32(hb, out, hoff, 0, kPlain);
     }
   }
+  if (Tl < a.T) stamp_tail();
 }
 
 }  // namespace
 
-#define PRNN_STACK(R, JJ) {kF16, R, JJ, reinterpret_cast<const void*>(&stack_team_kernel<R, JJ, true>)}
-const KernelEntry kStackKernels[] = {
-    // (rows per wave, 256-column chunks of each part), weights widened to
-    // fp32 registers.  Larger layers would have to keep them packed (7 x 7 at
-    // N = 1792): measured slower than running the layers one after another,
-    // which is what the host does for them.
-    PRNN_STACK(1, 1), PRNN_STACK(2, 2), PRNN_STACK(4, 4), PRNN_STACK(5, 5),
+#define PRNN_STACK(R, JJ, F) {kF16, R, JJ, reinterpret_cast<const void*>(&stack_team_kernel<R, JJ, F>)}
+// (rows per wave, 256-column chunks of each part), weights widened to fp32.
+const KernelEntry kStackFusedKernels[] = {
+    PRNN_STACK(1, 1, true), PRNN_STACK(2, 2, true), PRNN_STACK(4, 4, true), PRNN_STACK(5, 5, true),
+    {0, 0, 0, nullptr},
+};
+const KernelEntry kStackBlockedKernels[] = {
+    PRNN_STACK(1, 1, false), PRNN_STACK(2, 2, false), PRNN_STACK(4, 4, false), PRNN_STACK(5, 5, false),
+    PRNN_STACK(7, 7, false),
     {0, 0, 0, nullptr},
 };
 

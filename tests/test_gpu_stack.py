@@ -1,9 +1,9 @@
-"""GPU parity of a stack of dense layers run as one wavefront (through the C ABI).
+"""GPU parity of a stack of dense layers run as a wavefront (through the C ABI).
 
-``prnn_forward_stack_dense`` runs layer 0's input projection, then every
-layer of the stack at the same time (layer l, batch row b on its own XCD),
-layer l + 1 reading layer l's outputs as they appear; for layers too large
-for that (N > 1280) it runs them one after another.  It is compared with
+``prnn_forward_stack_dense`` runs layer 0's input projection, then the layers
+at the same time (layer l, batch row b on its own XCD): in blocks of steps,
+layer l + 1 one block behind layer l (BLOCKED, the default), or fused per
+step (FUSED); or one layer after another (LAYERS, and for N > 1792).  It is compared with
 ``oracle.forward_stack_dense`` element by element on every layer's output, at
 the recurrence's fp16 bar (|H - H_ref| <= 2e-2 (1 + |H_ref|)), for stacks of
 2 to 8 layers, full and ragged sizes, with and without initial states.
@@ -30,11 +30,13 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def run_stack(handle, st, h0=True):
+def run_stack(handle, st, h0=True, mode=binding.STACK_AUTO):
+    handle.set_stack_mode(mode)
     layers = [{k: dev(v) for k, v in ly.items()} for ly in st["layers"]]
     h0s = [dev(h) for h in st["h0s"]] if h0 else None
     outs = handle.forward_stack_dense(layers, dev(st["x"]), h0s)
     handle.synchronize()
+    handle.set_stack_mode(binding.STACK_AUTO)
     return [o.cpu().numpy() for o in outs]
 
 
@@ -50,6 +52,8 @@ def check(st, got, h0=True):
 # multiple of 4, of 256, or of the 256 waves of a team).
 CASES = [
     (2, 1, 2048, 6, "randn"),
+    (3, 2, 640, 150, "randn"),   # two blocks of 75 steps
+    (2, 4, 1792, 97, "zeros"),   # blocks of 49 and 48 steps
     (2, 4, 1152, 256, "zeros"),
     (2, 4, 1792, 64, "randn"),
     (4, 2, 256, 32, "randn"),
@@ -68,6 +72,29 @@ def test_stack_parity(handle, L, B, N, T, h0):
     ratios = check(st, got)
     print(f"stack L={L} B={B} N={N} T={T}: error ratios {[f'{r:.3g}' for r in ratios]}")
     assert max(ratios) <= 1.0
+
+
+@pytest.mark.parametrize("mode", [binding.STACK_BLOCKED, binding.STACK_FUSED, binding.STACK_LAYERS])
+@pytest.mark.parametrize("L,B,N,T", [(2, 4, 1152, 200), (4, 2, 256, 70), (3, 2, 777, 33)])
+def test_stack_modes_agree_with_the_oracle(handle, mode, L, B, N, T):
+    w = WORKLOADS["dense_f16_n1152"].with_(N=N, B=B, T=T, h0="randn", seed=500 + L + B)
+    st = generate_stack(w, L)
+    got = run_stack(handle, st, mode=mode)
+    ratios = check(st, got)
+    print(f"stack mode {mode} L={L} B={B} N={N} T={T}: error ratios {[f'{r:.3g}' for r in ratios]}")
+    assert max(ratios) <= 1.0
+
+
+def test_stack_forced_mode_that_does_not_fit(handle):
+    w = WORKLOADS["dense_f16_n1152"].with_(N=1792, B=2, T=4, seed=6)
+    st = generate_stack(w, 2)
+    with pytest.raises(PrnnError) as e:                       # fused needs N <= 1280
+        run_stack(handle, st, mode=binding.STACK_FUSED)
+    assert e.value.status == binding.NOT_SUPPORTED
+    handle.set_stack_mode(binding.STACK_AUTO)
+    with pytest.raises(PrnnError) as e:
+        handle.set_stack_mode(9)
+    assert e.value.status == binding.BAD_PARAM
 
 
 def test_stack_deterministic_and_grid_independent_parity(handle):
@@ -121,16 +148,15 @@ def test_stack_errors(handle):
 @pytest.mark.parametrize("N", [384, 1792])
 def test_stack_chunked_in_time(handle, N):
     """A stack over T steps equals two stack calls over T1 and T - T1 steps, the
-    second starting from every layer's last state (within 1e-6; wavefront at
-    N=384, layers one after another at N=1792)."""
-    w = WORKLOADS["dense_f16_n1152"].with_(N=N, B=2, T=12, h0="randn", seed=77)
+    second starting from every layer's last state (within 1e-6)."""
+    w = WORKLOADS["dense_f16_n1152"].with_(N=N, B=2, T=140, h0="randn", seed=77)
     st = generate_stack(w, 3)
     layers = [{k: dev(v) for k, v in ly.items()} for ly in st["layers"]]
     x = dev(st["x"])
     h0s = [dev(v) for v in st["h0s"]]
     full = handle.forward_stack_dense(layers, x, h0s)
-    a = handle.forward_stack_dense(layers, x[:5].contiguous(), h0s)
-    b = handle.forward_stack_dense(layers, x[5:].contiguous(), [o[-1].contiguous() for o in a])
+    a = handle.forward_stack_dense(layers, x[:65].contiguous(), h0s)
+    b = handle.forward_stack_dense(layers, x[65:].contiguous(), [o[-1].contiguous() for o in a])
     handle.synchronize()
     for l in range(3):
         both = torch.cat([a[l], b[l]]).cpu().numpy()
