@@ -114,9 +114,9 @@ struct ProjArgs {
   uint32_t* status;   // kStatusRange if an fp32 x exceeds the fp16 range of its split
   int M, N, I;
   uint32_t x_bytes, u_bytes;
-  int tiles_n;        // 128-column tiles of X
-  int tiles;          // all 64 x 128 tiles
-  int per_xcd;        // tiles per XCD (grid = 8 per_xcd workgroups of 256)
+  int tiles_n;        // column tiles of X (set by launch_project)
+  int tiles;          // all tiles
+  int per_xcd;        // tiles per XCD (grid = 8 per_xcd workgroups)
 };
 // vec: I % 8 == 0 and x, U 16-byte aligned.
 hipError_t launch_project(const ProjArgs& a, bool x_f32, bool vec, hipStream_t stream);

@@ -444,7 +444,7 @@ prnnStatus_t prepare_project(prnnContext* h, int M, int N, int I, prnnDataType_t
   const size_t xb = (size_t)M * I * xe, ub = (size_t)N * I * 2, ob = (size_t)M * N * 4;
   if (overlap(X, ob, x, xb) || overlap(X, ob, U, ub) || (bias != nullptr && overlap(X, ob, bias, (size_t)N * 4)))
     return PRNN_STATUS_BAD_PARAM;
-  const long long tiles = (long long)((M + 63) / 64) * ((N + 127) / 128);  // 64 x 128 tiles of X
+  const long long tiles = (long long)((M + 63) / 64) * ((N + 63) / 64);  // at most 64 x 64 tiles of X
   if (xb > 0xFFFFFF00ull || ub > 0xFFFFFF00ull || tiles > (1ll << 28)) return PRNN_STATUS_NOT_SUPPORTED;
   a->x = x;
   a->U = U;
@@ -456,9 +456,9 @@ prnnStatus_t prepare_project(prnnContext* h, int M, int N, int I, prnnDataType_t
   a->I = I;
   a->x_bytes = static_cast<uint32_t>(xb);
   a->u_bytes = static_cast<uint32_t>(ub);
-  a->tiles_n = (N + 127) / 128;
-  a->tiles = static_cast<int>(tiles);
-  a->per_xcd = static_cast<int>((tiles + 7) / 8);
+  a->tiles_n = 0;  // the tiling is chosen at launch (launch_project)
+  a->tiles = 0;
+  a->per_xcd = 0;
   *vec = I % 8 == 0 && aligned(x, 16) && aligned(U, 16);
   return PRNN_STATUS_SUCCESS;
 }

@@ -12,11 +12,11 @@
 // (the fp16 range bounds |x| below 65504; a larger value raises
 // kStatusRange).  fp16 x enters as it is.
 //
-// A workgroup computes a 64 x 128 tile of X (64 rows of x, 128 rows of U)
-// with two groups of 4 waves, each over one half of the k range (more loads
+// A workgroup computes a 64 x BN tile of X (64 rows of x, BN = 128 or 64
+// rows of U) with two groups of 4 waves, each over one half of the k range (more loads
 // in flight per CU; the two partial tiles are added in a fixed order at the
-// end, through LDS).  Within a group, wave (wy, wx) computes a 32 x 64
-// quarter as 2 x 4 MFMA tiles.  Per 32-wide k-step a group stages x (split
+// end, through LDS).  Within a group, wave (wy, wx) computes a 32 x BN/2
+// quarter as 2 x BN/32 MFMA tiles.  Per 32-wide k-step a group stages x (split
 // into hi and lo) and U in LDS as fp16 rows of 32 values padded to 48 (a
 // 96-byte stride, the fastest of the strides 80 to 144 bytes measured at the
 // layer size), double buffered, so one barrier per k-step separates writing
@@ -35,10 +35,10 @@ namespace {
 typedef _Float16 ph8 __attribute__((ext_vector_type(8)));
 typedef float pf4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 64;        // rows of x per workgroup
-constexpr int kBN = 128;       // rows of U per workgroup
+constexpr int kBM = 64;        // rows of x per workgroup (rows of U: BN = 128 or 64)
 constexpr int kRow = 48;       // fp16 per LDS row (32 + 16 padding; the fastest of 40-72, measured)
-constexpr int kStage = (2 * kBM + kBN) * kRow;  // fp16 per buffer: x hi, x lo, U
+template <int BN>
+constexpr int stage_halves() { return (2 * kBM + BN) * kRow; }  // fp16 per buffer: x hi, x lo, U
 constexpr int kGroups = 2;                      // k-range halves per workgroup, 4 waves each
 constexpr int kDepth = 4;                       // k-steps of global loads in flight
 
@@ -93,21 +93,26 @@ __device__ __forceinline__ void split8(const u32x4& w0, const u32x4& w1, ph8& hi
 }
 
 // This thread's share of one k-step's global operands: 8 values of x (row
-// t / 4, columns 8 (t % 4)) and 16 of U (row t / 2, columns 16 (t % 2)).
+// t / 4, columns 8 (t % 4)) and of U 16 values (BN = 128: row t / 2, columns
+// 16 (t % 2)) or 8 (BN = 64: row t / 4, columns 8 (t % 4)).
 struct Staged {
   u32x4 x0, x1, u0, u1;
 };
 
-template <bool XF32, bool VEC>
+template <bool XF32, bool VEC, int BN>
 __device__ __forceinline__ void fetch(Staged& s, __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t ur, int mb, int nb,
                                       int k0, int I, int t) {
   u32x4 none;
   load8<XF32, VEC>(xr, mb + (t >> 2), k0 + 8 * (t & 3), I, s.x0, s.x1);
-  load8<false, VEC>(ur, nb + (t >> 1), k0 + 16 * (t & 1), I, s.u0, none);
-  load8<false, VEC>(ur, nb + (t >> 1), k0 + 16 * (t & 1) + 8, I, s.u1, none);
+  if (BN == 128) {
+    load8<false, VEC>(ur, nb + (t >> 1), k0 + 16 * (t & 1), I, s.u0, none);
+    load8<false, VEC>(ur, nb + (t >> 1), k0 + 16 * (t & 1) + 8, I, s.u1, none);
+  } else {
+    load8<false, VEC>(ur, nb + (t >> 2), k0 + 8 * (t & 3), I, s.u0, none);
+  }
 }
 
-template <bool XF32>
+template <bool XF32, int BN>
 __device__ __forceinline__ void stage(const Staged& s, _Float16* buf, int t, bool& range_ok) {
   _Float16* xhi = buf;
   _Float16* xlo = buf + kBM * kRow;
@@ -121,13 +126,19 @@ __device__ __forceinline__ void stage(const Staged& s, _Float16* buf, int t, boo
   } else {
     *reinterpret_cast<u32x4*>(xhi + xo) = s.x0;
   }
-  const int uo = (t >> 1) * kRow + 16 * (t & 1);
-  *reinterpret_cast<u32x4*>(u + uo) = s.u0;
-  *reinterpret_cast<u32x4*>(u + uo + 8) = s.u1;
+  if (BN == 128) {
+    const int uo = (t >> 1) * kRow + 16 * (t & 1);
+    *reinterpret_cast<u32x4*>(u + uo) = s.u0;
+    *reinterpret_cast<u32x4*>(u + uo + 8) = s.u1;
+  } else {
+    *reinterpret_cast<u32x4*>(u + (t >> 2) * kRow + 8 * (t & 3)) = s.u0;
+  }
 }
 
-template <bool XF32, bool VEC>
+template <bool XF32, bool VEC, int BN>
 __global__ void __launch_bounds__(256 * kGroups) project_kernel(ProjArgs a) {
+  constexpr int kStage = stage_halves<BN>();
+  constexpr int TN = BN / 32;  // 16-column MFMA tiles per wave
   __shared__ __attribute__((aligned(16))) _Float16 lds_all[kGroups * 2 * kStage];
   const int g = blockIdx.x;
   const int tile = (g & 7) * a.per_xcd + (g >> 3);
@@ -142,16 +153,16 @@ __global__ void __launch_bounds__(256 * kGroups) project_kernel(ProjArgs a) {
   const int r16 = lane & 15;
   const int q = lane >> 4;
   const int wy = wave >> 1, wx = wave & 1;
-  const int mb = tm * kBM, nb = tn * kBN;
+  const int mb = tm * kBM, nb = tn * BN;
   const int I = a.I;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t ur = make_rsrc(a.U, a.u_bytes);
 
-  pf4 acc[2][4];
+  pf4 acc[2][TN];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = pf4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TN; ++j) acc[i][j] = pf4{0.f, 0.f, 0.f, 0.f};
   bool range_ok = true;
 
   // This group's k-steps: [grp * half, grp * half + half), half a multiple
@@ -163,15 +174,15 @@ __global__ void __launch_bounds__(256 * kGroups) project_kernel(ProjArgs a) {
   // sets used in turn (set k % kDepth holds step k; an in-flight set is never
   // copied, which would wait for it).
   Staged st[kDepth];
-  fetch<XF32, VEC>(st[0], xr, ur, mb, nb, kbase, I, t);
-  stage<XF32>(st[0], lds, t, range_ok);
+  fetch<XF32, VEC, BN>(st[0], xr, ur, mb, nb, kbase, I, t);
+  stage<XF32, BN>(st[0], lds, t, range_ok);
 #pragma unroll
-  for (int d = 1; d <= kDepth; ++d) fetch<XF32, VEC>(st[d % kDepth], xr, ur, mb, nb, kbase + 32 * d, I, t);
+  for (int d = 1; d <= kDepth; ++d) fetch<XF32, VEC, BN>(st[d % kDepth], xr, ur, mb, nb, kbase + 32 * d, I, t);
   __syncthreads();
 
   auto step = [&](int kk, Staged& next) {
     const _Float16* buf = lds + (kk & 1) * kStage;
-    ph8 ahi[2], alo[2], b[4];
+    ph8 ahi[2], alo[2], b[TN];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int o = (32 * wy + 16 * i + r16) * kRow + 8 * q;
@@ -179,24 +190,24 @@ __global__ void __launch_bounds__(256 * kGroups) project_kernel(ProjArgs a) {
       if (XF32) alo[i] = *reinterpret_cast<const ph8*>(buf + kBM * kRow + o);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const ph8*>(buf + 2 * kBM * kRow + (64 * wx + 16 * j + r16) * kRow + 8 * q);
+    for (int j = 0; j < TN; ++j)
+      b[j] = *reinterpret_cast<const ph8*>(buf + 2 * kBM * kRow + ((BN / 2) * wx + 16 * j + r16) * kRow + 8 * q);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[i], b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[i], b[j], acc[i][j], 0, 0, 0);
     if (XF32) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[i], b[j], acc[i][j], 0, 0, 0);
     }
     // `next` holds step kk + 1: into the other buffer, then reload it with
     // step kk + 1 + kDepth.  Past the group's last step these load zeros and
     // fill a buffer nobody reads (no branch, see load8).
-    stage<XF32>(next, lds + ((kk + 1) & 1) * kStage, t, range_ok);
-    fetch<XF32, VEC>(next, xr, ur, mb, nb, kbase + 32 * (kk + 1 + kDepth), I, t);
+    stage<XF32, BN>(next, lds + ((kk + 1) & 1) * kStage, t, range_ok);
+    fetch<XF32, VEC, BN>(next, xr, ur, mb, nb, kbase + 32 * (kk + 1 + kDepth), I, t);
     __syncthreads();
   };
   for (int kk = 0; kk < half; kk += kDepth) {
@@ -205,14 +216,14 @@ __global__ void __launch_bounds__(256 * kGroups) project_kernel(ProjArgs a) {
   }
 
   // The second group's partial tile onto the first's: X = first + second.
-  float* red = reinterpret_cast<float*>(lds_all);  // [4 waves][8 tiles x 4][64 lanes]
+  float* red = reinterpret_cast<float*>(lds_all);  // [4 waves][2 TN tiles x 4][64 lanes]
   if (grp == 1) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[(wave * 32 + (i * 4 + j) * 4 + r) * 64 + lane] = acc[i][j][r];
+        for (int r = 0; r < 4; ++r) red[(wave * 8 * TN + (i * TN + j) * 4 + r) * 64 + lane] = acc[i][j][r];
   }
   __syncthreads();
   if (grp == 1) {
@@ -222,14 +233,14 @@ __global__ void __launch_bounds__(256 * kGroups) project_kernel(ProjArgs a) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[i][j][r] += red[(wave * 32 + (i * 4 + j) * 4 + r) * 64 + lane];
+      for (int r = 0; r < 4; ++r) acc[i][j][r] += red[(wave * 8 * TN + (i * TN + j) * 4 + r) * 64 + lane];
 
   // D layout: lane holds rows 4 q .. 4 q + 3 of column r16 of each 16 x 16 tile.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = nb + 64 * wx + 16 * j + r16;
+  for (int j = 0; j < TN; ++j) {
+    const int n = nb + (BN / 2) * wx + 16 * j + r16;
     if (n >= a.N) continue;
     const float bn = a.bias != nullptr ? a.bias[n] : 0.f;
 #pragma unroll
@@ -245,14 +256,29 @@ __global__ void __launch_bounds__(256 * kGroups) project_kernel(ProjArgs a) {
 
 }  // namespace
 
+template <int BN>
+const void* pick_project(bool x_f32, bool vec) {
+  return x_f32 ? (vec ? reinterpret_cast<const void*>(&project_kernel<true, true, BN>)
+                      : reinterpret_cast<const void*>(&project_kernel<true, false, BN>))
+               : (vec ? reinterpret_cast<const void*>(&project_kernel<false, true, BN>)
+                      : reinterpret_cast<const void*>(&project_kernel<false, false, BN>));
+}
+
+// 64 x 128 tiles, or 64 x 64 when 64 x 128 would leave half of the compute
+// units idle (fewer than 128 tiles: short sequences, such as one block of a
+// stack; measured at N = I = 1792: 256 rows 27.6 -> 22.4 us, while 1024 rows
+// are faster with the wide tiles, 31.5 vs 34.5 us).
 hipError_t launch_project(const ProjArgs& a, bool x_f32, bool vec, hipStream_t stream) {
-  const void* fn = x_f32 ? (vec ? reinterpret_cast<const void*>(&project_kernel<true, true>)
-                                : reinterpret_cast<const void*>(&project_kernel<true, false>))
-                         : (vec ? reinterpret_cast<const void*>(&project_kernel<false, true>)
-                                : reinterpret_cast<const void*>(&project_kernel<false, false>));
   ProjArgs args = a;
+  const long long tiles_m = (a.M + kBM - 1) / kBM;
+  const bool narrow = tiles_m * ((a.N + 127) / 128) < 128;
+  const int bn = narrow ? 64 : 128;
+  args.tiles_n = (a.N + bn - 1) / bn;
+  args.tiles = static_cast<int>(tiles_m * args.tiles_n);
+  args.per_xcd = (args.tiles + 7) / 8;
+  const void* fn = narrow ? pick_project<64>(x_f32, vec) : pick_project<128>(x_f32, vec);
   void* kargs[] = {&args};
-  return hipLaunchKernel(fn, dim3(8u * (unsigned)a.per_xcd), dim3(256 * kGroups), kargs, 0, stream);
+  return hipLaunchKernel(fn, dim3(8u * (unsigned)args.per_xcd), dim3(256 * kGroups), kargs, 0, stream);
 }
 
 }  // namespace prnn
