@@ -24,6 +24,11 @@
  * with the same number K of nonzeros in every row (same table: load-balanced
  * pruning row).
  *
+ * Around the recurrence: prnn_project computes X for a whole sequence on the
+ * matrix cores; prnn_forward_layer_* run a whole layer (projection, then the
+ * recurrence); prnn_forward_stack_dense runs a stack of layers with the
+ * layers at the same time on separate XCDs (same page, entire-network stage).
+ *
  * API style follows a cuDNN-like library ("persistent-rnn", "Who Would Use
  * This"): an opaque handle, a status code from every call, caller-owned device
  * buffers, and asynchronous execution on a caller-provided stream.
@@ -31,8 +36,10 @@
  * Conventions shared by every call below
  * --------------------------------------
  *  - All array arguments are DEVICE pointers owned by the caller.  The library
- *    reads W / col / val / X / h0, writes only H, and keeps no pointer after
- *    the work it enqueued has finished.  Buffers must stay valid until then.
+ *    reads the inputs, writes only the outputs each call names (H; X for
+ *    prnn_project; the workspace Xbuf of layer and stack calls), and keeps no
+ *    pointer after the work it enqueued has finished.  Buffers must stay
+ *    valid until then.
  *  - All arrays are dense, row-major, with the last index fastest:
  *      W   [N][N]   W[i*N + j] = weight from input neuron j to output neuron i
  *      col [N][K]   int16 column indices of row i's nonzeros, each in [0, N)
@@ -46,7 +53,9 @@
  *    runs (a step that never completes within the watchdog limit) is reported
  *    as PRNN_STATUS_EXECUTION_FAILED by prnn_synchronize() or prnn_destroy();
  *    until it has been reported, later forward calls on the handle are
- *    enqueued but do nothing (H is left as it was).
+ *    enqueued but do nothing (H is left as it was).  A call that enqueues
+ *    several launches (layer and stack calls) and fails after the first
+ *    leaves its outputs undefined.
  *  - One forward call may be in flight per handle at a time (the handle owns
  *    the exchange ring).  Use one handle per concurrently used stream.  A
  *    handle is not thread-safe.  Every call must be made with the handle's
