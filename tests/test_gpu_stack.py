@@ -161,3 +161,21 @@ def test_stack_chunked_in_time(handle, N):
     for l in range(3):
         both = torch.cat([a[l], b[l]]).cpu().numpy()
         np.testing.assert_allclose(both, full[l].cpu().numpy(), rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("mode", [binding.STACK_BLOCKED, binding.STACK_FUSED, binding.STACK_LAYERS])
+def test_stack_without_biases_or_states_and_fp16_input(handle, mode):
+    """bias None for every layer, no initial states (zeros), fp16 network input."""
+    w = WORKLOADS["dense_f16_n1152"].with_(N=320, B=2, T=70, seed=88)
+    st = generate_stack(w, 3)
+    for ly in st["layers"]:
+        ly["bias"] = None
+    x16 = st["x"].astype(np.float16)
+    handle.set_stack_mode(mode)
+    layers = [{"U": dev(ly["U"]), "W": dev(ly["W"]), "bias": None} for ly in st["layers"]]
+    outs = handle.forward_stack_dense(layers, dev(x16))
+    handle.synchronize()
+    handle.set_stack_mode(binding.STACK_AUTO)
+    refs = oracle.forward_stack_dense(st["layers"], x16, None)
+    for o, r in zip(outs, refs):
+        assert oracle.tolerance_ratio(o.cpu().numpy(), r, oracle.TOL_F16) <= 1.0
