@@ -282,6 +282,10 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
             "floor_us_per_step": round(floor_us, 3),
             "vs_floor": round(step_us / floor_us, 3) if floor_us > 0 else None,
             "gflop_per_s": round(w.flop_per_step * T / (full * 1e-3) / 1e9, 2),
+            "pct_fp32_vector_peak": round(100 * w.flop_per_step * T / (full * 1e-3) / FP32_VECTOR_PEAK, 3),
+            # the bytes a per-step re-read of W would move, per second, against 8 TB/s of HBM
+            "equiv_weight_tb_per_s": round(w.weight_bytes * T / (full * 1e-3) / 1e12, 3),
+            "equiv_weight_frac_of_hbm": round(w.weight_bytes * T / (full * 1e-3) / 8e12, 3),
             "max_err_ratio": err,
             "plan": plan,
         }
