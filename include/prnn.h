@@ -361,6 +361,17 @@ prnnStatus_t prnn_get_trace(prnnHandle_t handle, uint64_t* out, size_t capacity,
  * wg < 0 disables. */
 prnnStatus_t prnn_debug_skip_publish(prnnHandle_t handle, int wg, int step);
 
+/* TEST ONLY: from the next call on, until span is set to 0, every wave of the
+ * recurrent kernels (single layer and stack, every layout) sleeps before it
+ * publishes its rows of each timestep, for n < span periods of about 64
+ * shader clocks, n drawn per (workgroup, wave, timestep) from a hash of
+ * `seed`.  Rows then reach their consumers in a different order and at
+ * different times; the results must be bitwise those of span = 0.  span in
+ * [0, PRNN_DEBUG_JITTER_MAX], else BAD_PARAM.  Delays longer than the
+ * watchdog (prnn_set_watchdog_us) make the run report EXECUTION_FAILED. */
+#define PRNN_DEBUG_JITTER_MAX 1024
+prnnStatus_t prnn_debug_jitter(prnnHandle_t handle, uint32_t seed, int span);
+
 /* Static description of a status code; never NULL, never allocates. */
 const char* prnn_status_string(prnnStatus_t status);
 

@@ -49,6 +49,7 @@ SIGNATURES = {
     "prnn_set_math": (_I, [_H, _I]),
     "prnn_get_last_plan": (_I, [_H, _P]),
     "prnn_debug_skip_publish": (_I, [_H, _I, _I]),
+    "prnn_debug_jitter": (_I, [_H, ctypes.c_uint32, _I]),
     "prnn_set_trace": (_I, [_H, _I]),
     "prnn_get_trace": (_I, [_H, _P, ctypes.c_size_t, ctypes.POINTER(_I), _P]),
     "prnn_status_string": (ctypes.c_char_p, [_I]),
@@ -183,6 +184,10 @@ class Handle:
 
     def debug_skip_publish(self, wg: int, step: int):
         _check("prnn_debug_skip_publish", self._lib.prnn_debug_skip_publish(self._h, int(wg), int(step)))
+
+    def debug_jitter(self, seed: int, span: int):
+        """Test only: random publish delays of up to ``span`` sleep periods (0: off)."""
+        _check("prnn_debug_jitter", self._lib.prnn_debug_jitter(self._h, int(seed) & 0xFFFFFFFF, int(span)))
 
     def last_plan(self) -> dict:
         info = PlanInfo()

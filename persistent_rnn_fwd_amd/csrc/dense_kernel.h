@@ -217,6 +217,7 @@ __global__ void __launch_bounds__(256) dense_kernel(StepArgs a) {
     }
 
     const float sum = RowReduce<M>::reduce(acc, lane);
+    debug_jitter(a.jitter_seed, a.jitter_span, wave, t);
     if (owner && !(skipper && t == a.skip_step)) {
       const uint32_t hb = relu_bits(sum + x);
       const int row = row0 + my_row;

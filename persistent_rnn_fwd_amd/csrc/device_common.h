@@ -54,6 +54,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
+// Test-only delay before a wave publishes its rows (span = 0: off, one
+// scalar compare).  The wave sleeps n periods of s_sleep 1 (64 shader clocks
+// each), n < span drawn from (seed, workgroup, wave, step) by a 32-bit integer
+// hash (xor-shift-multiply rounds), the same for every lane.  It changes when
+// rows arrive, never what they hold: results must not depend on it.
+__device__ __forceinline__ void debug_jitter(uint32_t seed, uint32_t span, uint32_t wave, uint32_t t) {
+  if (span == 0u) return;
+  uint32_t x = seed ^ (blockIdx.x * 0x9E3779B1u) ^ (wave * 0x85EBCA77u) ^ (t * 0xC2B2AE3Du);
+  x ^= x >> 16;
+  x *= 0x7FEB352Du;
+  x ^= x >> 15;
+  x *= 0x846CA68Bu;
+  x ^= x >> 16;
+  for (uint32_t n = __builtin_amdgcn_readfirstlane(x % span); n > 0u; --n) __builtin_amdgcn_s_sleep(1);
+}
+
 // ReLU that keeps NaN (a < 0 is false for NaN) and returns +0 for any zero.
 __device__ __forceinline__ uint32_t relu_bits(float a) {
   return (a < 0.f) ? 0u : (__float_as_uint(a) & 0x7fffffffu);

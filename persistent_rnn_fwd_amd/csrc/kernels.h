@@ -30,6 +30,7 @@ struct StepArgs {
   uint32_t x_bytes;     // bytes of X (= bytes of H)
   uint64_t deadline;    // bound on one wait, in ticks of the 100 MHz clock
   int skip_wg, skip_step;  // test-only publish skip (skip_wg < 0: off)
+  uint32_t jitter_seed, jitter_span;  // test-only publish delay (span 0: off)
   uint64_t* trace;      // trace instances: kTraceWords per wave, [grid][8 waves][kTraceWords]
 };
 
@@ -100,6 +101,7 @@ struct StackArgs {
   uint32_t step0;
   uint32_t x_bytes;              // bytes of one [T][B][N] sequence (T = the launch's steps)
   uint64_t deadline;
+  uint32_t jitter_seed, jitter_span;  // test-only publish delay (span 0: off)
 };
 // (rmax = rows per wave, cap = chunks of each part)
 extern const KernelEntry kStackFusedKernels[];

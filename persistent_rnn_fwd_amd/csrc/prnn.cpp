@@ -42,6 +42,8 @@ struct prnnContext {
   int stack_mode = PRNN_STACK_AUTO;
   int skip_wg = -1;
   int skip_step = -1;
+  uint32_t jitter_seed = 0;
+  uint32_t jitter_span = 0;  // 0: no publish delays
   prnnPlanInfo_t last_plan{};
   bool have_plan = false;
   // Phase tracing: [num_cu][8 waves][kTraceWords] of the last traced call.
@@ -314,6 +316,8 @@ prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream
   a.deadline = static_cast<uint64_t>(h->watchdog_us) * 100ull;  // 100 MHz constant clock
   a.skip_wg = h->skip_wg;
   a.skip_step = h->skip_step;
+  a.jitter_seed = h->jitter_seed;
+  a.jitter_span = h->jitter_span;
   a.trace = nullptr;
   if (h->trace) {
     // records of workgroups without a batch row of their own stay zero
@@ -615,6 +619,13 @@ prnnStatus_t prnn_debug_skip_publish(prnnHandle_t h, int wg, int step) {
   return PRNN_STATUS_SUCCESS;
 }
 
+prnnStatus_t prnn_debug_jitter(prnnHandle_t h, uint32_t seed, int span) {
+  if (h == nullptr || span < 0 || span > PRNN_DEBUG_JITTER_MAX) return PRNN_STATUS_BAD_PARAM;
+  h->jitter_seed = seed;
+  h->jitter_span = static_cast<uint32_t>(span);
+  return PRNN_STATUS_SUCCESS;
+}
+
 prnnStatus_t prnn_synchronize(prnnHandle_t h, hipStream_t stream) {
   if (h == nullptr) return PRNN_STATUS_BAD_PARAM;
   if (hipStreamSynchronize(stream) != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
@@ -810,6 +821,8 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B
   a.base_rows = p.base_rows;
   a.extra_rows = p.extra_rows;
   a.deadline = static_cast<uint64_t>(h->watchdog_us) * 100ull;
+  a.jitter_seed = h->jitter_seed;
+  a.jitter_span = h->jitter_span;
   auto launch_stack = [&](int Tlaunch) -> prnnStatus_t {
     a.T = Tlaunch;
     a.step0 = static_cast<uint32_t>(h->step);

@@ -171,6 +171,7 @@ __global__ void __launch_bounds__(512) stack_team_kernel(StackArgs a) {
     const float sum = RowReduce<M>::reduce(acc, lane);
     asm volatile("" : "+v"(aborted_now) : "v"(sum));  // keep the test after the arithmetic
     if (aborted_now) return;
+    debug_jitter(a.jitter_seed, a.jitter_span, wave, t);
     if (owner) {
       const uint32_t hb = relu_bits(sum + x);
       __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), region, ((S & 1u) * a.Npad + row) * 4u, 0, kPlain);

@@ -239,6 +239,7 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
     clk.mark(kTrReduce);
     asm volatile("" : "+v"(aborted_now) : "v"(sum));  // keep the test after the arithmetic
     if (aborted_now) return;
+    debug_jitter(a.jitter_seed, a.jitter_span, p.wave, t);
     if (owner && !(p.rank == a.skip_wg && t == a.skip_step)) {
       const uint32_t hb = relu_bits(sum + x);
       const int row = p.r0 + my_row;
@@ -340,6 +341,7 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
     clk.mark(kTrReduce);
     asm volatile("" : "+v"(aborted_now) : "v"(sum));  // keep the test after the arithmetic
     if (aborted_now) return;
+    debug_jitter(a.jitter_seed, a.jitter_span, p.wave, t);
     if (owner && !(p.rank == a.skip_wg && t == a.skip_step)) {
       const uint32_t hb = relu_bits(sum + x);
       const int row = p.r0 + my_row;

@@ -206,6 +206,7 @@ __global__ void __launch_bounds__(512) dense_team_mfma_kernel(StepArgs a) {
     clk.mark(kTrReduce);
     asm volatile("" : "+v"(aborted_now) : "v"(sum));  // keep the test after the reads
     if (aborted_now) return;
+    debug_jitter(a.jitter_seed, a.jitter_span, wave, t);
     if (owner && !(rank == a.skip_wg && t == a.skip_step)) {
       const uint32_t hb = relu_bits(sum + x);
       __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), region, ((S & 1u) * a.Npad + my_row) * 4u, 0, kPlain);

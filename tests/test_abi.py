@@ -51,6 +51,7 @@ def test_null_handle_is_bad_param():
     assert lib.prnn_set_watchdog_us(None, 1) == bp
     assert lib.prnn_get_last_plan(None, None) == bp
     assert lib.prnn_debug_skip_publish(None, 0, 0) == bp
+    assert lib.prnn_debug_jitter(None, 0, 0) == bp
 
 
 def test_binding_refuses_cpu_tensors():
