@@ -15,6 +15,7 @@ from .rnn import (  # noqa: F401
     TOL_F16,
     TOL_F32,
     forward_dense,
+    forward_dense_half_h,
     forward_sparse,
     sparse_to_dense,
     tolerance_ratio,

@@ -70,6 +70,33 @@ def forward_dense(W, X, h0=None) -> np.ndarray:
     return H
 
 
+def forward_dense_half_h(W, X, h0=None) -> np.ndarray:
+    """The dense recurrence with the state rounded to fp16 before the product.
+
+        a[t, b, i] = X[t, b, i] + sum_j W[i, j] * r(h[t-1, b, j]),  H[t] = max(a, 0)
+
+    where r() rounds to IEEE binary16, to nearest with ties to even (numpy's
+    float16 conversion; a value beyond the fp16 range becomes infinite).  Only
+    the copy of the state that enters the product is rounded: H itself, X, h0
+    and every sum stay fp64.  This is a model of a kernel that stages the state
+    in fp16 beside fp16 weights with fp32 sums (the "fp16 weights, fp32
+    accumulation" precision), used to show what such staging costs against
+    forward_dense, which remains the definition."""
+    W = _f64(W)
+    X = _f64(X)
+    if W.ndim != 2 or W.shape[0] != W.shape[1]:
+        raise ValueError(f"W must be square, got {W.shape}")
+    N = W.shape[0]
+    T, B, h = _check_xh(X, h0, N)
+    H = np.empty((T, B, N), dtype=np.float64)
+    for t in range(T):
+        staged = h.astype(np.float16).astype(np.float64)   # r(h[t-1])
+        a = X[t] + staged @ W.T
+        h = np.maximum(a, 0.0)
+        H[t] = h
+    return H
+
+
 def forward_sparse(col, val, X, h0=None) -> np.ndarray:
     """Row-balanced sparse W: a[b, i] = X[t, b, i] + sum_k val[i, k] * h[b, col[i, k]]."""
     col = np.asarray(col).astype(np.int64)

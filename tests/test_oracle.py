@@ -360,17 +360,75 @@ def test_fp32_arithmetic_meets_fp32_bar():
     assert oracle.tolerance_ratio(H32, H, oracle.TOL_F32) < 0.2
 
 
-def test_fp16_hidden_state_model_meets_fp16_bar():
-    """fp16 weights with fp32 accumulation pass 2e-2 (1 + |h|) by a wide margin,
-    even if h were rounded to fp16 at every step."""
-    w = WORKLOADS["dense_f16_n1152"].with_(T=64)
+# ---------------------------------------------------------------------------
+# The half-h model (state rounded to fp16 before the product)
+# ---------------------------------------------------------------------------
+def test_half_h_model_rounding_by_hand():
+    """One neuron, W = [[1]]: H[t] = X[t] + r(H[t-1]).  Each expected value is
+    worked by hand from the binary16 grid (spacing 2^-10 on [1, 2)): 3/4 of a
+    step rounds up, exactly 1/2 of a step goes to the even neighbour, below 1/2
+    rounds down.  Only the product's copy is rounded, so H[0] keeps every bit."""
+    u = 2.0 ** -10
+    W = np.ones((1, 1))
+    cases = [  # (X[0], the value r(X[0]) that H[1] = 0 + r(H[0]) must equal)
+        (1 + 0.75 * u, 1 + u),        # rounds up
+        (1 + 0.5 * u, 1.0),           # tie: 1.0 has the even last bit
+        (1 + 1.5 * u, 1 + 2 * u),     # tie: 1 + 2u has the even last bit
+        (1 + 0.25 * u, 1.0),          # rounds down
+        (1 + 3 * u, 1 + 3 * u),       # on the grid: unchanged
+    ]
+    for x0, staged in cases:
+        X = np.array([x0, 0.0, 0.5]).reshape(3, 1, 1)
+        H = oracle.forward_dense_half_h(W, X)
+        assert H[0, 0, 0] == x0
+        assert H[1, 0, 0] == staged
+        assert H[2, 0, 0] == 0.5 + staged   # staged is on the grid, so r() keeps it
+    # h0 is staged like any other state: r(h0) enters step 0
+    H = oracle.forward_dense_half_h(W, np.zeros((1, 1, 1)), np.array([[1 + 0.75 * u]]))
+    assert H[0, 0, 0] == 1 + u
+    # beyond the fp16 range the staged state is infinite
+    H = oracle.forward_dense_half_h(W, np.array([70000.0, 0.0]).reshape(2, 1, 1))
+    assert H[0, 0, 0] == 70000.0 and np.isinf(H[1, 0, 0])
+    # a negative weight with a rounded state: -1 * r(1 + 0.75u) + 3
+    H = oracle.forward_dense_half_h(-W, np.array([1 + 0.75 * u, 3.0]).reshape(2, 1, 1))
+    assert H[1, 0, 0] == 3.0 - (1 + u)
+
+
+def test_half_h_model_equals_definition_on_fp16_grid():
+    """When every state is an fp16 value (integers below 2048) the rounding is
+    the identity, so the model equals the plain definition exactly."""
+    rng = np.random.default_rng(7)
+    N, B, T = 9, 3, 12
+    W = rng.choice([-1.0, 0.0, 0.0, 0.0, 0.0, 1.0], size=(N, N))
+    X = rng.integers(-3, 4, size=(T, B, N)).astype(np.float64)
+    h0 = rng.integers(0, 3, size=(B, N)).astype(np.float64)
+    H = oracle.forward_dense(W, X, h0)
+    assert np.abs(H).max() < 2048 and np.all(H == np.round(H))
+    np.testing.assert_array_equal(oracle.forward_dense_half_h(W, X, h0), H)
+    # identity weights: prefix sums, also exact
+    Xp = rng.integers(0, 40, size=(T, B, N)).astype(np.float64)
+    np.testing.assert_array_equal(oracle.forward_dense_half_h(np.eye(N), Xp, h0),
+                                  h0[None] + np.cumsum(Xp, axis=0))
+
+
+def test_half_h_model_differs_from_definition_off_grid():
+    """Off the fp16 grid the model must not collapse into the definition (a
+    model that forgot to round would pass the grid test above)."""
+    w = WORKLOADS["dense_f16_n1152"].with_(T=8)
+    d = generate(w)
+    Hq = oracle.forward_dense_half_h(d["W"], d["X"], d["h0"])
+    H = oracle.forward_dense(d["W"], d["X"], d["h0"])
+    assert np.array_equal(Hq[0], H[0])          # h0 = 0 stages exactly
+    assert not np.array_equal(Hq[1:], H[1:])
+    assert oracle.tolerance_ratio(Hq, H, oracle.TOL_F16) > 0
+
+
+@pytest.mark.parametrize("name", ["dense_f16_n1152", "dense_f16_n1792"])
+def test_fp16_hidden_state_model_meets_fp16_bar(name):
+    """Rounding the state to fp16 at every step stays well inside the fp16-weight
+    bar 2e-2 (1 + |h|) over the whole configured sequence (T = 256)."""
+    w = WORKLOADS[name]
     d = generate(w)
     H = oracle.forward_dense(d["W"], d["X"], d["h0"])
-    W32 = d["W"].astype(np.float32)
-    h = d["h0"]
-    H16 = np.empty_like(d["X"])
-    for t in range(w.T):
-        hq = h.astype(np.float16).astype(np.float32)
-        h = np.maximum(d["X"][t] + hq @ W32.T, np.float32(0))
-        H16[t] = h
-    assert oracle.tolerance_ratio(H16, H, oracle.TOL_F16) < 0.2
+    Hq = oracle.forward_dense_half_h(d["W"], d["X"], d["h0"])
+    assert oracle.tolerance_ratio(Hq, H, oracle.TOL_F16) < 0.2
