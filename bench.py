@@ -409,8 +409,11 @@ def trace_breakdown(torch, dev, Handle, g, wd, ws, T):
         wd.name: lambda: h.forward_dense(g[wd.name]["W"], g[wd.name]["X"], g[wd.name]["h0"], out=o),
         ws.name: lambda: h.forward_sparse(g[ws.name]["col"], g[ws.name]["val"], g[ws.name]["X"], g[ws.name]["h0"], out=o),
         "sync_floor": lambda: h.sync_floor(N, B, T, out=o),
+        wd.name + "_half_h": lambda: h.forward_dense(g[wd.name]["W"], g[wd.name]["X"], g[wd.name]["h0"], out=o),
     }
+    from persistent_rnn_fwd_amd import binding as _b
     for name, fn in runs.items():
+        h.set_math(_b.MATH_HALF if name.endswith("_half_h") else _b.MATH_AUTO)
         fn()
         fn()
         rec = h.get_trace().astype(np.float64)
@@ -421,6 +424,7 @@ def trace_breakdown(torch, dev, Handle, g, wd, ws, T):
                      "loop_us_per_step": round(float(us[:, 5].mean()), 3)}
         for i, n in enumerate(names):
             out[name][n] = {"mean_us": round(float(us[:, i].mean()), 3), "max_wave_us": round(float(us[:, i].max()), 3)}
+    h.set_math(_b.MATH_AUTO)
     h.set_trace(False)
     h.close()
     return out
@@ -575,26 +579,40 @@ def main():
     detail["sync_floor_us_per_step"] = round(floor_us, 3)
     detail["sync_floor_ms_per_call"] = round(f_full, 4)
 
-    # the dense layer on the matrix cores (h as fp16 hi + lo), not in the headline step
+    # the dense layers in the other math modes, not in the headline step:
+    # SPLIT (matrix cores, h as fp16 hi + lo) and HALF (h rounded to fp16,
+    # two products per v_dot2_f32_f16)
     from persistent_rnn_fwd_amd import binding as _b
-    h.set_math(_b.MATH_SPLIT)
-    full = timed(lambda: call(wd.name))
-    half = timed(lambda: call(wd.name, T // 2))
-    step_us = (full - half) * 1e3 / (T - T // 2)
-    h.synchronize()
-    split = {"ms_per_call": round(full, 4), "us_per_step_slope": round(step_us, 3),
-             "vs_sync_floor": round(step_us / floor_us, 3) if floor_us > 0 else None,
-             "plan": {k: v for k, v in h.last_plan().items() if k != "first_step"}}
-    if not args.no_check:
-        import oracle
-        call(wd.name)
+    w2 = WORKLOADS["dense_f16_n1152"]
+    host[w2.name] = generate(w2)
+    g[w2.name] = {k: torch.from_numpy(v).to(dev) for k, v in host[w2.name].items()}
+    out[w2.name] = torch.empty((w2.T, w2.B, w2.N), dtype=torch.float32, device=dev)
+    for mode, label, w in ((_b.MATH_SPLIT, "split_math", wd), (_b.MATH_HALF, "half_h", wd), (_b.MATH_HALF, "half_h", w2)):
+        h.set_math(mode)
+        fl = floor_us
+        if w is not wd:
+            f_a = timed(lambda: h.sync_floor(w.N, w.B, w.T, out=out[w.name]))
+            f_b = timed(lambda: h.sync_floor(w.N, w.B, w.T // 2, out=out[w.name][: w.T // 2]))
+            fl = (f_a - f_b) * 1e3 / (w.T - w.T // 2)
+        full = timed(lambda: call(w.name, w.T))
+        half = timed(lambda: call(w.name, w.T // 2))
+        step_us = (full - half) * 1e3 / (w.T - w.T // 2)
         h.synchronize()
-        d = host[wd.name]
-        split["max_err_ratio"] = round(float(oracle.tolerance_ratio(out[wd.name].cpu().numpy(),
-                                                                    oracle.forward_dense(d["W"], d["X"], d["h0"]),
-                                                                    oracle.TOL_F16)), 5)
-    h.set_math(_b.MATH_AUTO)
-    detail["dense_f16_n1792_split_math"] = split
+        alt = {"ms_per_call": round(full, 4), "timesteps_per_s": round(w.T / (full * 1e-3), 1),
+               "us_per_step_slope": round(step_us, 3), "sync_floor_us_per_step": round(fl, 3),
+               "vs_sync_floor": round(step_us / fl, 3) if fl > 0 else None,
+               "gflop_per_s": round(w.flop_per_step * w.T / (full * 1e-3) / 1e9, 2),
+               "plan": {k: v for k, v in h.last_plan().items() if k != "first_step"}}
+        if not args.no_check:
+            import oracle
+            call(w.name, w.T)
+            h.synchronize()
+            d = host[w.name]
+            alt["max_err_ratio"] = round(float(oracle.tolerance_ratio(out[w.name].cpu().numpy(),
+                                                                      oracle.forward_dense(d["W"], d["X"], d["h0"]),
+                                                                      oracle.TOL_F16)), 5)
+        h.set_math(_b.MATH_AUTO)
+        detail[f"{w.name}_{label}"] = alt
     detail["timed_launch_ms"] = {"dense_f16_n1792": percentiles(dense_list), "sparse10_f16_n1792": percentiles(sparse_list)}
     sd, ss = detail[wd.name]["us_per_step_slope"], detail[ws.name]["us_per_step_slope"]
     detail["dense_over_sparse10_step_time"] = round(sd / ss, 3) if ss > 0 else None

@@ -129,11 +129,21 @@ typedef enum {
  *   product sees h to about 2^-22 of |h| (fp32 h carries 2^-24).  Needs
  *   |h| < 65504; a larger value makes the call report EXECUTION_FAILED.
  *   TEAM layout, fp16 W, N <= 2048 only (else NOT_SUPPORTED).
+ * HALF: h_{t-1} is rounded to fp16 (to nearest, ties to even) before the
+ *   product, and each instruction adds two fp16 x fp16 products (exact in
+ *   fp32) to the fp32 sums: half the multiply-adds of EXACT.  The product sees
+ *   h to 2^-11 of |h|, the relative precision the fp16 weights themselves
+ *   carry; X, h0, H, the sums, the ReLU and the exchanged state stay fp32.
+ *   Needs every h (and h0) to round to a finite fp16 (|h| < 65520); a larger
+ *   value makes the call report EXECUTION_FAILED.  TEAM layout, fp16 W,
+ *   N <= 2048 only (else NOT_SUPPORTED).  Blocked and fused stacks use EXACT;
+ *   a layer-by-layer stack follows this setting.
  * AUTO: EXACT.  fp32 weights and sparse layers always use EXACT. */
 typedef enum {
   PRNN_MATH_AUTO = 0,
   PRNN_MATH_EXACT = 1,
-  PRNN_MATH_SPLIT = 2
+  PRNN_MATH_SPLIT = 2,
+  PRNN_MATH_HALF = 3
 } prnnMath_t;
 
 /* Launch plan of the last forward call on a handle (for tests and reports). */
@@ -147,8 +157,9 @@ typedef struct {
   int lds_bytes;     /* dynamic LDS per workgroup                              */
   int relay_slice;   /* SPREAD: words of h each workgroup relays (0: DIRECT)   */
   uint64_t first_step; /* ring step counter of the call's first timestep       */
-  int math;          /* PRNN_MATH_EXACT or PRNN_MATH_SPLIT (rows_per_wave and
-                        rmax then count rows per workgroup)                   */
+  int math;          /* PRNN_MATH_EXACT, PRNN_MATH_HALF or PRNN_MATH_SPLIT
+                        (SPLIT: rows_per_wave and rmax count rows per
+                        workgroup)                                            */
 } prnnPlanInfo_t;
 
 /* Creates a handle bound to the current HIP device.

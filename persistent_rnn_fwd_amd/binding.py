@@ -27,7 +27,7 @@ SUCCESS, BAD_PARAM, NOT_SUPPORTED, ALLOC_FAILED, EXECUTION_FAILED, INTERNAL_ERRO
 DATA_FLOAT, DATA_HALF = 0, 1
 EXCHANGE_AUTO, EXCHANGE_DIRECT, EXCHANGE_RELAY = 0, 1, 2
 LAYOUT_AUTO, LAYOUT_SPREAD, LAYOUT_TEAM = 0, 1, 2
-MATH_AUTO, MATH_EXACT, MATH_SPLIT = 0, 1, 2
+MATH_AUTO, MATH_EXACT, MATH_SPLIT, MATH_HALF = 0, 1, 2, 3
 STACK_AUTO, STACK_BLOCKED, STACK_FUSED, STACK_LAYERS = 0, 1, 2, 3
 TRACE_WORDS = 8  # per-wave trace record: see Handle.get_trace
 
@@ -176,7 +176,7 @@ class Handle:
         _check("prnn_set_stack_mode", self._lib.prnn_set_stack_mode(self._h, mode))
 
     def set_math(self, mode: int):
-        """MATH_AUTO, MATH_EXACT or MATH_SPLIT (dense fp16) for later calls."""
+        """MATH_AUTO, MATH_EXACT, MATH_SPLIT or MATH_HALF (dense fp16) for later calls."""
         _check("prnn_set_math", self._lib.prnn_set_math(self._h, int(mode)))
 
     def set_watchdog_us(self, us: int):

@@ -26,6 +26,7 @@
 namespace prnn {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));  // operand type of the dot2 builtin
 
 
 template <typename WT>
@@ -79,6 +80,13 @@ struct WChunk<_Float16> {
     fma_mix_hi(acc, lo, h.y);
     fma_mix_lo(acc, hi, h.z);
     fma_mix_hi(acc, hi, h.w);
+  }
+  // Half-h form: h as four fp16 values (h01, h23 packed).  Each instruction
+  // (v_dot2_f32_f16) adds two fp16 x fp16 products, exact in fp32, to the
+  // fp32 sum: half the multiply-add instructions of the fp32-h forms.
+  __device__ __forceinline__ void dot4(float& acc, const uint2& h) const {
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, lo), __builtin_bit_cast(fp16x2, h.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, hi), __builtin_bit_cast(fp16x2, h.y), acc, false);
   }
 };
 

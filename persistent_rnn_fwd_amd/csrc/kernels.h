@@ -75,6 +75,10 @@ extern const void* kFloorTeamKernel;
 // cap = 8 chunks of 256 columns, one per wave).
 extern const KernelEntry kDenseTeamMfmaKernels[];
 extern const KernelEntry kDenseTeamMfmaTraceKernels[];
+// Dense fp16 team layout with h_{t-1} rounded to fp16 (rmax = rows per wave,
+// cap = 256-column chunks).
+extern const KernelEntry kDenseTeamHalfKernels[];
+extern const KernelEntry kDenseTeamHalfTraceKernels[];
 // Trace instances (team layout only): the same kernels with phase timing.
 extern const KernelEntry kDenseTeamF16TraceKernels[];
 extern const KernelEntry kDenseTeamF32TraceKernels[];

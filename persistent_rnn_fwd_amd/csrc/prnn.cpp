@@ -178,7 +178,13 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
     p->lds_bytes = 8 * 520 * 2 + 2 * 8 * p->k->rmax * 4;  // per-wave fp16 hi/lo/zero slots + partials
     return (size_t)p->lds_bytes + 256 <= h->lds_per_block;
   }
-  if (kind == kDense) {
+  if (kind == kDense && wt == prnn::kF16 && h->math == PRNN_MATH_HALF) {
+    // h_{t-1} staged as fp16: packed weights, two rows of fp16 values
+    p->math = PRNN_MATH_HALF;
+    p->k = pick(h->trace ? prnn::kDenseTeamHalfTraceKernels : prnn::kDenseTeamHalfKernels, p->max_rows, p->chunks);
+    if (p->k == nullptr) return false;
+    p->lds_bytes = 2 * 256 * p->k->cap * 2;
+  } else if (kind == kDense) {
     const KernelEntry* table = h->trace ? (wt == prnn::kF32 ? prnn::kDenseTeamF32TraceKernels : prnn::kDenseTeamF16TraceKernels)
                                         : (wt == prnn::kF32 ? prnn::kDenseTeamF32Kernels : prnn::kDenseTeamF16Kernels);
     p->k = pick(table, p->max_rows, p->chunks);
@@ -213,6 +219,8 @@ bool plan(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Plan* p)
     }
     if (h->layout == PRNN_LAYOUT_TEAM) return false;
   }
+  // the matrix-core and half-h forms exist in the team layout only
+  if (kind == kDense && wt == prnn::kF16 && (h->math == PRNN_MATH_SPLIT || h->math == PRNN_MATH_HALF)) return false;
   if (h->trace) return false;  // trace instances exist for the team layout only
   return plan_spread(h, kind, N, B, K, wt, p);
 }
@@ -595,7 +603,8 @@ prnnStatus_t prnn_set_layout(prnnHandle_t h, prnnLayout_t layout) {
 
 prnnStatus_t prnn_set_math(prnnHandle_t h, prnnMath_t mode) {
   if (h == nullptr) return PRNN_STATUS_BAD_PARAM;
-  if (mode != PRNN_MATH_AUTO && mode != PRNN_MATH_EXACT && mode != PRNN_MATH_SPLIT) return PRNN_STATUS_BAD_PARAM;
+  if (mode != PRNN_MATH_AUTO && mode != PRNN_MATH_EXACT && mode != PRNN_MATH_SPLIT && mode != PRNN_MATH_HALF)
+    return PRNN_STATUS_BAD_PARAM;
   h->math = mode;
   return PRNN_STATUS_SUCCESS;
 }

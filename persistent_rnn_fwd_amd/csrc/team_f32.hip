@@ -43,7 +43,8 @@ __global__ void __launch_bounds__(512) floor_team_kernel(StepArgs a) {
     bool ok = true;
     if (t > 0) {
       const uint32_t prev = S - 1u;
-      ok = team_stage(region, prev & 1u, a.Npad, N, a.chunks, p.wave, p.lane, tag_bit(prev), a.deadline, hrow);
+      uint32_t unused = 0;
+      ok = team_stage(region, prev & 1u, a.Npad, N, a.chunks, p.wave, p.lane, tag_bit(prev), a.deadline, hrow, unused);
     }
     if (!ok && p.lane == 0) {
       abort_flag = 1;

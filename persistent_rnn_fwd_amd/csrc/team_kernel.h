@@ -24,6 +24,8 @@
 // still reaches the barrier; the workgroup then leaves together.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "dense_kernel.h"
@@ -59,11 +61,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t team_region(const StepArgs& a)
   return make_rsrc(a.ring + (size_t)xcc * 2 * a.Npad, 2u * a.Npad * 4u);
 }
 
+// 1 if f is finite and rounds to an fp16 infinity (|f| >= 65520), from the
+// magnitude bits alone (one unsigned compare, no branch).
+__device__ __forceinline__ uint32_t beyond_fp16(float f) {
+  const uint32_t m = __float_as_uint(f) & 0x7fffffffu;
+  return (m - 0x477FF000u) < (0x7F800000u - 0x477FF000u) ? 1u : 0u;  // [65520, inf)
+}
+
+// One staged 4-word chunk into the LDS row: fp32 as is, or rounded to fp16
+// (round to nearest even) for the half-h dense path, which also records in
+// `bad` a finite value beyond the fp16 range.
+__device__ __forceinline__ void store_chunk(float* d, const float4& f, uint32_t&) {
+  *reinterpret_cast<float4*>(d) = f;
+}
+__device__ __forceinline__ void store_chunk(_Float16* d, const float4& f, uint32_t& bad) {
+  const f16x2 a = {(_Float16)f.x, (_Float16)f.y};
+  const f16x2 b = {(_Float16)f.z, (_Float16)f.w};
+  bad |= beyond_fp16(f.x) | beyond_fp16(f.y) | beyond_fp16(f.z) | beyond_fp16(f.w);
+  *reinterpret_cast<uint2*>(d) = make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+}
+
 // Stages chunks w, w + 8, ... of ring slot `slot` into the LDS row `dst`
-// (Npad floats), waiting until every word carries `tag`.  Returns false if the
-// wait expired (the caller must still reach the workgroup barrier).
+// (Npad elements), waiting until every word carries `tag`.  Returns false if
+// the wait expired (the caller must still reach the workgroup barrier).
+template <typename HT>
 __device__ __forceinline__ bool team_stage(__amdgpu_buffer_rsrc_t region, uint32_t slot, int npad, int n, int jn,
-                                           int wave, int lane, uint32_t tag, uint64_t deadline, float* dst) {
+                                           int wave, int lane, uint32_t tag, uint64_t deadline, HT* dst,
+                                           uint32_t& bad) {
   const uint32_t base = slot * (uint32_t)npad * 4u;
   bool ok = true;
   for (int j = wave; j < jn; j += kTeamWaves) {
@@ -79,15 +103,19 @@ __device__ __forceinline__ bool team_stage(__amdgpu_buffer_rsrc_t region, uint32
       if (now_ticks() - t0 > deadline) { ok = false; break; }
     }
     if (!ok) break;
-    if (c < n) *reinterpret_cast<float4*>(dst + c) = chunk_values(v, c, n);
+    if (c < n) store_chunk(dst + c, chunk_values(v, c, n), bad);
   }
   return ok;
 }
 
 // h0 (or zeros) into the LDS row, all threads of the workgroup.
-__device__ __forceinline__ void team_stage_h0(const float* h0, int b, int n, int npad, float* dst) {
-  for (int c = threadIdx.x; c < npad; c += blockDim.x)
-    dst[c] = (h0 != nullptr && c < n) ? h0[(size_t)b * n + c] : 0.f;
+template <typename HT>
+__device__ __forceinline__ void team_stage_h0(const float* h0, int b, int n, int npad, HT* dst, uint32_t& bad) {
+  for (int c = threadIdx.x; c < npad; c += blockDim.x) {
+    const float f = (h0 != nullptr && c < n) ? h0[(size_t)b * n + c] : 0.f;
+    if (std::is_same<HT, _Float16>::value) bad |= beyond_fp16(f);
+    dst[c] = (HT)f;
+  }
 }
 
 // Phase timing for the trace instances; compiles to nothing otherwise.  The
@@ -152,13 +180,20 @@ __device__ __forceinline__ void team_stamp_tail(const StepArgs& a, const TeamPos
   }
 }
 
-template <typename WT, int RW, int J, bool WIDE = false, bool TRACE = false>
+//
+// HALF (fp16 W only): the staged row holds h_{t-1} rounded to fp16 and every
+// instruction adds two exact fp16 x fp16 products to the fp32 sums (dot4);
+// a finite h outside the fp16 range raises kStatusRange.
+template <typename WT, int RW, int J, bool WIDE = false, bool TRACE = false, bool HALF = false>
 __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
+  static_assert(!HALF || (std::is_same<WT, _Float16>::value && !WIDE), "half-h needs packed fp16 weights");
+  using HT = typename std::conditional<HALF, _Float16, float>::type;
   constexpr int M = pow2_at_least(RW);
   constexpr int kRow = 256 * J;   // LDS row: every chunk the instance can hold
-  // 16-byte aligned: the row is read and written as float4, and the static
-  // abort flag would otherwise leave the dynamic block at byte 4.
-  extern __shared__ __attribute__((aligned(16))) float lds[];  // [2][kRow] double-buffered h row
+  // 16-byte aligned: the row is read and written in 16- (8-) byte pieces, and
+  // the static abort flag would otherwise leave the dynamic block at byte 4.
+  extern __shared__ __attribute__((aligned(16))) float lds_words[];
+  HT* const lds = reinterpret_cast<HT*>(lds_words);  // [2][kRow] double-buffered h row
   __shared__ int abort_flag;
   const TeamPos p = team_pos(a);
   // A failed run stays failed until reported.  One thread reads the status
@@ -168,13 +203,14 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
   // below is read and multiplied without a bounds test and the compiler can
   // issue all the LDS reads of a step together.
   for (int c = a.Npad + (int)threadIdx.x; c < 2 * kRow; c += blockDim.x)
-    if (c % kRow >= a.Npad) lds[c] = 0.f;
+    if (c % kRow >= a.Npad) lds[c] = (HT)0.f;
   __syncthreads();
   if (abort_flag) return;
 
   const int N = a.N;
   const int jn = a.chunks;
   const bool vec = (N & 3) == 0;
+  uint32_t range_bad = 0;  // half-h: a staged value beyond the fp16 range
   if (!p.primary) {
     team_stamp_tail(a, p, team_region(a));
     return;
@@ -202,13 +238,13 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
 
   for (int t = 0; t < a.T; ++t) {
     const uint32_t S = a.step0 + (uint32_t)t;
-    float* hrow = lds + (t & 1) * kRow;
+    HT* hrow = lds + (t & 1) * kRow;
     bool ok = true;
     if (t == 0) {
-      team_stage_h0(a.h0, p.b, N, a.Npad, hrow);
+      team_stage_h0(a.h0, p.b, N, a.Npad, hrow, range_bad);
     } else {
       const uint32_t prev = S - 1u;
-      ok = team_stage(region, prev & 1u, a.Npad, N, jn, p.wave, p.lane, tag_bit(prev), a.deadline, hrow);
+      ok = team_stage(region, prev & 1u, a.Npad, N, jn, p.wave, p.lane, tag_bit(prev), a.deadline, hrow, range_bad);
     }
     if (!ok && p.lane == 0) {
       abort_flag = 1;
@@ -224,16 +260,26 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
     xoff += xstep;
     if (t + 1 < a.T) x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
 
-    float4 h[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) h[j] = *reinterpret_cast<const float4*>(hrow + 256 * j + 4 * p.lane);
     float acc[M];
 #pragma unroll
     for (int r = 0; r < M; ++r) acc[r] = 0.f;
+    if constexpr (HALF) {
+      uint2 h[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j)
+      for (int j = 0; j < J; ++j) h[j] = *reinterpret_cast<const uint2*>(hrow + 256 * j + 4 * p.lane);
 #pragma unroll
-      for (int r = 0; r < RW; ++r) w[r][j].fma4(acc[r], h[j]);
+      for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int r = 0; r < RW; ++r) w[r][j].dot4(acc[r], h[j]);
+    } else {
+      float4 h[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) h[j] = *reinterpret_cast<const float4*>(hrow + 256 * j + 4 * p.lane);
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int r = 0; r < RW; ++r) w[r][j].fma4(acc[r], h[j]);
+    }
     clk.mark(kTrCompute);
     const float sum = RowReduce<M>::reduce(acc, p.lane);
     clk.mark(kTrReduce);
@@ -249,6 +295,7 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
     }
     clk.mark(kTrEpilogue);
   }
+  if (HALF && wave_any(range_bad != 0) && p.lane == 0) atomicOr(a.status, kStatusRange);
   if (TRACE) clk.finish(trace_record(a, p), a.T);
 }
 
@@ -304,7 +351,8 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
       for (int c = threadIdx.x; c < N; c += blockDim.x) hrow[c] = a.h0 != nullptr ? a.h0[(size_t)p.b * N + c] : 0.f;
     } else {
       const uint32_t prev = S - 1u;
-      ok = team_stage(region, prev & 1u, a.Npad, N, jn, p.wave, p.lane, tag_bit(prev), a.deadline, hrow);
+      uint32_t unused = 0;
+      ok = team_stage(region, prev & 1u, a.Npad, N, jn, p.wave, p.lane, tag_bit(prev), a.deadline, hrow, unused);
     }
     if (!ok && p.lane == 0) {
       abort_flag = 1;
@@ -360,6 +408,10 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
 #define PRNN_SPARSE_TEAM(VT, VTAG, R, S) {VTAG, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<VT, R, S>)}
 #define PRNN_DENSE_TEAM_TRACE(WT, WTAG, R, JJ) \
   {WTAG, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<WT, R, JJ, false, true>)}
+#define PRNN_DENSE_TEAM_HALF(R, JJ) \
+  {kF16, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<_Float16, R, JJ, false, false, true>)}
+#define PRNN_DENSE_TEAM_HALF_TRACE(R, JJ) \
+  {kF16, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<_Float16, R, JJ, false, true, true>)}
 #define PRNN_DENSE_TEAM_WIDE_TRACE(R, JJ) \
   {kF16, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<_Float16, R, JJ, true, true>)}
 #define PRNN_SPARSE_TEAM_TRACE(VT, VTAG, R, S) \

@@ -51,6 +51,7 @@ def reference(kind, d):
 PATHS = [
     ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_EXACT),
     ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_SPLIT),
+    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_HALF),
     ("dense_f16_n1792", binding.LAYOUT_SPREAD, binding.MATH_EXACT),
     ("dense_f32_n256", binding.LAYOUT_TEAM, binding.MATH_AUTO),
     ("sparse10_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_AUTO),
