@@ -44,7 +44,7 @@ HBM_PEAK = 8.0e12             # MI355X HBM3E, bytes/s
 COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_rnn_fwd_n1792.json")
 KERNEL_SOURCES = ["device_common.h", "kernels.h", "dense_kernel.h", "sparse_kernel.h", "team_kernel.h", "team_mfma.h",
                   "dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip", "team_f16.hip", "team_f32.hip",
-                  "project.hip", "stack.hip"]
+                  "team_half.hip", "project.hip", "stack.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -68,7 +68,7 @@ def parse():
     ap.add_argument("--no-baselines", action="store_true", help="skip the library and torch-CPU loop baselines")
     ap.add_argument("--no-layers", action="store_true", help="skip the whole-layer (projection + recurrence) table")
     ap.add_argument("--profile-layers", action="store_true",
-                    help="with --only-timed: also run 5 input projections and one layer call (N=1792) and one "
+                    help="with --only-timed: also run 5 half-h dense calls, 5 input projections and one layer call (N=1792) and one "
                          "2-layer stack wavefront (N=1152), T=256, after the timed loop, for profilers")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config table (every workload, not timed "
                     "in the headline step)")
@@ -244,9 +244,16 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
     between T and T/2, the sync floor at the same N, B, T, and the error ratio
     of the timed output against the oracle."""
     import numpy as np
+    from persistent_rnn_fwd_amd import binding as _b
     rows = {}
     h = Handle()
-    for name, w in WORKLOADS.items():
+    # every workload in the default math, then the dense fp16 layers again with
+    # h_{t-1} staged as fp16 (the opt-in half-h math)
+    cases = [(name, w, _b.MATH_AUTO) for name, w in WORKLOADS.items()]
+    cases += [(name + "_half_h", w, _b.MATH_HALF) for name, w in WORKLOADS.items()
+              if w.kind == "dense" and w.w_dtype == "f16"]
+    for name, w, math in cases:
+        h.set_math(math)
         d = generate(w)
         g = {k: torch.from_numpy(v).to(dev) for k, v in d.items()}
         T, B, N = w.T, w.B, w.N
@@ -290,6 +297,7 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
             "plan": plan,
         }
         del g, o, fo
+    h.set_math(_b.MATH_AUTO)
     h.close()
     return rows
 
@@ -538,6 +546,11 @@ def main():
         for _ in range(5):
             h.project(gl["U"], gl["x"], gl["bias"], out=Xw)
         h.forward_layer_dense(gl["U"], gl["bias"], gl["W"], gl["x"], gl["h0"], out=out[wd.name], workspace=Xw)
+        from persistent_rnn_fwd_amd import binding as _b
+        h.set_math(_b.MATH_HALF)     # the dense layer with h staged as fp16
+        for _ in range(5):
+            call(wd.name)
+        h.set_math(_b.MATH_AUTO)
         st = generate_stack(WORKLOADS["dense_f16_n1152"], 2)  # the largest wavefront size
         layers = [{k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in ly.items()} for ly in st["layers"]]
         h.forward_stack_dense(layers, torch.from_numpy(st["x"]).to(dev))
