@@ -110,7 +110,8 @@ typedef enum {
  *          (all batch rows share the workgroup's resident rows).  h_{t-1}
  *          crosses between XCDs every step (see prnnExchange_t).
  *  TEAM:   each of the 8 XCDs runs one batch row's whole recurrence with up
- *          to 32 workgroups of 8 waves; a wave owns a few rows of W.  h_{t-1}
+ *          to 32 workgroups of 8 waves (16 for sparse fp16 layers that would
+ *          hold more than 16 rows per wave); a wave owns a few rows of W.  h_{t-1}
  *          is exchanged inside the XCD's L2 only.  With B < 8 the remaining
  *          XCDs compute nothing; they only mark their exchange memory as
  *          written for the call's last steps.  Holds W once per XCD: for
@@ -150,7 +151,9 @@ typedef enum {
 typedef struct {
   int layout;        /* PRNN_LAYOUT_SPREAD or PRNN_LAYOUT_TEAM                 */
   int grid;          /* workgroups launched                                    */
-  int waves_per_wg;  /* SPREAD: min(B, 4), one wave per batch row; TEAM: 8     */
+  int waves_per_wg;  /* SPREAD: min(B, 4), one wave per batch row; TEAM: 8,
+                        or 16 for sparse fp16 layers (and their floor) that
+                        would hold more than 16 rows per wave at 8          */
   int rows_per_wave; /* largest number of W rows one wave keeps resident       */
   int rmax;          /* compiled row capacity of the kernel instance           */
   int chunks;        /* dense: 256-column chunk capacity; sparse: 64-pair slots */
@@ -320,6 +323,14 @@ prnnStatus_t prnn_synchronize(prnnHandle_t handle, hipStream_t stream);
  * per XCD).  BAD_PARAM if negative. */
 prnnStatus_t prnn_set_grid(prnnHandle_t handle, int workgroups);
 
+/* Waves per workgroup of the TEAM layout for later calls: 0 (default) =
+ * automatic (16 for sparse fp16 layers that would hold more than 16 rows per
+ * wave at 8 waves and have a 16-wave instance, else 8), 8, or 16.  16 is
+ * offered to sparse fp16 layers and to prnn_sync_floor only; a forced count
+ * that the call cannot use makes it return NOT_SUPPORTED (or fall back to the
+ * SPREAD layout under LAYOUT_AUTO).  BAD_PARAM for any other value. */
+prnnStatus_t prnn_set_team_waves(prnnHandle_t handle, int waves);
+
 /* Exchange mode for later calls (default AUTO).  A forced RELAY that the
  * plan cannot use makes forward calls return NOT_SUPPORTED.  BAD_PARAM for an
  * unknown mode. */
@@ -357,9 +368,10 @@ prnnStatus_t prnn_set_trace(prnnHandle_t handle, int enable);
 
 /* Copies the trace of the last traced call into `out` (host memory,
  * `capacity` uint64 words), after synchronizing `stream`.  Record w (words
- * [8 w, 8 w + 8)) belongs to wave w % 8 of workgroup w / 8; records of
- * workgroups that serve no batch row of their own are zero.  *records
- * receives the number of records (grid * 8).  BAD_PARAM if no traced call
+ * [8 w, 8 w + 8)) belongs to wave w % V of workgroup w / V, V = the
+ * plan's waves_per_wg; records of workgroups that serve no batch row of
+ * their own are zero.  *records receives the number of records
+ * (grid * waves_per_wg).  BAD_PARAM if no traced call
  * was made, or if out is NULL or capacity < 8 * records (then *records is
  * still set, so out = NULL, capacity = 0 asks for the size). */
 prnnStatus_t prnn_get_trace(prnnHandle_t handle, uint64_t* out, size_t capacity, int* records,

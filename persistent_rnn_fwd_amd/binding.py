@@ -43,6 +43,7 @@ SIGNATURES = {
     "prnn_sync_floor": (_I, [_H, _I, _I, _I, _P, _P]),
     "prnn_synchronize": (_I, [_H, _P]),
     "prnn_set_grid": (_I, [_H, _I]),
+    "prnn_set_team_waves": (_I, [_H, _I]),
     "prnn_set_watchdog_us": (_I, [_H, ctypes.c_uint32]),
     "prnn_set_exchange": (_I, [_H, _I]),
     "prnn_set_layout": (_I, [_H, _I]),
@@ -163,6 +164,10 @@ class Handle:
     def set_grid(self, workgroups: int):
         _check("prnn_set_grid", self._lib.prnn_set_grid(self._h, int(workgroups)))
 
+    def set_team_waves(self, waves: int):
+        """Waves per team-layout workgroup for later calls: 0 (automatic), 8 or 16."""
+        _check("prnn_set_team_waves", self._lib.prnn_set_team_waves(self._h, int(waves)))
+
     def set_exchange(self, mode: int):
         """EXCHANGE_AUTO, EXCHANGE_DIRECT or EXCHANGE_RELAY for later calls."""
         _check("prnn_set_exchange", self._lib.prnn_set_exchange(self._h, int(mode)))
@@ -201,7 +206,7 @@ class Handle:
         _check("prnn_set_trace", self._lib.prnn_set_trace(self._h, 1 if enable else 0))
 
     def get_trace(self, stream: Optional[torch.cuda.Stream] = None):
-        """Phase records of the last traced call: uint64 array [grid * 8, 8]
+        """Phase records of the last traced call: uint64 array [grid * waves_per_wg, 8]
         (stage, barrier, compute, reduce, epilogue cycles; loop cycles; loop
         ticks of the 100 MHz clock; steps), one row per wave."""
         import numpy as np

@@ -49,6 +49,7 @@ struct KernelEntry {
   int rmax;    // compiled row capacity per workgroup
   int cap;     // dense: compiled chunk capacity J; sparse: slots per row SPR
   const void* fn;
+  int waves = 8;  // team layout: waves per workgroup the instance is compiled for
 };
 
 // Instance tables (each terminated by fn == nullptr).
@@ -61,6 +62,10 @@ extern const KernelEntry kDenseTeamF16Kernels[];   // team layout: rmax = rows p
 extern const KernelEntry kDenseTeamF32Kernels[];
 extern const KernelEntry kSparseTeamF16Kernels[];
 extern const KernelEntry kSparseTeamF32Kernels[];
+// Team layout with 16-wave workgroups (4 waves per SIMD), for sparse fp16
+// layers whose rows would exceed 16 per wave at 8 waves per workgroup.
+extern const KernelEntry kSparseTeamF16Kernels16[];
+extern const KernelEntry kSparseTeamF16TraceKernels16[];
 
 // Fills n words with v (grid-stride).
 void launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t stream);
@@ -85,6 +90,8 @@ extern const KernelEntry kDenseTeamF32TraceKernels[];
 extern const KernelEntry kSparseTeamF16TraceKernels[];
 extern const KernelEntry kSparseTeamF32TraceKernels[];
 extern const void* kFloorTeamTraceKernel;
+extern const void* kFloorTeamKernel16;       // the floor with 16-wave workgroups
+extern const void* kFloorTeamTraceKernel16;
 void launch_team_fill(uint32_t* ring, int npad, uint32_t v, hipStream_t stream);
 
 // A stack of dense fp16 layers as one wavefront (stack.hip).  Team x serves

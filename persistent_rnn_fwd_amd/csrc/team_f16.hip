@@ -31,6 +31,18 @@ const KernelEntry kSparseTeamF16Kernels[] = {
     {0, 0, 0, nullptr},
 };
 
+// 16-wave workgroups (at most 128 VGPRs): rows of one 64-pair slot, 12 rows per
+// wave for the 1 % layer at N = 5760, up to 16.  Wider rows (5 % at N = 5760:
+// 12 rows x 5 slots) spill at 128 VGPRs and keep 8-wave workgroups.
+const KernelEntry kSparseTeamF16Kernels16[] = {
+    PRNN_SPARSE_TEAM16(_Float16, kF16, 12, 1), PRNN_SPARSE_TEAM16(_Float16, kF16, 16, 1),
+    {0, 0, 0, nullptr},
+};
+const KernelEntry kSparseTeamF16TraceKernels16[] = {
+    PRNN_SPARSE_TEAM16_TRACE(_Float16, kF16, 12, 1),
+    {0, 0, 0, nullptr},
+};
+
 // Trace instances: the shapes of the configured layers (N = 1152 and 1792
 // dense; 10 % and 1 % sparse at N = 1152, 1792 and 5760).
 const KernelEntry kDenseTeamF16TraceKernels[] = {

@@ -20,12 +20,13 @@ const KernelEntry kSparseTeamF32Kernels[] = {
     {0, 0, 0, nullptr},
 };
 
-// The team layout's exchange and step protocol without weights or arithmetic.
-template <bool TRACE>
-__global__ void __launch_bounds__(512) floor_team_kernel(StepArgs a) {
+// The team layout's exchange and step protocol without weights or arithmetic
+// (WAVES = waves per workgroup, as the layer it is the floor of).
+template <bool TRACE, int WAVES = kTeamWaves>
+__global__ void __launch_bounds__(64 * WAVES) floor_team_kernel(StepArgs a) {
   extern __shared__ __attribute__((aligned(16))) float lds[];  // float4-staged rows
   __shared__ int abort_flag;
-  const TeamPos p = team_pos(a);
+  const TeamPos p = team_pos<WAVES>(a);
   if (threadIdx.x == 0) abort_flag = __builtin_nontemporal_load(a.status) != 0u;
   __syncthreads();
   if (abort_flag) return;
@@ -44,7 +45,8 @@ __global__ void __launch_bounds__(512) floor_team_kernel(StepArgs a) {
     if (t > 0) {
       const uint32_t prev = S - 1u;
       uint32_t unused = 0;
-      ok = team_stage(region, prev & 1u, a.Npad, N, a.chunks, p.wave, p.lane, tag_bit(prev), a.deadline, hrow, unused);
+      ok = team_stage<WAVES>(region, prev & 1u, a.Npad, N, a.chunks, p.wave, p.lane, tag_bit(prev), a.deadline, hrow,
+                             unused);
     }
     if (!ok && p.lane == 0) {
       abort_flag = 1;
@@ -66,7 +68,7 @@ __global__ void __launch_bounds__(512) floor_team_kernel(StepArgs a) {
     }
     clk.mark(kTrEpilogue);
   }
-  if (TRACE) clk.finish(trace_record(a, p), a.T);
+  if (TRACE) clk.finish(trace_record<WAVES>(a, p), a.T);
 }
 
 // Resets the team ring: every XCD fills its own region (so its L2 never holds
@@ -81,6 +83,8 @@ __global__ void team_fill_kernel(uint32_t* ring, int npad, uint32_t v) {
 
 const void* kFloorTeamKernel = reinterpret_cast<const void*>(&floor_team_kernel<false>);
 const void* kFloorTeamTraceKernel = reinterpret_cast<const void*>(&floor_team_kernel<true>);
+const void* kFloorTeamKernel16 = reinterpret_cast<const void*>(&floor_team_kernel<false, 16>);
+const void* kFloorTeamTraceKernel16 = reinterpret_cast<const void*>(&floor_team_kernel<true, 16>);
 
 // Trace instances (the N = 256 fp32 layer).
 const KernelEntry kDenseTeamF32TraceKernels[] = {

@@ -41,6 +41,7 @@ struct TeamPos {
   int nr, r0;                        // this wave's rows
 };
 
+template <int W = kTeamWaves>
 __device__ __forceinline__ TeamPos team_pos(const StepArgs& a) {
   TeamPos p;
   p.team = blockIdx.x & 7;
@@ -49,7 +50,7 @@ __device__ __forceinline__ TeamPos team_pos(const StepArgs& a) {
   p.primary = p.team < a.B;
   p.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform for the compiler
   p.lane = threadIdx.x & 63;
-  p.q = p.rank * kTeamWaves + p.wave;
+  p.q = p.rank * W + p.wave;
   p.nr = a.base_rows + (p.q < a.extra_rows ? 1 : 0);
   p.r0 = p.q * a.base_rows + min(p.q, a.extra_rows);
   return p;
@@ -82,15 +83,16 @@ __device__ __forceinline__ void store_chunk(_Float16* d, const float4& f, uint32
 }
 
 // Stages chunks w, w + 8, ... of ring slot `slot` into the LDS row `dst`
-// (Npad elements), waiting until every word carries `tag`.  Returns false if
-// the wait expired (the caller must still reach the workgroup barrier).
-template <typename HT>
+// (Npad elements), waiting until every word carries `tag`; W = waves per
+// workgroup.  Returns false if the wait expired (the caller must still reach
+// the workgroup barrier).
+template <int W = kTeamWaves, typename HT>
 __device__ __forceinline__ bool team_stage(__amdgpu_buffer_rsrc_t region, uint32_t slot, int npad, int n, int jn,
                                            int wave, int lane, uint32_t tag, uint64_t deadline, HT* dst,
                                            uint32_t& bad) {
   const uint32_t base = slot * (uint32_t)npad * 4u;
   bool ok = true;
-  for (int j = wave; j < jn; j += kTeamWaves) {
+  for (int j = wave; j < jn; j += W) {
     const int c = 256 * j + 4 * lane;
     u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(region, base + 4u * c, 0, kCoherent);
     const uint64_t t0 = now_ticks();
@@ -153,8 +155,9 @@ struct PhaseClock<true> {
   }
 };
 
+template <int W = kTeamWaves>
 __device__ __forceinline__ uint64_t* trace_record(const StepArgs& a, const TeamPos& p) {
-  return a.trace + ((size_t)blockIdx.x * kTeamWaves + (size_t)p.wave) * kTraceWords;
+  return a.trace + ((size_t)blockIdx.x * W + (size_t)p.wave) * kTraceWords;
 }
 
 // The dense recurrence in the team layout.  RW = rows per wave (capacity),
@@ -301,14 +304,15 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
 
 // The sparse recurrence in the team layout: the h row is staged once per
 // workgroup (all its waves serve the same batch row) and every wave gathers
-// from it for its own rows.  RW = rows per wave, SPR = 64-pair slots per row.
-template <typename VT, int RW, int SPR, bool TRACE = false>
-__global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
+// from it for its own rows.  RW = rows per wave, SPR = 64-pair slots per row,
+// WAVES = waves per workgroup (8, or 16 for layers with many rows per wave).
+template <typename VT, int RW, int SPR, bool TRACE = false, int WAVES = kTeamWaves>
+__global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
   constexpr int M = pow2_at_least(RW);
   extern __shared__ __attribute__((aligned(16))) float lds[];  // [2][lds_stride]: word N of each row stays 0
   __shared__ int abort_flag;
-  __shared__ uint2 place_scratch[kTeamWaves][64 * SPR];  // prologue only: pair placement
-  const TeamPos p = team_pos(a);
+  __shared__ uint2 place_scratch[WAVES][64 * SPR];  // prologue only: pair placement
+  const TeamPos p = team_pos<WAVES>(a);
   const int N = a.N;
   const int K = a.K;
   const int stride = a.lds_stride;
@@ -352,7 +356,7 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
     } else {
       const uint32_t prev = S - 1u;
       uint32_t unused = 0;
-      ok = team_stage(region, prev & 1u, a.Npad, N, jn, p.wave, p.lane, tag_bit(prev), a.deadline, hrow, unused);
+      ok = team_stage<WAVES>(region, prev & 1u, a.Npad, N, jn, p.wave, p.lane, tag_bit(prev), a.deadline, hrow, unused);
     }
     if (!ok && p.lane == 0) {
       abort_flag = 1;
@@ -399,7 +403,7 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
     }
     clk.mark(kTrEpilogue);
   }
-  if (TRACE) clk.finish(trace_record(a, p), a.T);
+  if (TRACE) clk.finish(trace_record<WAVES>(a, p), a.T);
 }
 
 
@@ -414,6 +418,10 @@ __global__ void __launch_bounds__(512) sparse_team_kernel(StepArgs a) {
   {kF16, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<_Float16, R, JJ, false, true, true>)}
 #define PRNN_DENSE_TEAM_WIDE_TRACE(R, JJ) \
   {kF16, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<_Float16, R, JJ, true, true>)}
+#define PRNN_SPARSE_TEAM16(VT, VTAG, R, S) \
+  {VTAG, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<VT, R, S, false, 16>), 16}
+#define PRNN_SPARSE_TEAM16_TRACE(VT, VTAG, R, S) \
+  {VTAG, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<VT, R, S, true, 16>), 16}
 #define PRNN_SPARSE_TEAM_TRACE(VT, VTAG, R, S) \
   {VTAG, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<VT, R, S, true>)}
 

@@ -48,6 +48,7 @@ def test_null_handle_is_bad_param():
     assert lib.prnn_sync_floor(None, 4, 1, 1, 16, None) == bp
     assert lib.prnn_synchronize(None, None) == bp
     assert lib.prnn_set_grid(None, 0) == bp
+    assert lib.prnn_set_team_waves(None, 0) == bp
     assert lib.prnn_set_watchdog_us(None, 1) == bp
     assert lib.prnn_get_last_plan(None, None) == bp
     assert lib.prnn_debug_skip_publish(None, 0, 0) == bp

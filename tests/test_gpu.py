@@ -269,6 +269,52 @@ def test_plan_of_headline_layer(handle):
     assert p["relay_slice"] == 1792 // 32   # auto picks the per-XCD relay at 256 workgroups
 
 
+def test_plan_of_large_sparse_layers(handle):
+    """Sparse fp16 layers that would hold more than 16 rows per wave at 8 waves
+    per workgroup run 16-wave workgroups where an instance fits the 128
+    registers of 4 waves per SIMD (1 % at N = 5760: 12 rows of one slot), and
+    8-wave workgroups otherwise (5 % at N = 5760: 23 rows of 5 slots)."""
+    for name, waves, rows in [("sparse1_f16_n5760", 16, 12), ("sparse5_f16_n5760", 8, 23),
+                              ("sparse10_f16_n2304", 8, 9)]:
+        w = WORKLOADS[name].with_(T=6)
+        d = generate(w, seed=71)
+        H = run(handle, "sparse", d)
+        p = handle.last_plan()
+        assert p["layout"] == binding.LAYOUT_TEAM and p["waves_per_wg"] == waves and p["rows_per_wave"] == rows, p
+        assert_parity(H, reference("sparse", d), oracle.TOL_F16, name)
+    # forced wave counts: 8 for the 1 % layer (23 rows per wave), 16 where no
+    # instance or kernel has it (NOT_SUPPORTED in the TEAM layout), bad values
+    w = WORKLOADS["sparse1_f16_n5760"].with_(T=6)
+    d = generate(w, seed=72)
+    handle.set_team_waves(8)
+    try:
+        H = run(handle, "sparse", d)
+        p = handle.last_plan()
+        assert p["waves_per_wg"] == 8 and p["rows_per_wave"] == 23
+        assert_parity(H, reference("sparse", d), oracle.TOL_F16, "forced 8 waves")
+        out = torch.empty((6, 4, 5760), device="cuda")
+        handle.sync_floor(5760, 4, 6, out=out)
+        assert handle.last_plan()["waves_per_wg"] == 8
+        handle.set_team_waves(16)
+        for name, kind in [("sparse5_f16_n5760", "sparse"), ("dense_f16_n1152", "dense")]:
+            w2 = WORKLOADS[name].with_(T=3)
+            with pytest.raises(PrnnError) as e:
+                run(handle, kind, generate(w2), layout=binding.LAYOUT_TEAM)
+            assert e.value.status == binding.NOT_SUPPORTED
+        with pytest.raises(PrnnError) as e:
+            handle.set_team_waves(12)
+        assert e.value.status == binding.BAD_PARAM
+    finally:
+        handle.set_team_waves(0)
+        handle.set_layout(binding.LAYOUT_AUTO)
+    # a ragged large layer, one slot per row, several forced grids
+    for N, grid in [(6001, 0), (4500, 192), (8000, 256)]:
+        w = Workload(f"sparse_{N}", "sparse", N, 3, 5, "f16", K=40, seed=N, h0="randn")
+        d = generate(w)
+        H = run(handle, "sparse", d, grid=grid)
+        assert_parity(H, reference("sparse", d), oracle.TOL_F16, f"N={N} grid={grid} {handle.last_plan()}")
+
+
 @pytest.mark.parametrize("name", ["dense_f16_n1792", "sparse10_f16_n1792", "sparse1_f16_n1792"])
 def test_team_and_spread_agree_bitwise(handle, name):
     """At N = 1792 both layouts give every wave the same 7 rows, the same
@@ -421,8 +467,10 @@ def test_trace_records_phases(gpu, name):
     assert np.array_equal(H0, H1) and np.array_equal(H0, H2)
     assert plan["layout"] == binding.LAYOUT_TEAM
     grid = plan["grid"]
-    assert tr.shape == (grid * 8, binding.TRACE_WORDS)
-    rec = tr.reshape(grid, 8, binding.TRACE_WORDS).astype(np.float64)
+    waves = plan["waves_per_wg"]
+    assert waves == (16 if name == "sparse1_f16_n5760" else 8)   # the N = 5760 layer runs 16-wave workgroups
+    assert tr.shape == (grid * waves, binding.TRACE_WORDS)
+    rec = tr.reshape(grid, waves, binding.TRACE_WORDS).astype(np.float64)
     serving = (np.arange(grid) % 8) < w.B
     live = rec[serving]
     assert np.all(live[..., 7] == w.T)
@@ -444,6 +492,12 @@ def test_trace_floor_and_errors(gpu):
         h.sync_floor(N, B, T, out=out)
         tr = h.get_trace()
         assert int((tr[:, 7] == T).sum()) == B * (h.last_plan()["grid"] // 8) * 8
+        # a layer too large for 16 rows per wave at 8 waves: 16-wave workgroups, 16 records each
+        h.sync_floor(5760, B, T, out=torch.empty((T, B, 5760), device="cuda"))
+        tr = h.get_trace()
+        p = h.last_plan()
+        assert p["waves_per_wg"] == 16 and tr.shape[0] == p["grid"] * 16
+        assert int((tr[:, 7] == T).sum()) == B * (p["grid"] // 8) * 16
         h.set_layout(binding.LAYOUT_SPREAD)     # trace instances are team-layout only
         w = WORKLOADS["dense_f16_n1792"].with_(T=4)
         g = to_dev(generate(w))

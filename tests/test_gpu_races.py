@@ -56,6 +56,7 @@ PATHS = [
     ("dense_f32_n256", binding.LAYOUT_TEAM, binding.MATH_AUTO),
     ("sparse10_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_AUTO),
     ("sparse10_f16_n1792", binding.LAYOUT_SPREAD, binding.MATH_AUTO),
+    ("sparse1_f16_n5760", binding.LAYOUT_TEAM, binding.MATH_AUTO),    # 16-wave workgroups
 ]
 
 
