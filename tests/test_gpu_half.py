@@ -238,3 +238,51 @@ def test_half_trace_and_watchdog(gpu):
         H2 = h.forward_dense(g["W"], g["X"], g["h0"])
         h.synchronize()
         np.testing.assert_array_equal(H2.cpu().numpy(), H0.cpu().numpy())
+
+
+def test_half_layer_and_stack(gpu):
+    """A whole dense layer follows the math setting (projection, then the
+    half-h recurrence); a layer-by-layer stack does too; the blocked and fused
+    stacks keep exact math (bitwise equal to the same stack with the default
+    setting)."""
+    from persistent_rnn_fwd_amd.inputs import generate_layer, generate_stack
+    import torch
+    w = WORKLOADS["dense_f16_n1792"].with_(T=48, h0="randn")
+    d = generate_layer(w, 1792)
+    g = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in d.items()}
+    ref = oracle.forward_layer_dense(d["U"], d["bias"], d["W"], d["x"], d["h0"])
+    with Handle() as h:
+        h.set_math(binding.MATH_HALF)
+        H = h.forward_layer_dense(g["U"], g["bias"], g["W"], g["x"], g["h0"])
+        h.synchronize()
+        assert h.last_plan()["math"] == binding.MATH_HALF
+        assert oracle.tolerance_ratio(H.cpu().numpy(), ref, oracle.TOL_F16) <= 1.0
+        h.set_math(binding.MATH_EXACT)
+        He = h.forward_layer_dense(g["U"], g["bias"], g["W"], g["x"], g["h0"])
+        h.synchronize()
+        assert not torch.equal(H, He)
+
+        sw = WORKLOADS["dense_f16_n1152"].with_(N=640, B=2, T=40, h0="randn", seed=31)
+        st = generate_stack(sw, 2)
+        layers = [{k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in ly.items()} for ly in st["layers"]]
+        x = torch.from_numpy(st["x"]).cuda()
+        h0s = [torch.from_numpy(v).cuda() for v in st["h0s"]]
+        refs = oracle.forward_stack_dense(st["layers"], st["x"], st["h0s"])
+
+        def stack(mode, math):
+            h.set_stack_mode(mode)
+            h.set_math(math)
+            outs = h.forward_stack_dense(layers, x, h0s)
+            h.synchronize()
+            h.set_stack_mode(binding.STACK_AUTO)
+            h.set_math(binding.MATH_AUTO)
+            return [o.cpu().numpy() for o in outs]
+
+        half_layers = stack(binding.STACK_LAYERS, binding.MATH_HALF)
+        exact_layers = stack(binding.STACK_LAYERS, binding.MATH_EXACT)
+        assert all(oracle.tolerance_ratio(a, r, oracle.TOL_F16) <= 1.0 for a, r in zip(half_layers, refs))
+        assert not all(np.array_equal(a, b) for a, b in zip(half_layers, exact_layers))
+        for mode in (binding.STACK_BLOCKED, binding.STACK_FUSED):
+            a = stack(mode, binding.MATH_HALF)
+            b = stack(mode, binding.MATH_AUTO)
+            assert all(np.array_equal(p, q) for p, q in zip(a, b)), mode
