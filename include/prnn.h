@@ -110,8 +110,8 @@ typedef enum {
  *          (all batch rows share the workgroup's resident rows).  h_{t-1}
  *          crosses between XCDs every step (see prnnExchange_t).
  *  TEAM:   each of the 8 XCDs runs one batch row's whole recurrence with up
- *          to 32 workgroups of 8 waves (16 for sparse fp16 layers that would
- *          hold more than 16 rows per wave); a wave owns a few rows of W.  h_{t-1}
+ *          to 32 workgroups of 8 waves (12 or 16 for sparse fp16 layers that
+ *          would hold more than 8 rows per wave); a wave owns a few rows of W.  h_{t-1}
  *          is exchanged inside the XCD's L2 only.  With B < 8 the remaining
  *          XCDs compute nothing; they only mark their exchange memory as
  *          written for the call's last steps.  Holds W once per XCD: for
@@ -152,8 +152,8 @@ typedef struct {
   int layout;        /* PRNN_LAYOUT_SPREAD or PRNN_LAYOUT_TEAM                 */
   int grid;          /* workgroups launched                                    */
   int waves_per_wg;  /* SPREAD: min(B, 4), one wave per batch row; TEAM: 8,
-                        or 16 for sparse fp16 layers (and their floor) that
-                        would hold more than 16 rows per wave at 8          */
+                        or 12 / 16 for sparse fp16 layers (and the floor)
+                        that would hold more than 8 rows per wave at 8      */
   int rows_per_wave; /* largest number of W rows one wave keeps resident       */
   int rmax;          /* compiled row capacity of the kernel instance           */
   int chunks;        /* dense: 256-column chunk capacity; sparse: 64-pair slots */
@@ -324,8 +324,10 @@ prnnStatus_t prnn_synchronize(prnnHandle_t handle, hipStream_t stream);
 prnnStatus_t prnn_set_grid(prnnHandle_t handle, int workgroups);
 
 /* Waves per workgroup of the TEAM layout for later calls: 0 (default) =
- * automatic (16 for sparse fp16 layers that would hold more than 16 rows per
- * wave at 8 waves and have a 16-wave instance, else 8), 8, or 16.  16 is
+ * automatic (for sparse fp16 layers that would hold more than 8 rows per
+ * wave at 8 waves: 12, or first 16 above 16 rows, where an instance of that
+ * count fits, else 8; the floor picks 12 or 16 by the same row counts; 8
+ * otherwise), 8, 12 or 16.  12 and 16 are
  * offered to sparse fp16 layers and to prnn_sync_floor only; a forced count
  * that the call cannot use makes it return NOT_SUPPORTED (or fall back to the
  * SPREAD layout under LAYOUT_AUTO).  BAD_PARAM for any other value. */

@@ -165,7 +165,7 @@ class Handle:
         _check("prnn_set_grid", self._lib.prnn_set_grid(self._h, int(workgroups)))
 
     def set_team_waves(self, waves: int):
-        """Waves per team-layout workgroup for later calls: 0 (automatic), 8 or 16."""
+        """Waves per team-layout workgroup for later calls: 0 (automatic), 8, 12 or 16."""
         _check("prnn_set_team_waves", self._lib.prnn_set_team_waves(self._h, int(waves)))
 
     def set_exchange(self, mode: int):

@@ -65,6 +65,7 @@ extern const KernelEntry kSparseTeamF32Kernels[];
 // Team layout with 16-wave workgroups (4 waves per SIMD), for sparse fp16
 // layers whose rows would exceed 16 per wave at 8 waves per workgroup.
 extern const KernelEntry kSparseTeamF16Kernels16[];
+extern const KernelEntry kSparseTeamF16Kernels12[];   // 12-wave workgroups (3 waves per SIMD)
 extern const KernelEntry kSparseTeamF16TraceKernels16[];
 
 // Fills n words with v (grid-stride).
@@ -92,6 +93,8 @@ extern const KernelEntry kSparseTeamF32TraceKernels[];
 extern const void* kFloorTeamTraceKernel;
 extern const void* kFloorTeamKernel16;       // the floor with 16-wave workgroups
 extern const void* kFloorTeamTraceKernel16;
+extern const void* kFloorTeamKernel12;       // ... and with 12-wave workgroups
+extern const void* kFloorTeamTraceKernel12;
 void launch_team_fill(uint32_t* ring, int npad, uint32_t v, hipStream_t stream);
 
 // A stack of dense fp16 layers as one wavefront (stack.hip).  Team x serves

@@ -152,21 +152,27 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
   }
   P = std::min(P, (N + 7) / 8);  // at least one row per workgroup on average
   if (P < 1 || 8 * P > h->num_cu) return false;
-  // Sparse fp16 layers (and their floor) with more than 16 rows per wave at 8
-  // waves per workgroup run 16-wave workgroups: 4 waves per SIMD, half the
-  // rows per wave (measured at N = 5760, 1 %: 1.78 against 2.05 us per step).
+  // Sparse fp16 layers (and their floor) with more than 8 rows per wave at 8
+  // waves per workgroup run 12-wave workgroups (3 waves per SIMD), above 16
+  // rows 16-wave ones (4 per SIMD) first, where an instance fits: fewer rows
+  // per wave.  Measured, us per step: 1 % at N = 5760 2.05 (8 waves), 1.85
+  // (16), 1.82 (12); 5 % at N = 5760 3.44 -> 2.89 (12); 10 % at N = 2304
+  // 1.70 -> 1.48 (12).  At 7 rows per wave (N = 1792) more waves were slower.
   const int rows8 = (N + 8 * P - 1) / (8 * P);
-  const bool can16 = (kind == kSparse && wt == prnn::kF16) || kind == kFloor;
-  if (h->team_waves == 16 && !can16) return false;
-  int W = h->team_waves != 0 ? h->team_waves : (can16 && rows8 > 16 ? 16 : 8);
-  const int Q = P * W;  // waves per team
+  const bool wide_ok = (kind == kSparse && wt == prnn::kF16) || kind == kFloor;
+  if (h->team_waves > 8 && !wide_ok) return false;
+  auto set_waves = [&](int W) {
+    const int Q = P * W;  // waves per team
+    p->waves = W;
+    p->block = 64 * W;
+    p->base_rows = N / Q;
+    p->extra_rows = N % Q;
+    p->max_rows = (N + Q - 1) / Q;
+  };
+  int W = h->team_waves != 0 ? h->team_waves : (!wide_ok || rows8 <= 8 ? 8 : rows8 > 16 ? 16 : 12);
   p->G = P;
   p->grid = 8 * P;
-  p->waves = W;
-  p->block = 64 * W;
-  p->base_rows = N / Q;
-  p->extra_rows = N % Q;
-  p->max_rows = (N + Q - 1) / Q;
+  set_waves(W);
   p->chunks = (N + 255) / 256;
   const int Npad = (N + 3) & ~3;
   if (kind == kDense && wt == prnn::kF16 && h->math == PRNN_MATH_SPLIT) {
@@ -202,26 +208,26 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
     p->spr = (K + 63) / 64;
     const KernelEntry* table = h->trace ? (wt == prnn::kF32 ? prnn::kSparseTeamF32TraceKernels : prnn::kSparseTeamF16TraceKernels)
                                         : (wt == prnn::kF32 ? prnn::kSparseTeamF32Kernels : prnn::kSparseTeamF16Kernels);
+    // 16 waves, else 12, else 8 (a forced count: that one only)
     if (W == 16) {
       p->k = pick(h->trace ? prnn::kSparseTeamF16TraceKernels16 : prnn::kSparseTeamF16Kernels16, p->max_rows, p->spr);
       if (p->k == nullptr && h->team_waves == 16) return false;
-      if (p->k == nullptr) {  // no 16-wave instance for this shape: 8 waves
-        W = 8;
-        p->waves = 8;
-        p->block = 512;
-        p->base_rows = N / (P * 8);
-        p->extra_rows = N % (P * 8);
-        p->max_rows = rows8;
-      }
+      if (p->k == nullptr) set_waves(W = 12);
+    }
+    if (W == 12) {
+      p->k = h->trace ? nullptr : pick(prnn::kSparseTeamF16Kernels12, p->max_rows, p->spr);
+      if (p->k == nullptr && h->team_waves == 12) return false;
+      if (p->k == nullptr) set_waves(W = 8);
     }
     if (W == 8) p->k = pick(table, p->max_rows, p->spr);
     p->lds_stride = sparse_lds_stride(N);
     p->lds_bytes = 2 * p->lds_stride * 4;
   } else {
     static const KernelEntry floor_team = {0, 64, 1 << 30, nullptr};
+    static const KernelEntry floor_team12 = {0, 64, 1 << 30, nullptr, 12};
     static const KernelEntry floor_team16 = {0, 64, 1 << 30, nullptr, 16};
     if (p->max_rows > 64) return false;
-    p->k = W == 16 ? &floor_team16 : &floor_team;  // the caller substitutes the team floor kernel
+    p->k = W == 16 ? &floor_team16 : W == 12 ? &floor_team12 : &floor_team;  // the caller substitutes the kernel
     p->lds_bytes = 2 * Npad * 4;
   }
   if (p->k == nullptr) return false;
@@ -609,7 +615,7 @@ prnnStatus_t prnn_set_grid(prnnHandle_t h, int workgroups) {
 }
 
 prnnStatus_t prnn_set_team_waves(prnnHandle_t h, int waves) {
-  if (h == nullptr || (waves != 0 && waves != 8 && waves != 16)) return PRNN_STATUS_BAD_PARAM;
+  if (h == nullptr || (waves != 0 && waves != 8 && waves != 12 && waves != 16)) return PRNN_STATUS_BAD_PARAM;
   h->team_waves = waves;
   return PRNN_STATUS_SUCCESS;
 }
@@ -953,13 +959,19 @@ prnnStatus_t prnn_sync_floor(prnnHandle_t h, int N, int B, int T, float* H, hipS
   static KernelEntry floor_team_trace = {0, 64, 1 << 30, nullptr};
   static KernelEntry floor_team16 = {0, 64, 1 << 30, nullptr, 16};
   static KernelEntry floor_team16_trace = {0, 64, 1 << 30, nullptr, 16};
+  static KernelEntry floor_team12 = {0, 64, 1 << 30, nullptr, 12};
+  static KernelEntry floor_team12_trace = {0, 64, 1 << 30, nullptr, 12};
   if (p.layout == PRNN_LAYOUT_TEAM) {
     floor_team.fn = prnn::kFloorTeamKernel;
     floor_team_trace.fn = prnn::kFloorTeamTraceKernel;
     floor_team16.fn = prnn::kFloorTeamKernel16;
     floor_team16_trace.fn = prnn::kFloorTeamTraceKernel16;
+    floor_team12.fn = prnn::kFloorTeamKernel12;
+    floor_team12_trace.fn = prnn::kFloorTeamTraceKernel12;
     if (p.waves == 16)
       p.k = h->trace ? &floor_team16_trace : &floor_team16;
+    else if (p.waves == 12)
+      p.k = h->trace ? &floor_team12_trace : &floor_team12;
     else
       p.k = h->trace ? &floor_team_trace : &floor_team;
   }

@@ -38,6 +38,15 @@ const KernelEntry kSparseTeamF16Kernels16[] = {
     PRNN_SPARSE_TEAM16(_Float16, kF16, 12, 1), PRNN_SPARSE_TEAM16(_Float16, kF16, 16, 1),
     {0, 0, 0, nullptr},
 };
+// 12-wave workgroups (3 waves per SIMD, at most 168 VGPRs): the large layers,
+// 15 rows per wave at N = 5760 (5 %: 5 slots), 6 at N = 2304, and up to 11
+// rows of 1 or 2 slots (N up to 4224 on 256 workgroups).
+const KernelEntry kSparseTeamF16Kernels12[] = {
+    PRNN_SPARSE_TEAM12(_Float16, kF16, 15, 5), PRNN_SPARSE_TEAM12(_Float16, kF16, 6, 4),
+    PRNN_SPARSE_TEAM12(_Float16, kF16, 6, 9), PRNN_SPARSE_TEAM12(_Float16, kF16, 6, 10),
+    PRNN_SPARSE_TEAM12(_Float16, kF16, 11, 1), PRNN_SPARSE_TEAM12(_Float16, kF16, 11, 2),
+    {0, 0, 0, nullptr},
+};
 const KernelEntry kSparseTeamF16TraceKernels16[] = {
     PRNN_SPARSE_TEAM16_TRACE(_Float16, kF16, 12, 1),
     {0, 0, 0, nullptr},

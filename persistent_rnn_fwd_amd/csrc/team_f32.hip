@@ -84,6 +84,8 @@ __global__ void team_fill_kernel(uint32_t* ring, int npad, uint32_t v) {
 const void* kFloorTeamKernel = reinterpret_cast<const void*>(&floor_team_kernel<false>);
 const void* kFloorTeamTraceKernel = reinterpret_cast<const void*>(&floor_team_kernel<true>);
 const void* kFloorTeamKernel16 = reinterpret_cast<const void*>(&floor_team_kernel<false, 16>);
+const void* kFloorTeamKernel12 = reinterpret_cast<const void*>(&floor_team_kernel<false, 12>);
+const void* kFloorTeamTraceKernel12 = reinterpret_cast<const void*>(&floor_team_kernel<true, 12>);
 const void* kFloorTeamTraceKernel16 = reinterpret_cast<const void*>(&floor_team_kernel<true, 16>);
 
 // Trace instances (the N = 256 fp32 layer).

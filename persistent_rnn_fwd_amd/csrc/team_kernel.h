@@ -418,6 +418,8 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
   {kF16, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<_Float16, R, JJ, false, true, true>)}
 #define PRNN_DENSE_TEAM_WIDE_TRACE(R, JJ) \
   {kF16, R, JJ, reinterpret_cast<const void*>(&dense_team_kernel<_Float16, R, JJ, true, true>)}
+#define PRNN_SPARSE_TEAM12(VT, VTAG, R, S) \
+  {VTAG, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<VT, R, S, false, 12>), 12}
 #define PRNN_SPARSE_TEAM16(VT, VTAG, R, S) \
   {VTAG, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<VT, R, S, false, 16>), 16}
 #define PRNN_SPARSE_TEAM16_TRACE(VT, VTAG, R, S) \

@@ -270,12 +270,14 @@ def test_plan_of_headline_layer(handle):
 
 
 def test_plan_of_large_sparse_layers(handle):
-    """Sparse fp16 layers that would hold more than 16 rows per wave at 8 waves
-    per workgroup run 16-wave workgroups where an instance fits the 128
-    registers of 4 waves per SIMD (1 % at N = 5760: 12 rows of one slot), and
-    8-wave workgroups otherwise (5 % at N = 5760: 23 rows of 5 slots)."""
-    for name, waves, rows in [("sparse1_f16_n5760", 16, 12), ("sparse5_f16_n5760", 8, 23),
-                              ("sparse10_f16_n2304", 8, 9)]:
+    """Sparse fp16 layers that would hold more than 8 rows per wave at 8 waves
+    per workgroup run 12-wave workgroups, above 16 rows 16-wave ones first,
+    where an instance fits (1 % at N = 5760: 16 waves of 12 rows; 5 % at
+    N = 5760, whose 12 x 5 block does not fit 4 waves per SIMD: 12 waves of 15
+    rows; N = 2304: 12 waves of 6 rows); N = 1792 keeps 8 waves of 7 rows."""
+    for name, waves, rows in [("sparse1_f16_n5760", 16, 12), ("sparse5_f16_n5760", 12, 15),
+                              ("sparse10_f16_n2304", 12, 6), ("sparse25_f16_n2304", 12, 6),
+                              ("sparse10u_f16_n2304", 12, 6), ("sparse10_f16_n1792", 8, 7)]:
         w = WORKLOADS[name].with_(T=6)
         d = generate(w, seed=71)
         H = run(handle, "sparse", d)
@@ -295,6 +297,11 @@ def test_plan_of_large_sparse_layers(handle):
         out = torch.empty((6, 4, 5760), device="cuda")
         handle.sync_floor(5760, 4, 6, out=out)
         assert handle.last_plan()["waves_per_wg"] == 8
+        handle.set_team_waves(12)
+        H = run(handle, "sparse", d)
+        p = handle.last_plan()
+        assert p["waves_per_wg"] == 12 and p["rows_per_wave"] == 15
+        assert_parity(H, reference("sparse", d), oracle.TOL_F16, "forced 12 waves")
         handle.set_team_waves(16)
         for name, kind in [("sparse5_f16_n5760", "sparse"), ("dense_f16_n1152", "dense")]:
             w2 = WORKLOADS[name].with_(T=3)
@@ -302,13 +309,13 @@ def test_plan_of_large_sparse_layers(handle):
                 run(handle, kind, generate(w2), layout=binding.LAYOUT_TEAM)
             assert e.value.status == binding.NOT_SUPPORTED
         with pytest.raises(PrnnError) as e:
-            handle.set_team_waves(12)
+            handle.set_team_waves(10)
         assert e.value.status == binding.BAD_PARAM
     finally:
         handle.set_team_waves(0)
         handle.set_layout(binding.LAYOUT_AUTO)
     # a ragged large layer, one slot per row, several forced grids
-    for N, grid in [(6001, 0), (4500, 192), (8000, 256)]:
+    for N, grid in [(6001, 0), (4500, 192), (8000, 256), (3001, 0), (2500, 256)]:
         w = Workload(f"sparse_{N}", "sparse", N, 3, 5, "f16", K=40, seed=N, h0="randn")
         d = generate(w)
         H = run(handle, "sparse", d, grid=grid)
