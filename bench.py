@@ -68,7 +68,8 @@ def parse():
     ap.add_argument("--no-baselines", action="store_true", help="skip the library and torch-CPU loop baselines")
     ap.add_argument("--no-layers", action="store_true", help="skip the whole-layer (projection + recurrence) table")
     ap.add_argument("--profile-layers", action="store_true",
-                    help="with --only-timed: also run 5 half-h dense calls, 5 input projections and one layer call (N=1792) and one "
+                    help="with --only-timed: also run 5 half-h dense calls, 3 calls of each N=5760 sparse layer, 5 input "
+                         "projections and one layer call (N=1792) and one "
                          "2-layer stack wavefront (N=1152), T=256, after the timed loop, for profilers")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config table (every workload, not timed "
                     "in the headline step)")
@@ -555,6 +556,14 @@ def main():
         for _ in range(5):
             call(wd.name)
         h.set_math(_b.MATH_AUTO)
+        for big in ("sparse1_f16_n5760", "sparse5_f16_n5760"):   # 16- and 12-wave workgroups
+            wb = WORKLOADS[big]
+            gb = {k: torch.from_numpy(v).to(dev) for k, v in generate(wb).items()}
+            ob = torch.empty((wb.T, wb.B, wb.N), dtype=torch.float32, device=dev)
+            for _ in range(3):
+                h.forward_sparse(gb["col"], gb["val"], gb["X"], gb["h0"], out=ob)
+            h.synchronize()
+            del gb, ob
         st = generate_stack(WORKLOADS["dense_f16_n1152"], 2)  # the largest wavefront size
         layers = [{k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in ly.items()} for ly in st["layers"]]
         h.forward_stack_dense(layers, torch.from_numpy(st["x"]).to(dev))
