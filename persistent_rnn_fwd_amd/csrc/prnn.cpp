@@ -37,7 +37,7 @@ struct prnnContext {
   // after a reset and after a relay call.  Elsewhere the ring is reset first.
   uint64_t relay_next_step = 0;
   int forced_grid = 0;
-  int team_waves = 0;  // TEAM layout waves per workgroup: 0 = automatic, 8 or 16
+  int team_waves = 0;  // TEAM layout waves per workgroup: 0 = automatic, 8, 12 or 16
   uint32_t watchdog_us = 200000;
   int math = PRNN_MATH_AUTO;
   int stack_mode = PRNN_STACK_AUTO;

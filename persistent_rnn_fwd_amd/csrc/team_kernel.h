@@ -6,8 +6,9 @@
 // With B < 8 the teams x >= B compute nothing: they stamp their region with
 // the tags of the call's last two steps and leave (team_stamp_tail).
 //
-// Within a team, the N rows of W are split over its P * 8 waves (balanced to
-// within one row); a wave keeps its rows in registers for all T steps.  Per
+// Within a team, the N rows of W are split over its P * V waves (balanced to
+// within one row; V = 8 waves per workgroup, 12 or 16 for sparse layers with
+// many rows per wave); a wave keeps its rows in registers for all T steps.  Per
 // step the team exchanges h_{t-1} through its own XCD's region of the ring,
 // ring[xcd][2][Npad], with ordinary stores and loads that stay in the XCD's
 // L2: no data crosses between XCDs inside the time loop.  Words carry the
@@ -17,7 +18,7 @@
 // step of every call, so it always holds steps S-1 and S-2 when step S
 // starts, whatever batch row the team on it serves.
 //
-// Per step each of the 8 waves stages its share of h_{t-1} (chunks w, w+8,
+// Per step each of the V waves stages its share of h_{t-1} (chunks w, w+V,
 // ...) from the region into a double-buffered LDS row, spinning on the tags;
 // one workgroup barrier later every wave multiplies its rows with the whole
 // row from LDS.  A wave whose wait expires raises a workgroup abort flag but
@@ -305,7 +306,7 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
 // The sparse recurrence in the team layout: the h row is staged once per
 // workgroup (all its waves serve the same batch row) and every wave gathers
 // from it for its own rows.  RW = rows per wave, SPR = 64-pair slots per row,
-// WAVES = waves per workgroup (8, or 16 for layers with many rows per wave).
+// WAVES = waves per workgroup (8; 12 or 16 for layers with many rows per wave).
 template <typename VT, int RW, int SPR, bool TRACE = false, int WAVES = kTeamWaves>
 __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
   constexpr int M = pow2_at_least(RW);
