@@ -80,12 +80,14 @@ typedef enum {
   PRNN_STATUS_NOT_SUPPORTED = 2,    /* valid, but outside what fits on chip / this GPU   */
   PRNN_STATUS_ALLOC_FAILED = 3,     /* device or pinned allocation failed                */
   PRNN_STATUS_EXECUTION_FAILED = 4, /* a launched step never completed (watchdog)        */
-  PRNN_STATUS_INTERNAL_ERROR = 5    /* a HIP runtime call failed                         */
+  PRNN_STATUS_INTERNAL_ERROR = 5,   /* a HIP runtime call failed                         */
+  PRNN_STATUS_MAX_ENUM = 0x7FFFFFFF  /* not a value: keeps every int in the type's range */
 } prnnStatus_t;
 
 typedef enum {
   PRNN_DATA_FLOAT = 0, /* fp32 */
-  PRNN_DATA_HALF = 1   /* fp16 (IEEE binary16); products and sums are taken in fp32 */
+  PRNN_DATA_HALF = 1,  /* fp16 (IEEE binary16); products and sums are taken in fp32 */
+  PRNN_DATA_MAX_ENUM = 0x7FFFFFFF  /* not a value: keeps every int in the type's range */
 } prnnDataType_t;
 
 /* How workgroups exchange h_{t-1} each step.
@@ -101,7 +103,8 @@ typedef enum {
 typedef enum {
   PRNN_EXCHANGE_AUTO = 0,
   PRNN_EXCHANGE_DIRECT = 1,
-  PRNN_EXCHANGE_RELAY = 2
+  PRNN_EXCHANGE_RELAY = 2,
+  PRNN_EXCHANGE_MAX_ENUM = 0x7FFFFFFF  /* not a value: keeps every int in the type's range */
 } prnnExchange_t;
 
 /* How the recurrence is laid out on the GPU.
@@ -120,7 +123,8 @@ typedef enum {
 typedef enum {
   PRNN_LAYOUT_AUTO = 0,
   PRNN_LAYOUT_SPREAD = 1,
-  PRNN_LAYOUT_TEAM = 2
+  PRNN_LAYOUT_TEAM = 2,
+  PRNN_LAYOUT_MAX_ENUM = 0x7FFFFFFF  /* not a value: keeps every int in the type's range */
 } prnnLayout_t;
 
 /* How the dense fp16 recurrence forms W h_{t-1}.
@@ -144,7 +148,8 @@ typedef enum {
   PRNN_MATH_AUTO = 0,
   PRNN_MATH_EXACT = 1,
   PRNN_MATH_SPLIT = 2,
-  PRNN_MATH_HALF = 3
+  PRNN_MATH_HALF = 3,
+  PRNN_MATH_MAX_ENUM = 0x7FFFFFFF  /* not a value: keeps every int in the type's range */
 } prnnMath_t;
 
 /* Launch plan of the last forward call on a handle (for tests and reports). */
@@ -291,7 +296,8 @@ typedef enum {
   PRNN_STACK_AUTO = 0,
   PRNN_STACK_BLOCKED = 1,
   PRNN_STACK_FUSED = 2,
-  PRNN_STACK_LAYERS = 3
+  PRNN_STACK_LAYERS = 3,
+  PRNN_STACK_MAX_ENUM = 0x7FFFFFFF  /* not a value: keeps every int in the type's range */
 } prnnStackMode_t;
 
 /* Stack mode for later calls (default AUTO).  A forced mode the shape

@@ -532,6 +532,7 @@ const char* prnn_status_string(prnnStatus_t s) {
     case PRNN_STATUS_ALLOC_FAILED: return "PRNN_STATUS_ALLOC_FAILED";
     case PRNN_STATUS_EXECUTION_FAILED: return "PRNN_STATUS_EXECUTION_FAILED";
     case PRNN_STATUS_INTERNAL_ERROR: return "PRNN_STATUS_INTERNAL_ERROR";
+    case PRNN_STATUS_MAX_ENUM: break;
   }
   return "PRNN_STATUS_UNKNOWN";
 }

@@ -1,0 +1,102 @@
+// Host-side sanitizer driver: runs the C ABI of libprnn through every path
+// the host library plans and checks (dense layers in each math mode, sparse
+// layers at each wave count, the floor, projection, layers, tracing,
+// argument errors) with the host code built under AddressSanitizer and
+// UndefinedBehaviorSanitizer (device code is built normally).  Every launch
+// stays inside the buffers allocated here.  Prints "driver ok" on success.
+#include <hip/hip_runtime.h>
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+#include "prnn.h"
+#define CHECK(x, want)                                                                      \
+  do {                                                                                     \
+    prnnStatus_t s_ = (x);                                                                 \
+    if (s_ != (want)) {                                                                    \
+      printf("FAIL line %d: %s -> %d (want %d)\n", __LINE__, #x, (int)s_, (int)(want));    \
+      return 1;                                                                            \
+    }                                                                                      \
+  } while (0)
+template <typename T> T* dalloc(size_t n) { void* p = nullptr; if (hipMalloc(&p, n * sizeof(T)) != hipSuccess) { printf("hipMalloc failed\n"); exit(2); } return (T*)p; }
+int main() {
+  const prnnStatus_t OK = PRNN_STATUS_SUCCESS, BP = PRNN_STATUS_BAD_PARAM, NS = PRNN_STATUS_NOT_SUPPORTED;
+  prnnHandle_t h = nullptr;
+  CHECK(prnn_create(nullptr), BP);
+  CHECK(prnn_create(&h), OK);
+  const int N = 5760, B = 4, T = 12, K = 288, I = 1792;
+  float* X = dalloc<float>((size_t)T * B * N);
+  float* H = dalloc<float>((size_t)T * B * N);
+  float* Xb = dalloc<float>((size_t)T * B * N);
+  float* h0 = dalloc<float>((size_t)B * N);
+  float* x = dalloc<float>((size_t)T * B * I);
+  uint16_t* W = dalloc<uint16_t>((size_t)2048 * 2048);
+  uint16_t* U = dalloc<uint16_t>((size_t)N * I);
+  int16_t* col = dalloc<int16_t>((size_t)N * K);
+  uint16_t* val = dalloc<uint16_t>((size_t)N * K);
+  std::vector<float> hx((size_t)T * B * N, 0.25f), hh0((size_t)B * N, 0.f), hxi((size_t)T * B * I, 0.5f);
+  std::vector<uint16_t> hw((size_t)2048 * 2048, 0x1419), hu((size_t)N * I, 0x0c00), hv((size_t)N * K, 0x211f);
+  std::vector<int16_t> hc((size_t)N * K);
+  for (int i = 0; i < N; ++i) {
+    for (int k = 0; k < K; ++k) hc[(size_t)i * K + k] = (int16_t)((k * 20 + i) % N);
+    std::sort(hc.begin() + (size_t)i * K, hc.begin() + (size_t)(i + 1) * K);
+  }
+  (void)hipMemcpy(X, hx.data(), hx.size() * 4, hipMemcpyHostToDevice);
+  (void)hipMemcpy(h0, hh0.data(), hh0.size() * 4, hipMemcpyHostToDevice);
+  (void)hipMemcpy(x, hxi.data(), hxi.size() * 4, hipMemcpyHostToDevice);
+  (void)hipMemcpy(W, hw.data(), hw.size() * 2, hipMemcpyHostToDevice);
+  (void)hipMemcpy(U, hu.data(), hu.size() * 2, hipMemcpyHostToDevice);
+  (void)hipMemcpy(val, hv.data(), hv.size() * 2, hipMemcpyHostToDevice);
+  (void)hipMemcpy(col, hc.data(), hc.size() * 2, hipMemcpyHostToDevice);
+  // dense layers in every math mode, sparse layers at every wave count
+  for (int math : {PRNN_MATH_AUTO, PRNN_MATH_EXACT, PRNN_MATH_SPLIT, PRNN_MATH_HALF}) {
+    CHECK(prnn_set_math(h, (prnnMath_t)math), OK);
+    for (int n : {7, 257, 1152, 1792, 2048})
+      CHECK(prnn_forward_dense(h, n, B, T, PRNN_DATA_HALF, W, X, h0, H, nullptr), OK);
+  }
+  CHECK(prnn_set_math(h, PRNN_MATH_AUTO), OK);
+  for (int waves : {0, 8, 12, 16}) {
+    CHECK(prnn_set_team_waves(h, waves), OK);
+    CHECK(prnn_forward_sparse(h, N, B, T, 58, col, PRNN_DATA_HALF, val, X, h0, H, nullptr), OK);
+    CHECK(prnn_sync_floor(h, N, B, T, H, nullptr), OK);
+  }
+  CHECK(prnn_set_team_waves(h, 0), OK);
+  CHECK(prnn_forward_sparse(h, 2304, B, T, 230, col, PRNN_DATA_HALF, val, X, h0, H, nullptr), OK);
+  CHECK(prnn_forward_sparse(h, 1792, B, T, 179, col, PRNN_DATA_HALF, val, X, nullptr, H, nullptr), OK);
+  // projection and layers
+  CHECK(prnn_project(h, T * B, 1792, I, PRNN_DATA_FLOAT, x, PRNN_DATA_HALF, U, h0, Xb, nullptr), OK);
+  CHECK(prnn_forward_layer_dense(h, 1792, I, B, T, PRNN_DATA_FLOAT, x, PRNN_DATA_HALF, U, nullptr, PRNN_DATA_HALF, W,
+                                 h0, Xb, H, nullptr), OK);
+  // tracing
+  CHECK(prnn_set_trace(h, 1), OK);
+  CHECK(prnn_forward_dense(h, 1792, B, T, PRNN_DATA_HALF, W, X, h0, H, nullptr), OK);
+  int records = 0;
+  CHECK(prnn_get_trace(h, nullptr, 0, &records, nullptr), BP);
+  std::vector<uint64_t> tr((size_t)records * 8);
+  CHECK(prnn_get_trace(h, tr.data(), tr.size(), &records, nullptr), OK);
+  CHECK(prnn_sync_floor(h, N, B, T, H, nullptr), OK);
+  CHECK(prnn_get_trace(h, nullptr, 0, &records, nullptr), BP);
+  tr.assign((size_t)records * 8, 0);
+  CHECK(prnn_get_trace(h, tr.data(), tr.size(), &records, nullptr), OK);
+  CHECK(prnn_set_trace(h, 0), OK);
+  prnnPlanInfo_t info;
+  CHECK(prnn_get_last_plan(h, &info), OK);
+  // argument errors and unsupported shapes
+  CHECK(prnn_forward_dense(h, 0, B, T, PRNN_DATA_HALF, W, X, h0, H, nullptr), BP);
+  CHECK(prnn_forward_dense(h, 64, 9, T, PRNN_DATA_HALF, W, X, h0, H, nullptr), BP);
+  CHECK(prnn_forward_dense(h, 64, B, T, PRNN_DATA_HALF, nullptr, X, h0, H, nullptr), BP);
+  CHECK(prnn_forward_dense(h, 64, B, T, PRNN_DATA_HALF, W, X, h0, X, nullptr), BP);
+  CHECK(prnn_forward_sparse(h, 64, B, T, 0, col, PRNN_DATA_HALF, val, X, h0, H, nullptr), BP);
+  CHECK(prnn_forward_dense(h, 64, B, 0, PRNN_DATA_HALF, W, X, h0, H, nullptr), OK);
+  CHECK(prnn_set_team_waves(h, 10), BP);
+  CHECK(prnn_set_math(h, (prnnMath_t)7), BP);
+  CHECK(prnn_set_math(h, PRNN_MATH_HALF), OK);
+  uint16_t* W4 = dalloc<uint16_t>((size_t)4096 * 4096);
+  CHECK(prnn_forward_dense(h, 4096, 1, 2, PRNN_DATA_HALF, W4, X, h0, H, nullptr), NS);
+  CHECK(prnn_set_math(h, PRNN_MATH_AUTO), OK);
+  CHECK(prnn_synchronize(h, nullptr), OK);
+  CHECK(prnn_destroy(h), OK);
+  CHECK(prnn_destroy(nullptr), OK);
+  printf("driver ok: %d trace records, last plan grid %d waves %d\n", records, info.grid, info.waves_per_wg);
+  return 0;
+}

@@ -82,6 +82,21 @@ def test_workload_parity(handle, name, seed_off):
     assert_parity(H, reference(w.kind, d), tol_of(d), name)
 
 
+# the configured workloads (dense fp32 N=256; dense and 10 % sparse N=1152; dense, 10 % and 1 % sparse
+# N=1792; 1 % sparse N=5760) with a third seed
+CONFIGURED = ["dense_f32_n256", "dense_f16_n1152", "sparse10_f16_n1152", "dense_f16_n1792", "sparse10_f16_n1792",
+              "sparse1_f16_n1792", "sparse1_f16_n5760"]
+
+
+@pytest.mark.parametrize("name", CONFIGURED)
+def test_configured_workload_parity_third_seed(handle, name):
+    w = WORKLOADS[name]
+    d = generate(w, seed=w.seed + 3000)
+    H = run(handle, w.kind, d)
+    assert np.isfinite(H).all()
+    assert_parity(H, reference(w.kind, d), tol_of(d), name)
+
+
 @pytest.mark.parametrize("name", ["dense_f16_n1792", "sparse10_f16_n1792"])
 def test_workload_parity_random_h0(handle, name):
     w = WORKLOADS[name].with_(h0="randn", T=64)
