@@ -170,6 +170,12 @@ typedef struct {
                         workgroup)                                            */
 } prnnPlanInfo_t;
 
+/* Environment: PRNN_LOG set to anything but "" or "0" when a handle is
+ * created makes that handle print one line to stderr per launch (its plan:
+ * layout, grid, waves per workgroup, rows per wave, kernel instance, LDS,
+ * math) and one per failed run reported by prnn_synchronize.  Otherwise the
+ * library prints nothing. */
+
 /* Creates a handle bound to the current HIP device.
  * Returns NOT_SUPPORTED if the device is not gfx950, ALLOC_FAILED if the small
  * internal buffers (status word, exchange ring) cannot be allocated,

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -38,6 +39,7 @@ struct prnnContext {
   uint64_t relay_next_step = 0;
   int forced_grid = 0;
   int team_waves = 0;  // TEAM layout waves per workgroup: 0 = automatic, 8, 12 or 16
+  bool log = false;    // PRNN_LOG set (and not "0") when the handle was created: plans to stderr
   uint32_t watchdog_us = 200000;
   int math = PRNN_MATH_AUTO;
   int stack_mode = PRNN_STACK_AUTO;
@@ -69,6 +71,7 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 }
 
 struct Plan {
+  const char* what = "recurrence";  // log label
   int layout = PRNN_LAYOUT_SPREAD;
   int math = PRNN_MATH_EXACT;
   int grid = 0, block = 0;
@@ -343,6 +346,18 @@ StepArgs base_args(prnnContext* h, int N, int B, int T, const float* X, const fl
   return a;
 }
 
+// One line per launch on stderr when the handle logs (PRNN_LOG).
+void log_plan(const prnnContext* h, const char* what, int N, int B, int T, const prnnPlanInfo_t& info) {
+  if (!h->log) return;
+  static const char* maths[] = {"auto", "exact", "split", "half"};
+  std::fprintf(stderr,
+               "prnn: %s N=%d B=%d T=%d layout=%s grid=%d waves/wg=%d rows/wave=%d instance=(%d,%d) lds=%d "
+               "math=%s first_step=%llu\n",
+               what, N, B, T, info.layout == PRNN_LAYOUT_TEAM ? "team" : "spread", info.grid, info.waves_per_wg,
+               info.rows_per_wave, info.rmax, info.chunks, info.lds_bytes,
+               info.math >= 0 && info.math <= 3 ? maths[info.math] : "?", (unsigned long long)info.first_step);
+}
+
 prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream_t stream) {
   if (p.lds_bytes > 65536 &&
       hipFuncSetAttribute(p.k->fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes) != hipSuccess)
@@ -378,6 +393,7 @@ prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream
   info.relay_slice = p.relay_slice;
   info.math = p.math;
   info.first_step = h->step;
+  log_plan(h, p.what, a.N, a.B, T, info);
   h->have_plan = true;
   h->trace_records = h->trace ? p.grid * p.waves : 0;
   h->step += static_cast<uint64_t>(T);
@@ -564,6 +580,11 @@ prnnStatus_t prnn_create(prnnHandle_t* handle) {
     return PRNN_STATUS_INTERNAL_ERROR;
   }
   h->placement_round_robin = check_placement(h->num_cu);
+  const char* log = std::getenv("PRNN_LOG");
+  h->log = log != nullptr && log[0] != '\0' && std::strcmp(log, "0") != 0;
+  if (h->log)
+    std::fprintf(stderr, "prnn: handle on device %d, %d compute units, %zu bytes of LDS per workgroup, team layout %s\n",
+                 h->device, h->num_cu, (size_t)h->lds_per_block, h->placement_round_robin ? "available" : "unavailable");
   *handle = h;
   return PRNN_STATUS_SUCCESS;
 }
@@ -677,6 +698,9 @@ prnnStatus_t prnn_synchronize(prnnHandle_t h, hipStream_t stream) {
   uint32_t s = 0;
   if (hipMemcpy(&s, h->d_status, 4, hipMemcpyDeviceToHost) != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
   if (s != 0) {
+    if (h->log)
+      std::fprintf(stderr, "prnn: run failed:%s%s\n", (s & 1u) ? " a wait for h_{t-1} expired (watchdog)" : "",
+                   (s & 2u) ? " a value outside the fp16 range" : "");
     // Report once; clear the status and force a ring reset before the next run.
     prnn::launch_fill(h->d_status, 64, 0u, stream);
     if (hipStreamSynchronize(stream) != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
@@ -936,6 +960,7 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B
   info.relay_slice = 0;
   info.math = PRNN_MATH_EXACT;
   info.first_step = h->step;
+  log_plan(h, "stack", N, B, T, info);
   h->have_plan = true;
   h->trace_records = 0;
   return PRNN_STATUS_SUCCESS;
@@ -962,6 +987,7 @@ prnnStatus_t prnn_sync_floor(prnnHandle_t h, int N, int B, int T, float* H, hipS
   static KernelEntry floor_team16_trace = {0, 64, 1 << 30, nullptr, 16};
   static KernelEntry floor_team12 = {0, 64, 1 << 30, nullptr, 12};
   static KernelEntry floor_team12_trace = {0, 64, 1 << 30, nullptr, 12};
+  p.what = "floor";
   if (p.layout == PRNN_LAYOUT_TEAM) {
     floor_team.fn = prnn::kFloorTeamKernel;
     floor_team_trace.fn = prnn::kFloorTeamTraceKernel;

@@ -663,3 +663,33 @@ def test_split_trace_and_watchdog(gpu):
         H2 = h.forward_dense(g["W"], g["X"], g["h0"])
         h.synchronize()
         np.testing.assert_array_equal(H2.cpu().numpy(), H0)
+
+
+def test_log_lines_on_stderr(gpu, capfd, monkeypatch):
+    """PRNN_LOG=1 when a handle is created: one stderr line per launch with its
+    plan and one per failed run that prnn_synchronize reports; without it the
+    library prints nothing."""
+    w = WORKLOADS["sparse1_f16_n5760"].with_(T=4)
+    d = generate(w, seed=81)
+    g = to_dev(d)
+    monkeypatch.setenv("PRNN_LOG", "1")
+    with Handle() as h:
+        h.forward_sparse(g["col"], g["val"], g["X"], g["h0"])
+        h.synchronize()
+        h.sync_floor(w.N, w.B, w.T, out=torch.empty((w.T, w.B, w.N), device="cuda"))
+        h.synchronize()
+        h.set_watchdog_us(2000)
+        h.debug_skip_publish(2, 1)
+        h.forward_sparse(g["col"], g["val"], g["X"], g["h0"])
+        with pytest.raises(PrnnError):
+            h.synchronize()
+    err = capfd.readouterr().err
+    assert "prnn: handle on device" in err
+    assert "prnn: recurrence N=5760 B=4 T=4 layout=team grid=256 waves/wg=16 rows/wave=12 instance=(12,1)" in err
+    assert "prnn: floor N=5760 B=4 T=4 layout=team grid=256 waves/wg=16" in err
+    assert "prnn: run failed: a wait for h_{t-1} expired (watchdog)" in err
+    monkeypatch.delenv("PRNN_LOG")
+    with Handle() as h:
+        h.forward_sparse(g["col"], g["val"], g["X"], g["h0"])
+        h.synchronize()
+    assert "prnn:" not in capfd.readouterr().err
