@@ -170,6 +170,15 @@ typedef struct {
                         workgroup)                                            */
 } prnnPlanInfo_t;
 
+/* HIP graphs: forward, layer, stack and floor calls may be captured (stream
+ * capture).  A captured call resets the handle's exchange state inside the
+ * captured sequence (a fill kernel, no memset) and counts its steps from 0,
+ * so every replay starts afresh; after the first capture every call on the
+ * handle does so (one extra small kernel per call).  Nothing is allocated
+ * while capturing: a call whose exchange buffer would have to grow returns
+ * NOT_SUPPORTED, so run one call of the largest shape before capturing.  As
+ * for any call, one graph replay or call at a time per handle. */
+
 /* Environment: PRNN_LOG set to anything but "" or "0" when a handle is
  * created makes that handle print one line to stderr per launch (its plan:
  * layout, grid, waves per workgroup, rows per wave, kernel instance, LDS,

@@ -40,6 +40,9 @@ struct prnnContext {
   int forced_grid = 0;
   int team_waves = 0;  // TEAM layout waves per workgroup: 0 = automatic, 8, 12 or 16
   bool log = false;    // PRNN_LOG set (and not "0") when the handle was created: plans to stderr
+  // A call was captured into a HIP graph: replays may run at any time, so from
+  // then on every call starts from a reset ring (one fill kernel per call).
+  bool captured = false;
   uint32_t watchdog_us = 200000;
   int math = PRNN_MATH_AUTO;
   int stack_mode = PRNN_STACK_AUTO;
@@ -270,6 +273,17 @@ prnnStatus_t ensure_ring(prnnContext* h, const Plan& p, int B, int Npad, hipStre
   const bool team = p.layout == PRNN_LAYOUT_TEAM;
   const size_t words = team ? 16ull * (size_t)Npad : 18ull * (size_t)B * (size_t)Npad;
   if (words * 4ull > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
+  // Under stream capture the call becomes a graph node that may be replayed
+  // at any time, after any other call: its ring is reset inside the captured
+  // sequence (a fill kernel) and its steps count from 0, and every later call
+  // on the handle resets the ring as well.  Nothing may be allocated here
+  // while capturing.
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+  const bool capturing = cs != hipStreamCaptureStatusNone;
+  if (capturing) h->captured = true;
+  if (h->captured) h->ring_valid = false;
+  if (words > h->ring_cap_words && capturing) return PRNN_STATUS_NOT_SUPPORTED;
   if (words > h->ring_cap_words) {
     if (h->d_ring != nullptr) {
       if (hipDeviceSynchronize() != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;

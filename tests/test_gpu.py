@@ -693,3 +693,45 @@ def test_log_lines_on_stderr(gpu, capfd, monkeypatch):
         h.forward_sparse(g["col"], g["val"], g["X"], g["h0"])
         h.synchronize()
     assert "prnn:" not in capfd.readouterr().err
+
+
+@pytest.mark.parametrize("kind,name,T", [("dense", "dense_f16_n1152", 15), ("sparse", "sparse10_f16_n1792", 13),
+                                         ("dense", "dense_f32_n256", 7)])
+def test_graph_capture_and_replay(gpu, kind, name, T):
+    """A call captured into a HIP graph replays correctly any number of times,
+    with eager calls of another length on the same handle between the replays:
+    every replay and every eager call equals, bitwise, a fresh handle's result."""
+    w = WORKLOADS[name].with_(T=T, h0="randn")
+    d, d2 = generate(w, seed=91), generate(w.with_(T=T + 2), seed=92)
+    g, g2 = to_dev(d), to_dev(d2)
+
+    def call(h, gg, out=None):
+        if kind == "dense":
+            return h.forward_dense(gg["W"], gg["X"], gg["h0"], out=out)
+        return h.forward_sparse(gg["col"], gg["val"], gg["X"], gg["h0"], out=out)
+
+    with Handle() as fresh:
+        ref = call(fresh, g).clone()
+        ref2 = call(fresh, g2).clone()
+        fresh.synchronize()
+    with Handle() as h:
+        call(h, g2)                      # warm-up: the exchange buffer exists before capture
+        h.synchronize()
+        out = torch.full_like(ref, float("nan"))
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            call(h, g, out=out)
+        torch.cuda.synchronize()
+        for rep in range(4):
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            h.synchronize()
+            assert torch.equal(out, ref), f"replay {rep}"
+            e = call(h, g2)
+            h.synchronize()
+            assert torch.equal(e, ref2), f"eager call after replay {rep}"
+    assert oracle.tolerance_ratio(ref.cpu().numpy(), reference(kind, d), tol_of(d)) <= 1.0
