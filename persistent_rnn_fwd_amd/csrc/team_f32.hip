@@ -8,7 +8,7 @@ const KernelEntry kDenseTeamF32Kernels[] = {
     PRNN_DENSE_TEAM(float, kF32, 1, 1), PRNN_DENSE_TEAM(float, kF32, 2, 1), PRNN_DENSE_TEAM(float, kF32, 4, 1),
     PRNN_DENSE_TEAM(float, kF32, 7, 1), PRNN_DENSE_TEAM(float, kF32, 8, 1), PRNN_DENSE_TEAM(float, kF32, 2, 2),
     PRNN_DENSE_TEAM(float, kF32, 4, 2), PRNN_DENSE_TEAM(float, kF32, 8, 2), PRNN_DENSE_TEAM(float, kF32, 4, 4),
-    PRNN_DENSE_TEAM(float, kF32, 5, 5), PRNN_DENSE_TEAM(float, kF32, 4, 7),
+    PRNN_DENSE_TEAM(float, kF32, 5, 5), PRNN_DENSE_TEAM(float, kF32, 4, 7), PRNN_DENSE_TEAM(float, kF32, 7, 7),
     {0, 0, 0, nullptr},
 };
 

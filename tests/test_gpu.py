@@ -284,6 +284,22 @@ def test_plan_of_headline_layer(handle):
     assert p["relay_slice"] == 1792 // 32   # auto picks the per-XCD relay at 256 workgroups
 
 
+def test_dense_fp32_n1792_team_layout(handle):
+    """fp32 W at N = 1792 runs in the team layout (7 rows x 7 chunks per wave,
+    widened like fp16); the spread layout has no instance of that size."""
+    w = WORKLOADS["dense_f16_n1792"].with_(w_dtype="f32", T=48, h0="randn")
+    d = generate(w, seed=97)
+    H = run(handle, "dense", d)
+    p = handle.last_plan()
+    assert p["layout"] == binding.LAYOUT_TEAM and p["rows_per_wave"] == 7 and p["rmax"] == 7, p
+    assert_parity(H, reference("dense", d), oracle.TOL_F32, "fp32 N=1792")
+    np.testing.assert_array_equal(run(handle, "dense", d), H)   # repeatable
+    with pytest.raises(PrnnError) as e:
+        run(handle, "dense", d, layout=binding.LAYOUT_SPREAD)
+    assert e.value.status == binding.NOT_SUPPORTED
+    handle.set_layout(binding.LAYOUT_AUTO)
+
+
 def test_plan_of_large_sparse_layers(handle):
     """Sparse fp16 layers that would hold more than 8 rows per wave at 8 waves
     per workgroup run 12-wave workgroups, above 16 rows 16-wave ones first,
