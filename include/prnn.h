@@ -118,7 +118,7 @@ typedef enum {
  *          is exchanged inside the XCD's L2 only.  With B < 8 the remaining
  *          XCDs compute nothing; they only mark their exchange memory as
  *          written for the call's last steps.  Holds W once per XCD: for
- *          dense fp16 W up to N = 2048.
+ *          dense fp16 W up to N = 2560, fp32 W up to N = 1792.
  *  AUTO:   TEAM when an instance fits, else SPREAD (the default). */
 typedef enum {
   PRNN_LAYOUT_AUTO = 0,
@@ -141,7 +141,7 @@ typedef enum {
  *   carry; X, h0, H, the sums, the ReLU and the exchanged state stay fp32.
  *   Needs every h (and h0) to round to a finite fp16 (|h| < 65520); a larger
  *   value makes the call report EXECUTION_FAILED.  TEAM layout, fp16 W,
- *   N <= 2048 only (else NOT_SUPPORTED).  Blocked and fused stacks use EXACT;
+ *   N <= 2560 only (else NOT_SUPPORTED).  Blocked and fused stacks use EXACT;
  *   a layer-by-layer stack follows this setting.
  * AUTO: EXACT.  fp32 weights and sparse layers always use EXACT. */
 typedef enum {

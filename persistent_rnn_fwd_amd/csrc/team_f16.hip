@@ -13,7 +13,7 @@ const KernelEntry kDenseTeamF16Kernels[] = {
     PRNN_DENSE_TEAM_WIDE(4, 4), PRNN_DENSE_TEAM_WIDE(8, 4), PRNN_DENSE_TEAM_WIDE(4, 5),
     PRNN_DENSE_TEAM_WIDE(5, 5), PRNN_DENSE_TEAM_WIDE(6, 5), PRNN_DENSE_TEAM_WIDE(7, 7),
     PRNN_DENSE_TEAM(_Float16, kF16, 8, 5), PRNN_DENSE_TEAM(_Float16, kF16, 8, 7), PRNN_DENSE_TEAM(_Float16, kF16, 6, 8),
-    PRNN_DENSE_TEAM(_Float16, kF16, 8, 8),
+    PRNN_DENSE_TEAM(_Float16, kF16, 8, 8), PRNN_DENSE_TEAM(_Float16, kF16, 9, 9), PRNN_DENSE_TEAM(_Float16, kF16, 10, 10),
     {0, 0, 0, nullptr},
 };
 

@@ -5,12 +5,14 @@
 namespace prnn {
 
 const KernelEntry kDenseTeamHalfKernels[] = {
-    // (rows per wave, 256-column chunks): the shapes of the fp16 table
+    // (rows per wave, 256-column chunks): the shapes of the fp16 table, up to
+    // 10 x 10 (N = 2560, 245 VGPRs)
     PRNN_DENSE_TEAM_HALF(1, 1), PRNN_DENSE_TEAM_HALF(2, 1), PRNN_DENSE_TEAM_HALF(4, 1), PRNN_DENSE_TEAM_HALF(8, 1),
     PRNN_DENSE_TEAM_HALF(1, 2), PRNN_DENSE_TEAM_HALF(2, 2), PRNN_DENSE_TEAM_HALF(4, 2), PRNN_DENSE_TEAM_HALF(8, 2),
     PRNN_DENSE_TEAM_HALF(2, 4), PRNN_DENSE_TEAM_HALF(4, 4), PRNN_DENSE_TEAM_HALF(8, 4), PRNN_DENSE_TEAM_HALF(4, 5),
     PRNN_DENSE_TEAM_HALF(5, 5), PRNN_DENSE_TEAM_HALF(6, 5), PRNN_DENSE_TEAM_HALF(8, 5), PRNN_DENSE_TEAM_HALF(7, 7),
-    PRNN_DENSE_TEAM_HALF(8, 7), PRNN_DENSE_TEAM_HALF(6, 8), PRNN_DENSE_TEAM_HALF(8, 8),
+    PRNN_DENSE_TEAM_HALF(8, 7), PRNN_DENSE_TEAM_HALF(6, 8), PRNN_DENSE_TEAM_HALF(8, 8), PRNN_DENSE_TEAM_HALF(9, 9),
+    PRNN_DENSE_TEAM_HALF(10, 10),
     {0, 0, 0, nullptr},
 };
 

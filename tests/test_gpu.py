@@ -130,6 +130,23 @@ DENSE_SHAPES = [
 LAYOUTS = [binding.LAYOUT_AUTO, binding.LAYOUT_SPREAD]
 
 
+@pytest.mark.parametrize("N,B,T", [(2100, 2, 6), (2304, 4, 5), (2560, 3, 4)])
+@pytest.mark.parametrize("math", [binding.MATH_EXACT, binding.MATH_HALF])
+def test_dense_fp16_beyond_2048(handle, N, B, T, math):
+    """Dense fp16 layers of 2049 to 2560 neurons in the team layout: 9 or 10
+    rows x 9 or 10 chunks per wave (packed fp16 weights), exact or half-h."""
+    w = Workload(f"dense_{N}", "dense", N, B, T, "f16", seed=N + 7, h0="randn")
+    d = generate(w)
+    handle.set_math(math)
+    try:
+        H = run(handle, "dense", d)
+        p = handle.last_plan()
+    finally:
+        handle.set_math(binding.MATH_AUTO)
+    assert p["layout"] == binding.LAYOUT_TEAM and p["math"] == math and p["rmax"] == p["chunks"] == -(-N // 256), p
+    assert_parity(H, reference("dense", d), oracle.TOL_F16, f"N={N} math={math}")
+
+
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("N,B,T,wdt,grid", DENSE_SHAPES)
 def test_dense_shapes(handle, N, B, T, wdt, grid, layout):

@@ -180,10 +180,10 @@ def test_half_range_reported(gpu, where):
 
 
 def test_half_scope(handle):
-    """Half-h exists for fp16 W in the team layout only: beyond 2048 neurons
+    """Half-h exists for fp16 W in the team layout only: beyond 2560 neurons
     or in the spread layout the call is NOT_SUPPORTED; fp32 W and sparse
     layers keep exact math."""
-    w = Workload("dense_2049", "dense", 2049, 4, 2, "f16", seed=5)
+    w = Workload("dense_2561", "dense", 2561, 4, 2, "f16", seed=5)
     d = generate(w)
     with pytest.raises(PrnnError) as e:
         run(handle, d)
