@@ -170,6 +170,16 @@ struct TeamChunk { using type = WChunk<WT>; };
 template <>
 struct TeamChunk<_Float16, true> { using type = WChunkWide; };
 
+// Widened instances keep as many of their rows widened as 196 weight VGPRs
+// hold (the 7 x 7 instance: every row) and the rest packed.  Both forms do one
+// fused multiply-add per weight with one rounding, so the split changes no
+// result, only how fast the rows issue.
+constexpr int kWideWeightRegs = 196;
+constexpr int team_wide_rows(bool wide, int rw, int j) {
+  const int fit = (kWideWeightRegs / j - 2 * rw) / 2;  // 4 registers widened, 2 packed per chunk
+  return !wide ? 0 : fit < 0 ? 0 : fit < rw ? fit : rw;
+}
+
 // Keeps this XCD's region continuous when the team serves no batch row of its
 // own (B < 8): the next call only needs the tags of this call's last two
 // steps, so the team stamps those on its rows and leaves.  No one reads the
@@ -219,12 +229,21 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
     team_stamp_tail(a, p, team_region(a));
     return;
   }
-  typename TeamChunk<WT, WIDE>::type w[RW][J];
+  // rows [0, WR) widened, [WR, RW) packed; the indexes below are constants
+  // once the loops are unrolled
+  constexpr int WR = team_wide_rows(WIDE, RW, J);
+  typename TeamChunk<WT, WIDE>::type ww[WR > 0 ? WR : 1][J];
+  WChunk<WT> wp[RW > WR ? RW - WR : 1][J];
 #pragma unroll
   for (int r = 0; r < RW; ++r)
 #pragma unroll
-    for (int j = 0; j < J; ++j)
-      w[r][j].load(a.W, (size_t)(p.r0 + r) * N, 256 * j + 4 * p.lane, N, r < p.nr && j < jn, vec);
+    for (int j = 0; j < J; ++j) {
+      const bool live = r < p.nr && j < jn;
+      if (r < WR)
+        ww[r < WR ? r : 0][j].load(a.W, (size_t)(p.r0 + r) * N, 256 * j + 4 * p.lane, N, live, vec);
+      else
+        wp[r < WR ? 0 : r - WR][j].load(a.W, (size_t)(p.r0 + r) * N, 256 * j + 4 * p.lane, N, live, vec);
+    }
 
   const __amdgpu_buffer_rsrc_t region = team_region(a);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
@@ -274,7 +293,7 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
 #pragma unroll
       for (int j = 0; j < J; ++j)
 #pragma unroll
-        for (int r = 0; r < RW; ++r) w[r][j].dot4(acc[r], h[j]);
+        for (int r = 0; r < RW; ++r) wp[r][j].dot4(acc[r], h[j]);
     } else {
       float4 h[J];
 #pragma unroll
@@ -282,7 +301,12 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
 #pragma unroll
       for (int j = 0; j < J; ++j)
 #pragma unroll
-        for (int r = 0; r < RW; ++r) w[r][j].fma4(acc[r], h[j]);
+        for (int r = 0; r < RW; ++r) {
+          if (r < WR)
+            ww[r < WR ? r : 0][j].fma4(acc[r], h[j]);
+          else
+            wp[r < WR ? 0 : r - WR][j].fma4(acc[r], h[j]);
+        }
     }
     clk.mark(kTrCompute);
     const float sum = RowReduce<M>::reduce(acc, p.lane);
