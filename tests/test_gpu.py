@@ -235,6 +235,27 @@ def test_cyclic_shift_bitwise(handle):
         run(handle, "sparse", {"col": col, "val": np.ones((N, 1), np.float32), "X": X, "h0": h0}), ref)
 
 
+@pytest.mark.parametrize("N,wdt", [(1792, np.float16), (2048, np.float16), (2304, np.float16),
+                                   (2560, np.float16), (1792, np.float32), (1000, np.float32)])
+def test_small_integer_weights_bitwise(handle, N, wdt):
+    """Three +-1 weights per row in random columns and small integer inputs keep
+    every partial sum an exact fp32 integer (|h| < 2^13 over six steps), so
+    any summation order gives the fp64 result bit for bit: every row of the
+    widened, packed and partly widened team instances is checked exactly."""
+    rng = np.random.default_rng(N + 17)
+    T, B = 6, 4
+    W = np.zeros((N, N), wdt)
+    for _ in range(3):
+        W[np.arange(N), rng.integers(0, N, N)] += rng.choice([-1, 1], N).astype(wdt)
+    X = rng.integers(-5, 6, size=(T, B, N)).astype(np.float32)
+    h0 = rng.integers(0, 6, size=(B, N)).astype(np.float32)
+    ref = oracle.forward_dense(W, X, h0)
+    assert np.abs(ref).max() < 2 ** 13
+    H = run(handle, "dense", {"W": W, "X": X, "h0": h0})
+    assert handle.last_plan()["layout"] == binding.LAYOUT_TEAM, handle.last_plan()
+    np.testing.assert_array_equal(H, ref)
+
+
 def test_sparse_matches_dense_copy(handle):
     w = WORKLOADS["sparse10_f16_n1152"].with_(T=32, h0="randn")
     d = generate(w, seed=5)
