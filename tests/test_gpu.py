@@ -693,6 +693,28 @@ def test_split_range_reported(gpu):
         assert_parity(H.cpu().numpy(), reference("dense", d), oracle.TOL_F16)
 
 
+def test_split_scope(handle):
+    """The matrix-core form exists for fp16 W in the team layout up to 2048
+    neurons: beyond that (where exact and half-h math still run) or in the
+    spread layout the call is NOT_SUPPORTED; fp32 W keeps exact math."""
+    handle.set_math(binding.MATH_SPLIT)
+    try:
+        d = generate(Workload("dense_2304", "dense", 2304, 4, 2, "f16", seed=6))
+        with pytest.raises(PrnnError) as e:
+            run(handle, "dense", d)
+        assert e.value.status == binding.NOT_SUPPORTED
+        d = generate(WORKLOADS["dense_f16_n1152"].with_(T=3))
+        with pytest.raises(PrnnError) as e:
+            run(handle, "dense", d, layout=binding.LAYOUT_SPREAD)
+        assert e.value.status == binding.NOT_SUPPORTED
+        d = generate(WORKLOADS["dense_f32_n256"])
+        H = run(handle, "dense", d)
+        assert handle.last_plan()["math"] == binding.MATH_EXACT
+        assert_parity(H, reference("dense", d), oracle.TOL_F32, "fp32 W under SPLIT")
+    finally:
+        handle.set_math(binding.MATH_AUTO)
+
+
 def test_split_trace_and_watchdog(gpu):
     w = WORKLOADS["dense_f16_n1792"].with_(T=24)
     d = generate(w, seed=45)
