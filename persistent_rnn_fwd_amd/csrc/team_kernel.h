@@ -276,6 +276,12 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
     clk.mark(kTrStage);
     __syncthreads();
     clk.mark(kTrBarrier);
+    // Waves 4-7 share their SIMDs with waves 0-3, which win the issue
+    // arbitration at equal priority and leave their partners to finish the
+    // step's arithmetic alone.  Raising the later waves for the arithmetic
+    // evens the pairs out: 1.32 -> 1.28 us per step at N = 1792 (exact), the
+    // same results.
+    if (p.wave >= kTeamWaves / 2) __builtin_amdgcn_s_setprio(2);
     // The abort flag is read together with the row and tested only before
     // the stores, so it adds no LDS round trip to the step's path.
     int aborted_now = abort_flag;
@@ -311,6 +317,7 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
     clk.mark(kTrCompute);
     const float sum = RowReduce<M>::reduce(acc, p.lane);
     clk.mark(kTrReduce);
+    __builtin_amdgcn_s_setprio(0);
     asm volatile("" : "+v"(aborted_now) : "v"(sum));  // keep the test after the arithmetic
     if (aborted_now) return;
     debug_jitter(a.jitter_seed, a.jitter_span, p.wave, t);
@@ -390,6 +397,14 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
     clk.mark(kTrStage);
     __syncthreads();
     clk.mark(kTrBarrier);
+    // Three or four waves per SIMD (12- and 16-wave workgroups): the later
+    // waves of each SIMD are raised for the gathers, as in the dense kernel
+    // (N = 5760: 1 % 1.78 -> 1.68, 5 % 2.99 -> 2.86 us per step, the same
+    // results).  With 8 waves it did not pay (N = 1152: 0.90 -> 0.95).
+    if constexpr (WAVES > kTeamWaves) {
+      if (p.wave >= 8) __builtin_amdgcn_s_setprio(3);
+      else if (p.wave >= 4) __builtin_amdgcn_s_setprio(2);
+    }
     // The abort flag is read together with the row and tested only before
     // the stores, so it adds no LDS round trip to the step's path.
     int aborted_now = abort_flag;
@@ -416,6 +431,7 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
     clk.mark(kTrCompute);
     const float sum = RowReduce<M>::reduce(acc, p.lane);
     clk.mark(kTrReduce);
+    if constexpr (WAVES > kTeamWaves) __builtin_amdgcn_s_setprio(0);
     asm volatile("" : "+v"(aborted_now) : "v"(sum));  // keep the test after the arithmetic
     if (aborted_now) return;
     debug_jitter(a.jitter_seed, a.jitter_span, p.wave, t);
