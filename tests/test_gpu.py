@@ -130,7 +130,7 @@ DENSE_SHAPES = [
 LAYOUTS = [binding.LAYOUT_AUTO, binding.LAYOUT_SPREAD]
 
 
-@pytest.mark.parametrize("N,B,T", [(2100, 2, 6), (2304, 4, 5), (2560, 3, 4)])
+@pytest.mark.parametrize("N,B,T", [(2100, 2, 6), (2304, 4, 5), (2304, 1, 7), (2560, 3, 4), (2560, 8, 5)])
 @pytest.mark.parametrize("math", [binding.MATH_EXACT, binding.MATH_HALF])
 def test_dense_fp16_beyond_2048(handle, N, B, T, math):
     """Dense fp16 layers of 2049 to 2560 neurons in the team layout: 9 or 10
