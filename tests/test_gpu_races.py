@@ -47,25 +47,29 @@ def reference(kind, d):
     return oracle.forward_sparse(d["col"], d["val"], d["X"], d["h0"])
 
 
-# (workload, layout, math)
+# (workload, layout, math, N: 0 = the workload's own)
 PATHS = [
-    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_EXACT),
-    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_SPLIT),
-    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_HALF),
-    ("dense_f16_n1792", binding.LAYOUT_SPREAD, binding.MATH_EXACT),
-    ("dense_f32_n256", binding.LAYOUT_TEAM, binding.MATH_AUTO),
-    ("sparse10_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_AUTO),
-    ("sparse10_f16_n1792", binding.LAYOUT_SPREAD, binding.MATH_AUTO),
-    ("sparse1_f16_n5760", binding.LAYOUT_TEAM, binding.MATH_AUTO),    # 16-wave workgroups
+    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_EXACT, 0),
+    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_SPLIT, 0),
+    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_HALF, 0),
+    ("dense_f16_n1792", binding.LAYOUT_SPREAD, binding.MATH_EXACT, 0),
+    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_EXACT, 2048),   # partly widened rows
+    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_EXACT, 2560),   # 10 rows x 10 chunks
+    ("dense_f32_n256", binding.LAYOUT_TEAM, binding.MATH_AUTO, 0),
+    ("sparse10_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_AUTO, 0),
+    ("sparse10_f16_n1792", binding.LAYOUT_SPREAD, binding.MATH_AUTO, 0),
+    ("sparse1_f16_n5760", binding.LAYOUT_TEAM, binding.MATH_AUTO, 0),    # 16-wave workgroups
+    ("sparse5_f16_n5760", binding.LAYOUT_TEAM, binding.MATH_AUTO, 0),    # 12-wave workgroups
 ]
 
 
 def path_id(p):
-    return f"{p[0]}-{'team' if p[1] == binding.LAYOUT_TEAM else 'spread'}-math{p[2]}"
+    n = f"-n{p[3]}" if p[3] else ""
+    return f"{p[0]}{n}-{'team' if p[1] == binding.LAYOUT_TEAM else 'spread'}-math{p[2]}"
 
 
-def setup(h, name, layout, math, T, seed):
-    w = WORKLOADS[name].with_(T=T)
+def setup(h, name, layout, math, T, seed, N=0):
+    w = WORKLOADS[name].with_(T=T, **({"N": N} if N else {}))
     d = generate(w, seed=seed)
     h.set_layout(layout)
     h.set_math(math)
@@ -74,9 +78,9 @@ def setup(h, name, layout, math, T, seed):
 
 @pytest.mark.parametrize("path", PATHS, ids=path_id)
 def test_twenty_repeats_bitwise_with_nan_poisoned_outputs(gpu, path):
-    name, layout, math = path
+    name, layout, math, N = path
     with Handle() as h:
-        kind, d, g = setup(h, name, layout, math, T=40, seed=61)
+        kind, d, g = setup(h, name, layout, math, T=40, seed=61, N=N)
         first = forward(h, kind, g)
         assert not np.isnan(first).any()
         tol = oracle.TOL_F32 if name.startswith("dense_f32") else oracle.TOL_F16
@@ -88,9 +92,9 @@ def test_twenty_repeats_bitwise_with_nan_poisoned_outputs(gpu, path):
 
 @pytest.mark.parametrize("path", PATHS, ids=path_id)
 def test_publish_jitter_leaves_results_bitwise_unchanged(gpu, path):
-    name, layout, math = path
+    name, layout, math, N = path
     with Handle() as h:
-        kind, d, g = setup(h, name, layout, math, T=48, seed=62)
+        kind, d, g = setup(h, name, layout, math, T=48, seed=62, N=N)
         base = forward(h, kind, g)
         assert not np.isnan(base).any()
         for seed in SEEDS:
