@@ -6,15 +6,15 @@ namespace prnn {
 
 const KernelEntry kDenseTeamF16Kernels[] = {
     // (rows per wave, 256-column chunks).  Widened fp16 (fp32 registers, 4 per
-    // weight quad) where rows * chunks <= 50; 8 x 8 with half its rows widened
-    // (196 weight registers); packed fp16 elsewhere.
+    // weight quad) where rows * chunks <= 50; 8 x 8 and 9 x 9 with 4 rows and
+    // 1 row widened (what 196 weight registers hold); packed fp16 elsewhere.
     PRNN_DENSE_TEAM_WIDE(1, 1), PRNN_DENSE_TEAM_WIDE(2, 1), PRNN_DENSE_TEAM_WIDE(4, 1),
     PRNN_DENSE_TEAM_WIDE(8, 1), PRNN_DENSE_TEAM_WIDE(1, 2), PRNN_DENSE_TEAM_WIDE(2, 2),
     PRNN_DENSE_TEAM_WIDE(4, 2), PRNN_DENSE_TEAM_WIDE(8, 2), PRNN_DENSE_TEAM_WIDE(2, 4),
     PRNN_DENSE_TEAM_WIDE(4, 4), PRNN_DENSE_TEAM_WIDE(8, 4), PRNN_DENSE_TEAM_WIDE(4, 5),
     PRNN_DENSE_TEAM_WIDE(5, 5), PRNN_DENSE_TEAM_WIDE(6, 5), PRNN_DENSE_TEAM_WIDE(7, 7),
     PRNN_DENSE_TEAM(_Float16, kF16, 8, 5), PRNN_DENSE_TEAM(_Float16, kF16, 8, 7), PRNN_DENSE_TEAM(_Float16, kF16, 6, 8),
-    PRNN_DENSE_TEAM_WIDE(8, 8), PRNN_DENSE_TEAM(_Float16, kF16, 9, 9), PRNN_DENSE_TEAM(_Float16, kF16, 10, 10),
+    PRNN_DENSE_TEAM_WIDE(8, 8), PRNN_DENSE_TEAM_WIDE(9, 9), PRNN_DENSE_TEAM(_Float16, kF16, 10, 10),
     {0, 0, 0, nullptr},
 };
 
