@@ -78,6 +78,17 @@ def parse():
     return ap.parse_args()
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return " ".join(line.split(":", 1)[1].split())
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def percentiles(xs):
     import numpy as np
     p10, p50, p90 = np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])
@@ -692,27 +703,29 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
         Ts, spent, steps_done = 8, 0.0, 0
-        while spent < args.cpu_seconds and Ts <= T:
-            for w in (wd, ws):
-                d = host[w.name]
-                a = time.perf_counter()
-                if w.kind == "dense":
-                    oracle.forward_dense(d["W"], d["X"][:Ts], d["h0"])
-                else:
-                    oracle.forward_sparse(d["col"], d["val"], d["X"][:Ts], d["h0"])
-                spent += time.perf_counter() - a
-                steps_done += Ts
-            Ts = min(2 * Ts, T) if Ts < T else Ts
+        # one thread: the BLAS pools the oracle's numpy products use are
+        # limited to 1 for the whole sample (numpy itself runs on one)
+        with threadpool_limits(limits=1):
+            while spent < args.cpu_seconds and Ts <= T:
+                for w in (wd, ws):
+                    d = host[w.name]
+                    a = time.perf_counter()
+                    if w.kind == "dense":
+                        oracle.forward_dense(d["W"], d["X"][:Ts], d["h0"])
+                    else:
+                        oracle.forward_sparse(d["col"], d["val"], d["X"][:Ts], d["h0"])
+                    spent += time.perf_counter() - a
+                    steps_done += Ts
+                Ts = min(2 * Ts, T) if Ts < T else Ts
         cpu = {
             "value": round(steps_done / spent, 1),
             "unit": "timesteps/s",
-            "cores": threads,
+            "cores": 1,
             "kind": "oracle",
-            "sample": f"fp64 numpy oracle, dense + 10% sparse N=1792 B=4, {steps_done} timesteps "
-                      f"in {spent:.1f} s ({os.cpu_count()} host CPUs visible)",
+            "sample": f"fp64 numpy oracle on one thread, dense + 10% sparse N=1792 B=4, {steps_done} timesteps "
+                      f"in {spent:.1f} s (host: {os.cpu_count()} CPUs visible, {_cpu_model()})",
         }
 
     h.close()

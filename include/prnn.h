@@ -47,15 +47,25 @@
  *      X   [T][B][N] fp32 pre-activations
  *      h0  [B][N]   fp32 initial state, or NULL for zeros
  *      H   [T][B][N] fp32 output: H[t] is the state after consuming X[t]
- *    X, h0 and H need 4-byte alignment; W, col and val need 4-byte alignment.
+ *    X, h0 and H need 4-byte alignment; W, col and val need the alignment of
+    their element type (fp16 2 bytes, fp32 4, int16 2).  A dense W that is
+    16-byte aligned is loaded with vector loads, any other W element by
+    element (the result is the same).
  *  - Calls are asynchronous: a SUCCESS return means the work was enqueued on
- *    `stream` (NULL = the default stream).  An error found while the kernel
- *    runs (a step that never completes within the watchdog limit) is reported
- *    as PRNN_STATUS_EXECUTION_FAILED by prnn_synchronize() or prnn_destroy();
- *    until it has been reported, later forward calls on the handle are
- *    enqueued but do nothing (H is left as it was).  A call that enqueues
- *    several launches (layer and stack calls) and fails after the first
- *    leaves its outputs undefined.
+ *    `stream` (NULL = the default stream).  An error found while a kernel
+ *    runs (a step that never completes within the watchdog limit, or a value
+ *    outside the fp16 range where a path needs it) is sticky: the failing
+ *    kernel marks a host-visible copy of the handle's status (pinned host
+ *    memory), and the next call on the handle that enqueues work (forward,
+ *    layer, stack, projection or floor), prnn_synchronize() or prnn_destroy(),
+ *    whichever comes first, returns PRNN_STATUS_EXECUTION_FAILED without
+ *    waiting for the GPU; that call enqueues nothing.  The failure is
+ *    reported once; the handle is then usable again (its exchange ring is
+ *    reset before the next launch).  Calls enqueued after the failing one but
+ *    before the failure reached the host (made while it was still running)
+ *    return SUCCESS and do nothing: their kernels see the failure at entry and
+ *    leave H as it was.  A call that enqueues several launches (layer and
+ *    stack calls) and fails after the first leaves its outputs undefined.
  *  - One forward call may be in flight per handle at a time (the handle owns
  *    the exchange ring).  Use one handle per concurrently used stream.  A
  *    handle is not thread-safe.  Every call must be made with the handle's
@@ -79,7 +89,7 @@ typedef enum {
   PRNN_STATUS_BAD_PARAM = 1,        /* invalid argument; nothing was enqueued            */
   PRNN_STATUS_NOT_SUPPORTED = 2,    /* valid, but outside what fits on chip / this GPU   */
   PRNN_STATUS_ALLOC_FAILED = 3,     /* device or pinned allocation failed                */
-  PRNN_STATUS_EXECUTION_FAILED = 4, /* a launched step never completed (watchdog)        */
+  PRNN_STATUS_EXECUTION_FAILED = 4, /* an earlier launch failed on the GPU (sticky, below) */
   PRNN_STATUS_INTERNAL_ERROR = 5,   /* a HIP runtime call failed                         */
   PRNN_STATUS_MAX_ENUM = 0x7FFFFFFF  /* not a value: keeps every int in the type's range */
 } prnnStatus_t;
@@ -182,13 +192,13 @@ typedef struct {
 /* Environment: PRNN_LOG set to anything but "" or "0" when a handle is
  * created makes that handle print one line to stderr per launch (its plan:
  * layout, grid, waves per workgroup, rows per wave, kernel instance, LDS,
- * math) and one per failed run reported by prnn_synchronize.  Otherwise the
+ * math) and one per failed run when it is reported.  Otherwise the
  * library prints nothing. */
 
 /* Creates a handle bound to the current HIP device.
  * Returns NOT_SUPPORTED if the device is not gfx950, ALLOC_FAILED if the small
- * internal buffers (status word, exchange ring) cannot be allocated,
- * BAD_PARAM if handle is NULL. */
+ * internal buffers (the device status word and its 64-byte pinned host
+ * mirror) cannot be allocated, BAD_PARAM if handle is NULL. */
 prnnStatus_t prnn_create(prnnHandle_t* handle);
 
 /* Waits for all work the handle enqueued, frees its buffers and the handle.
@@ -234,9 +244,9 @@ prnnStatus_t prnn_forward_sparse(prnnHandle_t handle, int N, int B, int T, int K
  * x_type: PRNN_DATA_FLOAT or PRNN_DATA_HALF.  Runs on the matrix cores with
  * fp32 accumulation.  An fp32 x enters as fp16 hi = fp16(x) plus
  * lo = fp16(x - hi), whose products with the fp16 U are exact: x is seen to
- * about 2^-22 of |x|.  A finite |x| >= 65520 does not fit the split; the
- * handle then reports EXECUTION_FAILED at prnn_synchronize (X is not valid)
- * and the next forward call on the handle does nothing until that report.
+ * about 2^-22 of |x|.  A finite |x| >= 65520 does not fit the split; X is
+ * then not valid and the failure is reported as EXECUTION_FAILED (sticky, see
+ * the conventions above).
  * BAD_PARAM: NULL handle, x, U or X (when M > 0); M < 0, N < 1, I < 1;
  * unknown types; x, U, bias or X not aligned to their element size; X
  * overlapping x, U or bias.  NOT_SUPPORTED: fp32 U; x or U over 4 GiB.
@@ -297,7 +307,7 @@ prnnStatus_t prnn_forward_layer_sparse(prnnHandle_t handle, int N, int I, int B,
  * input, the workspace or another output, the workspace overlapping an
  * input.  NOT_SUPPORTED: L B > 8 or L > 8, sizes over 4 GiB, and what
  * prnn_project or (one layer after another) prnn_forward_dense does not
- * support.  EXECUTION_FAILED (at prnn_synchronize):
+ * support.  EXECUTION_FAILED (sticky, at the next call; see the conventions):
  * a bounded wait expired, or x exceeded the fp16 range of its split.
  * T == 0 enqueues nothing and returns SUCCESS. */
 /* How prnn_forward_stack_dense runs the layers (see there).
@@ -333,8 +343,9 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t handle, int L, int N, int I, 
 prnnStatus_t prnn_sync_floor(prnnHandle_t handle, int N, int B, int T, float* H,
                              hipStream_t stream);
 
-/* Waits for `stream`, then reports whether any run on the handle hit the
- * watchdog (EXECUTION_FAILED, sticky until reported here or by destroy). */
+/* Waits for `stream`, then reports whether any run on the handle failed
+ * (EXECUTION_FAILED: a wait hit the watchdog, or a value left the fp16 range
+ * of a path that needs it) and that failure has not been reported yet. */
 prnnStatus_t prnn_synchronize(prnnHandle_t handle, hipStream_t stream);
 /* (After a reported failure the handle is usable again: its exchange ring is
  * reset before the next forward call.) */

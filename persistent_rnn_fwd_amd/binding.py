@@ -7,6 +7,7 @@ another implementation.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 from typing import Optional
@@ -378,6 +379,20 @@ class Handle:
 
 
 _default_handles = {}
+
+
+@atexit.register
+def _close_default_handles():
+    """Destroys the module's default handles at interpreter exit, before the
+    HIP runtime and torch tear down (handlers run in reverse order of
+    registration, and torch registers its own when it is imported, before
+    this module's)."""
+    while _default_handles:
+        _, h = _default_handles.popitem()
+        try:
+            h.close()
+        except Exception:
+            pass
 
 
 def default_handle() -> Handle:

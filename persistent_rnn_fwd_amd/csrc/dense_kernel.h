@@ -35,7 +35,8 @@ struct WChunk;  // four consecutive weights of one row
 template <>
 struct WChunk<float> {
   float4 w;
-  // vec: n % 4 == 0, so a chunk is either entirely inside the row or outside.
+  // vec: n % 4 == 0 and W 16-byte aligned, so a chunk is either entirely
+  // inside the row or outside, and its load is naturally aligned.
   __device__ __forceinline__ void load(const void* W, size_t row_off, int c, int n, bool live, bool vec) {
     const float* p = reinterpret_cast<const float*>(W) + row_off;
     if (vec) {
@@ -142,7 +143,7 @@ __global__ void __launch_bounds__(256) dense_kernel(StepArgs a) {
   const int jn = a.chunks;
 
   // Prologue: this workgroup's rows of W into registers, once per call.
-  const bool vec = (N & 3) == 0;
+  const bool vec = (N & 3) == 0 && a.w_vec != 0;
   WChunk<WT> w[RMAX][J];
 #pragma unroll
   for (int r = 0; r < RMAX; ++r)
@@ -185,7 +186,7 @@ __global__ void __launch_bounds__(256) dense_kernel(StepArgs a) {
         // Then read the row once and multiply each 1 KiB chunk as it lands.
         if (!relay_slice(ex, row_bytes, lane, N, tag, a.deadline) ||
             !wait_slices(ex, a.relay_slice, row_bytes, lane, N, tag, a.deadline)) {
-          if (lane == 0) atomicOr(a.status, kStatusTimeout);
+          if (lane == 0) report_failure(a.status, a.status_host, kStatusTimeout);
           return;
         }
 #pragma unroll
@@ -208,7 +209,7 @@ __global__ void __launch_bounds__(256) dense_kernel(StepArgs a) {
         // Direct exchange, or a relayed row that was not complete yet: wait
         // for the whole row, then (re)compute the sums from scratch.
         if (!gather_row<J>(v, ex.local, row_bytes, lane, jn, N, tag, a.deadline)) {
-          if (lane == 0) atomicOr(a.status, kStatusTimeout);
+          if (lane == 0) report_failure(a.status, a.status_host, kStatusTimeout);
           return;
         }
 #pragma unroll
@@ -241,7 +242,7 @@ __global__ void __launch_bounds__(256) dense_kernel(StepArgs a) {
   if (a.T > 0) {
     const uint32_t last = a.step0 + (uint32_t)(a.T - 1);
     if (!relay_slice(ex, (uint32_t)(((last & 1u) * a.B + b) * a.Npad) * 4u, lane, N, tag_bit(last), a.deadline)) {
-      if (lane == 0) atomicOr(a.status, kStatusTimeout);
+      if (lane == 0) report_failure(a.status, a.status_host, kStatusTimeout);
     }
   }
 }
@@ -271,7 +272,7 @@ __global__ void __launch_bounds__(256) floor_kernel(StepArgs a) {
       if (!relay_slice(ex, row_bytes, lane, N, tag_bit(prev), a.deadline) ||
           (a.relay_slice > 0 && !wait_slices(ex, a.relay_slice, row_bytes, lane, N, tag_bit(prev), a.deadline)) ||
           !gather_row<J>(v, ex.local, row_bytes, lane, jn, N, tag_bit(prev), a.deadline)) {
-        if (lane == 0) atomicOr(a.status, kStatusTimeout);
+        if (lane == 0) report_failure(a.status, a.status_host, kStatusTimeout);
         return;
       }
 #pragma unroll
@@ -298,7 +299,7 @@ __global__ void __launch_bounds__(256) floor_kernel(StepArgs a) {
   if (a.T > 0) {
     const uint32_t last = a.step0 + (uint32_t)(a.T - 1);
     if (!relay_slice(ex, (uint32_t)(((last & 1u) * a.B + b) * a.Npad) * 4u, lane, N, tag_bit(last), a.deadline)) {
-      if (lane == 0) atomicOr(a.status, kStatusTimeout);
+      if (lane == 0) report_failure(a.status, a.status_host, kStatusTimeout);
     }
   }
 }

@@ -46,6 +46,21 @@ constexpr int kPlain = 0;
 constexpr uint32_t kStatusTimeout = 1u;
 constexpr uint32_t kStatusRange = 2u;  // a value reached the fp16 range of an hi + lo split
 
+// A failed run: sets `bits` in the device status word, which every later
+// kernel on the handle reads at entry (and then does nothing until the
+// failure has been reported), and marks the host-visible mirror of the
+// handle (pinned host memory: word 0 for an expired wait, word 1 for a value
+// out of range) with a system-scope store, so that the host learns of the
+// failure at its next call without waiting for the GPU.  Every writer of a
+// mirror word stores the same value, so no atomic is needed there.
+__device__ __forceinline__ void report_failure(uint32_t* status, uint32_t* host, uint32_t bits) {
+  atomicOr(status, bits);
+  if (host != nullptr) {
+    if (bits & kStatusTimeout) __hip_atomic_store(host + 0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (bits & kStatusRange) __hip_atomic_store(host + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
 // Raw buffer resource over [p, p + bytes): out-of-range accesses read 0 and
 // drop writes instead of faulting.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {

@@ -17,6 +17,7 @@ struct StepArgs {
   uint32_t* ring;       // spread layout: [2][B][Npad] tagged words; team layout: [8][2][Npad]
   uint32_t* relay;      // [8][2][B][Npad]: one copy of the ring per XCD (relay mode)
   uint32_t* status;     // device status word (0 = ok)
+  uint32_t* status_host;  // host-visible mirror of failures (pinned host memory), or nullptr
   int N, B, T, K, Npad;
   int lds_stride;       // sparse: words per LDS row of h, multiple of 4, >= N + 1
   int G;                // workgroups per batch group
@@ -25,6 +26,7 @@ struct StepArgs {
   int chunks;           // 256-column chunks of a row: ceil(N / 256)
   int spr;              // sparse: 64-pair slots per row, ceil(K / 64)
   int relay_slice;      // words of a row each workgroup relays (0 = direct mode)
+  int w_vec;            // dense: W is 16-byte aligned, so rows of N % 4 == 0 (MFMA: N % 8 == 0) load as vectors
   uint32_t step0;       // ring step counter at t = 0
   uint32_t ring_bytes;
   uint32_t x_bytes;     // bytes of X (= bytes of H)
@@ -111,6 +113,7 @@ struct StackArgs {
   int Tl[kMaxStack];             // steps of layer l in this launch (<= T; 0: idle)
   uint32_t* ring;                // [8][2][Npad]
   uint32_t* status;
+  uint32_t* status_host;         // host-visible mirror of failures, or nullptr
   int L, N, B, T, Npad, chunks, base_rows, extra_rows;
   uint32_t step0;
   uint32_t x_bytes;              // bytes of one [T][B][N] sequence (T = the launch's steps)
@@ -128,6 +131,7 @@ struct ProjArgs {
   const float* bias;  // [N] or nullptr
   float* X;           // [M][N]
   uint32_t* status;   // kStatusRange if an fp32 x exceeds the fp16 range of its split
+  uint32_t* status_host;  // host-visible mirror of failures, or nullptr
   int M, N, I;
   uint32_t x_bytes, u_bytes;
   int tiles_n;        // column tiles of X (set by launch_project)

@@ -21,6 +21,15 @@ struct prnnContext {
   int num_cu = 0;
   size_t lds_per_block = 0;
   uint32_t* d_status = nullptr;
+  // Host-visible mirror of failures (pinned host memory: word 0 = a wait
+  // expired, word 1 = a value outside the fp16 range), written by the failing
+  // kernel; h_status_dev is its address on the device.  The next call on the
+  // handle reads it without waiting for the GPU.
+  volatile uint32_t* h_status = nullptr;
+  uint32_t* h_status_dev = nullptr;
+  // A reported failure leaves the device status word set until the next
+  // enqueued call clears it (first, on that call's stream).
+  bool status_dirty = false;
   // Exchange memory.  Spread layout: [2][B][Npad] ring followed by 8
   // XCD-local copies of it.  Team layout: [8][2][Npad], one region per XCD.
   uint32_t* d_ring = nullptr;
@@ -266,11 +275,38 @@ prnnStatus_t hip_status(hipError_t e) {
   return PRNN_STATUS_INTERNAL_ERROR;
 }
 
+// A failed run whose mirror reached the host, reported once: the mirror is
+// cleared, the device status word is cleared by the next enqueued call, and
+// the ring is reset before the next launch.
+bool take_failure(prnnContext* h) {
+  const uint32_t timeout = h->h_status[0], range = h->h_status[1];
+  if ((timeout | range) == 0u) return false;
+  h->h_status[0] = 0u;
+  h->h_status[1] = 0u;
+  h->status_dirty = true;
+  h->ring_valid = false;
+  if (h->log)
+    std::fprintf(stderr, "prnn: run failed:%s%s\n", timeout ? " a wait for h_{t-1} expired (watchdog)" : "",
+                 range ? " a value outside the fp16 range" : "");
+  return true;
+}
+
+// Clears the device status word of a reported failure, on `stream`, before
+// the call's own kernels.
+prnnStatus_t clear_reported_status(prnnContext* h, hipStream_t stream) {
+  if (!h->status_dirty) return PRNN_STATUS_SUCCESS;
+  prnn::launch_fill(h->d_status, 64, 0u, stream);
+  if (hipGetLastError() != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+  h->status_dirty = false;
+  return PRNN_STATUS_SUCCESS;
+}
+
 // Makes the exchange memory fit the plan's layout and, when the layout or its
 // shape changed, a run failed, or relay continuity was broken, resets it on
 // `stream` and restarts the step counter.
 prnnStatus_t ensure_ring(prnnContext* h, const Plan& p, int B, int Npad, hipStream_t stream) {
   const bool team = p.layout == PRNN_LAYOUT_TEAM;
+  if (clear_reported_status(h, stream) != PRNN_STATUS_SUCCESS) return PRNN_STATUS_INTERNAL_ERROR;
   const size_t words = team ? 16ull * (size_t)Npad : 18ull * (size_t)B * (size_t)Npad;
   if (words * 4ull > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
   // Under stream capture the call becomes a graph node that may be replayed
@@ -345,6 +381,7 @@ StepArgs base_args(prnnContext* h, int N, int B, int T, const float* X, const fl
   a.relay = h->d_ring + 2ull * B * Npad;
   a.relay_slice = p.relay_slice;
   a.status = h->d_status;
+  a.status_host = h->h_status_dev;
   a.N = N;
   a.B = B;
   a.T = T;
@@ -448,7 +485,7 @@ prnnStatus_t prepare_dense(prnnContext* h, int N, int B, int T, prnnDataType_t w
   if (w_type != PRNN_DATA_FLOAT && w_type != PRNN_DATA_HALF) return PRNN_STATUS_BAD_PARAM;
   if (*empty) return PRNN_STATUS_SUCCESS;
   if (W == nullptr) return PRNN_STATUS_BAD_PARAM;
-  if (!aligned(W, 4)) return PRNN_STATUS_BAD_PARAM;
+  if (!aligned(W, w_type == PRNN_DATA_FLOAT ? 4 : 2)) return PRNN_STATUS_BAD_PARAM;
   const size_t wb = (size_t)N * N * (w_type == PRNN_DATA_FLOAT ? 4 : 2);
   if (overlap(W, wb, H, (size_t)T * B * N * 4)) return PRNN_STATUS_BAD_PARAM;
   if ((size_t)T * B * N * 4 > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
@@ -464,6 +501,7 @@ prnnStatus_t run_dense(prnnContext* h, const Plan& p, int N, int B, int T, const
   if (st != PRNN_STATUS_SUCCESS) return st;
   StepArgs a = base_args(h, N, B, T, X, h0, H, p, Npad);
   a.W = W;
+  a.w_vec = aligned(W, 16) ? 1 : 0;  // W needs only element alignment; vector loads where it allows them
   return launch(h, p, a, T, stream);
 }
 
@@ -521,6 +559,7 @@ prnnStatus_t prepare_project(prnnContext* h, int M, int N, int I, prnnDataType_t
   a->bias = bias;
   a->X = X;
   a->status = h->d_status;
+  a->status_host = h->h_status_dev;
   a->M = M;
   a->N = N;
   a->I = I;
@@ -587,12 +626,25 @@ prnnStatus_t prnn_create(prnnHandle_t* handle) {
     return PRNN_STATUS_ALLOC_FAILED;
   }
   h->d_status = static_cast<uint32_t*>(p);
+  void* hp = nullptr;
+  if (hipHostMalloc(&hp, 64, hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(p);
+    delete h;
+    return PRNN_STATUS_ALLOC_FAILED;
+  }
+  h->h_status = static_cast<volatile uint32_t*>(hp);
+  for (int i = 0; i < 16; ++i) h->h_status[i] = 0u;
+  void* hd = nullptr;
   prnn::launch_fill(h->d_status, 64, 0u, nullptr);
-  if (hipDeviceSynchronize() != hipSuccess) {
+  if (hipHostGetDevicePointer(&hd, hp, 0) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipHostFree(hp);
     (void)hipFree(p);
     delete h;
     return PRNN_STATUS_INTERNAL_ERROR;
   }
+  h->h_status_dev = static_cast<uint32_t*>(hd);
   h->placement_round_robin = check_placement(h->num_cu);
   const char* log = std::getenv("PRNN_LOG");
   h->log = log != nullptr && log[0] != '\0' && std::strcmp(log, "0") != 0;
@@ -607,12 +659,11 @@ prnnStatus_t prnn_destroy(prnnHandle_t h) {
   if (h == nullptr) return PRNN_STATUS_SUCCESS;
   prnnStatus_t st = PRNN_STATUS_SUCCESS;
   if (hipDeviceSynchronize() != hipSuccess) st = PRNN_STATUS_INTERNAL_ERROR;
-  uint32_t s = 0;
-  if (h->d_status != nullptr && hipMemcpy(&s, h->d_status, 4, hipMemcpyDeviceToHost) == hipSuccess && s != 0)
-    st = PRNN_STATUS_EXECUTION_FAILED;
+  if (h->h_status != nullptr && take_failure(h)) st = PRNN_STATUS_EXECUTION_FAILED;
   if (h->d_ring != nullptr) (void)hipFree(h->d_ring);
   if (h->d_trace != nullptr) (void)hipFree(h->d_trace);
   if (h->d_status != nullptr) (void)hipFree(h->d_status);
+  if (h->h_status != nullptr) (void)hipHostFree(const_cast<uint32_t*>(h->h_status));
   delete h;
   return st;
 }
@@ -709,23 +760,12 @@ prnnStatus_t prnn_debug_jitter(prnnHandle_t h, uint32_t seed, int span) {
 prnnStatus_t prnn_synchronize(prnnHandle_t h, hipStream_t stream) {
   if (h == nullptr) return PRNN_STATUS_BAD_PARAM;
   if (hipStreamSynchronize(stream) != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
-  uint32_t s = 0;
-  if (hipMemcpy(&s, h->d_status, 4, hipMemcpyDeviceToHost) != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
-  if (s != 0) {
-    if (h->log)
-      std::fprintf(stderr, "prnn: run failed:%s%s\n", (s & 1u) ? " a wait for h_{t-1} expired (watchdog)" : "",
-                   (s & 2u) ? " a value outside the fp16 range" : "");
-    // Report once; clear the status and force a ring reset before the next run.
-    prnn::launch_fill(h->d_status, 64, 0u, stream);
-    if (hipStreamSynchronize(stream) != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
-    h->ring_valid = false;
-    return PRNN_STATUS_EXECUTION_FAILED;
-  }
-  return PRNN_STATUS_SUCCESS;
+  return take_failure(h) ? PRNN_STATUS_EXECUTION_FAILED : PRNN_STATUS_SUCCESS;
 }
 
 prnnStatus_t prnn_forward_dense(prnnHandle_t h, int N, int B, int T, prnnDataType_t w_type, const void* W,
                                 const float* X, const float* h0, float* H, hipStream_t stream) {
+  if (h != nullptr && take_failure(h)) return PRNN_STATUS_EXECUTION_FAILED;
   Plan p;
   bool empty = false;
   prnnStatus_t st = prepare_dense(h, N, B, T, w_type, W, X, h0, H, &p, &empty);
@@ -736,6 +776,7 @@ prnnStatus_t prnn_forward_dense(prnnHandle_t h, int N, int B, int T, prnnDataTyp
 prnnStatus_t prnn_forward_sparse(prnnHandle_t h, int N, int B, int T, int K, const int16_t* col,
                                  prnnDataType_t val_type, const void* val, const float* X, const float* h0,
                                  float* H, hipStream_t stream) {
+  if (h != nullptr && take_failure(h)) return PRNN_STATUS_EXECUTION_FAILED;
   Plan p;
   bool empty = false;
   prnnStatus_t st = prepare_sparse(h, N, B, T, K, col, val_type, val, X, h0, H, &p, &empty);
@@ -745,10 +786,13 @@ prnnStatus_t prnn_forward_sparse(prnnHandle_t h, int N, int B, int T, int K, con
 
 prnnStatus_t prnn_project(prnnHandle_t h, int M, int N, int I, prnnDataType_t x_type, const void* x,
                           prnnDataType_t u_type, const void* U, const float* bias, float* X, hipStream_t stream) {
+  if (h != nullptr && take_failure(h)) return PRNN_STATUS_EXECUTION_FAILED;
   prnn::ProjArgs a;
   bool vec = false;
   prnnStatus_t st = prepare_project(h, M, N, I, x_type, x, u_type, U, bias, X, &a, &vec);
   if (st != PRNN_STATUS_SUCCESS || M == 0) return st;
+  st = clear_reported_status(h, stream);
+  if (st != PRNN_STATUS_SUCCESS) return st;
   return hip_status(prnn::launch_project(a, x_type == PRNN_DATA_FLOAT, vec, stream));
 }
 
@@ -756,6 +800,7 @@ prnnStatus_t prnn_forward_layer_dense(prnnHandle_t h, int N, int I, int B, int T
                                       const void* x, prnnDataType_t u_type, const void* U, const float* bias,
                                       prnnDataType_t w_type, const void* W, const float* h0, float* Xbuf, float* H,
                                       hipStream_t stream) {
+  if (h != nullptr && take_failure(h)) return PRNN_STATUS_EXECUTION_FAILED;
   Plan p;
   bool empty = false;
   prnnStatus_t st = prepare_dense(h, N, B, T, w_type, W, Xbuf, h0, H, &p, &empty);
@@ -764,6 +809,8 @@ prnnStatus_t prnn_forward_layer_dense(prnnHandle_t h, int N, int I, int B, int T
   bool vec = false;
   st = prepare_layer_projection(h, N, I, B, T, x_type, x, u_type, U, bias, Xbuf, h0, W,
                                 (size_t)N * N * (w_type == PRNN_DATA_FLOAT ? 4 : 2), nullptr, 0, &a, &vec);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  st = clear_reported_status(h, stream);
   if (st != PRNN_STATUS_SUCCESS) return st;
   st = hip_status(prnn::launch_project(a, x_type == PRNN_DATA_FLOAT, vec, stream));
   if (st != PRNN_STATUS_SUCCESS) return st;
@@ -774,6 +821,7 @@ prnnStatus_t prnn_forward_layer_sparse(prnnHandle_t h, int N, int I, int B, int 
                                        const void* x, prnnDataType_t u_type, const void* U, const float* bias,
                                        const int16_t* col, prnnDataType_t val_type, const void* val,
                                        const float* h0, float* Xbuf, float* H, hipStream_t stream) {
+  if (h != nullptr && take_failure(h)) return PRNN_STATUS_EXECUTION_FAILED;
   Plan p;
   bool empty = false;
   prnnStatus_t st = prepare_sparse(h, N, B, T, K, col, val_type, val, Xbuf, h0, H, &p, &empty);
@@ -782,6 +830,8 @@ prnnStatus_t prnn_forward_layer_sparse(prnnHandle_t h, int N, int I, int B, int 
   bool vec = false;
   st = prepare_layer_projection(h, N, I, B, T, x_type, x, u_type, U, bias, Xbuf, h0, col, (size_t)N * K * 2, val,
                                 (size_t)N * K * (val_type == PRNN_DATA_FLOAT ? 4 : 2), &a, &vec);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  st = clear_reported_status(h, stream);
   if (st != PRNN_STATUS_SUCCESS) return st;
   st = hip_status(prnn::launch_project(a, x_type == PRNN_DATA_FLOAT, vec, stream));
   if (st != PRNN_STATUS_SUCCESS) return st;
@@ -793,6 +843,7 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B
                                       const void* const* W, const float* const* h0, float* Xbuf, float* const* H,
                                       hipStream_t stream) {
   if (h == nullptr || L < 1 || N < 1 || I < 1 || B < 1 || B > 8 || T < 0) return PRNN_STATUS_BAD_PARAM;
+  if (take_failure(h)) return PRNN_STATUS_EXECUTION_FAILED;
   if (x_type != PRNN_DATA_FLOAT && x_type != PRNN_DATA_HALF) return PRNN_STATUS_BAD_PARAM;
   if (L > prnn::kMaxStack || L * B > 8) return PRNN_STATUS_NOT_SUPPORTED;
   if (T == 0) return PRNN_STATUS_SUCCESS;
@@ -896,6 +947,7 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B
   }
   a.ring = h->d_ring;
   a.status = h->d_status;
+  a.status_host = h->h_status_dev;
   a.L = L;
   a.N = N;
   a.B = B;
@@ -990,6 +1042,7 @@ prnnStatus_t prnn_set_stack_mode(prnnHandle_t h, prnnStackMode_t mode) {
 
 prnnStatus_t prnn_sync_floor(prnnHandle_t h, int N, int B, int T, float* H, hipStream_t stream) {
   if (h == nullptr || N < 1 || B < 1 || B > 8 || T < 0) return PRNN_STATUS_BAD_PARAM;
+  if (take_failure(h)) return PRNN_STATUS_EXECUTION_FAILED;
   if (T == 0) return PRNN_STATUS_SUCCESS;
   if (H == nullptr || !aligned(H, 4)) return PRNN_STATUS_BAD_PARAM;
   if ((size_t)T * B * N * 4 > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;

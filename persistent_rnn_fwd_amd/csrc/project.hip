@@ -227,7 +227,7 @@ __global__ void __launch_bounds__(256 * kGroups) project_kernel(ProjArgs a) {
   }
   __syncthreads();
   if (grp == 1) {
-    if (XF32 && wave_any(!range_ok) && lane == 0) atomicOr(a.status, kStatusRange);
+    if (XF32 && wave_any(!range_ok) && lane == 0) report_failure(a.status, a.status_host, kStatusRange);
     return;
   }
 #pragma unroll
@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(256 * kGroups) project_kernel(ProjArgs a) {
         if (m < a.M) a.X[(size_t)m * a.N + n] = acc[i][j][r] + bn;
       }
   }
-  if (XF32 && wave_any(!range_ok) && lane == 0) atomicOr(a.status, kStatusRange);
+  if (XF32 && wave_any(!range_ok) && lane == 0) report_failure(a.status, a.status_host, kStatusRange);
 }
 
 }  // namespace

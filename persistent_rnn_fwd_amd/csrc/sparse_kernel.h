@@ -220,7 +220,7 @@ __global__ void __launch_bounds__(256) sparse_kernel(StepArgs a) {
       const uint32_t row0_bytes = (uint32_t)(((prev & 1u) * a.B + b) * a.Npad) * 4u;
       if (!relay_slice(ex, row0_bytes, lane, N, tag, a.deadline) ||
           (a.relay_slice > 0 && !wait_slices(ex, a.relay_slice, row0_bytes, lane, N, tag, a.deadline))) {
-        if (lane == 0) atomicOr(a.status, kStatusTimeout);
+        if (lane == 0) report_failure(a.status, a.status_host, kStatusTimeout);
         return;
       }
       for (int j0 = 0; j0 < jn; j0 += kStageChunks) {
@@ -229,7 +229,7 @@ __global__ void __launch_bounds__(256) sparse_kernel(StepArgs a) {
         const int n = N - 256 * j0;
         u32x4 v[kStageChunks];
         if (!gather_row<kStageChunks>(v, ex.local, row_bytes, lane, jn - j0, n, tag, a.deadline)) {
-          if (lane == 0) atomicOr(a.status, kStatusTimeout);
+          if (lane == 0) report_failure(a.status, a.status_host, kStatusTimeout);
           return;
         }
 #pragma unroll
@@ -277,7 +277,7 @@ __global__ void __launch_bounds__(256) sparse_kernel(StepArgs a) {
   if (a.T > 0) {
     const uint32_t last = a.step0 + (uint32_t)(a.T - 1);
     if (!relay_slice(ex, (uint32_t)(((last & 1u) * a.B + b) * a.Npad) * 4u, lane, N, tag_bit(last), a.deadline)) {
-      if (lane == 0) atomicOr(a.status, kStatusTimeout);
+      if (lane == 0) report_failure(a.status, a.status_host, kStatusTimeout);
     }
   }
 }

@@ -150,7 +150,7 @@ __global__ void __launch_bounds__(512) stack_team_kernel(StackArgs a) {
     }
     if (!ok && lane == 0) {
       abort_flag = 1;
-      atomicOr(a.status, kStatusTimeout);
+      report_failure(a.status, a.status_host, kStatusTimeout);
     }
     __syncthreads();
     int aborted_now = abort_flag;

@@ -50,7 +50,7 @@ __global__ void __launch_bounds__(64 * WAVES) floor_team_kernel(StepArgs a) {
     }
     if (!ok && p.lane == 0) {
       abort_flag = 1;
-      atomicOr(a.status, kStatusTimeout);
+      report_failure(a.status, a.status_host, kStatusTimeout);
     }
     clk.mark(kTrStage);
     __syncthreads();

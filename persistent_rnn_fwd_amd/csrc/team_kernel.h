@@ -223,7 +223,7 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
 
   const int N = a.N;
   const int jn = a.chunks;
-  const bool vec = (N & 3) == 0;
+  const bool vec = (N & 3) == 0 && a.w_vec != 0;
   uint32_t range_bad = 0;  // half-h: a staged value beyond the fp16 range
   if (!p.primary) {
     team_stamp_tail(a, p, team_region(a));
@@ -271,7 +271,7 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
     }
     if (!ok && p.lane == 0) {
       abort_flag = 1;
-      atomicOr(a.status, kStatusTimeout);
+      report_failure(a.status, a.status_host, kStatusTimeout);
     }
     clk.mark(kTrStage);
     __syncthreads();
@@ -330,7 +330,7 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
     }
     clk.mark(kTrEpilogue);
   }
-  if (HALF && wave_any(range_bad != 0) && p.lane == 0) atomicOr(a.status, kStatusRange);
+  if (HALF && wave_any(range_bad != 0) && p.lane == 0) report_failure(a.status, a.status_host, kStatusRange);
   if (TRACE) clk.finish(trace_record(a, p), a.T);
 }
 
@@ -392,7 +392,7 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
     }
     if (!ok && p.lane == 0) {
       abort_flag = 1;
-      atomicOr(a.status, kStatusTimeout);
+      report_failure(a.status, a.status_host, kStatusTimeout);
     }
     clk.mark(kTrStage);
     __syncthreads();

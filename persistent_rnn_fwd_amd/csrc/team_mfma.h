@@ -80,7 +80,7 @@ __global__ void __launch_bounds__(512) dense_team_mfma_kernel(StepArgs a) {
   // 256 wave + 32 s + 8 q + e, e < 8.  Zero outside the matrix.
   half8 w[TR][KS];
   const uint16_t* W16 = reinterpret_cast<const uint16_t*>(a.W);
-  const bool vec = (N & 7) == 0;
+  const bool vec = (N & 7) == 0 && a.w_vec != 0;
 #pragma unroll
   for (int i = 0; i < TR; ++i)
 #pragma unroll
@@ -152,7 +152,7 @@ __global__ void __launch_bounds__(512) dense_team_mfma_kernel(StepArgs a) {
     }
     if (!ok && lane == 0) {
       abort_flag = 1;
-      atomicOr(a.status, kStatusTimeout);
+      report_failure(a.status, a.status_host, kStatusTimeout);
     }
     clk.mark(kTrStage);
 
@@ -214,7 +214,7 @@ __global__ void __launch_bounds__(512) dense_team_mfma_kernel(StepArgs a) {
     }
     clk.mark(kTrEpilogue);
   }
-  if (wave_any(!range_ok) && lane == 0) atomicOr(a.status, kStatusRange);
+  if (wave_any(!range_ok) && lane == 0) report_failure(a.status, a.status_host, kStatusRange);
   if (TRACE) {
     TeamPos p;
     p.wave = wave;

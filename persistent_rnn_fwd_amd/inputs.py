@@ -19,7 +19,9 @@ Value distributions (the pages state none):
   sparse W  ~ N(0, 0.8^2 / K)   on K distinct columns per row, drawn uniformly
                                 without replacement and stored sorted
   X         ~ N(0, 1)           fp32, the pre-activations W_x x_t + b
-  h0        = 0                 (or |N(0,1)| when asked for)
+  h0        = 0                 (or N(0,1), signed, when asked for: an initial
+                                state is any fp32 vector, not only a ReLU output;
+                                |N(0,1)| with "absrandn")
 
 Unbalanced rows ("magnitude" pruning), for the pages' load-balanced vs
 unbalanced pruning comparison: a dense Gaussian matrix whose rows carry
@@ -65,7 +67,7 @@ class Workload:
     w_dtype: str         # "f32" or "f16" (dense W, or sparse values)
     K: int = 0           # nonzeros per row (sparse only)
     seed: int = 0
-    h0: str = "zeros"    # "zeros" or "randn" (|N(0,1)|)
+    h0: str = "zeros"    # "zeros", "randn" (N(0,1), signed) or "absrandn" (|N(0,1)|)
     rows: str = "balanced"  # sparse: "balanced" (K per row) or "magnitude" (K on average, padded)
 
     @property
@@ -182,6 +184,8 @@ def generate(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
     if w.h0 == "zeros":
         out["h0"] = np.zeros((w.B, w.N), dtype=np.float32)
     elif w.h0 == "randn":
+        out["h0"] = rng_h.standard_normal((w.B, w.N)).astype(np.float32)
+    elif w.h0 == "absrandn":
         out["h0"] = np.abs(rng_h.standard_normal((w.B, w.N))).astype(np.float32)
     else:
         raise ValueError(f"unknown h0 mode {w.h0!r}")
@@ -212,7 +216,8 @@ def generate_layer(w: Workload, I: int, seed: Optional[int] = None, x_dtype: str
 def generate_stack(w: Workload, L: int, seed: Optional[int] = None) -> Dict[str, object]:
     """L dense layers of width N = I = w.N: ``layers`` = [{U, bias, W}] (fp16
     U and W as in ``generate_layer`` and ``generate``), the input ``x`` fp32
-    [T, B, N] and per-layer ``h0s`` (zeros, or |N(0,1)| with w.h0 == "randn")."""
+    [T, B, N] and per-layer ``h0s`` (zeros, N(0,1) with w.h0 == "randn", |N(0,1)|
+    with "absrandn")."""
     if w.kind != "dense":
         raise ValueError("stacks are dense")
     seed = w.seed if seed is None else seed
@@ -228,8 +233,9 @@ def generate_stack(w: Workload, L: int, seed: Optional[int] = None) -> Dict[str,
         })
         if l == 0:
             h0 = base["h0"]
-        elif w.h0 == "randn":
-            h0 = np.abs(rng_b.standard_normal((w.B, w.N))).astype(np.float32)
+        elif w.h0 in ("randn", "absrandn"):
+            h0 = rng_b.standard_normal((w.B, w.N)).astype(np.float32)
+            h0 = np.abs(h0) if w.h0 == "absrandn" else h0
         else:
             h0 = np.zeros((w.B, w.N), dtype=np.float32)
         h0s.append(h0)
