@@ -429,6 +429,38 @@ prnnStatus_t prnn_debug_skip_publish(prnnHandle_t handle, int wg, int step);
 #define PRNN_DEBUG_JITTER_MAX 1024
 prnnStatus_t prnn_debug_jitter(prnnHandle_t handle, uint32_t seed, int span);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ * The operation, argument meanings, layouts, ownership and argument errors of
+ * prnn_forward_dense with its default options (TEAM layout, EXACT math), but
+ * no handle: the exchange ring lives in a fixed array in the library's device
+ * memory (16 * PRNN_NOALLOC_MAX_N words + 256 bytes, about 160 KiB), one copy
+ * per device, held until the process ends.  No call allocates anything.
+ *  - N > PRNN_NOALLOC_MAX_N returns NOT_SUPPORTED (the array's capacity), as
+ *    do shapes the TEAM layout cannot take (fp32 W beyond N = 1792).
+ *  - status: NULL, or one caller-owned device word (4-byte aligned).  The call
+ *    first sets it to 0 on `stream`; a run that fails (a wait for h_{t-1}
+ *    expired) sets it nonzero and leaves H undefined.  Read it once the
+ *    stream's work has finished.  With NULL, failures are not reported (every
+ *    kernel still exits).
+ *  - Every call resets the array on `stream` (two small fill kernels, no
+ *    memset, so calls can be captured into a graph) and counts its steps
+ *    from 0.
+ *  - Every call on a device shares that device's array and leaves it as its
+ *    run left it: calls that overlap in time on one device (on different
+ *    streams, or graph replays running at once) race and give wrong results.
+ *    Run one at a time per device.
+ *  - The first call on a device looks up the array's address and checks how
+ *    workgroups are placed on the XCDs (a small kernel and a synchronous
+ *    copy); it cannot be made while `stream` is being captured and then
+ *    returns NOT_SUPPORTED: make one call outside capture first.
+ *  - Call with the device current.  T == 0 returns SUCCESS and enqueues
+ *    nothing. */
+#define PRNN_NOALLOC_MAX_N 2560
+prnnStatus_t prnn_forward_dense_noalloc(int N, int B, int T, prnnDataType_t w_type, const void* W,
+                                        const float* X, const float* h0, float* H, uint32_t* status,
+                                        hipStream_t stream);
+
 /* Static description of a status code; never NULL, never allocates. */
 const char* prnn_status_string(prnnStatus_t status);
 

@@ -60,6 +60,7 @@ SIGNATURES = {
     "prnn_forward_layer_sparse": (_I, [_H, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
     "prnn_forward_stack_dense": (_I, [_H, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "prnn_set_stack_mode": (_I, [_H, _I]),
+    "prnn_forward_dense_noalloc": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
 }
 
 
@@ -409,3 +410,31 @@ def forward_dense(W, X, h0=None, out=None, stream=None):
 
 def forward_sparse(col, val, X, h0=None, out=None, stream=None):
     return default_handle().forward_sparse(col, val, X, h0, out, stream)
+
+
+NOALLOC_MAX_N = 2560  # PRNN_NOALLOC_MAX_N
+
+
+def forward_dense_noalloc(W: torch.Tensor, X: torch.Tensor, h0: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
+    """prnn_forward_dense_noalloc: the dense recurrence without a handle, on the
+    library's fixed device array (nothing allocated by the library).  status:
+    None or a one-element int32/uint32 device tensor, 0 after a good run."""
+    lib = load_library()
+    T, B, N = X.shape
+    _need(W, "W", (torch.float32, torch.float16), (N, N))
+    _need(X, "X", (torch.float32,), (T, B, N))
+    if h0 is not None:
+        _need(h0, "h0", (torch.float32,), (B, N))
+    if out is None:
+        out = torch.empty((T, B, N), dtype=torch.float32, device=X.device)
+    _need(out, "out", (torch.float32,), (T, B, N))
+    if status is not None:
+        _need(status, "status", (torch.int32, torch.uint32), (1,))
+    wt = DATA_FLOAT if W.dtype == torch.float32 else DATA_HALF
+    st = lib.prnn_forward_dense_noalloc(N, B, T, wt, W.data_ptr(), X.data_ptr(),
+                                        h0.data_ptr() if h0 is not None else None, out.data_ptr(),
+                                        status.data_ptr() if status is not None else None, _stream_ptr(stream))
+    _check("prnn_forward_dense_noalloc", st)
+    return out

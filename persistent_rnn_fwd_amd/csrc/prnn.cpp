@@ -11,6 +11,7 @@
 #include <cstring>
 #include <new>
 
+#include "host_internal.h"
 #include "kernels.h"
 
 using prnn::KernelEntry;
@@ -590,6 +591,33 @@ prnnStatus_t prepare_layer_projection(prnnContext* h, int N, int I, int B, int T
 }
 
 }  // namespace
+
+prnnStatus_t prnn::forward_dense_on(const DeviceFacts& dev, uint32_t* ring, uint32_t* status, int N, int B, int T,
+                                    prnnDataType_t w_type, const void* W, const float* X, const float* h0, float* H,
+                                    hipStream_t stream) {
+  // A context on the stack (nothing allocated): default options, the team
+  // layout only (its exchange memory is what `ring` holds), no host mirror.
+  prnnContext c;
+  c.num_cu = dev.num_cu;
+  c.lds_per_block = dev.lds_per_block;
+  c.placement_round_robin = dev.placement_round_robin;
+  c.layout = PRNN_LAYOUT_TEAM;
+  c.d_ring = ring;
+  c.d_status = status;
+  Plan p;
+  bool empty = false;
+  prnnStatus_t st = prepare_dense(&c, N, B, T, w_type, W, X, h0, H, &p, &empty);
+  if (st != PRNN_STATUS_SUCCESS || empty) return st;
+  const int Npad = (N + 3) & ~3;
+  // every call starts from a reset ring (step 0) and a clear status word
+  prnn::launch_fill(status, 1, 0u, stream);
+  prnn::launch_team_fill(ring, Npad, kRingResetWord, stream);
+  if (hipGetLastError() != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+  StepArgs a = base_args(&c, N, B, T, X, h0, H, p, Npad);
+  a.W = W;
+  a.w_vec = aligned(W, 16) ? 1 : 0;
+  return launch(&c, p, a, T, stream);
+}
 
 extern "C" {
 
