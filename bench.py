@@ -73,6 +73,7 @@ def parse():
                          "2-layer stack wavefront (N=1152), T=256, after the timed loop, for profilers")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config table (every workload, not timed "
                     "in the headline step)")
+    ap.add_argument("--no-config-loops", action="store_true", help="skip the per-config library loop baselines")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain copy kernel of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -251,7 +252,103 @@ def library_baselines(torch, dev, host, wd, ws, T, persistent_ms):
     return out
 
 
-def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=False):
+def config_library_loops(torch, dev, w, d, persistent_ms, reps=5):
+    """The workload as per-step library loops on the GPU, fp32 throughout:
+    dense GEMM (hipBLAS through torch.addmm, with the sparse matrix's dense
+    equivalent for sparse layers), eager and captured in one HIP graph, and
+    for sparse layers a CSR SpMM (torch.sparse.mm) loop.  Returns timesteps/s
+    per loop and the persistent kernel's speedup over each (the pages compare
+    the sparse persistent kernel with dense and sparse GEMM loops)."""
+    import warnings
+    import numpy as np
+    warnings.filterwarnings("ignore", message="Sparse CSR tensor support")
+    stream = torch.cuda.current_stream()
+    T, B, N = w.T, w.B, w.N
+    if w.kind == "dense":
+        W32 = d["W"].astype(np.float32)
+    else:
+        W32 = np.zeros((N, N), np.float32)
+        np.add.at(W32, (np.repeat(np.arange(N), d["col"].shape[1]), d["col"].astype(np.int64).ravel()),
+                  d["val"].astype(np.float32).ravel())
+    Wt = torch.from_numpy(W32.T.copy()).to(dev)
+    X = torch.from_numpy(d["X"]).to(dev)
+    h0 = torch.from_numpy(d["h0"]).to(dev)
+    Hb = torch.empty((T, B, N), dtype=torch.float32, device=dev)
+
+    def gemm_loop(H_):
+        h = h0
+        for t in range(T):
+            torch.addmm(X[t], h, Wt, out=H_[t])
+            H_[t].relu_()
+            h = H_[t]
+
+    def time_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in es:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in es]))
+
+    out = {}
+    per_s = lambda ms: round(T / (ms * 1e-3), 1)
+    mine = per_s(persistent_ms)
+    g_ms = time_ms(lambda: gemm_loop(Hb))
+    out["dense_gemm_eager"] = per_s(g_ms)
+    ref = Hb.clone()
+    try:
+        Hg = torch.empty_like(Hb)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            gemm_loop(Hg)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            gemm_loop(Hg)
+        bad = 0
+        for _ in range(2):
+            Hg.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            bad += int(not torch.equal(Hg, ref))
+            gemm_loop(Hb)
+            torch.cuda.synchronize()
+        out["dense_gemm_graph"] = None if bad else per_s(time_ms(graph.replay))
+        del graph
+    except Exception as e:  # context only: report, do not fail the bench
+        out["dense_gemm_graph"] = None
+        out["dense_gemm_graph_error"] = f"{type(e).__name__}: {str(e)[:120]}"
+    if w.kind == "sparse":
+        try:
+            K = d["col"].shape[1]
+            crow = torch.arange(0, (N + 1) * K, K, dtype=torch.int64, device=dev)[: N + 1]
+            colt = torch.from_numpy(d["col"].astype(np.int64).reshape(-1)).to(dev)
+            valt = torch.from_numpy(d["val"].astype(np.float32).reshape(-1)).to(dev)
+            Wcsr = torch.sparse_csr_tensor(crow, colt, valt, size=(N, N))
+
+            def spmm_loop():
+                h = h0
+                for t in range(T):
+                    y = torch.sparse.mm(Wcsr, h.t().contiguous())
+                    torch.add(X[t], y.t(), out=Hb[t])
+                    Hb[t].relu_()
+                    h = Hb[t]
+            out["sparse_gemm_eager"] = per_s(time_ms(spmm_loop))
+        except Exception as e:
+            out["sparse_gemm_eager"] = None
+            out["sparse_gemm_error"] = f"{type(e).__name__}: {str(e)[:120]}"
+    out["speedup"] = {k: (round(mine / v, 2) if v else None) for k, v in list(out.items())
+                      if k in ("dense_gemm_eager", "dense_gemm_graph", "sparse_gemm_eager")}
+    del Wt, X, h0, Hb, ref
+    return out
+
+
+def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=False, loops=True):
     """Per workload: timesteps/s of a full call, per-step time by the slope
     between T and T/2, the sync floor at the same N, B, T, and the error ratio
     of the timed output against the oracle."""
@@ -312,6 +409,8 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
             "max_err_ratio": err,
             "plan": plan,
         }
+        if loops and not name.endswith("_half_h"):
+            rows[name]["library_loops_timesteps_per_s"] = config_library_loops(torch, dev, w, d, full)
         del g, o, fo
     h.set_math(_b.MATH_AUTO)
     h.close()
@@ -658,7 +757,8 @@ def main():
     # size, error ratio against the oracle (not part of the headline step)
     configs = None
     if not args.no_configs:
-        configs = per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=args.no_check)
+        configs = per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=args.no_check,
+                                   loops=not args.no_config_loops)
 
     detail["trace_us_per_step"] = trace_breakdown(torch, dev, Handle, g, wd, ws, T)
     if not args.no_layers:
