@@ -136,7 +136,10 @@ struct ProjArgs {
   uint32_t x_bytes, u_bytes;
   int tiles_n;        // column tiles of X (set by launch_project)
   int tiles;          // all tiles
-  int per_xcd;        // tiles per XCD (grid = 8 per_xcd workgroups)
+  int per_xcd;        // workgroups per XCD (grid = 8 per_xcd workgroups)
+  int xcd_rows;       // the 8 XCDs as an xcd_rows x (8 / xcd_rows) grid over the tiles
+  int xcd_tile_rows;  // tile rows per XCD row of that grid
+  int xcd_tile_cols;  // tile columns per XCD column of that grid
 };
 // vec: I % 8 == 0 and x, U 16-byte aligned.
 hipError_t launch_project(const ProjArgs& a, bool x_f32, bool vec, hipStream_t stream);

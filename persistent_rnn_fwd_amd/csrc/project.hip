@@ -24,8 +24,8 @@
 // products.  Each wave reads its operands straight in the MFMA layout (lane l: row l % 16, values 8 (l / 16) .. + 7 of the
 // k-step): 8 LDS reads feed 16 products, the 8 hi products first so that no
 // product waits for the one before it.  Workgroup g runs on XCD g % 8, and
-// the tiles are dealt so that each XCD takes a contiguous run of them (the
-// same rows of x).
+// each XCD takes a rectangle of tiles (launch_project), so that its L2 holds
+// the rows of x and U that its tiles share.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -140,11 +140,19 @@ __global__ void __launch_bounds__(256 * kGroups) project_kernel(ProjArgs a) {
   constexpr int kStage = stage_halves<BN>();
   constexpr int TN = BN / 32;  // 16-column MFMA tiles per wave
   __shared__ __attribute__((aligned(16))) _Float16 lds_all[kGroups * 2 * kStage];
+  // Workgroup g runs on XCD g % 8.  The XCDs form an xr x (8 / xr) grid over
+  // the tiles: XCD (i, j) takes tile rows [i Rm, (i + 1) Rm) and tile columns
+  // [j Rn, (j + 1) Rn), so its L2 holds 1 / xr of x and xr / 8 of U (the
+  // split that fetches the fewest bytes, chosen by the host).
   const int g = blockIdx.x;
-  const int tile = (g & 7) * a.per_xcd + (g >> 3);
-  if (tile >= a.tiles) return;  // whole workgroup: the barriers below stay uniform
-  const int tm = tile / a.tiles_n;
-  const int tn = tile - tm * a.tiles_n;
+  const int xcd = g & 7, local = g >> 3;
+  const int xi = xcd / (8 / a.xcd_rows), xj = xcd % (8 / a.xcd_rows);
+  const int lr = local / a.xcd_tile_cols, lc = local - lr * a.xcd_tile_cols;
+  const int tm = xi * a.xcd_tile_rows + lr;
+  const int tn = xj * a.xcd_tile_cols + lc;
+  const int tiles_m = (a.M + kBM - 1) / kBM;
+  // whole workgroups leave: the barriers below stay uniform
+  if (lr >= a.xcd_tile_rows || tm >= tiles_m || lc >= a.xcd_tile_cols || tn >= a.tiles_n) return;
   const int grp = threadIdx.x >> 8;
   const int t = threadIdx.x & 255;  // thread within the group
   _Float16* lds = lds_all + grp * 2 * kStage;
@@ -268,6 +276,11 @@ const void* pick_project(bool x_f32, bool vec) {
 // units idle (fewer than 128 tiles: short sequences, such as one block of a
 // stack; measured at N = I = 1792: 256 rows 27.6 -> 22.4 us, while 1024 rows
 // are faster with the wide tiles, 31.5 vs 34.5 us).
+//
+// XCD grid: the 8 XCDs as xr x (8 / xr) rectangles of tiles (xr = 1, 2, 4, 8),
+// the split for which the eight L2 caches fetch the fewest bytes (each XCD
+// reads the x rows of its tile rows and the U rows of its tile columns);
+// among equal splits, the one with the fewest idle workgroups.
 hipError_t launch_project(const ProjArgs& a, bool x_f32, bool vec, hipStream_t stream) {
   ProjArgs args = a;
   const long long tiles_m = (a.M + kBM - 1) / kBM;
@@ -275,7 +288,22 @@ hipError_t launch_project(const ProjArgs& a, bool x_f32, bool vec, hipStream_t s
   const int bn = narrow ? 64 : 128;
   args.tiles_n = (a.N + bn - 1) / bn;
   args.tiles = static_cast<int>(tiles_m * args.tiles_n);
-  args.per_xcd = (args.tiles + 7) / 8;
+  const double xrow_bytes = (double)kBM * a.I * (x_f32 ? 4.0 : 2.0), ucol_bytes = (double)bn * a.I * 2.0;
+  long long best_groups = -1;
+  double best_bytes = 0.0;
+  for (int xr = 1; xr <= 8; xr *= 2) {
+    const long long rm = (tiles_m + xr - 1) / xr, rn = (args.tiles_n + (8 / xr) - 1) / (8 / xr);
+    const double bytes = 8.0 * ((double)rm * xrow_bytes + (double)rn * ucol_bytes);
+    const long long groups = rm * rn;  // workgroups per XCD
+    if (best_groups < 0 || bytes < best_bytes * 0.999 || (bytes <= best_bytes * 1.001 && groups < best_groups)) {
+      best_groups = groups;
+      best_bytes = bytes;
+      args.xcd_rows = xr;
+      args.xcd_tile_rows = static_cast<int>(rm);
+      args.xcd_tile_cols = static_cast<int>(rn);
+    }
+  }
+  args.per_xcd = static_cast<int>(best_groups);
   const void* fn = narrow ? pick_project<64>(x_f32, vec) : pick_project<128>(x_f32, vec);
   void* kargs[] = {&args};
   return hipLaunchKernel(fn, dim3(8u * (unsigned)args.per_xcd), dim3(256 * kGroups), kargs, 0, stream);
