@@ -418,7 +418,6 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
 
 
 MFMA_F16_PEAK = 2.5e15  # MI355X dense fp16 matrix peak, flop/s
-FP32_NONPACKED_PEAK = 256 * 4 * 16 * 2 * 2.4e9  # non-packed fp32 FMA: 78.6 TFLOP/s
 
 
 def layer_table(torch, dev, Handle, timed, no_check=False):
@@ -790,10 +789,10 @@ def main():
         "peak": FP32_VECTOR_PEAK / 1e12,
         "unit": "TFLOP/s",
         "frac": round(achieved / FP32_VECTOR_PEAK, 5),
-        # the published peak counts packed fp32 FMA (2 per lane); this build issues the
-        # non-packed v_fmac_f32: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz
-        "peak_nonpacked_fp32": FP32_NONPACKED_PEAK / 1e12,
-        "frac_of_nonpacked_peak": round(achieved / FP32_NONPACKED_PEAK, 5),
+        # one XCD per batch row: at B < 8 only B of the 8 XCDs do arithmetic
+        "serving_xcds": min(dom.B, 8),
+        "peak_of_serving_xcds": FP32_VECTOR_PEAK * min(dom.B, 8) / 8 / 1e12,
+        "frac_of_serving_xcds_peak": round(achieved / (FP32_VECTOR_PEAK * min(dom.B, 8) / 8), 5),
         "traffic": traffic,
         "mean_launch_ms": round(dom_ms, 4),
         "flop_per_launch": flop_per_launch,
