@@ -129,6 +129,13 @@ typedef enum {
  *          XCDs compute nothing; they only mark their exchange memory as
  *          written for the call's last steps.  Holds W once per XCD: for
  *          dense fp16 W up to N = 2560, fp32 W up to N = 1792.
+ *          Larger dense fp16 layers ("persistent-rnn", "Important
+ *          Constraints": the layer size is bounded by what stays on chip)
+ *          split each batch row over 2 XCDs (N <= 3584, B <= 4) or 4 XCDs
+ *          (N <= 5120, B <= 2), each holding a part of the rows; the parts
+ *          exchange their rows of h_{t-1} through device-coherent memory
+ *          every step.  EXACT math only (SPLIT and HALF: NOT_SUPPORTED), no
+ *          phase tracing (NOT_SUPPORTED while tracing is on).
  *  AUTO:   TEAM when an instance fits, else SPREAD (the default). */
 typedef enum {
   PRNN_LAYOUT_AUTO = 0,
@@ -178,6 +185,8 @@ typedef struct {
   int math;          /* PRNN_MATH_EXACT, PRNN_MATH_HALF or PRNN_MATH_SPLIT
                         (SPLIT: rows_per_wave and rmax count rows per
                         workgroup)                                            */
+  int xcds_per_row;  /* TEAM: XCDs serving one batch row (1; 2 or 4 for dense
+                        fp16 layers beyond one XCD's registers); SPREAD: 0   */
 } prnnPlanInfo_t;
 
 /* HIP graphs: forward, layer, stack and floor calls may be captured (stream
@@ -365,6 +374,16 @@ prnnStatus_t prnn_set_grid(prnnHandle_t handle, int workgroups);
  * SPREAD layout under LAYOUT_AUTO).  BAD_PARAM for any other value. */
 prnnStatus_t prnn_set_team_waves(prnnHandle_t handle, int waves);
 
+/* XCDs per batch row of dense fp16 layers in the TEAM layout, for later
+ * calls: 0 = automatic (the default: one XCD per batch row where the team
+ * instances hold the layer, else the fewest XCDs of a split that holds it),
+ * 1, 2 or 4 (2: B <= 4, 4: B <= 2; see prnnLayout_t).  A forced width that
+ * the call cannot use makes it return NOT_SUPPORTED (or fall back to the
+ * SPREAD layout under LAYOUT_AUTO).  prnn_sync_floor follows the dense fp16
+ * layer of the same N and B.  fp32 W and sparse layers always use one XCD
+ * per batch row.  BAD_PARAM for any other value. */
+prnnStatus_t prnn_set_xcds_per_row(prnnHandle_t handle, int xcds);
+
 /* Exchange mode for later calls (default AUTO).  A forced RELAY that the
  * plan cannot use makes forward calls return NOT_SUPPORTED.  BAD_PARAM for an
  * unknown mode. */
@@ -432,10 +451,12 @@ prnnStatus_t prnn_debug_jitter(prnnHandle_t handle, uint32_t seed, int span);
 /* For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.
  * The operation, argument meanings, layouts, ownership and argument errors of
- * prnn_forward_dense with its default options (TEAM layout, EXACT math), but
- * no handle: the exchange ring lives in a fixed array in the library's device
- * memory (16 * PRNN_NOALLOC_MAX_N words + 256 bytes, about 160 KiB), one copy
- * per device, held until the process ends.  No call allocates anything.
+ * prnn_forward_dense with its default options (TEAM layout, EXACT math, the
+ * automatic XCDs per batch row), but no handle: the exchange ring lives in a
+ * fixed array in the library's device memory (32 * PRNN_NOALLOC_MAX_N words +
+ * 256 bytes, about 320 KiB: the team ring and, for dense fp16 layers split
+ * over several XCDs per batch row, their shared ring), one copy per device,
+ * held until the process ends.  No call allocates anything.
  *  - N > PRNN_NOALLOC_MAX_N returns NOT_SUPPORTED (the array's capacity), as
  *    do shapes the TEAM layout cannot take (fp32 W beyond N = 1792).
  *  - status: NULL, or one caller-owned device word (4-byte aligned).  The call
@@ -443,9 +464,9 @@ prnnStatus_t prnn_debug_jitter(prnnHandle_t handle, uint32_t seed, int span);
  *    expired) sets it nonzero and leaves H undefined.  Read it once the
  *    stream's work has finished.  With NULL, failures are not reported (every
  *    kernel still exits).
- *  - Every call resets the array on `stream` (two small fill kernels, no
- *    memset, so calls can be captured into a graph) and counts its steps
- *    from 0.
+ *  - Every call resets the array on `stream` (two or three small fill
+ *    kernels, no memset, so calls can be captured into a graph) and counts
+ *    its steps from 0.
  *  - Every call on a device shares that device's array and leaves it as its
  *    run left it: calls that overlap in time on one device (on different
  *    streams, or graph replays running at once) race and give wrong results.

@@ -45,6 +45,7 @@ SIGNATURES = {
     "prnn_synchronize": (_I, [_H, _P]),
     "prnn_set_grid": (_I, [_H, _I]),
     "prnn_set_team_waves": (_I, [_H, _I]),
+    "prnn_set_xcds_per_row": (_I, [_H, _I]),
     "prnn_set_watchdog_us": (_I, [_H, ctypes.c_uint32]),
     "prnn_set_exchange": (_I, [_H, _I]),
     "prnn_set_layout": (_I, [_H, _I]),
@@ -76,6 +77,7 @@ class PlanInfo(ctypes.Structure):
         ("relay_slice", ctypes.c_int),
         ("first_step", ctypes.c_uint64),
         ("math", ctypes.c_int),
+        ("xcds_per_row", ctypes.c_int),
     ]
 
     def as_dict(self):
@@ -185,6 +187,10 @@ class Handle:
     def set_math(self, mode: int):
         """MATH_AUTO, MATH_EXACT, MATH_SPLIT or MATH_HALF (dense fp16) for later calls."""
         _check("prnn_set_math", self._lib.prnn_set_math(self._h, int(mode)))
+
+    def set_xcds_per_row(self, xcds: int):
+        """XCDs per batch row of dense fp16 layers for later calls: 0 (automatic), 1, 2 or 4."""
+        _check("prnn_set_xcds_per_row", self._lib.prnn_set_xcds_per_row(self._h, int(xcds)))
 
     def set_watchdog_us(self, us: int):
         _check("prnn_set_watchdog_us", self._lib.prnn_set_watchdog_us(self._h, int(us)))

@@ -27,6 +27,8 @@ struct StepArgs {
   int spr;              // sparse: 64-pair slots per row, ceil(K / 64)
   int relay_slice;      // words of a row each workgroup relays (0 = direct mode)
   int w_vec;            // dense: W is 16-byte aligned, so rows of N % 4 == 0 (MFMA: N % 8 == 0) load as vectors
+  int xcds_per_row;     // split team layout: XCDs per batch row (2 or 4; 0 otherwise)
+  int part_rows;        // split team layout: rows per part, a multiple of 256
   uint32_t step0;       // ring step counter at t = 0
   uint32_t ring_bytes;
   uint32_t x_bytes;     // bytes of X (= bytes of H)
@@ -83,6 +85,11 @@ extern const void* kFloorTeamKernel;
 // cap = 8 chunks of 256 columns, one per wave).
 extern const KernelEntry kDenseTeamMfmaKernels[];
 extern const KernelEntry kDenseTeamMfmaTraceKernels[];
+// Dense fp16 layers split over 2 or 4 XCDs per batch row (team_split.hip):
+// rmax = rows per wave, cap = 256-column chunks of the row.  The ring is the
+// team ring [8][2][Npad] followed by a shared ring [8][2][Npad].
+extern const KernelEntry kDenseSplitF16Kernels[];
+extern const void* kFloorSplitKernel;  // the split layout's floor (rows per wave <= 64)
 // Dense fp16 team layout with h_{t-1} rounded to fp16 (rmax = rows per wave,
 // cap = 256-column chunks).
 extern const KernelEntry kDenseTeamHalfKernels[];

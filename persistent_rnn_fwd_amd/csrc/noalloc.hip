@@ -5,7 +5,9 @@
 // array instead of a handle's buffer.
 //
 // The array, `scratch`, holds the ring of the largest layer the call accepts
-// (16 * 2560 words, [8 XCD][2 slots][Npad]) and one internal status word.  Each
+// (32 * 2560 words: [8 XCD][2 slots][Npad], and as much again for the shared
+// ring of a layer split over several XCDs per batch row) and one internal
+// status word: about 320 KiB.  Each
 // device the library runs on holds its own copy of it until the process ends.
 // Host code never uses the array's name as an address: at a device's first
 // call the address of that device's copy is looked up once (with the device
@@ -22,7 +24,7 @@
 namespace {
 
 constexpr int kNoAllocMaxN = PRNN_NOALLOC_MAX_N;
-constexpr size_t kRingWords = 16u * (size_t)kNoAllocMaxN;   // team ring at N = kNoAllocMaxN
+constexpr size_t kRingWords = 32u * (size_t)kNoAllocMaxN;   // team ring + shared ring at N = kNoAllocMaxN
 constexpr size_t kScratchWords = kRingWords + 64;            // + the internal status word (padded)
 constexpr int kMaxDevices = 64;
 

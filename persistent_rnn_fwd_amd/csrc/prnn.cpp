@@ -39,6 +39,7 @@ struct prnnContext {
   int exchange = PRNN_EXCHANGE_AUTO;
   int layout = PRNN_LAYOUT_AUTO;
   int ring_layout = -1;  // layout the ring was last reset for
+  int ring_xp = -1;      // ... and its XCDs per batch row (team layouts)
   int ring_B = -1;
   int ring_Npad = -1;
   bool ring_valid = false;
@@ -49,6 +50,7 @@ struct prnnContext {
   uint64_t relay_next_step = 0;
   int forced_grid = 0;
   int team_waves = 0;  // TEAM layout waves per workgroup: 0 = automatic, 8, 12 or 16
+  int xcds_per_row = 0;  // TEAM layout, dense fp16: XCDs per batch row, 0 = automatic, 1, 2 or 4
   bool log = false;    // PRNN_LOG set (and not "0") when the handle was created: plans to stderr
   // A call was captured into a HIP graph: replays may run at any time, so from
   // then on every call starts from a reset ring (one fill kernel per call).
@@ -95,6 +97,8 @@ struct Plan {
   int spr = 0;               // sparse: 64-pair slots per row
   int relay_slice = 0;       // spread: words each workgroup relays (0 = direct)
   int lds_stride = 0;        // sparse: words per LDS row
+  int xcds_per_row = 1;      // team: XCDs per batch row (2 or 4: split team layout)
+  int part_rows = 0;         // split team layout: rows per part
   const KernelEntry* k = nullptr;
   int lds_bytes = 0;
 };
@@ -110,6 +114,40 @@ const KernelEntry* pick(const KernelEntry* table, int rows, int cap) {
 }
 
 int sparse_lds_stride(int N) { return (N + 1 + 3) & ~3; }
+
+// Split team layout (dense fp16): the instance holding rows of an xp-way part
+// on P workgroups of 8 waves per XCD, or null.  Parts are whole 256-column
+// chunks, ceil(chunks / xp) of them each (the last part takes the rest).
+const KernelEntry* split_instance(int N, int P, int xp, int* part_rows) {
+  const int chunks = (N + 255) / 256;
+  *part_rows = 256 * ((chunks + xp - 1) / xp);
+  const int Q = P * 8;
+  return pick(prnn::kDenseSplitF16Kernels, (std::min(*part_rows, N) + Q - 1) / Q, chunks);
+}
+
+// XCDs per batch row of a dense fp16 layer in the team layout: 1 (the whole
+// row on one XCD), or 2 / 4 (split: B <= 4 / B <= 2), or 0 when no form fits.
+// A forced value (prnn_set_xcds_per_row) is taken as it is.  Automatically:
+// one XCD up to N = 1792, where every row of a wave stays widened to fp32;
+// beyond that a split, whose exchange costs 0.4-0.9 us per step more but whose
+// waves hold fewer rows, all or mostly widened.  Measured (B = 4 / B = 2, us
+// per step, 1 / 2 / 4 XCDs): N = 1792 1.29 / 1.55 / 1.85; N = 2048 1.81 / 1.50
+// / 1.62; N = 2304 2.45 / 2.09 / 1.81; N = 2560 2.87 / 2.08 / 2.00; N = 3072
+// - / 2.69 / 2.23.  So four XCDs where B <= 2 and N > 2048, else two.
+int choose_xcds_per_row(const prnnContext* h, int N, int B, int P, bool single_fits) {
+  int part_rows = 0;
+  auto split_ok = [&](int xp) {
+    return !h->trace && h->math != PRNN_MATH_SPLIT && h->math != PRNN_MATH_HALF && B <= 8 / xp &&
+           split_instance(N, P, xp, &part_rows) != nullptr;
+  };
+  if (h->xcds_per_row == 1) return single_fits ? 1 : 0;
+  if (h->xcds_per_row > 1) return split_ok(h->xcds_per_row) ? h->xcds_per_row : 0;
+  if (single_fits && N <= 1792) return 1;
+  if (N > 2048 && split_ok(4)) return 4;
+  if (split_ok(2)) return 2;
+  if (split_ok(4)) return 4;
+  return single_fits ? 1 : 0;
+}
 
 // Spread layout: up to one workgroup per compute unit, each batch group of
 // four batch rows on its own set of workgroups, one wave per batch row.
@@ -175,6 +213,29 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
   // (16), 1.82 (12); 5 % at N = 5760 3.44 -> 2.89 (12); 10 % at N = 2304
   // 1.70 -> 1.48 (12).  At 7 rows per wave (N = 1792) more waves were slower.
   const int rows8 = (N + 8 * P - 1) / (8 * P);
+  // The floor of a dense fp16 layer that runs split over several XCDs per
+  // batch row is the split layout's protocol (8-wave workgroups).
+  if (kind == kFloor && h->team_waves == 0) {
+    const int chunks = (N + 255) / 256;
+    const int xp = choose_xcds_per_row(h, N, B, P, pick(prnn::kDenseTeamF16Kernels, rows8, chunks) != nullptr);
+    if (xp > 1) {
+      static const KernelEntry floor_split = {0, 64, 1 << 30, nullptr};  // the caller substitutes the kernel
+      int part_rows = 0;
+      (void)split_instance(N, P, xp, &part_rows);
+      p->G = P;
+      p->grid = 8 * P;
+      p->waves = 8;
+      p->block = 512;
+      p->chunks = chunks;
+      p->xcds_per_row = xp;
+      p->part_rows = part_rows;
+      p->max_rows = (std::min(part_rows, N) + 8 * P - 1) / (8 * P);
+      p->base_rows = p->extra_rows = 0;
+      p->k = &floor_split;
+      p->lds_bytes = 2 * ((N + 3) & ~3) * 4;
+      return p->max_rows <= 64 && (size_t)p->lds_bytes + 256 <= h->lds_per_block;
+    }
+  }
   const bool wide_ok = (kind == kSparse && wt == prnn::kF16) || kind == kFloor;
   if (h->team_waves > 8 && !wide_ok) return false;
   auto set_waves = [&](int W) {
@@ -217,7 +278,19 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
   } else if (kind == kDense) {
     const KernelEntry* table = h->trace ? (wt == prnn::kF32 ? prnn::kDenseTeamF32TraceKernels : prnn::kDenseTeamF16TraceKernels)
                                         : (wt == prnn::kF32 ? prnn::kDenseTeamF32Kernels : prnn::kDenseTeamF16Kernels);
-    p->k = pick(table, p->max_rows, p->chunks);
+    const KernelEntry* single = pick(table, p->max_rows, p->chunks);
+    const int xp = wt == prnn::kF16 ? choose_xcds_per_row(h, N, B, P, single != nullptr) : 1;
+    if (xp == 0) return false;
+    if (xp == 1) {
+      p->k = single;
+    } else {  // (split_instance is not null: choose_xcds_per_row checked it)
+      int part_rows = 0;
+      p->k = split_instance(N, P, xp, &part_rows);
+      p->xcds_per_row = xp;
+      p->part_rows = part_rows;
+      p->max_rows = (std::min(part_rows, N) + 8 * P - 1) / (8 * P);
+      p->base_rows = p->extra_rows = 0;  // per part, derived on the device
+    }
     if (p->k == nullptr) return false;
     p->lds_bytes = 2 * 256 * p->k->cap * 4;  // two rows of every chunk the instance holds
   } else if (kind == kSparse) {
@@ -308,7 +381,8 @@ prnnStatus_t clear_reported_status(prnnContext* h, hipStream_t stream) {
 prnnStatus_t ensure_ring(prnnContext* h, const Plan& p, int B, int Npad, hipStream_t stream) {
   const bool team = p.layout == PRNN_LAYOUT_TEAM;
   if (clear_reported_status(h, stream) != PRNN_STATUS_SUCCESS) return PRNN_STATUS_INTERNAL_ERROR;
-  const size_t words = team ? 16ull * (size_t)Npad : 18ull * (size_t)B * (size_t)Npad;
+  // team: [8][2][Npad] (+ the split layout's shared ring, as large)
+  const size_t words = team ? (p.xcds_per_row > 1 ? 32ull : 16ull) * (size_t)Npad : 18ull * (size_t)B * (size_t)Npad;
   if (words * 4ull > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
   // Under stream capture the call becomes a graph node that may be replayed
   // at any time, after any other call: its ring is reset inside the captured
@@ -335,14 +409,17 @@ prnnStatus_t ensure_ring(prnnContext* h, const Plan& p, int B, int Npad, hipStre
     h->ring_valid = false;
   }
   if (!team && p.relay_slice > 0 && h->step != h->relay_next_step) h->ring_valid = false;
-  const bool same = h->ring_layout == p.layout && h->ring_Npad == Npad && (team || h->ring_B == B);
+  const bool same = h->ring_layout == p.layout && h->ring_Npad == Npad && (team || h->ring_B == B) &&
+                    (!team || h->ring_xp == p.xcds_per_row);
   if (!h->ring_valid || !same) {
-    if (team)
+    if (team) {
       prnn::launch_team_fill(h->d_ring, Npad, kRingResetWord, stream);
-    else
+      if (p.xcds_per_row > 1) prnn::launch_fill(h->d_ring + 16ull * Npad, 16ull * Npad, kRingResetWord, stream);
+    } else
       prnn::launch_fill(h->d_ring, words, kRingResetWord, stream);
     if (hipGetLastError() != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
     h->ring_layout = p.layout;
+    h->ring_xp = p.xcds_per_row;
     h->ring_B = B;
     h->ring_Npad = Npad;
     h->ring_valid = true;
@@ -393,6 +470,8 @@ StepArgs base_args(prnnContext* h, int N, int B, int T, const float* X, const fl
   a.chunks = p.chunks;
   a.spr = p.spr;
   a.lds_stride = p.lds_stride;
+  a.xcds_per_row = p.xcds_per_row > 1 ? p.xcds_per_row : 0;
+  a.part_rows = p.part_rows;
   a.ring_bytes = static_cast<uint32_t>(2ull * B * Npad * 4);
   a.x_bytes = static_cast<uint32_t>((size_t)T * B * N * 4);
   return a;
@@ -403,9 +482,10 @@ void log_plan(const prnnContext* h, const char* what, int N, int B, int T, const
   if (!h->log) return;
   static const char* maths[] = {"auto", "exact", "split", "half"};
   std::fprintf(stderr,
-               "prnn: %s N=%d B=%d T=%d layout=%s grid=%d waves/wg=%d rows/wave=%d instance=(%d,%d) lds=%d "
-               "math=%s first_step=%llu\n",
-               what, N, B, T, info.layout == PRNN_LAYOUT_TEAM ? "team" : "spread", info.grid, info.waves_per_wg,
+               "prnn: %s N=%d B=%d T=%d layout=%s xcds/row=%d grid=%d waves/wg=%d rows/wave=%d instance=(%d,%d) "
+               "lds=%d math=%s first_step=%llu\n",
+               what, N, B, T, info.layout == PRNN_LAYOUT_TEAM ? "team" : "spread", info.xcds_per_row, info.grid,
+               info.waves_per_wg,
                info.rows_per_wave, info.rmax, info.chunks, info.lds_bytes,
                info.math >= 0 && info.math <= 3 ? maths[info.math] : "?", (unsigned long long)info.first_step);
 }
@@ -444,6 +524,7 @@ prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream
   info.lds_bytes = p.lds_bytes;
   info.relay_slice = p.relay_slice;
   info.math = p.math;
+  info.xcds_per_row = p.layout == PRNN_LAYOUT_TEAM ? p.xcds_per_row : 0;
   info.first_step = h->step;
   log_plan(h, p.what, a.N, a.B, T, info);
   h->have_plan = true;
@@ -609,9 +690,11 @@ prnnStatus_t prnn::forward_dense_on(const DeviceFacts& dev, uint32_t* ring, uint
   prnnStatus_t st = prepare_dense(&c, N, B, T, w_type, W, X, h0, H, &p, &empty);
   if (st != PRNN_STATUS_SUCCESS || empty) return st;
   const int Npad = (N + 3) & ~3;
-  // every call starts from a reset ring (step 0) and a clear status word
+  // every call starts from a reset ring (step 0) and a clear status word;
+  // `ring` holds [8][2][Npad] words and, for a split plan, as many again
   prnn::launch_fill(status, 1, 0u, stream);
   prnn::launch_team_fill(ring, Npad, kRingResetWord, stream);
+  if (p.xcds_per_row > 1) prnn::launch_fill(ring + 16ull * Npad, 16ull * Npad, kRingResetWord, stream);
   if (hipGetLastError() != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
   StepArgs a = base_args(&c, N, B, T, X, h0, H, p, Npad);
   a.W = W;
@@ -732,6 +815,12 @@ prnnStatus_t prnn_set_grid(prnnHandle_t h, int workgroups) {
 prnnStatus_t prnn_set_team_waves(prnnHandle_t h, int waves) {
   if (h == nullptr || (waves != 0 && waves != 8 && waves != 12 && waves != 16)) return PRNN_STATUS_BAD_PARAM;
   h->team_waves = waves;
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t prnn_set_xcds_per_row(prnnHandle_t h, int xcds) {
+  if (h == nullptr || (xcds != 0 && xcds != 1 && xcds != 2 && xcds != 4)) return PRNN_STATUS_BAD_PARAM;
+  h->xcds_per_row = xcds;
   return PRNN_STATUS_SUCCESS;
 }
 
@@ -1090,7 +1179,11 @@ prnnStatus_t prnn_sync_floor(prnnHandle_t h, int N, int B, int T, float* H, hipS
     floor_team16_trace.fn = prnn::kFloorTeamTraceKernel16;
     floor_team12.fn = prnn::kFloorTeamKernel12;
     floor_team12_trace.fn = prnn::kFloorTeamTraceKernel12;
-    if (p.waves == 16)
+    static KernelEntry floor_split = {0, 64, 1 << 30, nullptr};
+    floor_split.fn = prnn::kFloorSplitKernel;
+    if (p.xcds_per_row > 1)
+      p.k = &floor_split;  // no trace instance: a traced split layer is not planned either
+    else if (p.waves == 16)
       p.k = h->trace ? &floor_team16_trace : &floor_team16;
     else if (p.waves == 12)
       p.k = h->trace ? &floor_team12_trace : &floor_team12;

@@ -133,16 +133,20 @@ LAYOUTS = [binding.LAYOUT_AUTO, binding.LAYOUT_SPREAD]
 @pytest.mark.parametrize("N,B,T", [(2100, 2, 6), (2304, 4, 5), (2304, 1, 7), (2560, 3, 4), (2560, 8, 5)])
 @pytest.mark.parametrize("math", [binding.MATH_EXACT, binding.MATH_HALF])
 def test_dense_fp16_beyond_2048(handle, N, B, T, math):
-    """Dense fp16 layers of 2049 to 2560 neurons in the team layout: 9 or 10
-    rows x 9 or 10 chunks per wave (packed fp16 weights), exact or half-h."""
+    """Dense fp16 layers of 2049 to 2560 neurons in the team layout on one XCD
+    per batch row (forced: automatically exact math splits them over several):
+    9 or 10 rows x 9 or 10 chunks per wave (packed fp16 weights), exact or
+    half-h."""
     w = Workload(f"dense_{N}", "dense", N, B, T, "f16", seed=N + 7, h0="randn")
     d = generate(w)
     handle.set_math(math)
+    handle.set_xcds_per_row(1)
     try:
         H = run(handle, "dense", d)
         p = handle.last_plan()
     finally:
         handle.set_math(binding.MATH_AUTO)
+        handle.set_xcds_per_row(0)
     assert p["layout"] == binding.LAYOUT_TEAM and p["math"] == math and p["rmax"] == p["chunks"] == -(-N // 256), p
     assert_parity(H, reference("dense", d), oracle.TOL_F16, f"N={N} math={math}")
 
@@ -235,13 +239,15 @@ def test_cyclic_shift_bitwise(handle):
         run(handle, "sparse", {"col": col, "val": np.ones((N, 1), np.float32), "X": X, "h0": h0}), ref)
 
 
-@pytest.mark.parametrize("N,wdt", [(1792, np.float16), (2048, np.float16), (2304, np.float16),
-                                   (2560, np.float16), (1792, np.float32), (1000, np.float32)])
-def test_small_integer_weights_bitwise(handle, N, wdt):
+@pytest.mark.parametrize("N,wdt,xcds", [(1792, np.float16, 0), (2048, np.float16, 1), (2304, np.float16, 1),
+                                        (2560, np.float16, 1), (2048, np.float16, 0), (2560, np.float16, 0),
+                                        (1792, np.float32, 0), (1000, np.float32, 0)])
+def test_small_integer_weights_bitwise(handle, N, wdt, xcds):
     """Three +-1 weights per row in random columns and small integer inputs keep
     every partial sum an exact fp32 integer (|h| < 2^13 over six steps), so
     any summation order gives the fp64 result bit for bit: every row of the
-    widened, packed and partly widened team instances is checked exactly."""
+    widened, packed and partly widened team instances (one XCD per batch row,
+    forced beyond N = 1792, or split automatically) is checked exactly."""
     rng = np.random.default_rng(N + 17)
     T, B = 6, 4
     W = np.zeros((N, N), wdt)
@@ -251,8 +257,14 @@ def test_small_integer_weights_bitwise(handle, N, wdt):
     h0 = rng.integers(0, 6, size=(B, N)).astype(np.float32)
     ref = oracle.forward_dense(W, X, h0)
     assert np.abs(ref).max() < 2 ** 13
-    H = run(handle, "dense", {"W": W, "X": X, "h0": h0})
-    assert handle.last_plan()["layout"] == binding.LAYOUT_TEAM, handle.last_plan()
+    handle.set_xcds_per_row(xcds)
+    try:
+        H = run(handle, "dense", {"W": W, "X": X, "h0": h0})
+        p = handle.last_plan()
+    finally:
+        handle.set_xcds_per_row(0)
+    assert p["layout"] == binding.LAYOUT_TEAM, p
+    assert p["xcds_per_row"] == (1 if xcds == 1 or N <= 1792 else 2), p
     np.testing.assert_array_equal(H, ref)
 
 
@@ -761,8 +773,9 @@ def test_log_lines_on_stderr(gpu, capfd, monkeypatch):
             h.synchronize()
     err = capfd.readouterr().err
     assert "prnn: handle on device" in err
-    assert "prnn: recurrence N=5760 B=4 T=4 layout=team grid=256 waves/wg=16 rows/wave=12 instance=(12,1)" in err
-    assert "prnn: floor N=5760 B=4 T=4 layout=team grid=256 waves/wg=16" in err
+    assert ("prnn: recurrence N=5760 B=4 T=4 layout=team xcds/row=1 grid=256 waves/wg=16 rows/wave=12 "
+            "instance=(12,1)") in err
+    assert "prnn: floor N=5760 B=4 T=4 layout=team xcds/row=1 grid=256 waves/wg=16" in err
     assert "prnn: run failed: a wait for h_{t-1} expired (watchdog)" in err
     monkeypatch.delenv("PRNN_LOG")
     with Handle() as h:

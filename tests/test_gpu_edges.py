@@ -52,7 +52,8 @@ PATHS = [
     ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_SPLIT, 0),
     ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_HALF, 0),
     ("dense_f16_n1792", binding.LAYOUT_SPREAD, binding.MATH_EXACT, 0),
-    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_EXACT, 2560),
+    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_EXACT, 2560),        # split over 2 XCDs per row
+    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_EXACT, 2560, 1),     # one XCD, 10 rows x 10 chunks
     ("dense_f32_n256", binding.LAYOUT_TEAM, binding.MATH_AUTO, 0),
     ("dense_f32_n256", binding.LAYOUT_SPREAD, binding.MATH_AUTO, 0),
     ("sparse10_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_AUTO, 0),
@@ -64,12 +65,13 @@ PATHS = [
 
 def path_id(p):
     n = f"-n{p[3]}" if p[3] else ""
-    return f"{p[0]}{n}-{'team' if p[1] == binding.LAYOUT_TEAM else 'spread'}-math{p[2]}"
+    x = f"-xcd{p[4]}" if len(p) > 4 else ""
+    return f"{p[0]}{n}-{'team' if p[1] == binding.LAYOUT_TEAM else 'spread'}-math{p[2]}{x}"
 
 
 @pytest.mark.parametrize("path", PATHS, ids=path_id)
 def test_signed_h0_every_path(gpu, path):
-    name, layout, math, N = path
+    name, layout, math, N, xcds = (*path, 0)[:5]
     w = WORKLOADS[name].with_(T=24, h0="randn", **({"N": N} if N else {}))
     d = generate(w, seed=w.seed + 4000)
     assert (d["h0"] < 0).mean() > 0.4
@@ -77,6 +79,7 @@ def test_signed_h0_every_path(gpu, path):
     with Handle() as h:
         h.set_layout(layout)
         h.set_math(math)
+        h.set_xcds_per_row(xcds)
         if "W" in d:
             H = h.forward_dense(g["W"], g["X"], g["h0"])
         else:

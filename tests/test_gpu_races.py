@@ -47,14 +47,15 @@ def reference(kind, d):
     return oracle.forward_sparse(d["col"], d["val"], d["X"], d["h0"])
 
 
-# (workload, layout, math, N: 0 = the workload's own)
+# (workload, layout, math, N: 0 = the workload's own[, XCDs per batch row: 0 = automatic])
 PATHS = [
     ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_EXACT, 0),
     ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_SPLIT, 0),
     ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_HALF, 0),
     ("dense_f16_n1792", binding.LAYOUT_SPREAD, binding.MATH_EXACT, 0),
-    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_EXACT, 2048),   # partly widened rows
-    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_EXACT, 2560),   # 10 rows x 10 chunks
+    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_EXACT, 2048, 1),   # partly widened rows
+    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_EXACT, 2560, 1),   # 10 rows x 10 chunks
+    ("dense_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_EXACT, 2560),      # split over 2 XCDs per row
     ("dense_f32_n256", binding.LAYOUT_TEAM, binding.MATH_AUTO, 0),
     ("sparse10_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_AUTO, 0),
     ("sparse10_f16_n1792", binding.LAYOUT_SPREAD, binding.MATH_AUTO, 0),
@@ -65,22 +66,24 @@ PATHS = [
 
 def path_id(p):
     n = f"-n{p[3]}" if p[3] else ""
-    return f"{p[0]}{n}-{'team' if p[1] == binding.LAYOUT_TEAM else 'spread'}-math{p[2]}"
+    x = f"-xcd{p[4]}" if len(p) > 4 else ""
+    return f"{p[0]}{n}-{'team' if p[1] == binding.LAYOUT_TEAM else 'spread'}-math{p[2]}{x}"
 
 
-def setup(h, name, layout, math, T, seed, N=0):
+def setup(h, name, layout, math, T, seed, N=0, xcds=0):
     w = WORKLOADS[name].with_(T=T, **({"N": N} if N else {}))
     d = generate(w, seed=seed)
     h.set_layout(layout)
     h.set_math(math)
+    h.set_xcds_per_row(xcds)
     return ("dense" if "W" in d else "sparse"), d, to_dev(d)
 
 
 @pytest.mark.parametrize("path", PATHS, ids=path_id)
 def test_twenty_repeats_bitwise_with_nan_poisoned_outputs(gpu, path):
-    name, layout, math, N = path
+    name, layout, math, N, xcds = (*path, 0)[:5]
     with Handle() as h:
-        kind, d, g = setup(h, name, layout, math, T=40, seed=61, N=N)
+        kind, d, g = setup(h, name, layout, math, T=40, seed=61, N=N, xcds=xcds)
         first = forward(h, kind, g)
         assert not np.isnan(first).any()
         tol = oracle.TOL_F32 if name.startswith("dense_f32") else oracle.TOL_F16
@@ -92,9 +95,9 @@ def test_twenty_repeats_bitwise_with_nan_poisoned_outputs(gpu, path):
 
 @pytest.mark.parametrize("path", PATHS, ids=path_id)
 def test_publish_jitter_leaves_results_bitwise_unchanged(gpu, path):
-    name, layout, math, N = path
+    name, layout, math, N, xcds = (*path, 0)[:5]
     with Handle() as h:
-        kind, d, g = setup(h, name, layout, math, T=48, seed=62, N=N)
+        kind, d, g = setup(h, name, layout, math, T=48, seed=62, N=N, xcds=xcds)
         base = forward(h, kind, g)
         assert not np.isnan(base).any()
         for seed in SEEDS:

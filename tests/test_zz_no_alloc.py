@@ -52,8 +52,11 @@ def test_noalloc_matches_prnn_forward_dense_two_calls(gpu):
         assert r <= 1.0, f"call {i}: error ratio {r:.3g}"
 
 
-def test_noalloc_without_status_and_at_its_capacity(gpu):
-    w = Workload("cap", "dense", binding.NOALLOC_MAX_N, 3, 6, "f16", seed=9, h0="randn")
+@pytest.mark.parametrize("N,B", [(binding.NOALLOC_MAX_N, 3), (2304, 2)])
+def test_noalloc_without_status_and_at_its_capacity(gpu, N, B):
+    """The largest layer the array holds (split over 2 XCDs per batch row by
+    default, like prnn_forward_dense), and a layer split over 4 (B <= 2)."""
+    w = Workload("cap", "dense", N, B, 6, "f16", seed=9, h0="randn")
     d, H_na, H_ref = one_call(w, 9, None)
     np.testing.assert_array_equal(H_na, H_ref)
     assert oracle.tolerance_ratio(H_na, oracle.forward_dense(d["W"], d["X"], d["h0"]), oracle.TOL_F16) <= 1.0
