@@ -515,6 +515,44 @@ def stack_table(torch, dev, Handle, timed, no_check=False):
     return rows
 
 
+def large_dense_table(torch, dev, Handle, timed, no_check=False):
+    """Dense fp16 layers beyond the headline size (T = 256, synthetic W ~
+    N(0, 0.8^2/N), X ~ N(0, 1)): per-step slope between T and T/2, the floor of
+    the same form, the XCDs per batch row the plan takes (split team layout
+    beyond N = 1792), and the error ratio of an 8-step call against the oracle."""
+    from persistent_rnn_fwd_amd.inputs import Workload, generate
+    rows = {}
+    h = Handle()
+    T = 256
+    for N, B in ((2048, 4), (2560, 4), (3072, 4), (3584, 4), (4096, 2), (5120, 2)):
+        w = Workload(f"dense_f16_n{N}_b{B}", "dense", N, B, T, "f16", seed=N + B)
+        d = generate(w)
+        W = torch.from_numpy(d["W"]).to(dev)
+        X = torch.from_numpy(d["X"]).to(dev)
+        o = torch.empty_like(X)
+        full = timed(lambda: h.forward_dense(W, X, out=o))
+        half = timed(lambda: h.forward_dense(W, X[:T // 2], out=o[:T // 2]))
+        plan = h.last_plan()
+        f_full = timed(lambda: h.sync_floor(N, B, T, out=o))
+        f_half = timed(lambda: h.sync_floor(N, B, T // 2, out=o[:T // 2]))
+        step = (full - half) / (T // 2) * 1e3
+        floor = (f_full - f_half) / (T // 2) * 1e3
+        row = {"N": N, "B": B, "T": T, "xcds_per_row": plan["xcds_per_row"], "rows_per_wave": plan["rows_per_wave"],
+               "timesteps_per_s": round(T / (full * 1e-3), 1), "us_per_step_slope": round(step, 3),
+               "floor_us_per_step": round(floor, 3), "vs_floor": round(step / floor, 3),
+               "gflop_per_s": round(2 * B * N * N / (step * 1e-6) / 1e9, 1)}
+        if not no_check:
+            import oracle
+            Hs = h.forward_dense(W, X[:8].contiguous())
+            h.synchronize()
+            row["max_err_ratio"] = round(float(oracle.tolerance_ratio(
+                Hs.cpu().numpy(), oracle.forward_dense(d["W"], d["X"][:8]), oracle.TOL_F16)), 6)
+        rows[w.name] = row
+        del W, X, o
+    h.close()
+    return rows
+
+
 def trace_breakdown(torch, dev, Handle, g, wd, ws, T):
     """Per-phase time per step from one traced call of each headline kernel
     and of the floor (team layout): mean over the waves that serve a batch
@@ -763,6 +801,7 @@ def main():
     if not args.no_layers:
         detail["layers"] = layer_table(torch, dev, Handle, timed, no_check=args.no_check)
         detail["stacks"] = stack_table(torch, dev, Handle, timed, no_check=args.no_check)
+        detail["large_dense"] = large_dense_table(torch, dev, Handle, timed, no_check=args.no_check)
 
     baselines = None
     if not args.no_baselines:
