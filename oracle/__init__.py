@@ -17,6 +17,7 @@ from .rnn import (  # noqa: F401
     forward_dense,
     forward_dense_half_h,
     forward_sparse,
+    forward_sparse_rows,
     sparse_to_dense,
     tolerance_ratio,
 )

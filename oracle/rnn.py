@@ -117,6 +117,39 @@ def forward_sparse(col, val, X, h0=None) -> np.ndarray:
     return H
 
 
+def forward_sparse_rows(col, val, row_len, X, h0=None) -> np.ndarray:
+    """Sparse W whose rows hold different numbers of nonzeros: row i is its
+    first row_len[i] pairs, a[b, i] = X[t, b, i] + sum_{k < row_len[i]}
+    val[i, k] * h[b, col[i, k]].  Pairs at k >= row_len[i] are not part of W
+    and contribute nothing, whatever they hold (values, NaN, columns out of
+    range).  This is the unbalanced sparsity that the pages set against
+    load-balanced pruning ("Sparse Persistent RNNs: Squeezing Large Recurrent
+    Networks On-Chip", table "Measured effects reported in the paper",
+    load-balanced pruning row), stored at the width K of the longest row."""
+    col = np.asarray(col).astype(np.int64)
+    val = _f64(val)
+    X = _f64(X)
+    if col.ndim != 2 or col.shape != val.shape:
+        raise ValueError("col and val must both be [N, K]")
+    N, K = col.shape
+    row_len = np.asarray(row_len).astype(np.int64)
+    if row_len.shape != (N,) or (row_len.size and (row_len.min() < 0 or row_len.max() > K)):
+        raise ValueError("row_len must be [N] with entries in [0, K]")
+    live = np.arange(K)[None, :] < row_len[:, None]            # [N, K]: pair k belongs to row i
+    if live.any() and (col[live].min() < 0 or col[live].max() >= N):
+        raise ValueError("column index out of range")
+    safe_col = np.where(live, col, 0)                           # never index with a pair outside its row
+    T, B, h = _check_xh(X, h0, N)
+    H = np.empty((T, B, N), dtype=np.float64)
+    for t in range(T):
+        with np.errstate(invalid="ignore", over="ignore"):    # products outside the rows are discarded
+            terms = h[:, safe_col] * val[None, :, :]            # [B, N, K]
+        a = X[t] + np.where(live[None, :, :], terms, 0.0).sum(axis=2)
+        h = np.maximum(a, 0.0)
+        H[t] = h
+    return H
+
+
 def sparse_to_dense(col, val, N: Optional[int] = None) -> np.ndarray:
     """The dense fp64 matrix a row-balanced (col, val) pair stands for.
 

@@ -28,8 +28,10 @@ unbalanced pruning comparison: a dense Gaussian matrix whose rows carry
 log-normal scales exp(N(0, 0.1^2)) is pruned by keeping the N K largest
 magnitudes of the whole matrix, so rows keep different numbers of entries
 (K on average); each row's kept values are rescaled to L2 norm 0.8 and the
-rows are stored in the row-balanced format at the width of the longest row,
-padded with distinct unused columns of value 0.
+rows are stored in the row-balanced format at the width of the longest row:
+each row's kept entries first (sorted by column), then padding on distinct
+unused columns (sorted) with value 0, and ``row_len`` [N] int32 gives the
+number of kept entries of each row.
 
 Layers (input projection + recurrence, "Optimizing Performance of Recurrent
 Neural Networks on GPUs", Abstract): on top of a recurrence workload, the
@@ -133,7 +135,8 @@ def draw_sparse_pattern(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
 
 def draw_magnitude_pruned(rng: np.random.Generator, N: int, K: int, wdt, sigma: float = 0.1):
     """Unbalanced sparse W (see the module docstring), stored row-balanced at
-    the width of the longest row: returns (col int16 [N, Kmax], val [N, Kmax])."""
+    the width of the longest row: returns (col int16 [N, Kmax], val [N, Kmax],
+    row_len int32 [N]), each row's kept entries first."""
     if not 1 <= K <= N or N > 32767:
         raise ValueError("need 1 <= K <= N <= 32767")
     scale = np.exp(rng.normal(0.0, sigma, size=N))
@@ -146,16 +149,15 @@ def draw_magnitude_pruned(rng: np.random.Generator, N: int, K: int, wdt, sigma: 
     kmax = int(keep.sum(axis=1).max())
     col = np.empty((N, kmax), dtype=np.int16)
     val = np.zeros((N, kmax), dtype=np.float64)
+    row_len = keep.sum(axis=1).astype(np.int32)
     for i in range(N):
-        real = np.flatnonzero(keep[i])
+        real = np.flatnonzero(keep[i])                       # sorted
         v = g[i, real]
         v = v * (0.8 / np.sqrt(np.sum(v * v)))
-        pad = np.flatnonzero(~keep[i])[: kmax - real.size]   # distinct unused columns, value 0
-        c = np.concatenate([real, pad])
-        order = np.argsort(c)
-        col[i] = c[order]
-        val[i] = np.concatenate([v, np.zeros(pad.size)])[order]
-    return col, val.astype(wdt)
+        pad = np.flatnonzero(~keep[i])[: kmax - real.size]   # distinct unused columns, value 0, sorted
+        col[i] = np.concatenate([real, pad])
+        val[i, : real.size] = v
+    return col, val.astype(wdt), row_len
 
 
 def generate(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
@@ -163,7 +165,8 @@ def generate(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
 
     Returns a dict with host numpy arrays:
       dense : ``W`` [N, N] (float32 or float16), row i = output neuron i
-      sparse: ``col`` int16 [N, K], ``val`` [N, K] (float32 or float16)
+      sparse: ``col`` int16 [N, K], ``val`` [N, K] (float32 or float16);
+              unbalanced rows also ``row_len`` int32 [N] (entries per row)
       both  : ``X`` float32 [T, B, N], ``h0`` float32 [B, N]
     """
     seed = w.seed if seed is None else seed
@@ -174,7 +177,7 @@ def generate(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
     if w.kind == "dense":
         out["W"] = (rng_w.standard_normal((w.N, w.N)) * (0.8 / np.sqrt(w.N))).astype(wdt)
     elif w.kind == "sparse" and w.rows == "magnitude":
-        out["col"], out["val"] = draw_magnitude_pruned(rng_w, w.N, w.K, wdt)
+        out["col"], out["val"], out["row_len"] = draw_magnitude_pruned(rng_w, w.N, w.K, wdt)
     elif w.kind == "sparse":
         out["col"] = draw_sparse_pattern(rng_w, w.N, w.K)
         out["val"] = (rng_w.standard_normal((w.N, w.K)) * (0.8 / np.sqrt(w.K))).astype(wdt)

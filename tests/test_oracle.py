@@ -120,6 +120,101 @@ def test_brute_force_sparse_exact(seed):
     np.testing.assert_array_equal(H, np.array(ref, dtype=np.float64))
 
 
+def _brute_sparse_rows(col, val, row_len, X, h0):
+    """Rows of unequal length in exact rationals: row i sums its first
+    row_len[i] pairs and nothing else."""
+    T, B, N = len(X), len(X[0]), len(col)
+    h = [[Fraction(v) for v in row] for row in h0]
+    out = []
+    for t in range(T):
+        new = []
+        for b in range(B):
+            row = []
+            for i in range(N):
+                s = Fraction(X[t][b][i])
+                for k in range(row_len[i]):
+                    s += Fraction(val[i][k]) * h[b][col[i][k]]
+                row.append(s if s > 0 else Fraction(0))
+            new.append(row)
+        out.append(new)
+        h = new
+    return out
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_brute_force_sparse_rows_exact(seed):
+    """Lengths 0..K per row, and pairs past each row's length holding values
+    and columns (some out of range) that must not count."""
+    rng = np.random.default_rng(300 + seed)
+    N = int(rng.integers(1, 6))
+    K = int(rng.integers(1, N + 1))
+    B = int(rng.integers(1, 3))
+    T = int(rng.integers(1, 4))
+    col = np.stack([rng.choice(N, K, replace=False) for _ in range(N)])
+    val = rng.integers(-3, 4, size=(N, K)) / 2.0
+    row_len = rng.integers(0, K + 1, size=N)
+    for i in range(N):                                       # garbage past the row
+        col[i, row_len[i]:] = rng.integers(-3, N + 4, size=K - row_len[i])
+        val[i, row_len[i]:] = rng.integers(5, 9, size=K - row_len[i])
+    X = rng.integers(-3, 4, size=(T, B, N)) / 4.0
+    h0 = rng.integers(-2, 4, size=(B, N)) / 2.0
+    ref = _brute_sparse_rows(col.tolist(), val.tolist(), row_len.tolist(), X.tolist(), h0.tolist())
+    H = oracle.forward_sparse_rows(col, val, row_len, X, h0)
+    np.testing.assert_array_equal(H, np.array(ref, dtype=np.float64))
+
+
+def test_sparse_rows_full_length_is_row_balanced():
+    rng = np.random.default_rng(5)
+    N, K, T, B = 40, 7, 6, 3
+    col = np.stack([rng.choice(N, K, replace=False) for _ in range(N)])
+    val = rng.standard_normal((N, K))
+    X = rng.standard_normal((T, B, N))
+    h0 = rng.standard_normal((B, N))
+    np.testing.assert_array_equal(oracle.forward_sparse_rows(col, val, np.full(N, K), X, h0),
+                                  oracle.forward_sparse(col, val, X, h0))
+
+
+def test_sparse_rows_empty_rows_and_the_dense_copy():
+    """Empty rows give relu(x) whatever h is; the rest equals the dense matrix
+    of the pairs inside each row; NaN and infinities past a row's length never
+    reach H."""
+    rng = np.random.default_rng(6)
+    N, K, T, B = 30, 9, 5, 2
+    col = np.stack([rng.choice(N, K, replace=False) for _ in range(N)])
+    val = rng.standard_normal((N, K)) * 0.3
+    row_len = rng.integers(0, K + 1, size=N)
+    row_len[:4] = 0
+    X = rng.standard_normal((T, B, N))
+    h0 = rng.standard_normal((B, N))
+    Wd = np.zeros((N, N))
+    for i in range(N):
+        for k in range(row_len[i]):
+            Wd[i, col[i, k]] += val[i, k]
+        val[i, row_len[i]:] = np.nan if i % 2 else np.inf
+    H = oracle.forward_sparse_rows(col, val, row_len, X, h0)
+    assert np.isfinite(H).all()
+    np.testing.assert_array_equal(H[:, :, :4], np.maximum(X[:, :, :4], 0.0))
+    np.testing.assert_allclose(H, oracle.forward_dense(Wd, X, h0), rtol=1e-12, atol=1e-12)
+
+
+def test_sparse_rows_rejects_bad_lengths():
+    col = np.zeros((3, 2), np.int64)
+    val = np.zeros((3, 2))
+    X = np.zeros((1, 1, 3))
+    for bad in ([0, 3, 1], [-1, 0, 0], [0, 0]):
+        with pytest.raises(ValueError):
+            oracle.forward_sparse_rows(col, val, np.array(bad), X)
+
+
+def test_generator_unbalanced_rows_in_both_forms():
+    """The unbalanced workload read as rows of unequal length (row_len) and as
+    the padded row-balanced matrix is the same W."""
+    w = WORKLOADS["sparse10u_f16_n2304"].with_(T=3)
+    d = generate(w)
+    np.testing.assert_allclose(oracle.forward_sparse_rows(d["col"], d["val"], d["row_len"], d["X"], d["h0"]),
+                               oracle.forward_sparse(d["col"], d["val"], d["X"], d["h0"]), rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # closed forms
 # ---------------------------------------------------------------------------
@@ -312,15 +407,23 @@ def test_generator_sparse_pattern_and_values():
 
 def test_generator_magnitude_pruned_rows():
     """Unbalanced rows: K kept entries per row on average, stored at the longest
-    row's width with zero-valued padding on distinct unused columns; kept
-    values have row norm 0.8."""
+    row's width, kept entries first (sorted by column) then zero-valued padding
+    on distinct unused columns; row_len counts the kept entries; kept values
+    have row norm 0.8."""
     w = WORKLOADS["sparse10u_f16_n2304"]
     d = generate(w)
-    col, val = d["col"].astype(np.int64), d["val"].astype(np.float64)
+    col, val, row_len = d["col"].astype(np.int64), d["val"].astype(np.float64), d["row_len"]
     N = w.N
     assert col.shape == val.shape and col.shape[0] == N and col.shape[1] > w.K
-    assert (np.diff(col, axis=1) > 0).all() and col.min() >= 0 and col.max() < N
+    assert row_len.dtype == np.int32 and row_len.shape == (N,) and row_len.max() == col.shape[1]
+    assert col.min() >= 0 and col.max() < N
+    for i in range(0, N, 97):
+        L = row_len[i]
+        assert len(set(col[i].tolist())) == col.shape[1]                 # distinct
+        assert (np.diff(col[i, :L]) > 0).all() and (np.diff(col[i, L:]) > 0).all()
+        assert not val[i, L:].any()
     kept = (val != 0).sum(axis=1)
+    assert (kept <= row_len).all() and (row_len - kept).max() <= 2     # fp16 zeros of tiny values aside
     assert abs(kept.mean() - w.K) < 0.01 * w.K          # fp16 zeros of tiny values aside
     assert kept.max() == col.shape[1] or kept.max() >= 0.98 * col.shape[1]
     assert kept.max() > 1.3 * w.K                        # rows really are unbalanced
