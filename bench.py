@@ -44,7 +44,7 @@ HBM_PEAK = 8.0e12             # MI355X HBM3E, bytes/s
 COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_rnn_fwd_n1792.json")
 KERNEL_SOURCES = ["device_common.h", "kernels.h", "dense_kernel.h", "sparse_kernel.h", "team_kernel.h", "team_mfma.h",
                   "dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip", "team_f16.hip", "team_f32.hip",
-                  "team_half.hip", "team_split.hip", "project.hip", "stack.hip", "noalloc.hip", "host_internal.h"]
+                  "team_half.hip", "team_split.hip", "team_rows.hip", "project.hip", "stack.hip", "noalloc.hip", "host_internal.h"]
 
 
 def kernel_source_hash() -> str:
@@ -357,11 +357,13 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
     rows = {}
     h = Handle()
     # every workload in the default math, then the dense fp16 layers again with
-    # h_{t-1} staged as fp16 (the opt-in half-h math)
-    cases = [(name, w, _b.MATH_AUTO) for name, w in WORKLOADS.items()]
-    cases += [(name + "_half_h", w, _b.MATH_HALF) for name, w in WORKLOADS.items()
+    # h_{t-1} staged as fp16 (the opt-in half-h math), and the layers of
+    # unbalanced rows again as rows of unequal length (prnn_forward_sparse_rows)
+    cases = [(name, w, _b.MATH_AUTO, False) for name, w in WORKLOADS.items()]
+    cases += [(name + "_half_h", w, _b.MATH_HALF, False) for name, w in WORKLOADS.items()
               if w.kind == "dense" and w.w_dtype == "f16"]
-    for name, w, math in cases:
+    cases += [(name + "_rows", w, _b.MATH_AUTO, True) for name, w in WORKLOADS.items() if w.rows == "magnitude"]
+    for name, w, math, ragged in cases:
         h.set_math(math)
         d = generate(w)
         g = {k: torch.from_numpy(v).to(dev) for k, v in d.items()}
@@ -371,6 +373,8 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
         def call(t=T):
             if w.kind == "dense":
                 h.forward_dense(g["W"], g["X"][:t], g["h0"], out=o[:t])
+            elif ragged:
+                h.forward_sparse_rows(g["col"], g["val"], g["row_len"], g["X"][:t], g["h0"], out=o[:t])
             else:
                 h.forward_sparse(g["col"], g["val"], g["X"][:t], g["h0"], out=o[:t])
         full = timed(call)
@@ -392,6 +396,7 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
             call()
             h.synchronize()
             ref = (oracle.forward_dense(d["W"], d["X"], d["h0"]) if w.kind == "dense"
+                   else oracle.forward_sparse_rows(d["col"], d["val"], d["row_len"], d["X"], d["h0"]) if ragged
                    else oracle.forward_sparse(d["col"], d["val"], d["X"], d["h0"]))
             tol = oracle.TOL_F32 if w.w_dtype == "f32" else oracle.TOL_F16
             err = round(float(oracle.tolerance_ratio(o.cpu().numpy(), ref, tol)), 5)
@@ -409,7 +414,7 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
             "max_err_ratio": err,
             "plan": plan,
         }
-        if loops and not name.endswith("_half_h"):
+        if loops and not name.endswith(("_half_h", "_rows")):
             rows[name]["library_loops_timesteps_per_s"] = config_library_loops(torch, dev, w, d, full)
         del g, o, fo
     h.set_math(_b.MATH_AUTO)

@@ -238,6 +238,24 @@ prnnStatus_t prnn_forward_sparse(prnnHandle_t handle, int N, int B, int T, int K
                                  const float* X, const float* h0, float* H,
                                  hipStream_t stream);
 
+/* Sparse W whose rows hold different numbers of nonzeros ("Sparse Persistent
+ * RNNs: Squeezing Large Recurrent Networks On-Chip", table "Measured effects
+ * reported in the paper", load-balanced pruning row: unbalanced pruning).
+ * col and val are [N][K] as for prnn_forward_sparse, K the width of the
+ * longest row; row i is its first row_len[i] pairs (row_len: int32 [N],
+ * device memory, 4-byte aligned, read by the call on `stream`; lengths below
+ * 0 count as 0 and above K as K).  Pairs past a row's length are never used,
+ * whatever they hold.  Columns as for prnn_forward_sparse.  The rows are dealt
+ * to the waves by length, so a step costs the pairs that are there rather than
+ * N times the longest row.  TEAM layout, fp16 values, K <= 1024 (else
+ * NOT_SUPPORTED); a small ordering kernel runs before the recurrence (the
+ * handle keeps an [N] int32 buffer for it, grown outside stream capture).
+ * BAD_PARAM: as for prnn_forward_sparse, plus a NULL or misaligned row_len. */
+prnnStatus_t prnn_forward_sparse_rows(prnnHandle_t handle, int N, int B, int T, int K,
+                                      const int16_t* col, prnnDataType_t val_type, const void* val,
+                                      const int32_t* row_len, const float* X, const float* h0, float* H,
+                                      hipStream_t stream);
+
 /* Input projection of a layer ("Optimizing Performance of Recurrent Neural
  * Networks on GPUs", Abstract, single-layer stage: the input-side product of
  * every timestep is independent of the state, so a whole sequence's is one

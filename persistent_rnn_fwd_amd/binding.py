@@ -41,6 +41,7 @@ SIGNATURES = {
     "prnn_destroy": (_I, [_H]),
     "prnn_forward_dense": (_I, [_H, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "prnn_forward_sparse": (_I, [_H, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
+    "prnn_forward_sparse_rows": (_I, [_H, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P]),
     "prnn_sync_floor": (_I, [_H, _I, _I, _I, _P, _P]),
     "prnn_synchronize": (_I, [_H, _P]),
     "prnn_set_grid": (_I, [_H, _I]),
@@ -265,6 +266,30 @@ class Handle:
                                            X.data_ptr(), h0.data_ptr() if h0 is not None else None,
                                            out.data_ptr(), _stream_ptr(stream))
         _check("prnn_forward_sparse", st)
+        return out
+
+    def forward_sparse_rows(self, col: torch.Tensor, val: torch.Tensor, row_len: torch.Tensor, X: torch.Tensor,
+                            h0: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+        """Sparse W with rows of unequal length: col int16 [N, K], val fp16 [N, K],
+        row_len int32 [N] (row i is its first row_len[i] pairs)."""
+        T, B, N = X.shape
+        K = col.shape[1] if col.dim() == 2 else -1
+        _need(col, "col", (torch.int16,), (N, K))
+        _need(val, "val", (torch.float32, torch.float16), (N, K))
+        _need(row_len, "row_len", (torch.int32,), (N,))
+        _need(X, "X", (torch.float32,), (T, B, N))
+        if h0 is not None:
+            _need(h0, "h0", (torch.float32,), (B, N))
+        if out is None:
+            out = torch.empty((T, B, N), dtype=torch.float32, device=X.device)
+        _need(out, "out", (torch.float32,), (T, B, N))
+        vt = DATA_FLOAT if val.dtype == torch.float32 else DATA_HALF
+        st = self._lib.prnn_forward_sparse_rows(self._h, N, B, T, K, col.data_ptr(), vt, val.data_ptr(),
+                                                row_len.data_ptr(), X.data_ptr(),
+                                                h0.data_ptr() if h0 is not None else None, out.data_ptr(),
+                                                _stream_ptr(stream))
+        _check("prnn_forward_sparse_rows", st)
         return out
 
     # -- the input projection and whole layers ------------------------------

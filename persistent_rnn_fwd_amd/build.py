@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libprnn.so")
 RESOURCES = os.path.join(BUILD, "kernel_resources.json")  # per-kernel registers, scratch, LDS, occupancy
 SOURCES = ["dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip", "team_f16.hip", "team_f32.hip", "team_half.hip",
-           "team_split.hip", "project.hip", "stack.hip", "noalloc.hip", "prnn.cpp"]
+           "team_split.hip", "team_rows.hip", "project.hip", "stack.hip", "noalloc.hip", "prnn.cpp"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.
 FLAGS = [

@@ -28,6 +28,8 @@ struct StepArgs {
   int relay_slice;      // words of a row each workgroup relays (0 = direct mode)
   int w_vec;            // dense: W is 16-byte aligned, so rows of N % 4 == 0 (MFMA: N % 8 == 0) load as vectors
   int xcds_per_row;     // split team layout: XCDs per batch row (2 or 4; 0 otherwise)
+  const int32_t* row_len;  // sparse rows of unequal length: pairs of each row ([N], clamped to [0, K])
+  const int32_t* sorted;   // ... and the rows by slot count, most first ([N], sort_rows_kernel)
   int part_rows;        // split team layout: rows per part, a multiple of 256
   uint32_t step0;       // ring step counter at t = 0
   uint32_t ring_bytes;
@@ -71,6 +73,13 @@ extern const KernelEntry kSparseTeamF32Kernels[];
 extern const KernelEntry kSparseTeamF16Kernels16[];
 extern const KernelEntry kSparseTeamF16Kernels12[];   // 12-wave workgroups (3 waves per SIMD)
 extern const KernelEntry kSparseTeamF16TraceKernels16[];
+// Sparse fp16 rows of unequal length (team layout; 8- and 12-wave workgroups).
+extern const KernelEntry kSparseRowsF16Kernels[];
+extern const KernelEntry kSparseRowsF16Kernels12[];
+constexpr int kSparseRowsMaxK = 1024;  // longest row: 16 slots of 64 pairs
+// Orders the rows of a sparse layer of unequal rows by slot count (most
+// first; equal counts in row order) into sorted[N].  One workgroup.
+void launch_sort_rows(const int32_t* row_len, int n, int k, int32_t* sorted, hipStream_t stream);
 
 // Fills n words with v (grid-stride).
 void launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t stream);

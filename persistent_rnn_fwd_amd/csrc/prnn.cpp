@@ -67,6 +67,9 @@ struct prnnContext {
   // Phase tracing: [grid][waves per workgroup][kTraceWords] of the last traced call.
   bool trace = false;
   uint64_t* d_trace = nullptr;
+  // Sparse rows of unequal length: the rows ordered by slot count, [N].
+  int32_t* d_sorted = nullptr;
+  size_t sorted_cap = 0;
   int trace_records = 0;  // records written by the last traced call (0: none)
 };
 
@@ -75,7 +78,7 @@ namespace {
 constexpr uint32_t kRingResetWord = 0xFFFFFFFFu;  // tag 1 = "written at step -2 / -1"
 constexpr int kTeamMaxWgPerXcd = 32;
 
-enum Kind { kDense, kSparse, kFloor };
+enum Kind { kDense, kSparse, kFloor, kSparseRows };  // kSparseRows: rows of unequal length
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -236,7 +239,7 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
       return p->max_rows <= 64 && (size_t)p->lds_bytes + 256 <= h->lds_per_block;
     }
   }
-  const bool wide_ok = (kind == kSparse && wt == prnn::kF16) || kind == kFloor;
+  const bool wide_ok = ((kind == kSparse || kind == kSparseRows) && wt == prnn::kF16) || kind == kFloor;
   if (h->team_waves > 8 && !wide_ok) return false;
   auto set_waves = [&](int W) {
     const int Q = P * W;  // waves per team
@@ -293,6 +296,20 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
     }
     if (p->k == nullptr) return false;
     p->lds_bytes = 2 * 256 * p->k->cap * 4;  // two rows of every chunk the instance holds
+  } else if (kind == kSparseRows) {
+    // rows of unequal length: fp16 values, 12-wave workgroups where a 16-wave
+    // one would be taken for row-balanced layers, else 8
+    if (wt != prnn::kF16 || h->trace || h->team_waves == 16) return false;
+    p->spr = (K + 63) / 64;
+    if (W == 16) set_waves(W = 12);
+    if (W == 12) {
+      p->k = pick(prnn::kSparseRowsF16Kernels12, p->max_rows, p->spr);
+      if (p->k == nullptr && h->team_waves == 12) return false;
+      if (p->k == nullptr) set_waves(W = 8);
+    }
+    if (W == 8) p->k = pick(prnn::kSparseRowsF16Kernels, p->max_rows, p->spr);
+    p->lds_stride = sparse_lds_stride(N);
+    p->lds_bytes = 2 * p->lds_stride * 4;
   } else if (kind == kSparse) {
     p->spr = (K + 63) / 64;
     const KernelEntry* table = h->trace ? (wt == prnn::kF32 ? prnn::kSparseTeamF32TraceKernels : prnn::kSparseTeamF16TraceKernels)
@@ -322,7 +339,7 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
   if (p->k == nullptr) return false;
   // static LDS of the team kernels: flags, and for sparse the per-wave pair
   // placement scratch (waves x 64 x slots x 8 bytes)
-  const size_t static_lds = 256 + (kind == kSparse ? (size_t)W * 64 * p->k->cap * 8 : 0);
+  const size_t static_lds = 256 + (kind == kSparse || kind == kSparseRows ? (size_t)W * 64 * p->k->cap * 8 : 0);
   return (size_t)p->lds_bytes + static_lds <= h->lds_per_block;
 }
 
@@ -333,8 +350,9 @@ bool plan(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Plan* p)
       *p = t;
       return true;
     }
-    if (h->layout == PRNN_LAYOUT_TEAM) return false;
+    if (h->layout == PRNN_LAYOUT_TEAM || kind == kSparseRows) return false;
   }
+  if (kind == kSparseRows) return false;  // the team layout only
   // the matrix-core and half-h forms exist in the team layout only
   if (kind == kDense && wt == prnn::kF16 && (h->math == PRNN_MATH_SPLIT || h->math == PRNN_MATH_HALF)) return false;
   if (h->trace) return false;  // trace instances exist for the team layout only
@@ -618,6 +636,45 @@ prnnStatus_t run_sparse(prnnContext* h, const Plan& p, int N, int B, int T, int 
   return launch(h, p, a, T, stream);
 }
 
+// The handle's row order buffer for sparse rows of unequal length (grown as
+// needed; never while the stream is being captured).
+prnnStatus_t ensure_sorted(prnnContext* h, int N, hipStream_t stream) {
+  if ((size_t)N <= h->sorted_cap) return PRNN_STATUS_SUCCESS;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+  if (cs != hipStreamCaptureStatusNone) return PRNN_STATUS_NOT_SUPPORTED;
+  if (h->d_sorted != nullptr) {
+    if (hipDeviceSynchronize() != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+    (void)hipFree(h->d_sorted);
+    h->d_sorted = nullptr;
+    h->sorted_cap = 0;
+  }
+  void* mem = nullptr;
+  if (hipMalloc(&mem, (size_t)N * 4) != hipSuccess) return PRNN_STATUS_ALLOC_FAILED;
+  h->d_sorted = static_cast<int32_t*>(mem);
+  h->sorted_cap = (size_t)N;
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t run_sparse_rows(prnnContext* h, const Plan& p, int N, int B, int T, int K, const int16_t* col,
+                             const void* val, const int32_t* row_len, const float* X, const float* h0, float* H,
+                             hipStream_t stream) {
+  prnnStatus_t st = ensure_sorted(h, N, stream);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  const int Npad = (N + 3) & ~3;
+  st = ensure_ring(h, p, B, Npad, stream);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  prnn::launch_sort_rows(row_len, N, K, h->d_sorted, stream);
+  if (hipGetLastError() != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
+  StepArgs a = base_args(h, N, B, T, X, h0, H, p, Npad);
+  a.W = col;
+  a.V = val;
+  a.K = K;
+  a.row_len = row_len;
+  a.sorted = h->d_sorted;
+  return launch(h, p, a, T, stream);
+}
+
 // Argument checks of the input projection; fills the kernel arguments.
 prnnStatus_t prepare_project(prnnContext* h, int M, int N, int I, prnnDataType_t x_type, const void* x,
                              prnnDataType_t u_type, const void* U, const float* bias, float* X, prnn::ProjArgs* a,
@@ -773,6 +830,7 @@ prnnStatus_t prnn_destroy(prnnHandle_t h) {
   if (h->h_status != nullptr && take_failure(h)) st = PRNN_STATUS_EXECUTION_FAILED;
   if (h->d_ring != nullptr) (void)hipFree(h->d_ring);
   if (h->d_trace != nullptr) (void)hipFree(h->d_trace);
+  if (h->d_sorted != nullptr) (void)hipFree(h->d_sorted);
   if (h->d_status != nullptr) (void)hipFree(h->d_status);
   if (h->h_status != nullptr) (void)hipHostFree(const_cast<uint32_t*>(h->h_status));
   delete h;
@@ -899,6 +957,30 @@ prnnStatus_t prnn_forward_sparse(prnnHandle_t h, int N, int B, int T, int K, con
   prnnStatus_t st = prepare_sparse(h, N, B, T, K, col, val_type, val, X, h0, H, &p, &empty);
   if (st != PRNN_STATUS_SUCCESS || empty) return st;
   return run_sparse(h, p, N, B, T, K, col, val, X, h0, H, stream);
+}
+
+prnnStatus_t prnn_forward_sparse_rows(prnnHandle_t h, int N, int B, int T, int K, const int16_t* col,
+                                      prnnDataType_t val_type, const void* val, const int32_t* row_len,
+                                      const float* X, const float* h0, float* H, hipStream_t stream) {
+  if (h != nullptr && take_failure(h)) return PRNN_STATUS_EXECUTION_FAILED;
+  bool empty = false;
+  prnnStatus_t st = check_common(h, N, B, T, X, h0, H, &empty);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  if (val_type != PRNN_DATA_FLOAT && val_type != PRNN_DATA_HALF) return PRNN_STATUS_BAD_PARAM;
+  if (K < 1 || K > N || N > 32767) return PRNN_STATUS_BAD_PARAM;
+  if (empty) return PRNN_STATUS_SUCCESS;
+  if (col == nullptr || val == nullptr || row_len == nullptr) return PRNN_STATUS_BAD_PARAM;
+  if (!aligned(col, 2) || !aligned(val, val_type == PRNN_DATA_FLOAT ? 4 : 2) || !aligned(row_len, 4))
+    return PRNN_STATUS_BAD_PARAM;
+  const size_t hb = (size_t)T * B * N * 4;
+  if (overlap(col, (size_t)N * K * 2, H, hb) ||
+      overlap(val, (size_t)N * K * (val_type == PRNN_DATA_FLOAT ? 4 : 2), H, hb) || overlap(row_len, (size_t)N * 4, H, hb))
+    return PRNN_STATUS_BAD_PARAM;
+  if (hb > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
+  if (val_type != PRNN_DATA_HALF || K > prnn::kSparseRowsMaxK) return PRNN_STATUS_NOT_SUPPORTED;
+  Plan p;
+  if (!plan(h, kSparseRows, N, B, K, prnn::kF16, &p)) return PRNN_STATUS_NOT_SUPPORTED;
+  return run_sparse_rows(h, p, N, B, T, K, col, val, row_len, X, h0, H, stream);
 }
 
 prnnStatus_t prnn_project(prnnHandle_t h, int M, int N, int I, prnnDataType_t x_type, const void* x,

@@ -142,6 +142,26 @@ __device__ __forceinline__ void load_place_rows(P (&pr)[RW][SPR], const int16_t*
   }
 }
 
+// Rows of unequal length: row R of the block is layer row rows[R] with
+// lens[R] pairs in ns[R] = ceil(lens[R] / 64) slots (all wave-uniform); its
+// pairs are placed over those slots only, and slots beyond stay padding.
+template <int R, int RW, typename P, int SPR>
+__device__ __forceinline__ void load_place_rows_ragged(P (&pr)[RW][SPR], const int16_t* col, const void* val,
+                                                       const int (&rows)[RW], const int (&lens)[RW],
+                                                       const int (&ns)[RW], int K, int n, int lane, uint2* scratch) {
+  if constexpr (R < RW) {
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) {
+      const int k = 64 * s + lane;
+      const bool live = k < lens[R];
+      pr[R][s].load(col, val, live ? (size_t)rows[R] * K + k : 0, live, n);
+    }
+    if (ns[R] > 0) place_row_bank_aware<P, SPR>(pr[R], ns[R], lens[R], n, lane, scratch);
+    asm volatile("" ::: "memory");
+    load_place_rows_ragged<R + 1, RW, P, SPR>(pr, col, val, rows, lens, ns, K, n, lane, scratch);
+  }
+}
+
 constexpr int kStageChunks = 8;  // 16-byte loads in flight per lane while staging h
 
 // RMAX rows per workgroup are computed (padding rows carry zero values and

@@ -334,11 +334,55 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
   if (TRACE) clk.finish(trace_record(a, p), a.T);
 }
 
+// Rows [0, C) of slot S: every gather first, so their LDS latencies overlap,
+// then the multiply-adds (the FMA is inline asm, which the compiler does not
+// move loads across).
+template <int C, int S, typename P, int RW, int SPR>
+__device__ __forceinline__ void gather_fma_rows(P (&pr)[RW][SPR], const float* hrow, float (&acc)[pow2_at_least(RW)]) {
+  float hv[C > 0 ? C : 1];
+#pragma unroll
+  for (int r = 0; r < C; ++r) hv[r] = hrow[pr[r][S].column()];
+#pragma unroll
+  for (int r = 0; r < C; ++r) pr[r][S].fma(acc[r], hv[r]);
+}
+
+// Rows of unequal length: slot S of the first c rows (the rows that have it;
+// the wave's rows come longest first), one scalar dispatch per slot.
+template <int C, int S, typename P, int RW, int SPR>
+__device__ __forceinline__ void ragged_slot(P (&pr)[RW][SPR], int c, const float* hrow,
+                                            float (&acc)[pow2_at_least(RW)]) {
+  if constexpr (C > 0) {
+    if (c == C)
+      gather_fma_rows<C, S>(pr, hrow, acc);
+    else
+      ragged_slot<C - 1, S>(pr, c, hrow, acc);
+  }
+}
+template <int S, typename P, int RW, int SPR>
+__device__ __forceinline__ void ragged_slots(P (&pr)[RW][SPR], const int (&cnt)[SPR], const float* hrow,
+                                             float (&acc)[pow2_at_least(RW)]) {
+  if constexpr (S < SPR) {
+    if (cnt[S] == 0) return;  // no row has slot S, nor any later one
+    ragged_slot<RW, S>(pr, cnt[S], hrow, acc);
+    ragged_slots<S + 1>(pr, cnt, hrow, acc);
+  }
+}
+
 // The sparse recurrence in the team layout: the h row is staged once per
 // workgroup (all its waves serve the same batch row) and every wave gathers
 // from it for its own rows.  RW = rows per wave, SPR = 64-pair slots per row,
 // WAVES = waves per workgroup (8; 12 or 16 for layers with many rows per wave).
-template <typename VT, int RW, int SPR, bool TRACE = false, int WAVES = kTeamWaves>
+//
+// RAGGED: rows of unequal length (a.row_len), for the unbalanced sparsity the
+// pages set against load-balanced pruning ("Sparse Persistent RNNs", table
+// "Measured effects reported in the paper", load-balanced pruning row).  The
+// rows are ordered by slot count (a.sorted, most first) and dealt to the
+// team's Q waves in snake order: round r of the deal gives wave q the row at
+// r Q + q for even r and r Q + Q - 1 - q for odd r, so every wave's rows add
+// up to about the same number of slots.  A wave places each row's pairs over
+// that row's own slots and skips the slots it does not have, so a step costs
+// the pairs that are there, not the longest row times the rows.
+template <typename VT, int RW, int SPR, bool TRACE = false, int WAVES = kTeamWaves, bool RAGGED = false>
 __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
   constexpr int M = pow2_at_least(RW);
   extern __shared__ __attribute__((aligned(16))) float lds[];  // [2][lds_stride]: word N of each row stays 0
@@ -361,20 +405,50 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
   // The owned rows' pairs into registers, each row in bank-aware order so
   // that the gathers below hit distinct LDS banks.
   Pair<VT> pr[RW][SPR];
-  load_place_rows<0, RW, Pair<VT>, SPR>(pr, reinterpret_cast<const int16_t*>(a.W), a.V, p.r0, p.nr, a.spr, K, N,
-                                        p.lane, place_scratch[p.wave]);
+  int cnt[SPR];          // RAGGED: rows of the wave that have slot s (wave-uniform)
+  int nr = p.nr;         // rows this wave owns
+  int my_layer_row = 0;  // the layer row whose sum this lane owns
+  const int my_row = RowReduce<M>::owner_row(p.lane);
+  const int Q = a.G * WAVES;  // waves of the team
+  auto snake = [&](int r) { return r * Q + ((r & 1) ? Q - 1 - p.q : p.q); };
+  if constexpr (RAGGED) {
+    int rows[RW], lens[RW], ns[RW];
+    nr = 0;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int idx = snake(r);
+      const int row = idx < N ? a.sorted[idx] : 0;
+      const int len = idx < N ? min(max(a.row_len[row], 0), K) : 0;
+      rows[r] = __builtin_amdgcn_readfirstlane(row);
+      lens[r] = __builtin_amdgcn_readfirstlane(len);
+      ns[r] = (lens[r] + 63) >> 6;
+      if (idx < N) nr = r + 1;
+    }
+    load_place_rows_ragged<0, RW, Pair<VT>, SPR>(pr, reinterpret_cast<const int16_t*>(a.W), a.V, rows, lens, ns, K, N,
+                                                 p.lane, place_scratch[p.wave]);
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) {
+      cnt[s] = 0;
+#pragma unroll
+      for (int r = 0; r < RW; ++r) cnt[s] += ns[r] > s ? 1 : 0;
+    }
+    if (my_row >= 0 && my_row < nr) my_layer_row = a.sorted[snake(my_row)];
+  } else {
+    load_place_rows<0, RW, Pair<VT>, SPR>(pr, reinterpret_cast<const int16_t*>(a.W), a.V, p.r0, p.nr, a.spr, K, N,
+                                          p.lane, place_scratch[p.wave]);
+    my_layer_row = p.r0 + (my_row >= 0 && my_row < p.nr ? my_row : 0);
+  }
 
   const __amdgpu_buffer_rsrc_t region = team_region(a);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
-  const int my_row = RowReduce<M>::owner_row(p.lane);
-  const bool owner = my_row >= 0 && my_row < p.nr;
+  const bool owner = my_row >= 0 && my_row < nr;
   const int jn = a.chunks;
 
   // x of the row this lane owns.  The load for step t + 1 is issued right
   // after step t's staging: the next step's polls, whose waits also drain
   // every earlier load of the wave, then find it long finished.
   const uint32_t xstep = (uint32_t)a.B * (uint32_t)N * 4u;
-  uint32_t xoff = ((uint32_t)p.b * (uint32_t)N + (uint32_t)(p.r0 + (owner ? my_row : 0))) * 4u;
+  uint32_t xoff = ((uint32_t)p.b * (uint32_t)N + (uint32_t)my_layer_row) * 4u;
   float x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
   PhaseClock<TRACE> clk;
   clk.start();
@@ -415,9 +489,10 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
     float acc[M];
 #pragma unroll
     for (int r = 0; r < M; ++r) acc[r] = 0.f;
+    if constexpr (RAGGED) ragged_slots<0>(pr, cnt, hrow, acc);
 #pragma unroll
     for (int s = 0; s < SPR; ++s) {
-      if (s < a.spr) {
+      if (!RAGGED && s < a.spr) {
         // All of the slot's gathers are issued before its first FMA, so
         // their LDS latencies overlap (the FMA is inline asm, which the
         // compiler does not move loads across).
@@ -437,7 +512,7 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
     debug_jitter(a.jitter_seed, a.jitter_span, p.wave, t);
     if (owner && !(p.rank == a.skip_wg && t == a.skip_step)) {
       const uint32_t hb = relu_bits(sum + x);
-      const int row = p.r0 + my_row;
+      const int row = my_layer_row;
       // the exchange store first: the next step waits for it, not for H
       __builtin_amdgcn_raw_buffer_store_b32(hb | tag_bit(S), region, ((S & 1u) * a.Npad + row) * 4u, 0, kPlain);
       a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
@@ -465,6 +540,10 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
   {VTAG, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<VT, R, S, false, 16>), 16}
 #define PRNN_SPARSE_TEAM16_TRACE(VT, VTAG, R, S) \
   {VTAG, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<VT, R, S, true, 16>), 16}
+#define PRNN_SPARSE_ROWS(R, S) \
+  {kF16, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<_Float16, R, S, false, 8, true>)}
+#define PRNN_SPARSE_ROWS12(R, S) \
+  {kF16, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<_Float16, R, S, false, 12, true>), 12}
 #define PRNN_SPARSE_TEAM_TRACE(VT, VTAG, R, S) \
   {VTAG, R, S, reinterpret_cast<const void*>(&sparse_team_kernel<VT, R, S, true>)}
 

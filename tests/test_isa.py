@@ -26,7 +26,10 @@ INSTANCES = {
     "dense_half_7x7": ("dense_team_kernel<_Float16, 7, 7, false, false, true>",
                        "_ZN4prnn17dense_team_kernelIDF16_Li7ELi7ELb0ELb0ELb1EEEvNS_8StepArgsE", 49),
     "sparse_7x3": ("sparse_team_kernel<_Float16, 7, 3, false, 8>",
-                   "_ZN4prnn18sparse_team_kernelIDF16_Li7ELi3ELb0ELi8EEEvNS_8StepArgsE", 0),
+                   "_ZN4prnn18sparse_team_kernelIDF16_Li7ELi3ELb0ELi8ELb0EEEvNS_8StepArgsE", 0),
+    # rows of unequal length (the unbalanced 10 % layer at N = 2304)
+    "sparse_rows_6x10": ("sparse_team_kernel<_Float16, 6, 10, false, 12, true>",
+                         "_ZN4prnn18sparse_team_kernelIDF16_Li6ELi10ELb0ELi12ELb1EEEvNS_8StepArgsE", 0),
 }
 WEIGHT_LOADS = ("global_load_dwordx2", "global_load_ushort", "global_load_short_d16")
 LABEL = re.compile(r"^(\.LBB\w+):")
