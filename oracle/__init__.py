@@ -25,5 +25,6 @@ from .layer import (  # noqa: F401
     forward_layer_dense,
     forward_layer_sparse,
     forward_stack_dense,
+    forward_stack_sparse,
     project,
 )

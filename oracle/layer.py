@@ -74,3 +74,18 @@ def forward_stack_dense(layers: Sequence[dict], x, h0s: Optional[Sequence] = Non
         outs.append(H)
         inp = H
     return outs
+
+
+def forward_stack_sparse(layers: Sequence[dict], x, h0s: Optional[Sequence] = None) -> list:
+    """A stack of row-balanced sparse layers, given as dicts with keys U, bias,
+    col, val (the entire-network stage over the sparse layers of "Sparse
+    Persistent RNNs: Squeezing Large Recurrent Networks On-Chip").  Returns
+    every layer's H, fp64 [T, B, N_l]."""
+    outs = []
+    inp = _f64(x)
+    for l, layer in enumerate(layers):
+        h0 = None if h0s is None else h0s[l]
+        H = forward_layer_sparse(layer["U"], layer.get("bias"), layer["col"], layer["val"], inp, h0)
+        outs.append(H)
+        inp = H
+    return outs

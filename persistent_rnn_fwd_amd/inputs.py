@@ -217,23 +217,29 @@ def generate_layer(w: Workload, I: int, seed: Optional[int] = None, x_dtype: str
 
 
 def generate_stack(w: Workload, L: int, seed: Optional[int] = None) -> Dict[str, object]:
-    """L dense layers of width N = I = w.N: ``layers`` = [{U, bias, W}] (fp16
-    U and W as in ``generate_layer`` and ``generate``), the input ``x`` fp32
-    [T, B, N] and per-layer ``h0s`` (zeros, N(0,1) with w.h0 == "randn", |N(0,1)|
-    with "absrandn")."""
-    if w.kind != "dense":
-        raise ValueError("stacks are dense")
+    """L layers of width N = I = w.N: ``layers`` = [{U, bias, W}] for a dense
+    workload, [{U, bias, col, val}] (row-balanced, K per row) for a sparse one
+    (fp16 U, and W or val, as in ``generate_layer`` and ``generate``), the input
+    ``x`` fp32 [T, B, N] and per-layer ``h0s`` (zeros, N(0,1) with w.h0 ==
+    "randn", |N(0,1)| with "absrandn")."""
+    if w.kind == "sparse" and w.rows != "balanced":
+        raise ValueError("sparse stacks are row-balanced")
     seed = w.seed if seed is None else seed
     base = generate_layer(w, w.N, seed)
     layers, h0s = [], []
     for l in range(L):
         s_u, s_b, s_w = np.random.SeedSequence([seed, 2, l]).spawn(3)
         rng_u, rng_b, rng_w = (np.random.default_rng(t) for t in (s_u, s_b, s_w))
-        layers.append({
+        layer = {
             "U": (rng_u.standard_normal((w.N, w.N)) / np.sqrt(w.N)).astype(np.float16),
             "bias": (0.1 * rng_b.standard_normal(w.N)).astype(np.float32),
-            "W": (rng_w.standard_normal((w.N, w.N)) * (0.8 / np.sqrt(w.N))).astype(_np_dtype(w.w_dtype)),
-        })
+        }
+        if w.kind == "dense":
+            layer["W"] = (rng_w.standard_normal((w.N, w.N)) * (0.8 / np.sqrt(w.N))).astype(_np_dtype(w.w_dtype))
+        else:
+            layer["col"] = draw_sparse_pattern(rng_w, w.N, w.K)
+            layer["val"] = (rng_w.standard_normal((w.N, w.K)) * (0.8 / np.sqrt(w.K))).astype(_np_dtype(w.w_dtype))
+        layers.append(layer)
         if l == 0:
             h0 = base["h0"]
         elif w.h0 in ("randn", "absrandn"):

@@ -119,6 +119,51 @@ def test_stack_of_pass_through_layers():
         np.testing.assert_array_equal(H, np.maximum(x, 0.0))
 
 
+def test_sparse_stack_matches_rational_brute_force():
+    """Two sparse layers (K pairs per row, a repeated column in one row) in
+    exact rationals, each through its dense equivalent."""
+    rng = np.random.default_rng(15)
+    N, K, B, T = 4, 2, 2, 3
+    layers = []
+    for _ in range(2):
+        col = np.stack([rng.choice(N, K, replace=False) for _ in range(N)])
+        col[1] = [2, 2]
+        layers.append({"U": _ints(rng, (N, N), -2, 2), "bias": _ints(rng, (N,)), "col": col,
+                       "val": _ints(rng, (N, K), -1, 1)})
+    x = _ints(rng, (T, B, N))
+    h0s = [_ints(rng, (B, N), -1, 2) for _ in range(2)]
+    inp = x.tolist()
+    refs = []
+    for l, L in enumerate(layers):
+        Wd = [[Fraction(0)] * N for _ in range(N)]
+        for i in range(N):
+            for k in range(K):
+                Wd[i][int(L["col"][i][k])] += Fraction(L["val"][i][k])
+        X = [_brute_project(L["U"].tolist(), inp[t], L["bias"].tolist()) for t in range(T)]
+        H = _brute_recurrence(Wd, X, h0s[l].tolist())
+        refs.append(np.array(H, dtype=np.float64))
+        inp = H
+    got = oracle.forward_stack_sparse(layers, x, h0s)
+    assert len(got) == 2
+    for g, r in zip(got, refs):
+        np.testing.assert_array_equal(g, r)
+
+
+def test_sparse_stack_generator_and_dense_copy():
+    """The sparse stack generator gives each layer its own pattern and values;
+    the sparse stack equals the dense stack of the layers' dense copies."""
+    w = WORKLOADS["sparse10_f16_n1152"].with_(T=3, h0="randn")
+    st = generate_stack(w, 2)
+    L0, L1 = st["layers"]
+    assert L0["col"].shape == (w.N, w.K) and L0["val"].dtype == np.float16 and "W" not in L0
+    assert not np.array_equal(L0["col"], L1["col"])
+    dense = [{"U": L["U"], "bias": L["bias"], "W": oracle.sparse_to_dense(L["col"], L["val"], w.N)}
+             for L in st["layers"]]
+    for a, b in zip(oracle.forward_stack_sparse(st["layers"], st["x"], st["h0s"]),
+                    oracle.forward_stack_dense(dense, st["x"], st["h0s"])):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
 def test_layer_generator_shapes_and_scale():
     name, I = next(iter(LAYER_WORKLOADS.values()))
     w = WORKLOADS[name].with_(T=16)
