@@ -363,6 +363,35 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t handle, int L, int N, int I, 
                                       const void* const* W, const float* const* h0,
                                       float* Xbuf, float* const* H, hipStream_t stream);
 
+/* A stack of L row-balanced sparse layers of width N (the entire-network
+ * stage of "Optimizing Performance of Recurrent Neural Networks on GPUs",
+ * Abstract, over the sparse layers of "Sparse Persistent RNNs: Squeezing
+ * Large Recurrent Networks On-Chip"):
+ *
+ *   H[0]     = layer(x,        U[0], bias[0], col[0], val[0], h0[0])
+ *   H[l]     = layer(H[l - 1], U[l], bias[l], col[l], val[l], h0[l]),  l >= 1
+ *
+ * where layer() is prnn_forward_layer_sparse (projection into Xbuf, then the
+ * recurrence).  The layers run one after another (no wavefront).  x
+ * [T][B][I] (fp32 or fp16); U[0] [N][I], U[l >= 1] [N][N] fp16; col[l] int16
+ * [N][K] and val[l] [N][K] (val_type fp16 or fp32) as for
+ * prnn_forward_sparse; bias[l] [N] or NULL; h0[l] [B][N] or NULL; Xbuf
+ * [T][B][N] fp32 workspace; H[l] [T][B][N] fp32 outputs.  U, bias, col, val,
+ * h0 and H are host arrays of L device pointers (bias and h0 may be NULL
+ * arrays).  All device buffers are the caller's.
+ * BAD_PARAM: NULL handle/arrays/pointers, L < 1, N < 1, I < 1, B outside
+ * [1, 8], T < 0, K outside [1, N], N > 32767, unknown x_type or val_type,
+ * misalignment, any output overlapping any input, the workspace or another
+ * output, the workspace overlapping an input; nothing is enqueued then.
+ * NOT_SUPPORTED: what prnn_forward_layer_sparse does not support.
+ * EXECUTION_FAILED as for the other calls.  T == 0 enqueues nothing. */
+prnnStatus_t prnn_forward_stack_sparse(prnnHandle_t handle, int L, int N, int I, int B, int T, int K,
+                                       prnnDataType_t x_type, const void* x,
+                                       const void* const* U, const float* const* bias,
+                                       const int16_t* const* col, prnnDataType_t val_type,
+                                       const void* const* val, const float* const* h0,
+                                       float* Xbuf, float* const* H, hipStream_t stream);
+
 /* The exchange and step protocol of a dense call with the same N, B and T and
  * the same grid, without weights or arithmetic: the per-step floor that
  * synchronisation alone costs.  Writes H (values are step numbers, not a

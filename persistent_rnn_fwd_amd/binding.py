@@ -61,6 +61,7 @@ SIGNATURES = {
     "prnn_forward_layer_dense": (_I, [_H, _I, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P]),
     "prnn_forward_layer_sparse": (_I, [_H, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
     "prnn_forward_stack_dense": (_I, [_H, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "prnn_forward_stack_sparse": (_I, [_H, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
     "prnn_set_stack_mode": (_I, [_H, _I]),
     "prnn_forward_dense_noalloc": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
 }
@@ -398,6 +399,45 @@ class Handle:
         st = self._lib.prnn_forward_stack_dense(self._h, L, N, I, B, T, xt, x.data_ptr(), Up, bp, Wp, hp,
                                                 workspace.data_ptr(), Hp, _stream_ptr(stream))
         _check("prnn_forward_stack_dense", st)
+        return outs
+
+    def forward_stack_sparse(self, layers, x: torch.Tensor, h0s=None, outs=None,
+                             workspace: Optional[torch.Tensor] = None, stream=None):
+        """A stack of row-balanced sparse layers, one after another.  layers: list
+        of dicts with U (fp16 [N, I] for the first, [N, N] after), bias (fp32
+        [N] or None), col (int16 [N, K]) and val (fp16 or fp32 [N, K], one dtype
+        for all layers); x [T, B, I]; h0s: None or one [B, N] (or None) per
+        layer.  Returns the list of every layer's H [T, B, N]."""
+        L = len(layers)
+        T, B, I = x.shape
+        N, K = layers[0]["col"].shape
+        vdt = layers[0]["val"].dtype
+        _need(x, "x", (torch.float32, torch.float16), (T, B, I))
+        for l, ly in enumerate(layers):
+            _need(ly["U"], f"layers[{l}].U", (torch.float16,), (N, I if l == 0 else N))
+            _need(ly["col"], f"layers[{l}].col", (torch.int16,), (N, K))
+            _need(ly["val"], f"layers[{l}].val", (vdt,), (N, K))
+            if ly.get("bias") is not None:
+                _need(ly["bias"], f"layers[{l}].bias", (torch.float32,), (N,))
+            if h0s is not None and h0s[l] is not None:
+                _need(h0s[l], f"h0s[{l}]", (torch.float32,), (B, N))
+        if workspace is None:
+            workspace = torch.empty((T, B, N), dtype=torch.float32, device=x.device)
+        _need(workspace, "workspace", (torch.float32,), (T, B, N))
+        if outs is None:
+            outs = [torch.empty((T, B, N), dtype=torch.float32, device=x.device) for _ in range(L)]
+        for l, o in enumerate(outs):
+            _need(o, f"outs[{l}]", (torch.float32,), (T, B, N))
+        ptrs = lambda ts: (ctypes.c_void_p * L)(*[(t.data_ptr() if t is not None else None) for t in ts])
+        Up, Cp, Vp, Hp = (ptrs([ly["U"] for ly in layers]), ptrs([ly["col"] for ly in layers]),
+                          ptrs([ly["val"] for ly in layers]), ptrs(outs))
+        bp = ptrs([ly.get("bias") for ly in layers])
+        hp = ptrs(h0s) if h0s is not None else None
+        xt = DATA_FLOAT if x.dtype == torch.float32 else DATA_HALF
+        vt = DATA_FLOAT if vdt == torch.float32 else DATA_HALF
+        st = self._lib.prnn_forward_stack_sparse(self._h, L, N, I, B, T, K, xt, x.data_ptr(), Up, bp, Cp, vt, Vp, hp,
+                                                 workspace.data_ptr(), Hp, _stream_ptr(stream))
+        _check("prnn_forward_stack_sparse", st)
         return outs
 
     def sync_floor(self, N: int, B: int, T: int, out: Optional[torch.Tensor] = None,

@@ -1231,6 +1231,73 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B
   return PRNN_STATUS_SUCCESS;
 }
 
+prnnStatus_t prnn_forward_stack_sparse(prnnHandle_t h, int L, int N, int I, int B, int T, int K, prnnDataType_t x_type,
+                                       const void* x, const void* const* U, const float* const* bias,
+                                       const int16_t* const* col, prnnDataType_t val_type, const void* const* val,
+                                       const float* const* h0, float* Xbuf, float* const* H, hipStream_t stream) {
+  if (h == nullptr || L < 1 || N < 1 || I < 1 || B < 1 || B > 8 || T < 0) return PRNN_STATUS_BAD_PARAM;
+  if (take_failure(h)) return PRNN_STATUS_EXECUTION_FAILED;
+  if (x_type != PRNN_DATA_FLOAT && x_type != PRNN_DATA_HALF) return PRNN_STATUS_BAD_PARAM;
+  if (val_type != PRNN_DATA_FLOAT && val_type != PRNN_DATA_HALF) return PRNN_STATUS_BAD_PARAM;
+  if (K < 1 || K > N || N > 32767) return PRNN_STATUS_BAD_PARAM;
+  if (T == 0) return PRNN_STATUS_SUCCESS;
+  if (U == nullptr || col == nullptr || val == nullptr || H == nullptr || x == nullptr || Xbuf == nullptr)
+    return PRNN_STATUS_BAD_PARAM;
+  const size_t seq = (size_t)T * B * N * 4;
+  if (seq > 0xFFFFFFF0ull) return PRNN_STATUS_NOT_SUPPORTED;
+  if (!aligned(Xbuf, 4)) return PRNN_STATUS_BAD_PARAM;
+  const size_t vb = (size_t)N * K * (val_type == PRNN_DATA_FLOAT ? 4 : 2), cb = (size_t)N * K * 2;
+  // Every pointer and overlap is checked before anything is enqueued: H[l]
+  // is written while every layer's weights, biases and initial states, the
+  // workspace and the other outputs are read; the workspace is written
+  // before all of those are read.
+  for (int l = 0; l < L; ++l) {
+    const float* hl = h0 != nullptr ? h0[l] : nullptr;
+    const float* bl = bias != nullptr ? bias[l] : nullptr;
+    if (U[l] == nullptr || col[l] == nullptr || val[l] == nullptr || H[l] == nullptr) return PRNN_STATUS_BAD_PARAM;
+    if (!aligned(U[l], 2) || !aligned(col[l], 2) || !aligned(val[l], val_type == PRNN_DATA_FLOAT ? 4 : 2) ||
+        !aligned(H[l], 4) || (hl != nullptr && !aligned(hl, 4)) || (bl != nullptr && !aligned(bl, 4)))
+      return PRNN_STATUS_BAD_PARAM;
+    if (overlap(H[l], seq, Xbuf, seq)) return PRNN_STATUS_BAD_PARAM;
+    for (int m = 0; m < L; ++m) {
+      const float* hm = h0 != nullptr ? h0[m] : nullptr;
+      const float* bm = bias != nullptr ? bias[m] : nullptr;
+      const size_t ub = (size_t)N * (m == 0 ? I : N) * 2;
+      if ((m != l && overlap(H[l], seq, H[m], seq)) || overlap(H[l], seq, col[m], cb) || overlap(H[l], seq, val[m], vb) ||
+          overlap(H[l], seq, U[m], ub) || (hm != nullptr && overlap(H[l], seq, hm, (size_t)B * N * 4)) ||
+          (bm != nullptr && overlap(H[l], seq, bm, (size_t)N * 4)))
+        return PRNN_STATUS_BAD_PARAM;
+    }
+  }
+  for (int m = 0; m < L; ++m) {
+    const float* hm = h0 != nullptr ? h0[m] : nullptr;
+    const float* bm = bias != nullptr ? bias[m] : nullptr;
+    if (overlap(Xbuf, seq, col[m], cb) || overlap(Xbuf, seq, val[m], vb) ||
+        overlap(Xbuf, seq, U[m], (size_t)N * (m == 0 ? I : N) * 2) ||
+        (hm != nullptr && overlap(Xbuf, seq, hm, (size_t)B * N * 4)) || (bm != nullptr && overlap(Xbuf, seq, bm, (size_t)N * 4)))
+      return PRNN_STATUS_BAD_PARAM;
+  }
+  // Every layer's recurrence and layer 0's projection must have a plan.
+  Plan lp;
+  if (!plan(h, kSparse, N, B, K, val_type == PRNN_DATA_FLOAT ? prnn::kF32 : prnn::kF16, &lp))
+    return PRNN_STATUS_NOT_SUPPORTED;
+  prnn::ProjArgs pa;
+  bool vec = false;
+  prnnStatus_t st = prepare_layer_projection(h, N, I, B, T, x_type, x, PRNN_DATA_HALF, U[0],
+                                             bias != nullptr ? bias[0] : nullptr, Xbuf,
+                                             h0 != nullptr ? h0[0] : nullptr, col[0], cb, val[0], vb, &pa, &vec);
+  if (st != PRNN_STATUS_SUCCESS) return st;
+  // One layer after another (the sparse layers keep their pairs in registers
+  // in the team layout; the layers do not run as a wavefront).
+  for (int l = 0; l < L; ++l) {
+    st = prnn_forward_layer_sparse(h, N, l == 0 ? I : N, B, T, K, l == 0 ? x_type : PRNN_DATA_FLOAT,
+                                   l == 0 ? x : H[l - 1], PRNN_DATA_HALF, U[l], bias != nullptr ? bias[l] : nullptr,
+                                   col[l], val_type, val[l], h0 != nullptr ? h0[l] : nullptr, Xbuf, H[l], stream);
+    if (st != PRNN_STATUS_SUCCESS) return st;
+  }
+  return PRNN_STATUS_SUCCESS;
+}
+
 prnnStatus_t prnn_set_stack_mode(prnnHandle_t h, prnnStackMode_t mode) {
   if (h == nullptr) return PRNN_STATUS_BAD_PARAM;
   if (mode != PRNN_STACK_AUTO && mode != PRNN_STACK_BLOCKED && mode != PRNN_STACK_FUSED && mode != PRNN_STACK_LAYERS)

@@ -1,4 +1,5 @@
-"""GPU parity of a stack of dense layers run as a wavefront (through the C ABI).
+"""GPU parity of stacks of layers (through the C ABI): dense layers run as a
+wavefront, and row-balanced sparse layers one after another.
 
 ``prnn_forward_stack_dense`` runs layer 0's input projection, then the layers
 at the same time (layer l, batch row b on its own XCD): in blocks of steps,
@@ -8,6 +9,8 @@ step (FUSED); or one layer after another (LAYERS, and for N > 1792).  It is comp
 the recurrence's fp16 bar (|H - H_ref| <= 2e-2 (1 + |H_ref|)), for stacks of
 2 to 8 layers, full and ragged sizes, with and without initial states.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -177,5 +180,84 @@ def test_stack_without_biases_or_states_and_fp16_input(handle, mode):
     handle.synchronize()
     handle.set_stack_mode(binding.STACK_AUTO)
     refs = oracle.forward_stack_dense(st["layers"], x16, None)
+    for o, r in zip(outs, refs):
+        assert oracle.tolerance_ratio(o.cpu().numpy(), r, oracle.TOL_F16) <= 1.0
+
+
+# ---------------------------------------------------------------------------
+# stacks of row-balanced sparse layers (prnn_forward_stack_sparse: one layer
+# after another) against oracle.forward_stack_sparse
+# ---------------------------------------------------------------------------
+def run_sparse_stack(handle, st, h0=True, x_dtype=np.float32):
+    layers = [{k: dev(v) for k, v in ly.items()} for ly in st["layers"]]
+    h0s = [dev(h) for h in st["h0s"]] if h0 else None
+    outs = handle.forward_stack_sparse(layers, dev(st["x"].astype(x_dtype)), h0s)
+    handle.synchronize()
+    return [o.cpu().numpy() for o in outs]
+
+
+@pytest.mark.parametrize("name,L,B,T", [("sparse10_f16_n1152", 2, 4, 256), ("sparse10_f16_n1792", 3, 4, 40),
+                                        ("sparse1_f16_n5760", 2, 4, 16), ("sparse10_f16_n2304", 2, 2, 20)])
+def test_sparse_stack_parity(handle, name, L, B, T):
+    w = WORKLOADS[name].with_(T=T, B=B, h0="randn")
+    st = generate_stack(w, L)
+    got = run_sparse_stack(handle, st)
+    refs = oracle.forward_stack_sparse(st["layers"], st["x"], st["h0s"])
+    for l, (g, r) in enumerate(zip(got, refs)):
+        assert oracle.tolerance_ratio(g, r, oracle.TOL_F16) <= 1.0, f"{name} layer {l}"
+
+
+def test_sparse_stack_ragged_fp32_values_and_fp16_input(handle):
+    from persistent_rnn_fwd_amd.inputs import Workload
+    w = Workload("sparse_1000", "sparse", 1000, 3, 12, "f32", K=77, seed=41, h0="randn")
+    st = generate_stack(w, 3)
+    got = run_sparse_stack(handle, st, x_dtype=np.float16)
+    x16 = st["x"].astype(np.float16)
+    refs = oracle.forward_stack_sparse(st["layers"], x16, st["h0s"])
+    for g, r in zip(got, refs):
+        assert oracle.tolerance_ratio(g, r, oracle.TOL_F32) <= 1.0
+
+
+def test_sparse_stack_equals_layer_calls_bitwise(handle):
+    w = WORKLOADS["sparse10_f16_n1792"].with_(T=20, h0="randn")
+    st = generate_stack(w, 2)
+    got = run_sparse_stack(handle, st, h0=False)
+    layers = [{k: dev(v) for k, v in ly.items()} for ly in st["layers"]]
+    inp = dev(st["x"])
+    for l, ly in enumerate(layers):
+        H = handle.forward_layer_sparse(ly["U"], ly["bias"], ly["col"], ly["val"], inp)
+        handle.synchronize()
+        np.testing.assert_array_equal(H.cpu().numpy(), got[l])
+        inp = H
+
+
+def test_sparse_stack_errors(handle):
+    w = WORKLOADS["sparse10_f16_n1152"].with_(T=4)
+    st = generate_stack(w, 2)
+    layers = [{k: dev(v) for k, v in ly.items()} for ly in st["layers"]]
+    x = dev(st["x"])
+    outs = [torch.empty((w.T, w.B, w.N), device="cuda") for _ in range(2)]
+    with pytest.raises(PrnnError) as e:                      # two layers writing one output
+        handle.forward_stack_sparse(layers, x, outs=[outs[0], outs[0]])
+    assert e.value.status == binding.BAD_PARAM
+    with pytest.raises(PrnnError) as e:                      # the workspace is an output
+        handle.forward_stack_sparse(layers, x, outs=outs, workspace=outs[1])
+    assert e.value.status == binding.BAD_PARAM
+    lib = binding.load_library()
+    s = torch.cuda.current_stream().cuda_stream
+    arr = lambda ts: (ctypes.c_void_p * 2)(*[t.data_ptr() for t in ts])
+    U, C, V, H = (arr([ly["U"] for ly in layers]), arr([ly["col"] for ly in layers]),
+                  arr([ly["val"] for ly in layers]), arr(outs))
+    ws = torch.empty((w.T, w.B, w.N), device="cuda")
+    call = lambda L=2, K=w.K, vt=binding.DATA_HALF, T=w.T: lib.prnn_forward_stack_sparse(
+        handle._h, L, w.N, w.N, w.B, T, K, binding.DATA_FLOAT, x.data_ptr(), U, None, C, vt, V, None,
+        ws.data_ptr(), H, s)
+    assert call(L=0) == binding.BAD_PARAM
+    assert call(K=0) == binding.BAD_PARAM and call(K=w.N + 1) == binding.BAD_PARAM
+    assert call(vt=7) == binding.BAD_PARAM
+    assert call(T=0) == binding.SUCCESS
+    assert call() == binding.SUCCESS
+    handle.synchronize()
+    refs = oracle.forward_stack_sparse([dict(ly, bias=None) for ly in st["layers"]], st["x"], None)
     for o, r in zip(outs, refs):
         assert oracle.tolerance_ratio(o.cpu().numpy(), r, oracle.TOL_F16) <= 1.0
