@@ -92,8 +92,39 @@ int main() {
   CHECK(prnn_set_math(h, (prnnMath_t)7), BP);
   CHECK(prnn_set_math(h, PRNN_MATH_HALF), OK);
   uint16_t* W4 = dalloc<uint16_t>((size_t)4096 * 4096);
+  (void)hipMemset(W4, 0, (size_t)4096 * 4096 * 2);
   CHECK(prnn_forward_dense(h, 4096, 1, 2, PRNN_DATA_HALF, W4, X, h0, H, nullptr), NS);
   CHECK(prnn_set_math(h, PRNN_MATH_AUTO), OK);
+  // dense fp16 split over 2 and 4 XCDs per batch row, forced and automatic, and its floor
+  CHECK(prnn_forward_dense(h, 4096, 2, 2, PRNN_DATA_HALF, W4, X, h0, H, nullptr), OK);
+  CHECK(prnn_forward_dense(h, 3072, 4, 3, PRNN_DATA_HALF, W4, X, h0, H, nullptr), OK);
+  CHECK(prnn_sync_floor(h, 3072, 4, 3, H, nullptr), OK);
+  CHECK(prnn_set_xcds_per_row(h, 3), BP);
+  CHECK(prnn_set_xcds_per_row(h, 2), OK);
+  CHECK(prnn_forward_dense(h, 1792, 4, 3, PRNN_DATA_HALF, W4, X, h0, H, nullptr), OK);
+  CHECK(prnn_set_xcds_per_row(h, 1), OK);
+  CHECK(prnn_forward_dense(h, 3072, 4, 3, PRNN_DATA_HALF, W4, X, h0, H, nullptr), NS);
+  CHECK(prnn_set_xcds_per_row(h, 0), OK);
+  CHECK(prnn_get_last_plan(h, &info), OK);
+  // sparse rows of unequal length
+  int32_t* rl = dalloc<int32_t>(2304);
+  std::vector<int32_t> hrl(2304);
+  for (int i = 0; i < 2304; ++i) hrl[i] = (i * 37) % 700 - 20;  // also below 0 and above K
+  (void)hipMemcpy(rl, hrl.data(), hrl.size() * 4, hipMemcpyHostToDevice);
+  CHECK(prnn_forward_sparse_rows(h, 2304, B, T, 617, col, PRNN_DATA_HALF, val, rl, X, h0, H, nullptr), OK);
+  CHECK(prnn_forward_sparse_rows(h, 2304, B, T, 617, col, PRNN_DATA_HALF, val, nullptr, X, h0, H, nullptr), BP);
+  CHECK(prnn_forward_sparse_rows(h, 2304, B, T, 617, col, PRNN_DATA_FLOAT, val, rl, X, h0, H, nullptr), NS);
+  // a stack of two sparse layers, one after another
+  float* H2 = dalloc<float>((size_t)T * B * N);
+  const void* Us[2] = {U, U};
+  const int16_t* cols[2] = {col, col};
+  const void* vals[2] = {val, val};
+  float* Hs[2] = {H, H2};
+  CHECK(prnn_forward_stack_sparse(h, 2, 1152, 1152, B, T, 115, PRNN_DATA_FLOAT, x, Us, nullptr, cols, PRNN_DATA_HALF,
+                                  vals, nullptr, Xb, Hs, nullptr), OK);
+  float* Hsame[2] = {H, H};
+  CHECK(prnn_forward_stack_sparse(h, 2, 1152, 1152, B, T, 115, PRNN_DATA_FLOAT, x, Us, nullptr, cols, PRNN_DATA_HALF,
+                                  vals, nullptr, Xb, Hsame, nullptr), BP);
   CHECK(prnn_synchronize(h, nullptr), OK);
   CHECK(prnn_destroy(h), OK);
   CHECK(prnn_destroy(nullptr), OK);
