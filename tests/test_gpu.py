@@ -785,18 +785,28 @@ def test_log_lines_on_stderr(gpu, capfd, monkeypatch):
 
 
 @pytest.mark.parametrize("kind,name,T", [("dense", "dense_f16_n1152", 15), ("sparse", "sparse10_f16_n1792", 13),
-                                         ("dense", "dense_f32_n256", 7)])
+                                         ("dense", "dense_f32_n256", 7), ("dense", "split_n3072_b4", 9),
+                                         ("dense", "split_n4096_b2", 6), ("rows", "sparse10u_f16_n2304", 11)])
 def test_graph_capture_and_replay(gpu, kind, name, T):
     """A call captured into a HIP graph replays correctly any number of times,
     with eager calls of another length on the same handle between the replays:
-    every replay and every eager call equals, bitwise, a fresh handle's result."""
-    w = WORKLOADS[name].with_(T=T, h0="randn")
+    every replay and every eager call equals, bitwise, a fresh handle's result.
+    Also for dense layers split over 2 and 4 XCDs per batch row (the shared
+    ring's fill is captured too) and for sparse rows of unequal length (the
+    ordering kernel is captured)."""
+    if name.startswith("split_"):
+        N, B = int(name.split("_n")[1].split("_")[0]), int(name.split("_b")[1])
+        w = Workload(name, "dense", N, B, T, "f16", seed=N, h0="randn")
+    else:
+        w = WORKLOADS[name].with_(T=T, h0="randn")
     d, d2 = generate(w, seed=91), generate(w.with_(T=T + 2), seed=92)
     g, g2 = to_dev(d), to_dev(d2)
 
     def call(h, gg, out=None):
         if kind == "dense":
             return h.forward_dense(gg["W"], gg["X"], gg["h0"], out=out)
+        if kind == "rows":
+            return h.forward_sparse_rows(gg["col"], gg["val"], gg["row_len"], gg["X"], gg["h0"], out=out)
         return h.forward_sparse(gg["col"], gg["val"], gg["X"], gg["h0"], out=out)
 
     with Handle() as fresh:
@@ -823,4 +833,10 @@ def test_graph_capture_and_replay(gpu, kind, name, T):
             e = call(h, g2)
             h.synchronize()
             assert torch.equal(e, ref2), f"eager call after replay {rep}"
-    assert oracle.tolerance_ratio(ref.cpu().numpy(), reference(kind, d), tol_of(d)) <= 1.0
+        if name.startswith("split_"):
+            assert h.last_plan()["xcds_per_row"] > 1
+    if kind == "rows":
+        ref_np = oracle.forward_sparse_rows(d["col"], d["val"], d["row_len"], d["X"], d["h0"])
+    else:
+        ref_np = reference(kind, d)
+    assert oracle.tolerance_ratio(ref.cpu().numpy(), ref_np, tol_of(d)) <= 1.0
