@@ -73,6 +73,10 @@ extern const KernelEntry kSparseTeamF32Kernels[];
 extern const KernelEntry kSparseTeamF16Kernels16[];
 extern const KernelEntry kSparseTeamF16Kernels12[];   // 12-wave workgroups (3 waves per SIMD)
 extern const KernelEntry kSparseTeamF16TraceKernels16[];
+// Words between the two LDS rows of h in the sparse team kernels: at least
+// N + 1 for every layer an instance of rw rows per wave and `waves` waves per
+// workgroup serves (N <= rw x 32 waves per team), a multiple of 4.
+constexpr int sparse_team_stride(int rw, int waves) { return rw * 32 * waves + 4; }
 // Sparse fp16 rows of unequal length (team layout; 8- and 12-wave workgroups).
 extern const KernelEntry kSparseRowsF16Kernels[];
 extern const KernelEntry kSparseRowsF16Kernels12[];

@@ -308,7 +308,8 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
       if (p->k == nullptr) set_waves(W = 8);
     }
     if (W == 8) p->k = pick(prnn::kSparseRowsF16Kernels, p->max_rows, p->spr);
-    p->lds_stride = sparse_lds_stride(N);
+    if (p->k == nullptr) return false;
+    p->lds_stride = prnn::sparse_team_stride(p->k->rmax, W);
     p->lds_bytes = 2 * p->lds_stride * 4;
   } else if (kind == kSparse) {
     p->spr = (K + 63) / 64;
@@ -326,7 +327,8 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
       if (p->k == nullptr) set_waves(W = 8);
     }
     if (W == 8) p->k = pick(table, p->max_rows, p->spr);
-    p->lds_stride = sparse_lds_stride(N);
+    if (p->k == nullptr) return false;
+    p->lds_stride = prnn::sparse_team_stride(p->k->rmax, W);  // the instance's fixed row distance
     p->lds_bytes = 2 * p->lds_stride * 4;
   } else {
     static const KernelEntry floor_team = {0, 64, 1 << 30, nullptr};

@@ -385,13 +385,23 @@ __device__ __forceinline__ void ragged_slots(P (&pr)[RW][SPR], const int (&cnt)[
 template <typename VT, int RW, int SPR, bool TRACE = false, int WAVES = kTeamWaves, bool RAGGED = false>
 __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
   constexpr int M = pow2_at_least(RW);
-  extern __shared__ __attribute__((aligned(16))) float lds[];  // [2][lds_stride]: word N of each row stays 0
+  // The two LDS rows of h are `stride` words apart, a bound the instance fixes
+  // (N <= RW rows x at most 32 WAVES waves per team; the host passes the same
+  // value).  Where the registers allow one more per pair (kTwoSteps), the loop
+  // runs two steps per iteration: a gather's address is then the same at every
+  // step and the step's row is an immediate offset of the LDS read, instead of
+  // an address computed per pair and step (N = 1792, 10 %: 23 -> 1 address
+  // instructions per step).  Rows of more than 5 slots (25 % at N = 2304:
+  // 2.01 -> 2.08 us per step) and the blocks that would run out of registers
+  // keep one step per iteration.
+  constexpr int stride = sparse_team_stride(RW, WAVES);
+  constexpr bool kTwoSteps = SPR <= 5 && 2 * RW * SPR + 40 <= 512 / (WAVES / 4);
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // [2][stride]: word N of each row stays 0
   __shared__ int abort_flag;
   __shared__ uint2 place_scratch[WAVES][64 * SPR];  // prologue only: pair placement
   const TeamPos p = team_pos<WAVES>(a);
   const int N = a.N;
   const int K = a.K;
-  const int stride = a.lds_stride;
   if (threadIdx.x == 0) abort_flag = __builtin_nontemporal_load(a.status) != 0u;
   for (int c = N + (int)threadIdx.x; c < 2 * stride; c += blockDim.x)
     if (c % stride >= N) lds[c] = 0.f;
@@ -453,9 +463,9 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
   PhaseClock<TRACE> clk;
   clk.start();
 
-  for (int t = 0; t < a.T; ++t) {
+  // One step into the LDS row hrow; false when the run stops (a failure).
+  auto step = [&](int t, float* hrow) -> bool {
     const uint32_t S = a.step0 + (uint32_t)t;
-    float* hrow = lds + (t & 1) * stride;
     bool ok = true;
     if (t == 0) {
       for (int c = threadIdx.x; c < N; c += blockDim.x) hrow[c] = a.h0 != nullptr ? a.h0[(size_t)p.b * N + c] : 0.f;
@@ -508,7 +518,7 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
     clk.mark(kTrReduce);
     if constexpr (WAVES > kTeamWaves) __builtin_amdgcn_s_setprio(0);
     asm volatile("" : "+v"(aborted_now) : "v"(sum));  // keep the test after the arithmetic
-    if (aborted_now) return;
+    if (aborted_now) return false;
     debug_jitter(a.jitter_seed, a.jitter_span, p.wave, t);
     if (owner && !(p.rank == a.skip_wg && t == a.skip_step)) {
       const uint32_t hb = relu_bits(sum + x);
@@ -518,6 +528,16 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
       a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb);
     }
     clk.mark(kTrEpilogue);
+    return true;
+  };
+  if constexpr (kTwoSteps) {
+    for (int t = 0; t < a.T; t += 2) {
+      if (!step(t, lds)) return;
+      if (t + 1 < a.T && !step(t + 1, lds + stride)) return;
+    }
+  } else {
+    for (int t = 0; t < a.T; ++t)
+      if (!step(t, lds + (t & 1) * a.lds_stride)) return;
   }
   if (TRACE) clk.finish(trace_record<WAVES>(a, p), a.T);
 }
