@@ -33,6 +33,9 @@ struct Pair<_Float16> {
     p = v | (c << 16);
   }
   __device__ __forceinline__ int column() const { return (int)(p >> 16); }
+  __device__ __forceinline__ float value() const {  // the fp16 value, widened exactly
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xffffu));
+  }
   __device__ __forceinline__ void fma(float& acc, float h) const { fma_mix_lo(acc, p, h); }
   __device__ __forceinline__ uint2 raw() const { return make_uint2(p, 0u); }
   __device__ __forceinline__ void set_raw(uint2 r) { p = r.x; }

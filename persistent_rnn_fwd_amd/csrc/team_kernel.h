@@ -453,6 +453,22 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
   const bool owner = my_row >= 0 && my_row < nr;
   const int jn = a.chunks;
+  // Two-step instances of row-balanced fp16 layers keep each pair as its
+  // column and its value widened to fp32 (exact): the loop then needs no
+  // packed pair at all, and each product is a v_fmac_f32 instead of a
+  // v_fma_mix_f32 (the same fused multiply-add with one rounding).
+  constexpr bool kWidened = kTwoSteps && !RAGGED && std::is_same<VT, _Float16>::value;
+  int wcol[kWidened ? RW : 1][kWidened ? SPR : 1];
+  float wval[kWidened ? RW : 1][kWidened ? SPR : 1];
+  if constexpr (kWidened) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int s = 0; s < SPR; ++s) {
+        wcol[r][s] = pr[r][s].column();
+        wval[r][s] = pr[r][s].value();
+      }
+  }
 
   // x of the row this lane owns.  The load for step t + 1 is issued right
   // after step t's staging: the next step's polls, whose waits also drain
@@ -502,7 +518,13 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_team_kernel(StepArgs a) {
     if constexpr (RAGGED) ragged_slots<0>(pr, cnt, hrow, acc);
 #pragma unroll
     for (int s = 0; s < SPR; ++s) {
-      if (!RAGGED && s < a.spr) {
+      if (kWidened && s < a.spr) {
+        float hv[RW];
+#pragma unroll
+        for (int r = 0; r < RW; ++r) hv[r] = hrow[wcol[r][s]];
+#pragma unroll
+        for (int r = 0; r < RW; ++r) acc[r] = fmaf(wval[r][s], hv[r], acc[r]);
+      } else if (!RAGGED && s < a.spr) {
         // All of the slot's gathers are issued before its first FMA, so
         // their LDS latencies overlap (the FMA is inline asm, which the
         // compiler does not move loads across).
