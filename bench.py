@@ -383,12 +383,15 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
         h.synchronize()
         plan = {k: v for k, v in h.last_plan().items() if k != "first_step"}
         fo = torch.empty((T, B, N), dtype=torch.float32, device=dev)
-        # the floor in the layer's own plan: same layout and waves per workgroup
+        # the floor in the layer's own plan: same layout, waves per workgroup
+        # and XCDs per batch row
         if plan["layout"] == _b.LAYOUT_TEAM:
             h.set_team_waves(plan["waves_per_wg"])
+            h.set_xcds_per_row(plan["xcds_per_row"])
         f_full = timed(lambda: h.sync_floor(N, B, T, out=fo))
         f_half = timed(lambda: h.sync_floor(N, B, T // 2, out=fo[: T // 2]))
         h.set_team_waves(0)
+        h.set_xcds_per_row(0)
         floor_us = (f_full - f_half) * 1e3 / (T - T // 2)
         err = None
         if not no_check:

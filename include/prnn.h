@@ -135,7 +135,9 @@ typedef enum {
  *          (N <= 5120, B <= 2), each holding a part of the rows; the parts
  *          exchange their rows of h_{t-1} through device-coherent memory
  *          every step.  EXACT math only (SPLIT and HALF: NOT_SUPPORTED), no
- *          phase tracing (NOT_SUPPORTED while tracing is on).
+ *          phase tracing (NOT_SUPPORTED while tracing is on).  Heavy sparse
+ *          fp16 layers split the same way over 2 XCDs (see
+ *          prnn_set_xcds_per_row).
  *  AUTO:   TEAM when an instance fits, else SPREAD (the default). */
 typedef enum {
   PRNN_LAYOUT_AUTO = 0,
@@ -426,9 +428,13 @@ prnnStatus_t prnn_set_team_waves(prnnHandle_t handle, int waves);
  * instances hold the layer, else the fewest XCDs of a split that holds it),
  * 1, 2 or 4 (2: B <= 4, 4: B <= 2; see prnnLayout_t).  A forced width that
  * the call cannot use makes it return NOT_SUPPORTED (or fall back to the
- * SPREAD layout under LAYOUT_AUTO).  prnn_sync_floor follows the dense fp16
- * layer of the same N and B.  fp32 W and sparse layers always use one XCD
- * per batch row.  BAD_PARAM for any other value. */
+ * SPREAD layout under LAYOUT_AUTO).  Row-balanced sparse fp16 layers take 1
+ * or 2 (B <= 4; 4: NOT_SUPPORTED); automatically 2 where one XCD's waves
+ * would each hold more than 60 slots of 64 pairs (e.g. 5 % at N = 5760),
+ * else 1.  prnn_sync_floor runs a forced width (with the wave count of
+ * prnn_set_team_waves, 8 or 12), else the width of the dense fp16 layer of
+ * the same N and B.  fp32 W and fp32 values, and sparse rows of unequal
+ * length, always use one XCD per batch row.  BAD_PARAM for any other value. */
 prnnStatus_t prnn_set_xcds_per_row(prnnHandle_t handle, int xcds);
 
 /* Exchange mode for later calls (default AUTO).  A forced RELAY that the

@@ -102,7 +102,11 @@ extern const KernelEntry kDenseTeamMfmaTraceKernels[];
 // rmax = rows per wave, cap = 256-column chunks of the row.  The ring is the
 // team ring [8][2][Npad] followed by a shared ring [8][2][Npad].
 extern const KernelEntry kDenseSplitF16Kernels[];
-extern const void* kFloorSplitKernel;  // the split layout's floor (rows per wave <= 64)
+extern const void* kFloorSplitKernel;    // the split layout's floor (rows per wave <= 64)
+extern const void* kFloorSplitKernel12;  // ... with 12-wave workgroups
+// Sparse fp16 layers on 2 XCDs per batch row: rmax = rows per wave, cap =
+// 64-pair slots, waves = waves per workgroup (8 or 12).
+extern const KernelEntry kSparseSplitF16Kernels[];
 // Dense fp16 team layout with h_{t-1} rounded to fp16 (rmax = rows per wave,
 // cap = 256-column chunks).
 extern const KernelEntry kDenseTeamHalfKernels[];

@@ -128,6 +128,40 @@ const KernelEntry* split_instance(int N, int P, int xp, int* part_rows) {
   return pick(prnn::kDenseSplitF16Kernels, (std::min(*part_rows, N) + Q - 1) / Q, chunks);
 }
 
+// Sparse fp16 layer on two XCDs per batch row (B <= 4): each XCD holds a
+// part of whole 256-column chunks of rows.  12 waves per workgroup where a
+// part would hold more than 8 rows per wave at 8 waves, else 8 (a forced
+// count: that one only).  Fills the split fields, waves, rows and instance of
+// p; false when no instance holds the part.
+bool plan_sparse_split(const prnnContext* h, int N, int P, int spr, Plan* p) {
+  const int chunks = (N + 255) / 256;
+  const int part_rows = 256 * ((chunks + 1) / 2);
+  const int rows8 = (std::min(part_rows, N) + 8 * P - 1) / (8 * P);
+  const int order[2] = {rows8 > 8 ? 12 : 8, rows8 > 8 ? 8 : 12};
+  for (int w : order) {
+    if (h->team_waves != 0 && h->team_waves != w) continue;
+    const int rows = (std::min(part_rows, N) + P * w - 1) / (P * w);
+    const KernelEntry* k = nullptr;
+    for (const KernelEntry* e = prnn::kSparseSplitF16Kernels; e->fn != nullptr; ++e)
+      if (e->waves == w && e->rmax >= rows && e->cap >= spr &&
+          (k == nullptr || e->rmax < k->rmax || (e->rmax == k->rmax && e->cap < k->cap)))
+        k = e;
+    if (k == nullptr) continue;
+    p->k = k;
+    p->waves = w;
+    p->block = 64 * w;
+    p->max_rows = rows;
+    p->base_rows = p->extra_rows = 0;  // per part, derived on the device
+    p->part_rows = part_rows;
+    p->xcds_per_row = 2;
+    p->spr = spr;
+    p->lds_stride = 2 * k->rmax * 32 * w + 4;
+    p->lds_bytes = 2 * p->lds_stride * 4;
+    return true;
+  }
+  return false;
+}
+
 // XCDs per batch row of a dense fp16 layer in the team layout: 1 (the whole
 // row on one XCD), or 2 / 4 (split: B <= 4 / B <= 2), or 0 when no form fits.
 // A forced value (prnn_set_xcds_per_row) is taken as it is.  Automatically:
@@ -218,21 +252,28 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
   const int rows8 = (N + 8 * P - 1) / (8 * P);
   // The floor of a dense fp16 layer that runs split over several XCDs per
   // batch row is the split layout's protocol (8-wave workgroups).
-  if (kind == kFloor && h->team_waves == 0) {
+  if (kind == kFloor && (h->team_waves == 0 || h->xcds_per_row > 1)) {
     const int chunks = (N + 255) / 256;
-    const int xp = choose_xcds_per_row(h, N, B, P, pick(prnn::kDenseTeamF16Kernels, rows8, chunks) != nullptr);
+    // a forced width (the protocol needs no weight instance), else the width
+    // of the dense fp16 layer of the same N and B (one XCD per batch row when
+    // no dense form fits either)
+    if (h->xcds_per_row > 1 && B > 8 / h->xcds_per_row) return false;
+    const int xp = h->xcds_per_row > 1 ? h->xcds_per_row
+                                       : choose_xcds_per_row(h, N, B, P, pick(prnn::kDenseTeamF16Kernels, rows8, chunks) != nullptr);
     if (xp > 1) {
       static const KernelEntry floor_split = {0, 64, 1 << 30, nullptr};  // the caller substitutes the kernel
+      const int w = h->team_waves != 0 ? h->team_waves : 8;  // 12: the floor of a 12-wave split sparse layer
+      if (w != 8 && w != 12) return false;
       int part_rows = 0;
       (void)split_instance(N, P, xp, &part_rows);
       p->G = P;
       p->grid = 8 * P;
-      p->waves = 8;
-      p->block = 512;
+      p->waves = w;
+      p->block = 64 * w;
       p->chunks = chunks;
       p->xcds_per_row = xp;
       p->part_rows = part_rows;
-      p->max_rows = (std::min(part_rows, N) + 8 * P - 1) / (8 * P);
+      p->max_rows = (std::min(part_rows, N) + w * P - 1) / (w * P);
       p->base_rows = p->extra_rows = 0;
       p->k = &floor_split;
       p->lds_bytes = 2 * ((N + 3) & ~3) * 4;
@@ -311,6 +352,12 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
     if (p->k == nullptr) return false;
     p->lds_stride = prnn::sparse_team_stride(p->k->rmax, W);
     p->lds_bytes = 2 * p->lds_stride * 4;
+  } else if (kind == kSparse && wt == prnn::kF16 && h->xcds_per_row == 4) {
+    return false;  // sparse layers split over two XCDs at most
+  } else if (kind == kSparse && wt == prnn::kF16 && h->xcds_per_row == 2) {
+    if (h->trace || B > 4 || h->team_waves == 16) return false;
+    if (!plan_sparse_split(h, N, P, (K + 63) / 64, p)) return false;
+    W = p->waves;
   } else if (kind == kSparse) {
     p->spr = (K + 63) / 64;
     const KernelEntry* table = h->trace ? (wt == prnn::kF32 ? prnn::kSparseTeamF32TraceKernels : prnn::kSparseTeamF16TraceKernels)
@@ -330,6 +377,21 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
     if (p->k == nullptr) return false;
     p->lds_stride = prnn::sparse_team_stride(p->k->rmax, W);  // the instance's fixed row distance
     p->lds_bytes = 2 * p->lds_stride * 4;
+    // Automatically, fp16 layers whose rows of one wave hold more than 60
+    // 64-pair slots (too many registers for the widened two-step loop) run on
+    // two XCDs per batch row where B <= 4: fewer rows per wave, widened, at the
+    // price of the cross-XCD exchange.  Measured, us per step (one XCD -> two):
+    // 5 % at N = 5760 (15 x 5 slots) 2.86 -> 2.42; lighter layers lose (10 % at
+    // N = 2304 1.36 -> 1.87, 1 % at N = 5760 1.47 -> 1.71), 25 % at N = 2304
+    // (6 x 9) stays the same.
+    if (wt == prnn::kF16 && h->xcds_per_row == 0 && h->team_waves == 0 && !h->trace && B <= 4 &&
+        p->k->rmax * p->k->cap > 60) {
+      Plan s = *p;
+      if (plan_sparse_split(h, N, P, p->spr, &s)) {
+        *p = s;
+        W = p->waves;
+      }
+    }
   } else {
     static const KernelEntry floor_team = {0, 64, 1 << 30, nullptr};
     static const KernelEntry floor_team12 = {0, 64, 1 << 30, nullptr, 12};
@@ -1331,9 +1393,11 @@ prnnStatus_t prnn_sync_floor(prnnHandle_t h, int N, int B, int T, float* H, hipS
     floor_team12.fn = prnn::kFloorTeamKernel12;
     floor_team12_trace.fn = prnn::kFloorTeamTraceKernel12;
     static KernelEntry floor_split = {0, 64, 1 << 30, nullptr};
+    static KernelEntry floor_split12 = {0, 64, 1 << 30, nullptr, 12};
     floor_split.fn = prnn::kFloorSplitKernel;
+    floor_split12.fn = prnn::kFloorSplitKernel12;
     if (p.xcds_per_row > 1)
-      p.k = &floor_split;  // no trace instance: a traced split layer is not planned either
+      p.k = p.waves == 12 ? &floor_split12 : &floor_split;  // no trace instance: a traced split layer is not planned either
     else if (p.waves == 16)
       p.k = h->trace ? &floor_team16_trace : &floor_team16;
     else if (p.waves == 12)

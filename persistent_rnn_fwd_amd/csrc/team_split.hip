@@ -41,6 +41,7 @@ struct SplitPos {
   int nr, r0;  // this wave's rows (r0: row index in the layer)
 };
 
+template <int WAVES = kTeamWaves>
 __device__ __forceinline__ SplitPos split_pos(const StepArgs& a) {
   SplitPos p;
   const int xp = a.xcds_per_row;
@@ -57,8 +58,8 @@ __device__ __forceinline__ SplitPos split_pos(const StepArgs& a) {
   p.lane = threadIdx.x & 63;
   const int part_r0 = p.part * a.part_rows;
   const int len = max(0, min(a.part_rows, a.N - part_r0));
-  const int Q = a.G * kTeamWaves;
-  const int q = p.rank * kTeamWaves + p.wave;
+  const int Q = a.G * WAVES;
+  const int q = p.rank * WAVES + p.wave;
   const int base = len / Q, extra = len % Q;
   p.nr = base + (q < extra ? 1 : 0);
   p.r0 = part_r0 + q * base + min(q, extra);
@@ -73,12 +74,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t split_shared(const StepArgs& a
 // Stages chunks w, w + 8, ... of slot `slot` into the LDS row, each from the
 // XCD's region (its own part's chunks) or from the shared ring.  Returns false
 // if a wait expired.
+template <int WAVES = kTeamWaves>
 __device__ __forceinline__ bool split_stage(__amdgpu_buffer_rsrc_t region, __amdgpu_buffer_rsrc_t shared,
                                             int part, int part_chunks, uint32_t slot, int npad, int n, int jn,
                                             int wave, int lane, uint32_t tag, uint64_t deadline, float* dst) {
   const uint32_t base = slot * (uint32_t)npad * 4u;
   bool ok = true;
-  for (int j = wave; j < jn; j += kTeamWaves) {
+  for (int j = wave; j < jn; j += WAVES) {
     const __amdgpu_buffer_rsrc_t src = (j / part_chunks == part) ? region : shared;
     const int c = 256 * j + 4 * lane;
     u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(src, base + 4u * c, 0, kCoherent);
@@ -215,10 +217,11 @@ __global__ void __launch_bounds__(512) dense_split_kernel(StepArgs a) {
 // per-step floor of a split layer): the same grid, staging from both rings,
 // barrier and double publication; each wave publishes t + 1 for its rows
 // (at most 64 per wave).
-__global__ void __launch_bounds__(512) floor_split_kernel(StepArgs a) {
+template <int WAVES>
+__global__ void __launch_bounds__(64 * WAVES) floor_split_kernel(StepArgs a) {
   extern __shared__ __attribute__((aligned(16))) float lds[];  // [2][Npad]
   __shared__ int abort_flag;
-  const SplitPos p = split_pos(a);
+  const SplitPos p = split_pos<WAVES>(a);
   if (threadIdx.x == 0) abort_flag = __builtin_nontemporal_load(a.status) != 0u;
   __syncthreads();
   if (abort_flag) return;
@@ -236,8 +239,8 @@ __global__ void __launch_bounds__(512) floor_split_kernel(StepArgs a) {
     bool ok = true;
     if (t > 0) {
       const uint32_t prev = S - 1u;
-      ok = split_stage(region, shared, p.part, part_chunks, prev & 1u, a.Npad, N, a.chunks, p.wave, p.lane,
-                       tag_bit(prev), a.deadline, hrow);
+      ok = split_stage<WAVES>(region, shared, p.part, part_chunks, prev & 1u, a.Npad, N, a.chunks, p.wave, p.lane,
+                              tag_bit(prev), a.deadline, hrow);
     }
     if (!ok && p.lane == 0) {
       abort_flag = 1;
@@ -259,9 +262,129 @@ __global__ void __launch_bounds__(512) floor_split_kernel(StepArgs a) {
   }
 }
 
+// Row-balanced sparse layers split the same way (XP = 2 XCDs per batch row):
+// the sparse team kernel's pairs, placement and gathers over the rows of
+// this XCD's part, the split layout's staging and double publication.  The
+// LDS row holds all N values, at most XP x RW x 32 WAVES words; where the
+// registers allow, two steps per iteration with each pair as its column and
+// its value widened to fp32 (as in the sparse team kernel).
+template <int RW, int SPR, int WAVES, int XP>
+__global__ void __launch_bounds__(64 * WAVES) sparse_split_kernel(StepArgs a) {
+  constexpr int M = pow2_at_least(RW);
+  constexpr int stride = XP * RW * 32 * WAVES + 4;
+  constexpr bool kTwoSteps = SPR <= 5 && 2 * RW * SPR + 40 <= 512 / (WAVES / 4);
+  extern __shared__ __attribute__((aligned(16))) float lds[];  // [2][stride]: word N of each row stays 0
+  __shared__ int abort_flag;
+  __shared__ uint2 place_scratch[WAVES][64 * SPR];  // prologue only: pair placement
+  const SplitPos p = split_pos<WAVES>(a);
+  const int N = a.N;
+  const int K = a.K;
+  if (threadIdx.x == 0) abort_flag = __builtin_nontemporal_load(a.status) != 0u;
+  for (int c = N + (int)threadIdx.x; c < 2 * stride; c += blockDim.x)
+    if (c % stride >= N) lds[c] = 0.f;
+  __syncthreads();
+  if (abort_flag) return;
+  const __amdgpu_buffer_rsrc_t region = team_region(a);
+  const __amdgpu_buffer_rsrc_t shared = split_shared(a, p.b);
+  if (!p.primary) {
+    split_stamp_tail(a, p, region, shared);
+    return;
+  }
+  Pair<_Float16> pr[RW][SPR];
+  load_place_rows<0, RW, Pair<_Float16>, SPR>(pr, reinterpret_cast<const int16_t*>(a.W), a.V, p.r0, p.nr, a.spr, K, N,
+                                              p.lane, place_scratch[p.wave]);
+  int wcol[kTwoSteps ? RW : 1][kTwoSteps ? SPR : 1];
+  float wval[kTwoSteps ? RW : 1][kTwoSteps ? SPR : 1];
+  if constexpr (kTwoSteps) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int s = 0; s < SPR; ++s) {
+        wcol[r][s] = pr[r][s].column();
+        wval[r][s] = pr[r][s].value();
+      }
+  }
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
+  const int my_row = RowReduce<M>::owner_row(p.lane);
+  const bool owner = my_row >= 0 && my_row < p.nr;
+  const int part_chunks = a.part_rows / 256;
+  const uint32_t xstep = (uint32_t)a.B * (uint32_t)N * 4u;
+  uint32_t xoff = ((uint32_t)p.b * (uint32_t)N + (uint32_t)(p.r0 + (owner ? my_row : 0))) * 4u;
+  float x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
+
+  auto step = [&](int t, float* hrow) -> bool {
+    const uint32_t S = a.step0 + (uint32_t)t;
+    bool ok = true;
+    if (t == 0) {
+      for (int c = threadIdx.x; c < N; c += blockDim.x) hrow[c] = a.h0 != nullptr ? a.h0[(size_t)p.b * N + c] : 0.f;
+    } else {
+      const uint32_t prev = S - 1u;
+      ok = split_stage<WAVES>(region, shared, p.part, part_chunks, prev & 1u, a.Npad, N, a.chunks, p.wave, p.lane,
+                              tag_bit(prev), a.deadline, hrow);
+    }
+    if (!ok && p.lane == 0) {
+      abort_flag = 1;
+      report_failure(a.status, a.status_host, kStatusTimeout);
+    }
+    __syncthreads();
+    if constexpr (WAVES > kTeamWaves) {
+      if (p.wave >= 8) __builtin_amdgcn_s_setprio(3);
+      else if (p.wave >= 4) __builtin_amdgcn_s_setprio(2);
+    }
+    int aborted_now = abort_flag;
+    const float x = x_next;
+    xoff += xstep;
+    if (t + 1 < a.T) x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
+    float acc[M];
+#pragma unroll
+    for (int r = 0; r < M; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) {
+      if (s < a.spr) {
+        float hv[RW];
+        if constexpr (kTwoSteps) {
+#pragma unroll
+          for (int r = 0; r < RW; ++r) hv[r] = hrow[wcol[r][s]];
+#pragma unroll
+          for (int r = 0; r < RW; ++r) acc[r] = fmaf(wval[r][s], hv[r], acc[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < RW; ++r) hv[r] = hrow[pr[r][s].column()];
+#pragma unroll
+          for (int r = 0; r < RW; ++r) pr[r][s].fma(acc[r], hv[r]);
+        }
+      }
+    }
+    const float sum = RowReduce<M>::reduce(acc, p.lane);
+    if constexpr (WAVES > kTeamWaves) __builtin_amdgcn_s_setprio(0);
+    asm volatile("" : "+v"(aborted_now) : "v"(sum));  // keep the test after the arithmetic
+    if (aborted_now) return false;
+    debug_jitter(a.jitter_seed, a.jitter_span, p.wave, t);
+    if (owner && !(p.rank == a.skip_wg && t == a.skip_step)) {
+      const uint32_t hb = relu_bits(sum + x) | tag_bit(S);
+      const int row = p.r0 + my_row;
+      const uint32_t off = ((S & 1u) * a.Npad + row) * 4u;
+      __builtin_amdgcn_raw_buffer_store_b32(hb, shared, off, 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b32(hb, region, off, 0, kPlain);
+      a.H[((size_t)t * a.B + p.b) * N + row] = __uint_as_float(hb & 0x7fffffffu);
+    }
+    return true;
+  };
+  if constexpr (kTwoSteps) {
+    for (int t = 0; t < a.T; t += 2) {
+      if (!step(t, lds)) return;
+      if (t + 1 < a.T && !step(t + 1, lds + stride)) return;
+    }
+  } else {
+    for (int t = 0; t < a.T; ++t)
+      if (!step(t, lds + (t & 1) * stride)) return;
+  }
+}
+
 }  // namespace
 
-const void* kFloorSplitKernel = reinterpret_cast<const void*>(&floor_split_kernel);
+const void* kFloorSplitKernel = reinterpret_cast<const void*>(&floor_split_kernel<8>);
+const void* kFloorSplitKernel12 = reinterpret_cast<const void*>(&floor_split_kernel<12>);
 
 #define PRNN_DENSE_SPLIT(R, JJ) {kF16, R, JJ, reinterpret_cast<const void*>(&dense_split_kernel<R, JJ>)}
 
@@ -272,6 +395,16 @@ const KernelEntry kDenseSplitF16Kernels[] = {
     PRNN_DENSE_SPLIT(4, 8), PRNN_DENSE_SPLIT(5, 10), PRNN_DENSE_SPLIT(6, 12), PRNN_DENSE_SPLIT(7, 14),
     PRNN_DENSE_SPLIT(2, 8), PRNN_DENSE_SPLIT(3, 10), PRNN_DENSE_SPLIT(3, 12), PRNN_DENSE_SPLIT(4, 16),
     PRNN_DENSE_SPLIT(5, 20),
+    {0, 0, 0, nullptr},
+};
+
+#define PRNN_SPARSE_SPLIT(R, S, W) \
+  {kF16, R, S, reinterpret_cast<const void*>(&sparse_split_kernel<R, S, W, 2>), W}
+// Sparse fp16 layers on two XCDs per batch row: (rows per wave, 64-pair slots)
+// for the 2304- and 5760-neuron layers at 8 and 12 waves per workgroup.
+const KernelEntry kSparseSplitF16Kernels[] = {
+    PRNN_SPARSE_SPLIT(5, 4, 8), PRNN_SPARSE_SPLIT(5, 9, 8), PRNN_SPARSE_SPLIT(5, 10, 8), PRNN_SPARSE_SPLIT(12, 1, 8),
+    PRNN_SPARSE_SPLIT(12, 5, 8), PRNN_SPARSE_SPLIT(8, 5, 12), PRNN_SPARSE_SPLIT(4, 9, 12), PRNN_SPARSE_SPLIT(4, 10, 12),
     {0, 0, 0, nullptr},
 };
 

@@ -270,3 +270,152 @@ def test_split_floor_follows_the_layer(handle, N, B):
     assert handle.last_plan()["xcds_per_row"] == expect_xp(N, B)
     expect = torch.arange(1, T + 1, dtype=torch.float32, device="cuda").view(T, 1, 1).expand(T, B, N)
     assert torch.equal(out, expect)
+
+
+# ---------------------------------------------------------------------------
+# row-balanced sparse fp16 layers on two XCDs per batch row: automatic for
+# blocks of more than 60 slots per wave (5 % at N = 5760), forced at any size
+# ---------------------------------------------------------------------------
+def run_sparse(handle, d):
+    g = to_dev(d)
+    H = handle.forward_sparse(g["col"], g["val"], g["X"], g["h0"])
+    handle.synchronize()
+    return H.cpu().numpy()
+
+
+def sparse_ref(d):
+    return oracle.forward_sparse(d["col"], d["val"], d["X"], d["h0"])
+
+
+def test_sparse_split_automatic_for_the_5_percent_layer(handle):
+    from persistent_rnn_fwd_amd.inputs import WORKLOADS
+    w = WORKLOADS["sparse5_f16_n5760"].with_(T=40, h0="randn")
+    d = generate(w, seed=71)
+    H = run_sparse(handle, d)
+    p = handle.last_plan()
+    assert p["xcds_per_row"] == 2 and p["waves_per_wg"] == 12, p
+    assert oracle.tolerance_ratio(H, sparse_ref(d), oracle.TOL_F16) <= 1.0
+    for name in ("sparse1_f16_n5760", "sparse10_f16_n1792", "sparse25_f16_n2304"):   # lighter blocks stay on one XCD
+        run_sparse(handle, generate(WORKLOADS[name].with_(T=2)))
+        assert handle.last_plan()["xcds_per_row"] == 1, name
+
+
+@pytest.mark.parametrize("N,B,T,K", [(1000, 3, 6, 100), (2304, 4, 5, 576), (777, 4, 5, 50), (5760, 2, 4, 288),
+                                     (300, 1, 5, 17), (2304, 4, 4, 230)])
+def test_sparse_split_forced_parity(handle, N, B, T, K):
+    w = Workload(f"sparse_{N}", "sparse", N, B, T, "f16", K=K, seed=N + K, h0="randn")
+    d = generate(w)
+    handle.set_xcds_per_row(2)
+    try:
+        H = run_sparse(handle, d)
+        p = handle.last_plan()
+    finally:
+        handle.set_xcds_per_row(0)
+    assert p["layout"] == binding.LAYOUT_TEAM and p["xcds_per_row"] == 2, p
+    r = oracle.tolerance_ratio(H, sparse_ref(d), oracle.TOL_F16)
+    assert r <= 1.0, f"N={N} B={B} K={K}: error ratio {r:.3g} plan={p}"
+
+
+@pytest.mark.parametrize("N,K", [(1792, 179), (5760, 288)])
+def test_sparse_split_small_integers_bitwise(handle, N, K):
+    rng = np.random.default_rng(N + K)
+    T, B = 5, 4
+    col = np.stack([np.sort(rng.choice(N, K, replace=False)) for _ in range(N)]).astype(np.int16)
+    val = (rng.choice([-1.0, 1.0], (N, K)) * (rng.random((N, K)) < 0.03)).astype(np.float16)
+    X = rng.integers(-5, 6, size=(T, B, N)).astype(np.float32)
+    h0 = rng.integers(-5, 6, size=(B, N)).astype(np.float32)
+    d = {"col": col, "val": val, "X": X, "h0": h0}
+    ref = sparse_ref(d)
+    assert np.abs(ref).max() < 2 ** 20
+    handle.set_xcds_per_row(2)
+    try:
+        H = run_sparse(handle, d)
+        assert handle.last_plan()["xcds_per_row"] == 2
+    finally:
+        handle.set_xcds_per_row(0)
+    np.testing.assert_array_equal(H, ref)
+
+
+def test_sparse_split_limits(handle):
+    """Two XCDs need B <= 4; four are not offered to sparse layers; fp32
+    values keep one XCD per batch row."""
+    col = torch.zeros(1000, 10, dtype=torch.int16, device="cuda")
+    val = torch.zeros(1000, 10, dtype=torch.float16, device="cuda")
+    handle.set_layout(binding.LAYOUT_TEAM)
+    try:
+        for xcds, B in ((2, 5), (4, 2)):
+            handle.set_xcds_per_row(xcds)
+            with pytest.raises(PrnnError) as e:
+                handle.forward_sparse(col, val, torch.zeros(2, B, 1000, device="cuda"))
+            assert e.value.status == binding.NOT_SUPPORTED
+        handle.set_xcds_per_row(2)
+        handle.forward_sparse(col, val.float(), torch.zeros(2, 2, 1000, device="cuda"))
+        handle.synchronize()
+        assert handle.last_plan()["xcds_per_row"] == 1
+    finally:
+        handle.set_xcds_per_row(0)
+        handle.set_layout(binding.LAYOUT_AUTO)
+
+
+@pytest.mark.parametrize("waves", [8, 12])
+def test_sparse_split_floor_in_the_layer_plan(handle, waves):
+    """The floor with a forced width and wave count runs the split protocol in
+    that shape (the bench measures each layer's floor in its own plan)."""
+    N, B, T = 5760, 4, 6
+    out = torch.full((T, B, N), float("nan"), device="cuda")
+    handle.set_xcds_per_row(2)
+    handle.set_team_waves(waves)
+    try:
+        handle.sync_floor(N, B, T, out=out)
+        handle.synchronize()
+        p = handle.last_plan()
+    finally:
+        handle.set_xcds_per_row(0)
+        handle.set_team_waves(0)
+    assert p["xcds_per_row"] == 2 and p["waves_per_wg"] == waves, p
+    expect = torch.arange(1, T + 1, dtype=torch.float32, device="cuda").view(T, 1, 1).expand(T, B, N)
+    assert torch.equal(out, expect)
+
+
+def test_sparse_split_repeats_jitter_and_chunks_bitwise(gpu):
+    from persistent_rnn_fwd_amd.inputs import WORKLOADS
+    w = WORKLOADS["sparse5_f16_n5760"].with_(T=18, h0="randn")
+    d = generate(w, seed=73)
+    g = to_dev(d)
+    out = torch.empty_like(g["X"])
+    with Handle() as h:
+        out.fill_(float("nan"))
+        first = h.forward_sparse(g["col"], g["val"], g["X"], g["h0"], out=out).clone()
+        h.synchronize()
+        assert h.last_plan()["xcds_per_row"] == 2 and not torch.isnan(first).any()
+        for seed in (0, 1, 2):
+            h.debug_jitter(seed, 48 if seed else 0)
+            out.fill_(float("nan"))
+            h.forward_sparse(g["col"], g["val"], g["X"], g["h0"], out=out)
+            h.synchronize()
+            assert torch.equal(out, first)
+        h.debug_jitter(0, 0)
+        # the sequence in two calls, with a call of 3 batch rows between them
+        a = h.forward_sparse(g["col"], g["val"], g["X"][:7].contiguous(), g["h0"])
+        h.forward_sparse(g["col"], g["val"], g["X"][:4, :3].contiguous(), g["h0"][:3].contiguous())
+        b = h.forward_sparse(g["col"], g["val"], g["X"][7:].contiguous(), a[-1].contiguous())
+        h.synchronize()
+        assert torch.equal(torch.cat([a, b]), first)
+    assert oracle.tolerance_ratio(first.cpu().numpy(), sparse_ref(d), oracle.TOL_F16) <= 1.0
+
+
+def test_sparse_split_watchdog(gpu):
+    from persistent_rnn_fwd_amd.inputs import WORKLOADS
+    w = WORKLOADS["sparse5_f16_n5760"].with_(T=10, h0="randn")
+    d = generate(w, seed=75)
+    g = to_dev(d)
+    with Handle() as h:
+        h.set_watchdog_us(2000)
+        h.debug_skip_publish(3, 4)
+        h.forward_sparse(g["col"], g["val"], g["X"], g["h0"])
+        with pytest.raises(PrnnError) as e:
+            h.synchronize()
+        assert e.value.status == binding.EXECUTION_FAILED
+        H = h.forward_sparse(g["col"], g["val"], g["X"], g["h0"])
+        h.synchronize()
+        assert oracle.tolerance_ratio(H.cpu().numpy(), sparse_ref(d), oracle.TOL_F16) <= 1.0
