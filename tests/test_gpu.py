@@ -355,14 +355,21 @@ def test_plan_of_large_sparse_layers(handle):
     per workgroup run 12-wave workgroups, above 16 rows 16-wave ones first,
     where an instance fits (1 % at N = 5760: 16 waves of 12 rows; 5 % at
     N = 5760, whose 12 x 5 block does not fit 4 waves per SIMD: 12 waves of 15
-    rows; N = 2304: 12 waves of 6 rows); N = 1792 keeps 8 waves of 7 rows."""
-    for name, waves, rows in [("sparse1_f16_n5760", 16, 12), ("sparse5_f16_n5760", 12, 15),
-                              ("sparse10_f16_n2304", 12, 6), ("sparse25_f16_n2304", 12, 6),
-                              ("sparse10u_f16_n2304", 12, 6), ("sparse10_f16_n1792", 8, 7)]:
+    rows on one XCD, or, as it runs by default, 12 waves of 8 rows on two XCDs
+    per batch row; N = 2304: 12 waves of 6 rows); N = 1792 keeps 8 waves of 7
+    rows."""
+    for name, waves, rows, xcds in [("sparse1_f16_n5760", 16, 12, 0), ("sparse5_f16_n5760", 12, 15, 1),
+                                    ("sparse5_f16_n5760", 12, 8, 0), ("sparse10_f16_n2304", 12, 6, 0),
+                                    ("sparse25_f16_n2304", 12, 6, 0), ("sparse10u_f16_n2304", 12, 6, 0),
+                                    ("sparse10_f16_n1792", 8, 7, 0)]:
         w = WORKLOADS[name].with_(T=6)
         d = generate(w, seed=71)
-        H = run(handle, "sparse", d)
-        p = handle.last_plan()
+        handle.set_xcds_per_row(xcds)
+        try:
+            H = run(handle, "sparse", d)
+            p = handle.last_plan()
+        finally:
+            handle.set_xcds_per_row(0)
         assert p["layout"] == binding.LAYOUT_TEAM and p["waves_per_wg"] == waves and p["rows_per_wave"] == rows, p
         assert_parity(H, reference("sparse", d), oracle.TOL_F16, name)
     # forced wave counts: 8 for the 1 % layer (23 rows per wave), 16 where no

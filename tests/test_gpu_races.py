@@ -60,7 +60,7 @@ PATHS = [
     ("sparse10_f16_n1792", binding.LAYOUT_TEAM, binding.MATH_AUTO, 0),
     ("sparse10_f16_n1792", binding.LAYOUT_SPREAD, binding.MATH_AUTO, 0),
     ("sparse1_f16_n5760", binding.LAYOUT_TEAM, binding.MATH_AUTO, 0),    # 16-wave workgroups
-    ("sparse5_f16_n5760", binding.LAYOUT_TEAM, binding.MATH_AUTO, 0),    # 12-wave workgroups
+    ("sparse5_f16_n5760", binding.LAYOUT_TEAM, binding.MATH_AUTO, 0),    # two XCDs per batch row, 12-wave workgroups
 ]
 
 
