@@ -311,8 +311,7 @@ prnnStatus_t prnn_forward_layer_sparse(prnnHandle_t handle, int N, int I, int B,
  * Performance of Recurrent Neural Networks on GPUs", Abstract, entire-network
  * stage):
  *
- *   X_0       = prnn_project(x, U[0], bias[0])           (into Xbuf)
- *   H[0][t]   = max(0, X_0[t] + W[0] H[0][t-1])
+ *   H[0][t]   = max(0, bias[0] + U[0] x[t] + W[0] H[0][t-1])
  *   H[l][t]   = max(0, bias[l] + U[l] H[l-1][t] + W[l] H[l][t-1]),  l >= 1
  *   H[l][-1]  = h0[l] (zeros if h0 or h0[l] is NULL)
  *
@@ -320,17 +319,19 @@ prnnStatus_t prnn_forward_layer_sparse(prnnHandle_t handle, int N, int I, int B,
  * so the layers run at the same time on separate XCDs (layer l, batch row b
  * on XCD l B + b; hence L B <= 8), keeping their weights in registers
  * widened to fp32 (prnnStackMode_t: in blocks of steps, layer l + 1 one block
- * behind layer l with the input projections between the launches; or fused
- * per step).  Where the weights do not fit (N > 1792) the layers run one
- * after another (prnn_forward_layer_dense each, with layer l's output as
- * layer l + 1's input).  x [T][B][I] (fp32 or fp16); U[0] [N][I],
- * U[l >= 1] [N][N], W[l] [N][N], all fp16, 16-byte aligned; bias[l] [N] or
- * NULL; Xbuf [T][B][N] fp32 workspace; H[l] [T][B][N] fp32 outputs.  U, bias,
- * W, h0 and H are host arrays of L device pointers (bias and h0 may be NULL
- * arrays).  All device buffers are the caller's.  H[1] .. H[L-1] (blocked)
- * or H[0] .. H[L-2] (fused) also carry intermediate values (the next layer's
- * projected input, or a not-yet-written marker) before the results
- * overwrite them.  Not traced.
+ * behind layer l, each launch computing its blocks' input products itself
+ * before the recurrence; or fused per step).  Where the weights do not fit
+ * (N > 1792) the layers run one after another (prnn_forward_layer_dense
+ * each, with layer l's output as layer l + 1's input).  x [T][B][I] (fp32 or
+ * fp16); U[0] [N][I], U[l >= 1] [N][N], W[l] [N][N], all fp16, 16-byte
+ * aligned; bias[l] [N] or NULL; Xbuf [T][B][N] fp32 workspace (written by
+ * the fused mode and the layer-by-layer mode with layer 0's, or each layer's,
+ * input product; the blocked mode does not use it); H[l] [T][B][N] fp32
+ * outputs.  U, bias, W, h0 and H are host arrays of L device pointers (bias
+ * and h0 may be NULL arrays).  All device buffers are the caller's.  H[0] ..
+ * H[L-1] (blocked) or H[0] .. H[L-2] (fused) also carry intermediate values
+ * (the layer's projected input, or a not-yet-written marker) before the
+ * results overwrite them.  Not traced.
  * BAD_PARAM: NULL handle/arrays/pointers, L < 1, N < 1, I < 1, B outside
  * [1, 8], T < 0, unknown x_type, misalignment, any output overlapping any
  * input, the workspace or another output, the workspace overlapping an
@@ -340,8 +341,9 @@ prnnStatus_t prnn_forward_layer_sparse(prnnHandle_t handle, int N, int I, int B,
  * a bounded wait expired, or x exceeded the fp16 range of its split.
  * T == 0 enqueues nothing and returns SUCCESS. */
 /* How prnn_forward_stack_dense runs the layers (see there).
- * BLOCKED: blocks of about 64 steps, layer l one block behind layer l - 1,
- *   the input projections of the next blocks between the launches.
+ * BLOCKED: blocks of about 64 steps, layer l one block behind layer l - 1;
+ *   a launch starts with its blocks' input products (each workgroup its own
+ *   rows, on the matrix cores) and then runs the recurrence.
  * FUSED: one launch; each layer l >= 1 forms U_l H_{l-1}[t] itself at every
  *   step (N <= 1280).
  * LAYERS: one layer after another (prnn_forward_layer_dense each).
@@ -454,6 +456,33 @@ prnnStatus_t prnn_set_math(prnnHandle_t handle, prnnMath_t mode);
 /* Upper bound, in microseconds, on one wait for h_{t-1} (default 200000).
  * A wait that exceeds it stops the run and reports EXECUTION_FAILED. */
 prnnStatus_t prnn_set_watchdog_us(prnnHandle_t handle, uint32_t microseconds);
+
+/* How the persistent kernels are dispatched.  Every workgroup of such a
+ * kernel waits for the others' rows of h_{t-1}, so all of them must be
+ * resident at once.
+ *  - COOPERATIVE: hipLaunchCooperativeKernel; the runtime checks that the
+ *    grid fits the device and guarantees that it runs whole.
+ *  - PLAIN: hipLaunchKernel.  The library checks that the grid fits the
+ *    device with nothing else on it (occupancy of the kernel at its LDS size
+ *    times the compute units; NOT_SUPPORTED otherwise) and that workgroups
+ *    are dealt to the XCDs as the layouts assume.  Kernels of other streams
+ *    or processes that hold compute units while such a launch starts can
+ *    keep some of its workgroups waiting: the resident ones then stop when
+ *    the watchdog expires and the call reports EXECUTION_FAILED (nothing
+ *    hangs).  A stream's own kernels never overlap (streams are in order).
+ * The kernels and results are the same either way; a plain launch starts
+ * 10-20 us sooner after the kernel before it.  The default is PLAIN where
+ * plain launches deal workgroups to the XCDs as the layouts assume (checked
+ * when the handle is created), else COOPERATIVE.  Choosing a kind whose
+ * placement check failed leaves the layouts that need it unavailable
+ * (NOT_SUPPORTED from the calls that would use them).  BAD_PARAM for an
+ * unknown kind. */
+typedef enum {
+  PRNN_LAUNCH_COOPERATIVE = 0,
+  PRNN_LAUNCH_PLAIN = 1,
+  PRNN_LAUNCH_MAX_ENUM = 0x7FFFFFFF  /* not a value: keeps every int in the type's range */
+} prnnLaunch_t;
+prnnStatus_t prnn_set_launch(prnnHandle_t handle, prnnLaunch_t kind);
 
 /* Copies the plan of the last successful forward call into *info. */
 prnnStatus_t prnn_get_last_plan(prnnHandle_t handle, prnnPlanInfo_t* info);

@@ -30,6 +30,7 @@ EXCHANGE_AUTO, EXCHANGE_DIRECT, EXCHANGE_RELAY = 0, 1, 2
 LAYOUT_AUTO, LAYOUT_SPREAD, LAYOUT_TEAM = 0, 1, 2
 MATH_AUTO, MATH_EXACT, MATH_SPLIT, MATH_HALF = 0, 1, 2, 3
 STACK_AUTO, STACK_BLOCKED, STACK_FUSED, STACK_LAYERS = 0, 1, 2, 3
+LAUNCH_COOPERATIVE, LAUNCH_PLAIN = 0, 1
 TRACE_WORDS = 8  # per-wave trace record: see Handle.get_trace
 
 # Every function include/prnn.h declares, with its ctypes signature.
@@ -63,6 +64,7 @@ SIGNATURES = {
     "prnn_forward_stack_dense": (_I, [_H, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "prnn_forward_stack_sparse": (_I, [_H, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
     "prnn_set_stack_mode": (_I, [_H, _I]),
+    "prnn_set_launch": (_I, [_H, _I]),
     "prnn_forward_dense_noalloc": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
 }
 
@@ -193,6 +195,10 @@ class Handle:
     def set_xcds_per_row(self, xcds: int):
         """XCDs per batch row of dense fp16 layers for later calls: 0 (automatic), 1, 2 or 4."""
         _check("prnn_set_xcds_per_row", self._lib.prnn_set_xcds_per_row(self._h, int(xcds)))
+
+    def set_launch(self, kind: int):
+        """LAUNCH_COOPERATIVE or LAUNCH_PLAIN dispatch of the persistent kernels for later calls."""
+        _check("prnn_set_launch", self._lib.prnn_set_launch(self._h, int(kind)))
 
     def set_watchdog_us(self, us: int):
         _check("prnn_set_watchdog_us", self._lib.prnn_set_watchdog_us(self._h, int(us)))

@@ -14,6 +14,7 @@ struct DeviceFacts {
   int num_cu = 0;
   size_t lds_per_block = 0;
   bool placement_round_robin = false;  // workgroup i of a cooperative launch runs on XCD (i + c) % 8
+  bool plain_placement = false;        // ... and of a plain launch (then launched plainly)
 };
 
 // Words of exchange memory a team-layout call of width N needs: [8 XCD][2 slots][Npad].

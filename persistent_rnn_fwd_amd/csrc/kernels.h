@@ -129,12 +129,20 @@ void launch_team_fill(uint32_t* ring, int npad, uint32_t v, hipStream_t stream);
 constexpr int kMaxStack = 8;
 struct StackArgs {
   const void* W[kMaxStack];      // fp16 [N][N] recurrent weights
-  const void* U[kMaxStack];      // fp16 [N][N] input weights of layers >= 1 (U[0] unused)
-  const float* bias[kMaxStack];  // [N] or nullptr, layers >= 1 (layer 0's is in X0)
+  const void* U[kMaxStack];      // fp16 [N][p_cols] input weights (fused: layers >= 1 only)
+  const float* bias[kMaxStack];  // [N] or nullptr (fused: layers >= 1; layer 0's is in X0)
   const float* h0[kMaxStack];    // [B][N] or nullptr (zeros)
   float* H[kMaxStack];           // [Tl][B][N] outputs (fused: H[0 .. L-2] filled with 0xFFFFFFFF first)
   const float* X[kMaxStack];     // [Tl][B][N] pre-activations (fused: layer 0 only; may alias H[l])
   int Tl[kMaxStack];             // steps of layer l in this launch (<= T; 0: idle)
+  // Blocked mode: layer l's input for this launch's block ([Tl][B][p_cols],
+  // fp32 or fp16), whose product with U[l] plus bias[l] the launch writes
+  // into H[l] before the recurrence reads it there; nullptr: X[l] already
+  // holds the pre-activations.
+  const void* P[kMaxStack];
+  int p_cols[kMaxStack];         // I for layer 0, N above
+  int p_f32[kMaxStack];          // 1: fp32 input (split into two fp16 terms), 0: fp16
+  int p_vec[kMaxStack];          // 1: 16-byte loads (p_cols % 8 == 0, P and U 16-byte aligned)
   uint32_t* ring;                // [8][2][Npad]
   uint32_t* status;
   uint32_t* status_host;         // host-visible mirror of failures, or nullptr
@@ -145,6 +153,9 @@ struct StackArgs {
   uint32_t jitter_seed, jitter_span;  // test-only publish delay (span 0: off)
 };
 // (rmax = rows per wave, cap = chunks of each part)
+// Dynamic LDS a blocked launch needs for its in-launch input product (the
+// 64 x 64 tiles' staging; the recurrence's rows reuse it afterwards).
+constexpr int kStackProjLds = 73728;
 extern const KernelEntry kStackFusedKernels[];
 extern const KernelEntry kStackBlockedKernels[];
 

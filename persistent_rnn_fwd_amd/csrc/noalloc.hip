@@ -65,23 +65,31 @@ prnnStatus_t setup_device(int dev, hipStream_t stream, DeviceState** out) {
   d.ptr = static_cast<uint32_t*>(p);
   d.facts.num_cu = props.multiProcessorCount;
   d.facts.lds_per_block = props.sharedMemPerBlock;
-  // Workgroup placement over the XCDs, as prnn_create checks it, with the
-  // array as the output of the placement kernel (one word per workgroup).
+  // Workgroup placement over the XCDs, as prnn_create checks it (for
+  // cooperative and for plain launches), with the array as the output of the
+  // placement kernel (one word per workgroup).
   const int grid = d.facts.num_cu;
-  bool ok = grid >= 8 && (size_t)grid <= kRingWords && grid <= 1024;
-  uint32_t host[1024];
-  if (ok) {
-    uint32_t* out_words = d.ptr;
-    void* args[] = {&out_words};
-    ok = hipLaunchCooperativeKernel(prnn::kPlacementKernel, dim3(grid), dim3(64), args, 0, nullptr) == hipSuccess &&
-         hipMemcpy(host, d.ptr, (size_t)grid * 4, hipMemcpyDeviceToHost) == hipSuccess;
-  }
-  if (ok) {
-    const uint32_t c = host[0] % 8u;
-    for (int i = 0; i < grid && ok; ++i) ok = host[i] < 8u && (host[i] + 8u - (uint32_t)i % 8u) % 8u == c;
-  }
-  (void)hipGetLastError();
-  d.facts.placement_round_robin = ok;
+  auto placed = [&](bool cooperative) {
+    bool ok = grid >= 8 && (size_t)grid <= kRingWords && grid <= 1024;
+    uint32_t host[1024];
+    if (ok) {
+      uint32_t* out_words = d.ptr;
+      void* args[] = {&out_words};
+      const hipError_t e =
+          cooperative ? hipLaunchCooperativeKernel(prnn::kPlacementKernel, dim3(grid), dim3(64), args, 0, nullptr)
+                      : hipLaunchKernel(prnn::kPlacementKernel, dim3(grid), dim3(64), args, 0, nullptr);
+      ok = e == hipSuccess && hipMemcpy(host, d.ptr, (size_t)grid * 4, hipMemcpyDeviceToHost) == hipSuccess;
+    }
+    if (ok) {
+      const uint32_t c = host[0] % 8u;
+      for (int i = 0; i < grid && ok; ++i) ok = host[i] < 8u && (host[i] + 8u - (uint32_t)i % 8u) % 8u == c;
+    }
+    (void)hipGetLastError();
+    return ok;
+  };
+  d.facts.placement_round_robin = placed(true);
+  d.facts.plain_placement = placed(false);
+  const bool ok = d.facts.placement_round_robin || d.facts.plain_placement;
   return d.setup_status = ok ? PRNN_STATUS_SUCCESS : PRNN_STATUS_NOT_SUPPORTED;
 }
 

@@ -36,6 +36,20 @@ struct prnnContext {
   uint32_t* d_ring = nullptr;
   size_t ring_cap_words = 0;
   bool placement_round_robin = false;  // workgroup i runs on XCD (i + c) % 8
+  // Dispatch of the persistent kernels (prnn_set_launch), and whether each
+  // kind deals workgroups to the XCDs round-robin (placement_round_robin is
+  // the chosen kind's).
+  int launch_kind = PRNN_LAUNCH_COOPERATIVE;
+  bool coop_placement = false;
+  bool plain_placement = false;
+  // Workgroups per compute unit of the kernels launched plainly, at their
+  // block and LDS sizes (occupancy queries are not free).
+  struct Fit {
+    const void* fn;
+    int block, lds, per_cu;
+  };
+  Fit fits[48] = {};
+  int nfits = 0;
   int exchange = PRNN_EXCHANGE_AUTO;
   int layout = PRNN_LAYOUT_AUTO;
   int ring_layout = -1;  // layout the ring was last reset for
@@ -572,10 +586,29 @@ void log_plan(const prnnContext* h, const char* what, int N, int B, int T, const
                info.math >= 0 && info.math <= 3 ? maths[info.math] : "?", (unsigned long long)info.first_step);
 }
 
+// A persistent kernel's launch, cooperative or plain (prnn_set_launch).  A
+// plain one is refused (hipErrorCooperativeLaunchTooLarge, as the
+// cooperative launch reports it) unless the whole grid fits the device at
+// once.
+hipError_t launch_persistent(prnnContext* h, const void* fn, int grid, int block, void** args, int lds,
+                             hipStream_t stream) {
+  if (lds > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+    return hipErrorInvalidValue;
+  if (h->launch_kind != PRNN_LAUNCH_PLAIN)
+    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(block), args, static_cast<unsigned>(lds), stream);
+  int per_cu = -1;
+  for (int i = 0; i < h->nfits; ++i)
+    if (h->fits[i].fn == fn && h->fits[i].block == block && h->fits[i].lds == lds) per_cu = h->fits[i].per_cu;
+  if (per_cu < 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, static_cast<size_t>(lds)) != hipSuccess)
+      return hipErrorInvalidValue;
+    if (h->nfits < static_cast<int>(sizeof(h->fits) / sizeof(h->fits[0]))) h->fits[h->nfits++] = {fn, block, lds, per_cu};
+  }
+  if ((long long)per_cu * h->num_cu < grid) return hipErrorCooperativeLaunchTooLarge;
+  return hipLaunchKernel(fn, dim3(grid), dim3(block), args, static_cast<size_t>(lds), stream);
+}
+
 prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream_t stream) {
-  if (p.lds_bytes > 65536 &&
-      hipFuncSetAttribute(p.k->fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes) != hipSuccess)
-    return PRNN_STATUS_NOT_SUPPORTED;
   a.step0 = static_cast<uint32_t>(h->step);
   a.deadline = static_cast<uint64_t>(h->watchdog_us) * 100ull;  // 100 MHz constant clock
   a.skip_wg = h->skip_wg;
@@ -590,8 +623,7 @@ prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream
     a.trace = h->d_trace;
   }
   void* args[] = {&a};
-  hipError_t e = hipLaunchCooperativeKernel(p.k->fn, dim3(p.grid), dim3(p.block), args,
-                                            static_cast<unsigned>(p.lds_bytes), stream);
+  hipError_t e = launch_persistent(h, p.k->fn, p.grid, p.block, args, p.lds_bytes, stream);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return hip_status(e);
@@ -618,16 +650,19 @@ prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream
   return PRNN_STATUS_SUCCESS;
 }
 
-// The relay and team exchanges rely on workgroup i of a cooperative launch
-// running on XCD (i + c) % 8 for one constant c.  Checked once per handle.
-bool check_placement(int num_cu) {
+// The relay and team exchanges rely on workgroup i of a launch running on
+// XCD (i + c) % 8 for one constant c.  Checked once per handle for
+// cooperative launches, and for plain ones when they are chosen.
+bool check_placement(int num_cu, bool cooperative) {
   const int grid = num_cu;
   void* p = nullptr;
   if (grid < 8 || hipMalloc(&p, grid * 4) != hipSuccess) return false;
   uint32_t* d = static_cast<uint32_t*>(p);
   void* args[] = {&d};
-  bool ok = hipLaunchCooperativeKernel(prnn::kPlacementKernel, dim3(grid), dim3(64), args, 0, nullptr) == hipSuccess &&
-            hipDeviceSynchronize() == hipSuccess;
+  const hipError_t e =
+      cooperative ? hipLaunchCooperativeKernel(prnn::kPlacementKernel, dim3(grid), dim3(64), args, 0, nullptr)
+                  : hipLaunchKernel(prnn::kPlacementKernel, dim3(grid), dim3(64), args, 0, nullptr);
+  bool ok = e == hipSuccess && hipDeviceSynchronize() == hipSuccess;
   uint32_t* host = new (std::nothrow) uint32_t[grid];
   ok = ok && host != nullptr && hipMemcpy(host, d, grid * 4, hipMemcpyDeviceToHost) == hipSuccess;
   if (ok) {
@@ -802,7 +837,10 @@ prnnStatus_t prnn::forward_dense_on(const DeviceFacts& dev, uint32_t* ring, uint
   prnnContext c;
   c.num_cu = dev.num_cu;
   c.lds_per_block = dev.lds_per_block;
-  c.placement_round_robin = dev.placement_round_robin;
+  c.coop_placement = dev.placement_round_robin;
+  c.plain_placement = dev.plain_placement;
+  c.launch_kind = dev.plain_placement ? PRNN_LAUNCH_PLAIN : PRNN_LAUNCH_COOPERATIVE;
+  c.placement_round_robin = dev.plain_placement || dev.placement_round_robin;
   c.layout = PRNN_LAYOUT_TEAM;
   c.d_ring = ring;
   c.d_status = status;
@@ -877,12 +915,20 @@ prnnStatus_t prnn_create(prnnHandle_t* handle) {
     return PRNN_STATUS_INTERNAL_ERROR;
   }
   h->h_status_dev = static_cast<uint32_t*>(hd);
-  h->placement_round_robin = check_placement(h->num_cu);
+  // Plain launches where their workgroups are dealt as the layouts assume:
+  // they start 10-20 us sooner after the previous kernel than cooperative ones.
+  h->coop_placement = check_placement(h->num_cu, true);
+  h->plain_placement = check_placement(h->num_cu, false);
+  h->launch_kind = h->plain_placement ? PRNN_LAUNCH_PLAIN : PRNN_LAUNCH_COOPERATIVE;
+  h->placement_round_robin = h->plain_placement || h->coop_placement;  // the chosen kind's
   const char* log = std::getenv("PRNN_LOG");
   h->log = log != nullptr && log[0] != '\0' && std::strcmp(log, "0") != 0;
   if (h->log)
-    std::fprintf(stderr, "prnn: handle on device %d, %d compute units, %zu bytes of LDS per workgroup, team layout %s\n",
-                 h->device, h->num_cu, (size_t)h->lds_per_block, h->placement_round_robin ? "available" : "unavailable");
+    std::fprintf(stderr,
+                 "prnn: handle on device %d, %d compute units, %zu bytes of LDS per workgroup, team layout %s, "
+                 "%s launches\n",
+                 h->device, h->num_cu, (size_t)h->lds_per_block, h->placement_round_robin ? "available" : "unavailable",
+                 h->launch_kind == PRNN_LAUNCH_PLAIN ? "plain" : "cooperative");
   *handle = h;
   return PRNN_STATUS_SUCCESS;
 }
@@ -1186,8 +1232,13 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B
     return PRNN_STATUS_SUCCESS;
   }
   p.k = mode == PRNN_STACK_BLOCKED ? kb : kf;
-  p.lds_bytes = mode == PRNN_STACK_BLOCKED ? lds_b : lds_f;
-  // Layer 0's input projection, checked before anything is enqueued.
+  // Blocked launches compute their input products in the launch (in the LDS
+  // the recurrence's rows use afterwards).
+  p.lds_bytes = mode == PRNN_STACK_BLOCKED ? std::max(lds_b, prnn::kStackProjLds) : lds_f;
+  if ((size_t)p.lds_bytes + 256 > h->lds_per_block) return PRNN_STATUS_NOT_SUPPORTED;
+  // Layer 0's input projection (x, U[0], bias[0] and the workspace), checked
+  // before anything is enqueued; the fused mode runs it into the workspace
+  // first.
   prnn::ProjArgs pa;
   bool vec = false;
   prnnStatus_t st = prepare_layer_projection(h, N, I, B, T, x_type, x, PRNN_DATA_HALF, U[0],
@@ -1198,8 +1249,10 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B
   const int Npad = (N + 3) & ~3;
   st = ensure_ring(h, p, B, Npad, stream);
   if (st != PRNN_STATUS_SUCCESS) return st;
-  st = hip_status(prnn::launch_project(pa, x_type == PRNN_DATA_FLOAT, vec, stream));
-  if (st != PRNN_STATUS_SUCCESS) return st;
+  if (mode == PRNN_STACK_FUSED) {
+    st = hip_status(prnn::launch_project(pa, x_type == PRNN_DATA_FLOAT, vec, stream));
+    if (st != PRNN_STATUS_SUCCESS) return st;
+  }
 
   prnn::StackArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -1226,8 +1279,7 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B
     a.step0 = static_cast<uint32_t>(h->step);
     a.x_bytes = static_cast<uint32_t>((size_t)Tlaunch * B * N * 4);
     void* args[] = {&a};
-    hipError_t e = hipLaunchCooperativeKernel(p.k->fn, dim3(p.grid), dim3(p.block), args,
-                                              static_cast<unsigned>(p.lds_bytes), stream);
+    hipError_t e = launch_persistent(h, p.k->fn, p.grid, p.block, args, p.lds_bytes, stream);
     if (e != hipSuccess) {
       (void)hipGetLastError();
       return hip_status(e);
@@ -1247,34 +1299,40 @@ prnnStatus_t prnn_forward_stack_dense(prnnHandle_t h, int L, int N, int I, int B
     a.X[0] = Xbuf;
     st = launch_stack(T);
   } else {
-    // Blocks of about 64 steps; launch i runs layer l on block i - l.  Before
-    // launch i, the input projection of every layer l >= 1 that enters block
-    // i - l is written into that block of H[l] (the recurrence reads it there
-    // and overwrites it with the outputs).
+    // Blocks of about 64 steps; launch i runs layer l on block i - l.  The
+    // launch first writes each layer's input product for its block (from x
+    // for layer 0, from H[l - 1]'s block, finished by the launch before, for
+    // the others) into that block of H[l]; the recurrence reads it there and
+    // overwrites it with the outputs.  The workspace is not used.
     const int nb = std::max(1, (T + 32) / 64);
     const int tau = (T + nb - 1) / nb;
     const size_t blk = (size_t)tau * B * N;  // floats per full block
+    const size_t xe = x_type == PRNN_DATA_FLOAT ? 4 : 2;
     for (int i = 0; i < nb + L - 1 && st == PRNN_STATUS_SUCCESS; ++i) {
       int Tlaunch = 0;
       for (int l = 0; l < L; ++l) {
         const int k = i - l;
         const int len = (k >= 0 && k < nb) ? std::min(tau, T - k * tau) : 0;
         a.Tl[l] = std::max(len, 0);
+        a.P[l] = nullptr;
         if (a.Tl[l] == 0) continue;
         Tlaunch = std::max(Tlaunch, a.Tl[l]);
         a.H[l] = H[l] + (size_t)k * blk;
-        a.X[l] = l == 0 ? Xbuf + (size_t)k * blk : H[l] + (size_t)k * blk;
+        a.X[l] = a.H[l];
         a.h0[l] = k == 0 ? (h0 != nullptr ? h0[l] : nullptr) : H[l] + (size_t)k * blk - (size_t)B * N;
-        if (l > 0) {
-          prnn::ProjArgs pl;
-          bool vl = false;
-          st = prepare_project(h, a.Tl[l] * B, N, N, PRNN_DATA_FLOAT, H[l - 1] + (size_t)k * blk, PRNN_DATA_HALF,
-                               U[l], bias != nullptr ? bias[l] : nullptr, H[l] + (size_t)k * blk, &pl, &vl);
-          if (st == PRNN_STATUS_SUCCESS) st = hip_status(prnn::launch_project(pl, true, vl, stream));
-          if (st != PRNN_STATUS_SUCCESS) break;
+        if (l == 0) {
+          a.P[0] = static_cast<const char*>(x) + (size_t)k * tau * B * I * xe;
+          a.p_cols[0] = I;
+          a.p_f32[0] = x_type == PRNN_DATA_FLOAT ? 1 : 0;
+          a.p_vec[0] = vec ? 1 : 0;  // I % 8 == 0, x and U[0] 16-byte aligned: so is every block
+        } else {
+          a.P[l] = H[l - 1] + (size_t)k * blk;
+          a.p_cols[l] = N;
+          a.p_f32[l] = 1;
+          a.p_vec[l] = N % 8 == 0 ? 1 : 0;  // H[l - 1] and U[l] are 16-byte aligned
         }
       }
-      if (st == PRNN_STATUS_SUCCESS && Tlaunch > 0) st = launch_stack(Tlaunch);
+      if (Tlaunch > 0) st = launch_stack(Tlaunch);
     }
   }
   if (st != PRNN_STATUS_SUCCESS) return st;
@@ -1359,6 +1417,13 @@ prnnStatus_t prnn_forward_stack_sparse(prnnHandle_t h, int L, int N, int I, int 
                                    col[l], val_type, val[l], h0 != nullptr ? h0[l] : nullptr, Xbuf, H[l], stream);
     if (st != PRNN_STATUS_SUCCESS) return st;
   }
+  return PRNN_STATUS_SUCCESS;
+}
+
+prnnStatus_t prnn_set_launch(prnnHandle_t h, prnnLaunch_t kind) {
+  if (h == nullptr || (kind != PRNN_LAUNCH_COOPERATIVE && kind != PRNN_LAUNCH_PLAIN)) return PRNN_STATUS_BAD_PARAM;
+  h->launch_kind = kind;
+  h->placement_round_robin = kind == PRNN_LAUNCH_PLAIN ? h->plain_placement : h->coop_placement;
   return PRNN_STATUS_SUCCESS;
 }
 

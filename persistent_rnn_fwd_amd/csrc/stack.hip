@@ -9,12 +9,15 @@
 // runs Tl[l] steps of its layer from its own pre-activations X[l] (0 steps:
 // it only keeps its region current).  Two ways to feed the layers:
 //
-// Blocked (FUSED = false): every layer adds X[l][t], computed before the
-// launch.  The host cuts the sequence into blocks and launch i runs layer l
-// on block i - l: layer l + 1 runs one block behind layer l, and between
-// launches the input projection of the next blocks (U_l H_{l-1} + bias_l,
-// on the matrix cores) is written in place into H_l, which the recurrence
-// then reads (each element by the lane that later overwrites it).
+// Blocked (FUSED = false): the host cuts the sequence into blocks and launch
+// i runs layer l on block i - l, so layer l + 1 runs one block behind layer
+// l.  A launch starts with each layer's input product for its block (U_0 x +
+// bias_0, U_l H_{l-1} + bias_l; H_{l-1}'s block was finished by the launch
+// before): each workgroup computes, on the matrix cores, the product for the
+// rows it owns at every step of the block (project_tile) and writes it in
+// place into H_l's block, which the recurrence then reads (each element by
+// the lane that later overwrites it).  Only then are the weights loaded into
+// the registers the product used.
 //
 // Fused (FUSED = true): layer 0 adds X[0][t]; a layer l >= 1 keeps the rows
 // of [U_l | W_l] in
@@ -30,6 +33,7 @@
 // ReLU outputs are cleared of it), and layer l polls each word until bit 31
 // is clear.  Every step has its own words, so a lower layer may run any
 // number of steps ahead and nothing is ever overwritten: no backpressure.
+#include "project_tile.h"
 #include "team_kernel.h"
 
 namespace prnn {
@@ -56,9 +60,6 @@ __global__ void __launch_bounds__(512) stack_team_kernel(StackArgs a) {
   const int jn = a.chunks;
 
   if (threadIdx.x == 0) abort_flag = __builtin_nontemporal_load(a.status) != 0u;
-  // Words past N in each half stay zero (their weights are zero too).
-  for (int c = threadIdx.x; c < 2 * kParts * kHalf; c += blockDim.x)
-    if (c % kHalf >= N) lds[c] = 0.f;
   __syncthreads();
   if (abort_flag) return;
   const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (31 << 11)) & 7u;  // HW_REG_XCC_ID
@@ -80,6 +81,44 @@ __global__ void __launch_bounds__(512) stack_team_kernel(StackArgs a) {
   }
 
   const int Tl = a.Tl[layer];
+  if (!FUSED && a.P[layer] != nullptr) {
+    // This workgroup's rows [n0, n1) of the block's input product, 64 steps
+    // of the block at a time (8 waves x RW rows fit one 64-row tile).  Two
+    // k-steps of loads in flight: 2-layer stacks took 554 (N = 1792) and
+    // 431 us (N = 1152) per call against 571 and 443 with four and 583 and
+    // 454 with eight.
+    static_assert(FUSED || kTeamWaves * RW <= proj::kBM, "a workgroup's rows must fit one tile");
+    static_assert(kStackProjLds >= proj::lds_bytes<64>(), "LDS of the in-launch product");
+    constexpr int kInLaunchDepth = 2;
+    const int q0 = rank * kTeamWaves;
+    const int n0 = q0 * a.base_rows + min(q0, a.extra_rows);
+    const int n1 = n0 + kTeamWaves * a.base_rows + max(0, min(kTeamWaves, a.extra_rows - q0));
+    const int I = a.p_cols[layer];
+    const bool f32 = a.p_f32[layer] != 0, pv = a.p_vec[layer] != 0;
+    const uint32_t esize = f32 ? 4u : 2u;
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.P[layer], (uint32_t)Tl * (uint32_t)a.B * (uint32_t)I * esize);
+    const __amdgpu_buffer_rsrc_t ur = make_rsrc(a.U[layer], (uint32_t)N * (uint32_t)I * 2u);
+    const proj::TileRows rows{Tl, a.B, b};
+    const float* pb = a.bias[layer];
+    _Float16* plds = reinterpret_cast<_Float16*>(lds);
+    bool range_ok = true;
+    for (int mb = 0; mb < Tl; mb += proj::kBM) {
+      bool ok;
+      if (f32)
+        ok = pv ? proj::project_tile<true, true, 64, kInLaunchDepth>(pr, ur, pb, a.H[layer], N, rows, mb, n0, n1, I, plds)
+                : proj::project_tile<true, false, 64, kInLaunchDepth>(pr, ur, pb, a.H[layer], N, rows, mb, n0, n1, I, plds);
+      else
+        ok = pv ? proj::project_tile<false, true, 64, kInLaunchDepth>(pr, ur, pb, a.H[layer], N, rows, mb, n0, n1, I, plds)
+                : proj::project_tile<false, false, 64, kInLaunchDepth>(pr, ur, pb, a.H[layer], N, rows, mb, n0, n1, I, plds);
+      range_ok = range_ok && ok;
+    }
+    if (wave_any(!range_ok) && lane == 0) report_failure(a.status, a.status_host, kStatusRange);
+  }
+  // Words past N in each half stay zero (their weights are zero too).  The
+  // barrier also orders the product's stores before the recurrence's loads.
+  for (int c = threadIdx.x; c < 2 * kParts * kHalf; c += blockDim.x)
+    if (c % kHalf >= N) lds[c] = 0.f;
+  __syncthreads();
   const bool has_input = FUSED && layer > 0;
   const bool vec = (N & 3) == 0;
   // w[r][j]: (fused) j < J the input part (U_l), then the state part (W_l);

@@ -1,7 +1,7 @@
 // Host-side sanitizer driver: runs the C ABI of libprnn through every path
 // the host library plans and checks (dense layers in each math mode, sparse
-// layers at each wave count, the floor, projection, layers, tracing,
-// argument errors) with the host code built under AddressSanitizer and
+// layers at each wave count, the floor, projection, layers, stacks, both
+// dispatch kinds, tracing, argument errors) with the host code built under AddressSanitizer and
 // UndefinedBehaviorSanitizer (device code is built normally).  Every launch
 // stays inside the buffers allocated here.  Prints "driver ok" on success.
 #include <hip/hip_runtime.h>
@@ -61,6 +61,14 @@ int main() {
     CHECK(prnn_sync_floor(h, N, B, T, H, nullptr), OK);
   }
   CHECK(prnn_set_team_waves(h, 0), OK);
+  // both dispatch kinds (the occupancy cache of plain launches fills on the way)
+  for (int kind : {PRNN_LAUNCH_COOPERATIVE, PRNN_LAUNCH_PLAIN}) {
+    CHECK(prnn_set_launch(h, (prnnLaunch_t)kind), OK);
+    CHECK(prnn_forward_dense(h, 1792, B, T, PRNN_DATA_HALF, W, X, h0, H, nullptr), OK);
+    CHECK(prnn_forward_sparse(h, N, B, T, 58, col, PRNN_DATA_HALF, val, X, h0, H, nullptr), OK);
+  }
+  CHECK(prnn_set_launch(h, (prnnLaunch_t)5), BP);
+  CHECK(prnn_set_launch(nullptr, PRNN_LAUNCH_PLAIN), BP);
   CHECK(prnn_forward_sparse(h, 2304, B, T, 230, col, PRNN_DATA_HALF, val, X, h0, H, nullptr), OK);
   CHECK(prnn_forward_sparse(h, 1792, B, T, 179, col, PRNN_DATA_HALF, val, X, nullptr, H, nullptr), OK);
   // projection and layers
@@ -125,6 +133,14 @@ int main() {
   float* Hsame[2] = {H, H};
   CHECK(prnn_forward_stack_sparse(h, 2, 1152, 1152, B, T, 115, PRNN_DATA_FLOAT, x, Us, nullptr, cols, PRNN_DATA_HALF,
                                   vals, nullptr, Xb, Hsame, nullptr), BP);
+  // a stack of two dense layers in each mode (blocked: the input products inside the launches)
+  const void* Ws[2] = {W, W};
+  for (int mode : {PRNN_STACK_BLOCKED, PRNN_STACK_FUSED, PRNN_STACK_LAYERS}) {
+    CHECK(prnn_set_stack_mode(h, (prnnStackMode_t)mode), OK);
+    CHECK(prnn_forward_stack_dense(h, 2, 1152, 1152, B, T, PRNN_DATA_FLOAT, x, Us, nullptr, Ws, nullptr, Xb, Hs,
+                                   nullptr), OK);
+  }
+  CHECK(prnn_set_stack_mode(h, PRNN_STACK_AUTO), OK);
   CHECK(prnn_synchronize(h, nullptr), OK);
   CHECK(prnn_destroy(h), OK);
   CHECK(prnn_destroy(nullptr), OK);

@@ -1,7 +1,7 @@
 #!/bin/bash
 # Runs the host-sanitized driver (build it first: python tests/host_sanitize/build.py)
 # in a process of its own on an MI355X.  It must be the only process using the GPU:
-# its cooperative launches fail while another process holds the device.
+# the cooperative launches it makes fail while another process holds the device.
 # Any AddressSanitizer or UndefinedBehaviorSanitizer report aborts it.
 HERE=$(cd "$(dirname "$0")" && pwd)
 RT=$(ls -d /opt/rocm/llvm/lib/clang/*/lib/linux | tail -1)

@@ -31,6 +31,25 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_every_public_enum_spans_all_ints():
+    """Any int can cross the C ABI as an enum argument; an enum whose members
+    span only a few bits would make reading such a value undefined, so each
+    public enum carries a member at 0x7FFFFFFF."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    enums = re.findall(r"typedef enum \{(.*?)\}\s*(\w+);", text, flags=re.S)
+    assert len(enums) >= 7
+    for body, name in enums:
+        assert re.search(r"_MAX_ENUM\s*=\s*0x7FFFFFFF", body), name
+
+
+def test_null_handle_of_later_setters():
+    lib = binding.load_library()
+    bp = binding.BAD_PARAM
+    assert lib.prnn_set_launch(None, binding.LAUNCH_PLAIN) == bp
+    assert lib.prnn_set_launch(None, 0x7FFFFFFF) == bp
+    assert lib.prnn_set_stack_mode(None, binding.STACK_AUTO) == bp
+
+
 def test_status_strings():
     lib = binding.load_library()
     for code, name in binding.STATUS_NAMES.items():
