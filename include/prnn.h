@@ -271,11 +271,12 @@ prnnStatus_t prnn_forward_sparse_rows(prnnHandle_t handle, int N, int B, int T, 
  * device pointers owned by the caller; only X is written.
  * u_type: PRNN_DATA_HALF (PRNN_DATA_FLOAT returns NOT_SUPPORTED).
  * x_type: PRNN_DATA_FLOAT or PRNN_DATA_HALF.  Runs on the matrix cores with
- * fp32 accumulation.  An fp32 x enters as fp16 hi = fp16(x) plus
- * lo = fp16(x - hi), whose products with the fp16 U are exact: x is seen to
- * about 2^-22 of |x|.  A finite |x| >= 65520 does not fit the split; X is
- * then not valid and the failure is reported as EXECUTION_FAILED (sticky, see
- * the conventions above).
+ * fp32 accumulation.  An fp32 x enters as fp16 hi (x with the low 13 bits
+ * of its significand cleared) plus lo = fp16(x - hi), whose products with the
+ * fp16 U are exact: x is seen to about 2^-22 of |x|.  |x| >= 2^16 (infinities
+ * included) does not fit the split; X is then not valid and the failure is
+ * reported as EXECUTION_FAILED (sticky, see the conventions above).  A NaN in
+ * x gives NaN in the X rows that use it.
  * BAD_PARAM: NULL handle, x, U or X (when M > 0); M < 0, N < 1, I < 1;
  * unknown types; x, U, bias or X not aligned to their element size; X
  * overlapping x, U or bias.  NOT_SUPPORTED: fp32 U; x or U over 4 GiB.

@@ -7,10 +7,13 @@
 // depend on the state, so it is one matrix product ahead of the recurrence.)
 //
 // Products are v_mfma_f32_16x16x32_f16 with fp32 accumulation.  fp32 x enters
-// as two fp16 operands, hi = fp16(x) and lo = fp16(x - hi): both products with
-// the fp16 U are exact in the accumulators, so x is seen to about 2^-22 of |x|
-// (the fp16 range bounds |x| below 65504; a larger value clears range_ok).
-// fp16 x enters as it is.
+// as two fp16 operands: hi is x with the low 13 bits of its fp32 significand
+// cleared (11 significant bits, so exact in fp16 for 2^-14 <= |x| < 2^16) and
+// lo = fp16(x - hi), the difference being exact in fp32.  Both products with
+// the fp16 U are exact in the accumulators, so x is seen to about 2^-22 of
+// |x| (below 2^-14, to about 2^-25 absolute).  |x| >= 2^16, infinities
+// included, would make hi overflow fp16 and is reported as a range failure; a
+// NaN x passes on as NaN.  fp16 x enters as it is.
 //
 // The tile is 64 rows of x by BN = 128 or 64 rows of U, computed by 512
 // threads in two groups of 4 waves, each over one half of the k range (more
@@ -99,16 +102,17 @@ __device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, int row, int k, 
   }
 }
 
-// fp32 words -> hi and lo fp16 (see the file comment).
-__device__ __forceinline__ void split8(const u32x4& w0, const u32x4& w1, ph8& hi, ph8& lo, bool& range_ok) {
+// fp32 words -> hi and lo fp16 (see the file comment); `amax` keeps the
+// largest |x| seen (NaNs do not count), tested against 2^16 once at the end.
+__device__ __forceinline__ void split8(const u32x4& w0, const u32x4& w1, ph8& hi, ph8& lo, float& amax) {
   const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float f = __uint_as_float(w[e]);
-    const _Float16 h = (_Float16)f;
-    hi[e] = h;
-    lo[e] = (_Float16)(f - (float)h);  // the difference is exact in fp32
-    range_ok = range_ok && !(__builtin_isinf((float)h) && __builtin_isfinite(f));
+    const float h = __uint_as_float(w[e] & 0xFFFFE000u);
+    hi[e] = (_Float16)h;               // exact where in range
+    lo[e] = (_Float16)(f - h);         // f - h is exact in fp32
+    amax = __builtin_fmaxf(amax, __builtin_fabsf(f));
   }
 }
 
@@ -133,14 +137,14 @@ __device__ __forceinline__ void fetch(Staged& s, __amdgpu_buffer_rsrc_t xr, __am
 }
 
 template <bool XF32, int BN>
-__device__ __forceinline__ void stage(const Staged& s, _Float16* buf, int t, bool& range_ok) {
+__device__ __forceinline__ void stage(const Staged& s, _Float16* buf, int t, float& amax) {
   _Float16* xhi = buf;
   _Float16* xlo = buf + kBM * kRow;
   _Float16* u = buf + 2 * kBM * kRow;
   const int xo = (t >> 2) * kRow + 8 * (t & 3);
   if (XF32) {
     ph8 hi, lo;
-    split8(s.x0, s.x1, hi, lo, range_ok);
+    split8(s.x0, s.x1, hi, lo, amax);
     *reinterpret_cast<ph8*>(xhi + xo) = hi;
     *reinterpret_cast<ph8*>(xlo + xo) = lo;
   } else {
@@ -159,7 +163,7 @@ __device__ __forceinline__ void stage(const Staged& s, _Float16* buf, int t, boo
 // by all 512 threads of the workgroup (uniform control flow: every thread
 // calls it and passes the same barriers).  `lds_all` holds lds_bytes<BN>()
 // bytes; it is free again when the call returns.  Returns false in a thread
-// that met an fp32 x beyond the fp16 range.
+// that staged an fp32 x with |x| >= 2^16 (or infinite).
 template <bool XF32, bool VEC, int BN, int DEPTH = kDepth>
 __device__ __forceinline__ bool project_tile(__amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t ur, const float* bias,
                                              float* X, int ldx, const TileRows& rows, int mb, int nb, int n_end,
@@ -180,7 +184,7 @@ __device__ __forceinline__ bool project_tile(__amdgpu_buffer_rsrc_t xr, __amdgpu
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = pf4{0.f, 0.f, 0.f, 0.f};
-  bool range_ok = true;
+  float amax = 0.f;  // largest |x| staged by this thread
 
   // This group's k-steps: [grp * half, grp * half + half), half a multiple
   // of DEPTH.  Steps past the end of the row load zeros and add exactly
@@ -192,7 +196,7 @@ __device__ __forceinline__ bool project_tile(__amdgpu_buffer_rsrc_t xr, __amdgpu
   // copied, which would wait for it).
   Staged st[DEPTH];
   fetch<XF32, VEC, BN>(st[0], xr, ur, rows, mb, nb, kbase, I, t);
-  stage<XF32, BN>(st[0], lds, t, range_ok);
+  stage<XF32, BN>(st[0], lds, t, amax);
 #pragma unroll
   for (int d = 1; d <= DEPTH; ++d) fetch<XF32, VEC, BN>(st[d % DEPTH], xr, ur, rows, mb, nb, kbase + 32 * d, I, t);
   __syncthreads();
@@ -223,7 +227,7 @@ __device__ __forceinline__ bool project_tile(__amdgpu_buffer_rsrc_t xr, __amdgpu
     // `next` holds step kk + 1: into the other buffer, then reload it with
     // step kk + 1 + DEPTH.  Past the group's last step these load zeros and
     // fill a buffer nobody reads (no branch, see load8).
-    stage<XF32, BN>(next, lds + ((kk + 1) & 1) * kStage, t, range_ok);
+    stage<XF32, BN>(next, lds + ((kk + 1) & 1) * kStage, t, amax);
     fetch<XF32, VEC, BN>(next, xr, ur, rows, mb, nb, kbase + 32 * (kk + 1 + DEPTH), I, t);
     __syncthreads();
   };
@@ -267,7 +271,7 @@ __device__ __forceinline__ bool project_tile(__amdgpu_buffer_rsrc_t xr, __amdgpu
     }
   }
   __syncthreads();  // the reduction area is read before anyone reuses the LDS
-  return range_ok;
+  return !(amax >= 65536.f);
 }
 
 }  // namespace proj

@@ -113,17 +113,19 @@ def test_project_identity_rows(handle):
     np.testing.assert_array_equal(X.cpu().numpy(), (x + b).astype(np.float32))
 
 
-def test_project_range_reported(handle):
-    """A finite |x| beyond the fp16 split raises EXECUTION_FAILED at synchronize;
-    the handle works again afterwards."""
+@pytest.mark.parametrize("bad", [70000.0, -65536.0, np.inf, -np.inf])
+def test_project_range_reported(handle, bad):
+    """|x| >= 2^16 or an infinite x does not fit the fp16 split: EXECUTION_FAILED
+    at synchronize; the handle works again afterwards.  Just below 2^16 (hi =
+    65504, lo = 31) the split is exact."""
     rng = np.random.default_rng(5)
     U, x, b = draw(rng, 16, 32, 64)
-    x[3, 7] = 70000.0
+    x[3, 7] = bad
     handle.project(dev(U), dev(x), dev(b))
     with pytest.raises(PrnnError) as e:
         handle.synchronize()
     assert e.value.status == binding.EXECUTION_FAILED
-    x[3, 7] = 0.5
+    x[3, 7] = 65535.0
     X = handle.project(dev(U), dev(x), dev(b))
     handle.synchronize()
     assert proj_ratio(X.cpu().numpy(), U, x, b) <= 1.0
