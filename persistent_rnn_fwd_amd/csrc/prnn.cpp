@@ -1,6 +1,6 @@
 // Host side of the C ABI declared in include/prnn.h: handle, argument
 // checks, launch plan (layout, grid, kernel instance, exchange), exchange-ring
-// bookkeeping and cooperative launches.
+// bookkeeping and the launches (plain or cooperative).
 #include "prnn.h"
 
 #include <hip/hip_runtime.h>
@@ -592,8 +592,9 @@ void log_plan(const prnnContext* h, const char* what, int N, int B, int T, const
 // once.
 hipError_t launch_persistent(prnnContext* h, const void* fn, int grid, int block, void** args, int lds,
                              hipStream_t stream) {
+  // an LDS size the device does not take: NOT_SUPPORTED, as before any launch
   if (lds > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-    return hipErrorInvalidValue;
+    return hipErrorInvalidConfiguration;
   if (h->launch_kind != PRNN_LAUNCH_PLAIN)
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(block), args, static_cast<unsigned>(lds), stream);
   int per_cu = -1;
@@ -651,8 +652,8 @@ prnnStatus_t launch(prnnContext* h, const Plan& p, StepArgs& a, int T, hipStream
 }
 
 // The relay and team exchanges rely on workgroup i of a launch running on
-// XCD (i + c) % 8 for one constant c.  Checked once per handle for
-// cooperative launches, and for plain ones when they are chosen.
+// XCD (i + c) % 8 for one constant c.  Checked once per handle, for
+// cooperative and for plain launches.
 bool check_placement(int num_cu, bool cooperative) {
   const int grid = num_cu;
   void* p = nullptr;
