@@ -354,7 +354,7 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
     between T and T/2, the sync floor at the same N, B, T, and the error ratio
     of the timed output against the oracle."""
     import numpy as np
-    from persistent_rnn_fwd_amd import binding as _b
+    from persistent_rnn_fwd_amd import PrnnError, binding as _b
     rows = {}
     h = Handle()
     # every workload in the default math, then the dense fp16 layers again with
@@ -378,7 +378,16 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
                 h.forward_sparse_rows(g["col"], g["val"], g["row_len"], g["X"][:t], g["h0"], out=o[:t])
             else:
                 h.forward_sparse(g["col"], g["val"], g["X"][:t], g["h0"], out=o[:t])
-        full = timed(call)
+        try:
+            full = timed(call)
+        except PrnnError as e:
+            if e.status != _b.NOT_SUPPORTED:
+                raise
+            # the unbalanced 25 % layer's rows (up to 1010 pairs) do not fit
+            # the rows-of-unequal-length instances
+            rows[name] = {"N": N, "K": w.K, "T": T, "w": w.w_dtype, "not_supported": True}
+            del g, o
+            continue
         half = timed(lambda: call(T // 2))
         step_us = (full - half) * 1e3 / (T - T // 2)
         h.synchronize()

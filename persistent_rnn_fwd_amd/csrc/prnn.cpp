@@ -388,7 +388,17 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
       if (p->k == nullptr) set_waves(W = 8);
     }
     if (W == 8) p->k = pick(table, p->max_rows, p->spr);
-    if (p->k == nullptr) return false;
+    const bool may_split = wt == prnn::kF16 && h->xcds_per_row == 0 && h->team_waves == 0 && !h->trace && B <= 4;
+    if (p->k == nullptr) {
+      // No one-XCD instance holds the rows (more slots than any has): two
+      // XCDs per batch row, where an instance holds the part.
+      Plan s = *p;
+      if (!may_split || !plan_sparse_split(h, N, P, p->spr, &s)) return false;
+      *p = s;
+      W = p->waves;
+      const size_t static_lds = 256 + (size_t)W * 64 * p->k->cap * 8;
+      return (size_t)p->lds_bytes + static_lds <= h->lds_per_block;
+    }
     p->lds_stride = prnn::sparse_team_stride(p->k->rmax, W);  // the instance's fixed row distance
     p->lds_bytes = 2 * p->lds_stride * 4;
     // Automatically, fp16 layers whose rows of one wave hold more than 60
@@ -398,8 +408,7 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
     // 5 % at N = 5760 (15 x 5 slots) 2.86 -> 2.42; lighter layers lose (10 % at
     // N = 2304 1.36 -> 1.87, 1 % at N = 5760 1.47 -> 1.71), 25 % at N = 2304
     // (6 x 9) stays the same.
-    if (wt == prnn::kF16 && h->xcds_per_row == 0 && h->team_waves == 0 && !h->trace && B <= 4 &&
-        p->k->rmax * p->k->cap > 60) {
+    if (may_split && p->k->rmax * p->k->cap > 60) {
       Plan s = *p;
       if (plan_sparse_split(h, N, P, p->spr, &s)) {
         *p = s;

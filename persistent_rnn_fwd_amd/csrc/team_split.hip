@@ -401,10 +401,14 @@ const KernelEntry kDenseSplitF16Kernels[] = {
 #define PRNN_SPARSE_SPLIT(R, S, W) \
   {kF16, R, S, reinterpret_cast<const void*>(&sparse_split_kernel<R, S, W, 2>), W}
 // Sparse fp16 layers on two XCDs per batch row: (rows per wave, 64-pair slots)
-// for the 2304- and 5760-neuron layers at 8 and 12 waves per workgroup.
+// for the 2304- and 5760-neuron layers at 8 and 12 waves per workgroup; the
+// 16-slot ones hold rows of up to 1024 pairs at N = 2304 (the 25 % layer with
+// unbalanced rows, stored at its longest row's width), which no one-XCD
+// instance holds without spilling.
 const KernelEntry kSparseSplitF16Kernels[] = {
     PRNN_SPARSE_SPLIT(5, 4, 8), PRNN_SPARSE_SPLIT(5, 9, 8), PRNN_SPARSE_SPLIT(5, 10, 8), PRNN_SPARSE_SPLIT(12, 1, 8),
     PRNN_SPARSE_SPLIT(12, 5, 8), PRNN_SPARSE_SPLIT(8, 5, 12), PRNN_SPARSE_SPLIT(4, 9, 12), PRNN_SPARSE_SPLIT(4, 10, 12),
+    PRNN_SPARSE_SPLIT(5, 16, 8), PRNN_SPARSE_SPLIT(4, 16, 12),
     {0, 0, 0, nullptr},
 };
 

@@ -106,6 +106,7 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("sparse10_f16_n2304", "sparse", 2304, 4, 256, "f16", K=230, seed=106),
         Workload("sparse25_f16_n2304", "sparse", 2304, 4, 256, "f16", K=576, seed=107),
         Workload("sparse10u_f16_n2304", "sparse", 2304, 4, 256, "f16", K=230, seed=106, rows="magnitude"),
+        Workload("sparse25u_f16_n2304", "sparse", 2304, 4, 256, "f16", K=576, seed=107, rows="magnitude"),
         Workload("sparse5_f16_n5760", "sparse", 5760, 4, 256, "f16", K=288, seed=108),
     ]
 }

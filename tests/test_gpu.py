@@ -357,11 +357,13 @@ def test_plan_of_large_sparse_layers(handle):
     N = 5760, whose 12 x 5 block does not fit 4 waves per SIMD: 12 waves of 15
     rows on one XCD, or, as it runs by default, 12 waves of 8 rows on two XCDs
     per batch row; N = 2304: 12 waves of 6 rows); N = 1792 keeps 8 waves of 7
-    rows."""
+    rows; the unbalanced 25 % layer, stored at its longest row's 1010 pairs (16
+    slots), which no one-XCD instance holds: 8 waves of 5 rows on two XCDs per
+    batch row)."""
     for name, waves, rows, xcds in [("sparse1_f16_n5760", 16, 12, 0), ("sparse5_f16_n5760", 12, 15, 1),
                                     ("sparse5_f16_n5760", 12, 8, 0), ("sparse10_f16_n2304", 12, 6, 0),
                                     ("sparse25_f16_n2304", 12, 6, 0), ("sparse10u_f16_n2304", 12, 6, 0),
-                                    ("sparse10_f16_n1792", 8, 7, 0)]:
+                                    ("sparse25u_f16_n2304", 8, 5, 0), ("sparse10_f16_n1792", 8, 7, 0)]:
         w = WORKLOADS[name].with_(T=6)
         d = generate(w, seed=71)
         handle.set_xcds_per_row(xcds)
@@ -371,7 +373,20 @@ def test_plan_of_large_sparse_layers(handle):
         finally:
             handle.set_xcds_per_row(0)
         assert p["layout"] == binding.LAYOUT_TEAM and p["waves_per_wg"] == waves and p["rows_per_wave"] == rows, p
+        if name == "sparse25u_f16_n2304":
+            assert p["xcds_per_row"] == 2, p
         assert_parity(H, reference("sparse", d), oracle.TOL_F16, name)
+    # the 16-slot layer on one XCD: no instance (NOT_SUPPORTED in the TEAM layout)
+    d = generate(WORKLOADS["sparse25u_f16_n2304"].with_(T=4), seed=73)
+    handle.set_xcds_per_row(1)
+    handle.set_layout(binding.LAYOUT_TEAM)
+    try:
+        with pytest.raises(PrnnError) as e:
+            run(handle, "sparse", d)
+        assert e.value.status == binding.NOT_SUPPORTED
+    finally:
+        handle.set_xcds_per_row(0)
+        handle.set_layout(binding.LAYOUT_AUTO)
     # forced wave counts: 8 for the 1 % layer (23 rows per wave), 16 where no
     # instance or kernel has it (NOT_SUPPORTED in the TEAM layout), bad values
     w = WORKLOADS["sparse1_f16_n5760"].with_(T=6)

@@ -189,6 +189,22 @@ def test_ragged_rows_watchdog(gpu):
         assert oracle.tolerance_ratio(H.cpu().numpy(), ref_of(d), oracle.TOL_F16) <= 1.0
 
 
+def test_unbalanced_25_percent_layer_is_not_supported_as_rows(handle):
+    """The unbalanced 25 % layer's rows reach 1010 pairs (16 slots); no
+    rows-of-unequal-length instance holds 6 such rows per wave in registers:
+    NOT_SUPPORTED, nothing enqueued (the row-balanced call takes the padded
+    arrays on two XCDs per batch row)."""
+    w = WORKLOADS["sparse25u_f16_n2304"].with_(T=3, h0="randn")
+    d = generate(w, seed=5)
+    g = to_dev(d)
+    out = torch.full_like(g["X"], 7.0)
+    with pytest.raises(PrnnError) as e:
+        handle.forward_sparse_rows(g["col"], g["val"], g["row_len"], g["X"], g["h0"], out=out)
+    assert e.value.status == binding.NOT_SUPPORTED
+    handle.synchronize()
+    assert bool((out == 7.0).all())
+
+
 def test_ragged_rows_argument_errors(handle):
     lib = binding.load_library()
     s = torch.cuda.current_stream().cuda_stream
