@@ -252,6 +252,14 @@ prnnStatus_t prnn_forward_sparse(prnnHandle_t handle, int N, int B, int T, int K
  * N times the longest row.  TEAM layout, fp16 values, K <= 1024 (else
  * NOT_SUPPORTED); a small ordering kernel runs before the recurrence (the
  * handle keeps an [N] int32 buffer for it, grown outside stream capture).
+ * Where one XCD's waves cannot hold the rows (the longest row's slots of 64
+ * pairs times the rows per wave, e.g. rows of 1010 pairs at N = 2304), or
+ * with prnn_set_xcds_per_row(2), each batch row runs on two XCDs (B <= 4),
+ * each ordering and dealing the rows of its part; NOT_SUPPORTED when neither
+ * form holds the rows.  Such rows, each slot run for the rows that have it,
+ * can cost more than the row-balanced call on the same arrays padded with
+ * zero values: the rows of a wave's slots run as short batches of gathers in
+ * sequence.
  * BAD_PARAM: as for prnn_forward_sparse, plus a NULL or misaligned row_len. */
 prnnStatus_t prnn_forward_sparse_rows(prnnHandle_t handle, int N, int B, int T, int K,
                                       const int16_t* col, prnnDataType_t val_type, const void* val,
@@ -433,11 +441,13 @@ prnnStatus_t prnn_set_team_waves(prnnHandle_t handle, int waves);
  * the call cannot use makes it return NOT_SUPPORTED (or fall back to the
  * SPREAD layout under LAYOUT_AUTO).  Row-balanced sparse fp16 layers take 1
  * or 2 (B <= 4; 4: NOT_SUPPORTED); automatically 2 where one XCD's waves
- * would each hold more than 60 slots of 64 pairs (e.g. 5 % at N = 5760),
- * else 1.  prnn_sync_floor runs a forced width (with the wave count of
+ * would each hold more than 60 slots of 64 pairs (e.g. 5 % at N = 5760) or
+ * where no one-XCD instance holds the rows, else 1.  prnn_sync_floor runs a forced width (with the wave count of
  * prnn_set_team_waves, 8 or 12), else the width of the dense fp16 layer of
- * the same N and B.  fp32 W and fp32 values, and sparse rows of unequal
- * length, always use one XCD per batch row.  BAD_PARAM for any other value. */
+ * the same N and B.  Sparse rows of unequal length take 1 or 2 as well
+ * (automatically 2 only where one XCD cannot hold the rows).  fp32 W and
+ * fp32 values always use one XCD per batch row.  BAD_PARAM for any other
+ * value. */
 prnnStatus_t prnn_set_xcds_per_row(prnnHandle_t handle, int xcds);
 
 /* Exchange mode for later calls (default AUTO).  A forced RELAY that the

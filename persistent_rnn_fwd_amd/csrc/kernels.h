@@ -77,13 +77,17 @@ extern const KernelEntry kSparseTeamF16TraceKernels16[];
 // N + 1 for every layer an instance of rw rows per wave and `waves` waves per
 // workgroup serves (N <= rw x 32 waves per team), a multiple of 4.
 constexpr int sparse_team_stride(int rw, int waves) { return rw * 32 * waves + 4; }
-// Sparse fp16 rows of unequal length (team layout; 8- and 12-wave workgroups).
+// Sparse fp16 rows of unequal length (team layout; 8- and 12-wave workgroups;
+// and on two XCDs per batch row, team_split.hip).
 extern const KernelEntry kSparseRowsF16Kernels[];
 extern const KernelEntry kSparseRowsF16Kernels12[];
+extern const KernelEntry kSparseRowsSplitF16Kernels[];
 constexpr int kSparseRowsMaxK = 1024;  // longest row: 16 slots of 64 pairs
 // Orders the rows of a sparse layer of unequal rows by slot count (most
-// first; equal counts in row order) into sorted[N].  One workgroup.
-void launch_sort_rows(const int32_t* row_len, int n, int k, int32_t* sorted, hipStream_t stream);
+// first; equal counts in row order) into sorted[N], each segment of `seg`
+// rows on its own (seg = n: the whole layer; the part size on two XCDs per
+// batch row).  One workgroup per segment.
+void launch_sort_rows(const int32_t* row_len, int n, int k, int seg, int32_t* sorted, hipStream_t stream);
 
 // Fills n words with v (grid-stride).
 void launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t stream);

@@ -146,8 +146,10 @@ const KernelEntry* split_instance(int N, int P, int xp, int* part_rows) {
 // part of whole 256-column chunks of rows.  12 waves per workgroup where a
 // part would hold more than 8 rows per wave at 8 waves, else 8 (a forced
 // count: that one only).  Fills the split fields, waves, rows and instance of
-// p; false when no instance holds the part.
-bool plan_sparse_split(const prnnContext* h, int N, int P, int spr, Plan* p) {
+// p; false when no instance holds the part.  `table`: row-balanced
+// instances, or those of rows of unequal length.
+bool plan_sparse_split(const prnnContext* h, int N, int P, int spr, Plan* p,
+                       const KernelEntry* table = prnn::kSparseSplitF16Kernels) {
   const int chunks = (N + 255) / 256;
   const int part_rows = 256 * ((chunks + 1) / 2);
   const int rows8 = (std::min(part_rows, N) + 8 * P - 1) / (8 * P);
@@ -156,7 +158,7 @@ bool plan_sparse_split(const prnnContext* h, int N, int P, int spr, Plan* p) {
     if (h->team_waves != 0 && h->team_waves != w) continue;
     const int rows = (std::min(part_rows, N) + P * w - 1) / (P * w);
     const KernelEntry* k = nullptr;
-    for (const KernelEntry* e = prnn::kSparseSplitF16Kernels; e->fn != nullptr; ++e)
+    for (const KernelEntry* e = table; e->fn != nullptr; ++e)
       if (e->waves == w && e->rmax >= rows && e->cap >= spr &&
           (k == nullptr || e->rmax < k->rmax || (e->rmax == k->rmax && e->cap < k->cap)))
         k = e;
@@ -363,9 +365,20 @@ bool plan_team(const prnnContext* h, Kind kind, int N, int B, int K, int wt, Pla
       if (p->k == nullptr) set_waves(W = 8);
     }
     if (W == 8) p->k = pick(prnn::kSparseRowsF16Kernels, p->max_rows, p->spr);
-    if (p->k == nullptr) return false;
-    p->lds_stride = prnn::sparse_team_stride(p->k->rmax, W);
-    p->lds_bytes = 2 * p->lds_stride * 4;
+    if (p->k == nullptr || h->xcds_per_row == 2) {
+      // Rows of more slots than a one-XCD instance holds (or a forced width
+      // of two): two XCDs per batch row, where B <= 4 and an instance holds
+      // the part.
+      if (B > 4 || h->xcds_per_row == 4 || (h->xcds_per_row == 1 && p->k == nullptr)) return false;
+      Plan s = *p;
+      if (!plan_sparse_split(h, N, P, p->spr, &s, prnn::kSparseRowsSplitF16Kernels)) return false;
+      *p = s;
+      W = p->waves;
+    } else {
+      if (h->xcds_per_row == 4) return false;
+      p->lds_stride = prnn::sparse_team_stride(p->k->rmax, W);
+      p->lds_bytes = 2 * p->lds_stride * 4;
+    }
   } else if (kind == kSparse && wt == prnn::kF16 && h->xcds_per_row == 4) {
     return false;  // sparse layers split over two XCDs at most
   } else if (kind == kSparse && wt == prnn::kF16 && h->xcds_per_row == 2) {
@@ -773,7 +786,8 @@ prnnStatus_t run_sparse_rows(prnnContext* h, const Plan& p, int N, int B, int T,
   const int Npad = (N + 3) & ~3;
   st = ensure_ring(h, p, B, Npad, stream);
   if (st != PRNN_STATUS_SUCCESS) return st;
-  prnn::launch_sort_rows(row_len, N, K, h->d_sorted, stream);
+  // each XCD's part ordered on its own on two XCDs per batch row
+  prnn::launch_sort_rows(row_len, N, K, p.xcds_per_row > 1 ? p.part_rows : N, h->d_sorted, stream);
   if (hipGetLastError() != hipSuccess) return PRNN_STATUS_INTERNAL_ERROR;
   StepArgs a = base_args(h, N, B, T, X, h0, H, p, Npad);
   a.W = col;

@@ -18,20 +18,26 @@ namespace {
 constexpr int kSortThreads = 512;
 constexpr int kSortKeys = kSparseRowsMaxK / 64 + 1;  // slot counts 0 .. 16
 
-// Stable counting sort by slot count in one workgroup.  Thread t owns rows
-// [t seg, (t + 1) seg): it counts them per key into its own column of cnt,
-// the columns are scanned in (key, thread) order, and each thread then writes
-// its rows to their places in row order.  Key 0 = the most slots.
-__global__ void __launch_bounds__(kSortThreads) sort_rows_kernel(const int32_t* row_len, int n, int k,
+// Stable counting sort by slot count, one workgroup per segment of `seg`
+// rows (the whole layer, or one XCD's part of it on two XCDs per batch row):
+// workgroup g orders rows [g seg, min(n, (g + 1) seg)) and writes them, as
+// layer row indexes, to the same range of `sorted`.  Thread t owns rows
+// [t tseg, (t + 1) tseg) of the segment: it counts them per key into its own
+// column of cnt, the columns are scanned in (key, thread) order, and each
+// thread then writes its rows to their places in row order.  Key 0 = the
+// most slots.
+__global__ void __launch_bounds__(kSortThreads) sort_rows_kernel(const int32_t* row_len, int n, int k, int seg,
                                                                  int32_t* sorted) {
   __shared__ int cnt[kSortKeys * kSortThreads];  // [key][thread]
   __shared__ int part[kSortThreads];
   const int t = threadIdx.x;
-  const int seg = (n + kSortThreads - 1) / kSortThreads;
-  const int lo = min(n, t * seg), hi = min(n, lo + seg);
+  const int base = (int)blockIdx.x * seg;
+  const int len = min(seg, n - base);
+  const int tseg = (len + kSortThreads - 1) / kSortThreads;
+  const int lo = min(len, t * tseg), hi = min(len, lo + tseg);
   auto key_of = [&](int r) {
-    const int len = min(max(row_len[r], 0), k);
-    return (kSortKeys - 1) - ((len + 63) >> 6);
+    const int rl = min(max(row_len[base + r], 0), k);
+    return (kSortKeys - 1) - ((rl + 63) >> 6);
   };
   for (int key = 0; key < kSortKeys; ++key) cnt[key * kSortThreads + t] = 0;
   for (int r = lo; r < hi; ++r) cnt[key_of(r) * kSortThreads + t] += 1;  // this thread's column only
@@ -60,15 +66,16 @@ __global__ void __launch_bounds__(kSortThreads) sort_rows_kernel(const int32_t* 
   __syncthreads();
   for (int r = lo; r < hi; ++r) {
     const int c = key_of(r) * kSortThreads + t;
-    sorted[cnt[c]] = r;
+    sorted[base + cnt[c]] = base + r;
     cnt[c] += 1;
   }
 }
 
 }  // namespace
 
-void launch_sort_rows(const int32_t* row_len, int n, int k, int32_t* sorted, hipStream_t stream) {
-  hipLaunchKernelGGL(sort_rows_kernel, dim3(1), dim3(kSortThreads), 0, stream, row_len, n, k, sorted);
+void launch_sort_rows(const int32_t* row_len, int n, int k, int seg, int32_t* sorted, hipStream_t stream) {
+  hipLaunchKernelGGL(sort_rows_kernel, dim3((n + seg - 1) / seg), dim3(kSortThreads), 0, stream, row_len, n, k, seg,
+                     sorted);
 }
 
 // (rows per wave, 64-pair slots of the longest row)

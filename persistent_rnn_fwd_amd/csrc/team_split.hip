@@ -268,11 +268,16 @@ __global__ void __launch_bounds__(64 * WAVES) floor_split_kernel(StepArgs a) {
 // LDS row holds all N values, at most XP x RW x 32 WAVES words; where the
 // registers allow, two steps per iteration with each pair as its column and
 // its value widened to fp32 (as in the sparse team kernel).
-template <int RW, int SPR, int WAVES, int XP>
+// RAGGED: rows of unequal length (a.row_len), as in the sparse team kernel,
+// over the part: the part's rows ordered by slot count (a.sorted holds each
+// part's order in its own range) and dealt to the XCD's waves in snake order;
+// each row's pairs over its own slots, every slot run for the rows that have
+// it.
+template <int RW, int SPR, int WAVES, int XP, bool RAGGED = false>
 __global__ void __launch_bounds__(64 * WAVES) sparse_split_kernel(StepArgs a) {
   constexpr int M = pow2_at_least(RW);
   constexpr int stride = XP * RW * 32 * WAVES + 4;
-  constexpr bool kTwoSteps = SPR <= 5 && 2 * RW * SPR + 40 <= 512 / (WAVES / 4);
+  constexpr bool kTwoSteps = !RAGGED && SPR <= 5 && 2 * RW * SPR + 40 <= 512 / (WAVES / 4);
   extern __shared__ __attribute__((aligned(16))) float lds[];  // [2][stride]: word N of each row stays 0
   __shared__ int abort_flag;
   __shared__ uint2 place_scratch[WAVES][64 * SPR];  // prologue only: pair placement
@@ -291,8 +296,41 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_split_kernel(StepArgs a) {
     return;
   }
   Pair<_Float16> pr[RW][SPR];
-  load_place_rows<0, RW, Pair<_Float16>, SPR>(pr, reinterpret_cast<const int16_t*>(a.W), a.V, p.r0, p.nr, a.spr, K, N,
-                                              p.lane, place_scratch[p.wave]);
+  int cnt[SPR];   // RAGGED: rows of the wave that have slot s (wave-uniform)
+  int nr = p.nr;  // rows this wave owns
+  const int my_row = RowReduce<M>::owner_row(p.lane);
+  int my_layer_row = p.r0 + (my_row >= 0 && my_row < p.nr ? my_row : 0);  // the row whose sum this lane owns
+  if constexpr (RAGGED) {
+    const int part_r0 = p.part * a.part_rows;
+    const int len = max(0, min(a.part_rows, N - part_r0));
+    const int Q = a.G * WAVES;  // waves of the XCD
+    const int q = p.rank * WAVES + p.wave;
+    auto snake = [&](int r) { return r * Q + ((r & 1) ? Q - 1 - q : q); };
+    int rows[RW], lens[RW], ns[RW];
+    nr = 0;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int idx = snake(r);
+      const int row = idx < len ? a.sorted[part_r0 + idx] : 0;
+      const int rl = idx < len ? min(max(a.row_len[row], 0), K) : 0;
+      rows[r] = __builtin_amdgcn_readfirstlane(row);
+      lens[r] = __builtin_amdgcn_readfirstlane(rl);
+      ns[r] = (lens[r] + 63) >> 6;
+      if (idx < len) nr = r + 1;
+    }
+    load_place_rows_ragged<0, RW, Pair<_Float16>, SPR>(pr, reinterpret_cast<const int16_t*>(a.W), a.V, rows, lens, ns,
+                                                       K, N, p.lane, place_scratch[p.wave]);
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) {
+      cnt[s] = 0;
+#pragma unroll
+      for (int r = 0; r < RW; ++r) cnt[s] += ns[r] > s ? 1 : 0;
+    }
+    if (my_row >= 0 && my_row < nr) my_layer_row = a.sorted[part_r0 + snake(my_row)];
+  } else {
+    load_place_rows<0, RW, Pair<_Float16>, SPR>(pr, reinterpret_cast<const int16_t*>(a.W), a.V, p.r0, p.nr, a.spr, K,
+                                                N, p.lane, place_scratch[p.wave]);
+  }
   int wcol[kTwoSteps ? RW : 1][kTwoSteps ? SPR : 1];
   float wval[kTwoSteps ? RW : 1][kTwoSteps ? SPR : 1];
   if constexpr (kTwoSteps) {
@@ -305,11 +343,10 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_split_kernel(StepArgs a) {
       }
   }
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, a.x_bytes);
-  const int my_row = RowReduce<M>::owner_row(p.lane);
-  const bool owner = my_row >= 0 && my_row < p.nr;
+  const bool owner = my_row >= 0 && my_row < nr;
   const int part_chunks = a.part_rows / 256;
   const uint32_t xstep = (uint32_t)a.B * (uint32_t)N * 4u;
-  uint32_t xoff = ((uint32_t)p.b * (uint32_t)N + (uint32_t)(p.r0 + (owner ? my_row : 0))) * 4u;
+  uint32_t xoff = ((uint32_t)p.b * (uint32_t)N + (uint32_t)my_layer_row) * 4u;
   float x_next = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, xoff, 0, kPlain));
 
   auto step = [&](int t, float* hrow) -> bool {
@@ -338,9 +375,10 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_split_kernel(StepArgs a) {
     float acc[M];
 #pragma unroll
     for (int r = 0; r < M; ++r) acc[r] = 0.f;
+    if constexpr (RAGGED) ragged_slots<0>(pr, cnt, hrow, acc);
 #pragma unroll
     for (int s = 0; s < SPR; ++s) {
-      if (s < a.spr) {
+      if (!RAGGED && s < a.spr) {
         float hv[RW];
         if constexpr (kTwoSteps) {
 #pragma unroll
@@ -362,7 +400,7 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_split_kernel(StepArgs a) {
     debug_jitter(a.jitter_seed, a.jitter_span, p.wave, t);
     if (owner && !(p.rank == a.skip_wg && t == a.skip_step)) {
       const uint32_t hb = relu_bits(sum + x) | tag_bit(S);
-      const int row = p.r0 + my_row;
+      const int row = my_layer_row;
       const uint32_t off = ((S & 1u) * a.Npad + row) * 4u;
       __builtin_amdgcn_raw_buffer_store_b32(hb, shared, off, 0, kCoherent);
       __builtin_amdgcn_raw_buffer_store_b32(hb, region, off, 0, kPlain);
@@ -409,6 +447,12 @@ const KernelEntry kSparseSplitF16Kernels[] = {
     PRNN_SPARSE_SPLIT(5, 4, 8), PRNN_SPARSE_SPLIT(5, 9, 8), PRNN_SPARSE_SPLIT(5, 10, 8), PRNN_SPARSE_SPLIT(12, 1, 8),
     PRNN_SPARSE_SPLIT(12, 5, 8), PRNN_SPARSE_SPLIT(8, 5, 12), PRNN_SPARSE_SPLIT(4, 9, 12), PRNN_SPARSE_SPLIT(4, 10, 12),
     PRNN_SPARSE_SPLIT(5, 16, 8), PRNN_SPARSE_SPLIT(4, 16, 12),
+    {0, 0, 0, nullptr},
+};
+// Rows of unequal length on two XCDs per batch row: rows of up to 1024 pairs
+// at N = 2304 (the unbalanced 25 % layer), 5 rows per wave at 8 waves.
+const KernelEntry kSparseRowsSplitF16Kernels[] = {
+    {kF16, 5, 16, reinterpret_cast<const void*>(&sparse_split_kernel<5, 16, 8, 2, true>), 8},
     {0, 0, 0, nullptr},
 };
 

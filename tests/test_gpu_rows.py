@@ -6,7 +6,8 @@ pairs past each row's length holding values and columns that must not count;
 small-integer inputs that make every sum exact (bitwise); full-length rows
 against the row-balanced call; lengths outside [0, K] (clamped); empty rows;
 NaN-poisoned repeats and publish jitter; a forced watchdog expiry; argument
-errors.
+errors; rows on two XCDs per batch row (the unbalanced 25 % layer, whose rows
+no one-XCD instance holds, and forced widths).
 """
 import numpy as np
 import pytest
@@ -189,20 +190,82 @@ def test_ragged_rows_watchdog(gpu):
         assert oracle.tolerance_ratio(H.cpu().numpy(), ref_of(d), oracle.TOL_F16) <= 1.0
 
 
-def test_unbalanced_25_percent_layer_is_not_supported_as_rows(handle):
-    """The unbalanced 25 % layer's rows reach 1010 pairs (16 slots); no
-    rows-of-unequal-length instance holds 6 such rows per wave in registers:
-    NOT_SUPPORTED, nothing enqueued (the row-balanced call takes the padded
-    arrays on two XCDs per batch row)."""
-    w = WORKLOADS["sparse25u_f16_n2304"].with_(T=3, h0="randn")
-    d = generate(w, seed=5)
+@pytest.mark.parametrize("seed_off", [0, 1000])
+def test_unbalanced_25_percent_layer_on_two_xcds(handle, seed_off):
+    """The unbalanced 25 % layer's rows reach 1010 pairs (16 slots), more than
+    a one-XCD instance holds: it runs on two XCDs per batch row, each XCD's
+    part ordered by length on its own and dealt to its waves (8 waves of 5
+    rows); full size against the oracle.  Forced onto one XCD: NOT_SUPPORTED,
+    nothing enqueued."""
+    w = WORKLOADS["sparse25u_f16_n2304"].with_(h0="randn")
+    d = generate(w, seed=w.seed + seed_off)
+    H = run_rows(handle, d)
+    p = handle.last_plan()
+    assert p["xcds_per_row"] == 2 and p["waves_per_wg"] == 8 and p["rows_per_wave"] == 5, p
+    assert oracle.tolerance_ratio(H, ref_of(d), oracle.TOL_F16) <= 1.0
+    if seed_off == 0:
+        g = to_dev(generate(w.with_(T=3), seed=5))
+        out = torch.full_like(g["X"], 7.0)
+        handle.set_xcds_per_row(1)
+        try:
+            with pytest.raises(PrnnError) as e:
+                handle.forward_sparse_rows(g["col"], g["val"], g["row_len"], g["X"], g["h0"], out=out)
+            assert e.value.status == binding.NOT_SUPPORTED
+        finally:
+            handle.set_xcds_per_row(0)
+        handle.synchronize()
+        assert bool((out == 7.0).all())
+
+
+@pytest.mark.parametrize("N,K", [(2304, 1000), (1500, 700), (300, 200)])
+def test_rows_on_two_xcds_forced(handle, N, K):
+    """prnn_set_xcds_per_row(2) puts rows of unequal length on two XCDs per
+    batch row at any size an instance holds: random lengths 0 .. K with
+    garbage past each row, against the oracle; with +-1 values and small
+    integer inputs every sum is exact, so the result equals the oracle bit for
+    bit."""
+    d = ragged_case(N, 4, 5, K, seed=N + 7)
+    handle.set_xcds_per_row(2)
+    try:
+        H = run_rows(handle, d)
+        assert handle.last_plan()["xcds_per_row"] == 2
+        assert oracle.tolerance_ratio(H, ref_of(d), oracle.TOL_F16) <= 1.0
+        rng = np.random.default_rng(N)
+        T, B = 4, 4
+        row_len = rng.integers(0, K + 1, size=N).astype(np.int32)
+        col = np.empty((N, K), np.int16)
+        val = np.zeros((N, K), np.float16)
+        for i in range(N):
+            L = int(row_len[i])
+            col[i] = rng.choice(N, K, replace=False)
+            val[i, :L] = rng.choice([-1.0, 1.0], L) * (rng.random(L) < 0.02)
+            val[i, L:] = 7.0
+        e = {"col": col, "val": val, "row_len": row_len,
+             "X": rng.integers(-5, 6, size=(T, B, N)).astype(np.float32),
+             "h0": rng.integers(-5, 6, size=(B, N)).astype(np.float32)}
+        np.testing.assert_array_equal(run_rows(handle, e), ref_of(e))
+    finally:
+        handle.set_xcds_per_row(0)
+
+
+def test_rows_on_two_xcds_repeats_and_jitter_bitwise(gpu):
+    w = WORKLOADS["sparse25u_f16_n2304"].with_(T=24, h0="randn")
+    d = generate(w, seed=31)
     g = to_dev(d)
-    out = torch.full_like(g["X"], 7.0)
-    with pytest.raises(PrnnError) as e:
-        handle.forward_sparse_rows(g["col"], g["val"], g["row_len"], g["X"], g["h0"], out=out)
-    assert e.value.status == binding.NOT_SUPPORTED
-    handle.synchronize()
-    assert bool((out == 7.0).all())
+    out = torch.empty_like(g["X"])
+    with Handle() as h:
+        out.fill_(float("nan"))
+        first = h.forward_sparse_rows(g["col"], g["val"], g["row_len"], g["X"], g["h0"], out=out).clone()
+        h.synchronize()
+        assert h.last_plan()["xcds_per_row"] == 2
+        for seed in (0, 1, 2):
+            h.debug_jitter(seed, 48 if seed else 0)
+            out.fill_(float("nan"))
+            h.forward_sparse_rows(g["col"], g["val"], g["row_len"], g["X"], g["h0"], out=out)
+            h.synchronize()
+            assert torch.equal(out, first)
+        h.debug_jitter(0, 0)
+    assert oracle.tolerance_ratio(first.cpu().numpy(), ref_of(d), oracle.TOL_F16) <= 1.0
 
 
 def test_ragged_rows_argument_errors(handle):
