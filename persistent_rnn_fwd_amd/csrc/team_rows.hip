@@ -8,7 +8,8 @@
 // layer costs every row the longest row's work.  Here each row's length is an
 // input; the rows are ordered by how many 64-pair slots they fill (most
 // first) and dealt to the waves in snake order by the kernel, so that each
-// wave gets about the same number of slots and skips the ones its rows lack.
+// wave's rows have about the same slots in all; a wave runs its rows up to the
+// slots of its longest row, not the layer's.
 #include "team_kernel.h"
 
 namespace prnn {

@@ -271,8 +271,8 @@ __global__ void __launch_bounds__(64 * WAVES) floor_split_kernel(StepArgs a) {
 // RAGGED: rows of unequal length (a.row_len), as in the sparse team kernel,
 // over the part: the part's rows ordered by slot count (a.sorted holds each
 // part's order in its own range) and dealt to the XCD's waves in snake order;
-// each row's pairs over its own slots, every slot run for the rows that have
-// it.
+// each row's pairs over its own slots, each slot run for all the wave's rows
+// up to the slots of its longest row.
 template <int RW, int SPR, int WAVES, int XP, bool RAGGED = false>
 __global__ void __launch_bounds__(64 * WAVES) sparse_split_kernel(StepArgs a) {
   constexpr int M = pow2_at_least(RW);
@@ -296,8 +296,8 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_split_kernel(StepArgs a) {
     return;
   }
   Pair<_Float16> pr[RW][SPR];
-  int cnt[SPR];   // RAGGED: rows of the wave that have slot s (wave-uniform)
-  int nr = p.nr;  // rows this wave owns
+  int cnt_max = 0;  // RAGGED: slots of the wave's longest row (wave-uniform)
+  int nr = p.nr;    // rows this wave owns
   const int my_row = RowReduce<M>::owner_row(p.lane);
   int my_layer_row = p.r0 + (my_row >= 0 && my_row < p.nr ? my_row : 0);  // the row whose sum this lane owns
   if constexpr (RAGGED) {
@@ -320,12 +320,7 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_split_kernel(StepArgs a) {
     }
     load_place_rows_ragged<0, RW, Pair<_Float16>, SPR>(pr, reinterpret_cast<const int16_t*>(a.W), a.V, rows, lens, ns,
                                                        K, N, p.lane, place_scratch[p.wave]);
-#pragma unroll
-    for (int s = 0; s < SPR; ++s) {
-      cnt[s] = 0;
-#pragma unroll
-      for (int r = 0; r < RW; ++r) cnt[s] += ns[r] > s ? 1 : 0;
-    }
+    cnt_max = ns[0];  // the wave's rows come longest first
     if (my_row >= 0 && my_row < nr) my_layer_row = a.sorted[part_r0 + snake(my_row)];
   } else {
     load_place_rows<0, RW, Pair<_Float16>, SPR>(pr, reinterpret_cast<const int16_t*>(a.W), a.V, p.r0, p.nr, a.spr, K,
@@ -375,10 +370,9 @@ __global__ void __launch_bounds__(64 * WAVES) sparse_split_kernel(StepArgs a) {
     float acc[M];
 #pragma unroll
     for (int r = 0; r < M; ++r) acc[r] = 0.f;
-    if constexpr (RAGGED) ragged_slots<0>(pr, cnt, hrow, acc);
 #pragma unroll
     for (int s = 0; s < SPR; ++s) {
-      if (!RAGGED && s < a.spr) {
+      if (RAGGED ? s < cnt_max : s < a.spr) {
         float hv[RW];
         if constexpr (kTwoSteps) {
 #pragma unroll
