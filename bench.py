@@ -44,7 +44,7 @@ HBM_PEAK = 8.0e12             # MI355X HBM3E, bytes/s
 COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_rnn_fwd_n1792.json")
 KERNEL_SOURCES = ["device_common.h", "kernels.h", "dense_kernel.h", "sparse_kernel.h", "team_kernel.h", "team_mfma.h",
                   "dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip", "team_f16.hip", "team_f32.hip",
-                  "team_half.hip", "team_split.hip", "team_rows.hip", "project_tile.h", "project.hip", "stack.hip", "noalloc.hip",
+                  "team_half.hip", "team_split.hip", "team_rows.hip", "team_pinned.h", "project_tile.h", "project.hip", "stack.hip", "noalloc.hip",
                   "host_internal.h"]
 
 

@@ -200,12 +200,21 @@ __global__ void __launch_bounds__(512) stack_team_kernel(StackArgs a) {
     float acc[M];
 #pragma unroll
     for (int r = 0; r < M; ++r) acc[r] = 0.f;
+    if constexpr (!FUSED && kPinnedWeights && PinnedFma<RW, J>::kAvailable) {
+      // the weights at fixed registers, as in the layer kernel
+      float4 h[J];
 #pragma unroll
-    for (int j = 0; j < kParts * J; ++j) {
-      if (FUSED && j < J && !has_input) continue;  // layer 0 has no input part
-      const float4 h = *reinterpret_cast<const float4*>(inrow + 256 * j + 4 * lane);
+      for (int j = 0; j < J; ++j) h[j] = *reinterpret_cast<const float4*>(inrow + 256 * j + 4 * lane);
+      __builtin_amdgcn_sched_barrier(0);
+      PinnedFma<RW, J>::run(acc, w, h);
+    } else {
 #pragma unroll
-      for (int r = 0; r < RW; ++r) w[r][j].fma4(acc[r], h);
+      for (int j = 0; j < kParts * J; ++j) {
+        if (FUSED && j < J && !has_input) continue;  // layer 0 has no input part
+        const float4 h = *reinterpret_cast<const float4*>(inrow + 256 * j + 4 * lane);
+#pragma unroll
+        for (int r = 0; r < RW; ++r) w[r][j].fma4(acc[r], h);
+      }
     }
     const float sum = RowReduce<M>::reduce(acc, lane);
     asm volatile("" : "+v"(aborted_now) : "v"(sum));  // keep the test after the arithmetic

@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "team_pinned.h"
 #include "kernels.h"
 #include "dense_kernel.h"
 #include "sparse_kernel.h"
@@ -198,6 +199,15 @@ __device__ __forceinline__ void team_stamp_tail(const StepArgs& a, const TeamPos
 // HALF (fp16 W only): the staged row holds h_{t-1} rounded to fp16 and every
 // instruction adds two exact fp16 x fp16 products to the fp32 sums (dot4);
 // a finite h outside the fp16 range raises kStatusRange.
+// Widened weights at fixed registers (team_pinned.h) for the instances that
+// have them.  Left to itself the register allocator scattered the widened
+// weights (two components of a chunk near v20-v100, the other two near
+// v110-v190), and the step's multiply-add stream then issued at 2.6-2.7
+// cycles per instruction per SIMD against 2.07 with a regular assignment
+// (the same instructions replayed in a probe, every CU busy, two waves per
+// SIMD).  The order of the products in each sum does not change.
+constexpr bool kPinnedWeights = true;
+
 template <typename WT, int RW, int J, bool WIDE = false, bool TRACE = false, bool HALF = false>
 __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
   static_assert(!HALF || (std::is_same<WT, _Float16>::value && !WIDE), "half-h needs packed fp16 weights");
@@ -304,15 +314,21 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
       float4 h[J];
 #pragma unroll
       for (int j = 0; j < J; ++j) h[j] = *reinterpret_cast<const float4*>(hrow + 256 * j + 4 * p.lane);
+      if constexpr (kPinnedWeights && PinnedFma<RW, J>::kAvailable && WR == RW) {
+        // every read in flight before the first product, as in the loop below
+        __builtin_amdgcn_sched_barrier(0);
+        PinnedFma<RW, J>::run(acc, ww, h);
+      } else {
 #pragma unroll
-      for (int j = 0; j < J; ++j)
+        for (int j = 0; j < J; ++j)
 #pragma unroll
-        for (int r = 0; r < RW; ++r) {
-          if (r < WR)
-            ww[r < WR ? r : 0][j].fma4(acc[r], h[j]);
-          else
-            wp[r < WR ? 0 : r - WR][j].fma4(acc[r], h[j]);
-        }
+          for (int r = 0; r < RW; ++r) {
+            if (r < WR)
+              ww[r < WR ? r : 0][j].fma4(acc[r], h[j]);
+            else
+              wp[r < WR ? 0 : r - WR][j].fma4(acc[r], h[j]);
+          }
+      }
     }
     clk.mark(kTrCompute);
     const float sum = RowReduce<M>::reduce(acc, p.lane);
