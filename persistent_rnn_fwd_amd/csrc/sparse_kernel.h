@@ -64,6 +64,7 @@ struct Pair<float> {
 // same word at once.  A gather whose 32 lanes hit b distinct words in one
 // bank takes b cycles for that half (measured on gfx950).
 constexpr int kLdsBanks = 32;
+constexpr int kBitSlicedSlots = 5;  // slot capacities up to which ranks come from bit-sliced ballots
 
 // Bank-aware placement of one row's pairs (the pages' bank-aware layout,
 // our reading: every gather instruction should touch each LDS bank once).
@@ -86,16 +87,53 @@ __device__ __forceinline__ void place_row_bank_aware(P (&row)[SPR], int spr, int
     if (s < spr) scratch[64 * s + lane] = pad.raw();
   }
   // rank = number of pairs in lower banks + earlier pairs of the same bank
-  uint32_t base = 0;
-  for (int bank = 0; bank < kLdsBanks; ++bank) {
+  if constexpr (SPR <= kBitSlicedSlots) {
+    // Five ballots per slot hold its banks bit by bit.  Each lane then
+    // compares its own bank with every slot's lanes at once: a walk from the
+    // top bit down keeps the lanes still equal to it (eq) and collects those
+    // found lower (lt).  No scalar chain between banks, unlike the loop below.
+    uint64_t live[SPR], bit[SPR][5];
 #pragma unroll
     for (int s = 0; s < SPR; ++s) {
-      if (s < spr) {
-        const bool mine = 64 * s + lane < K && (row[s].column() & (kLdsBanks - 1)) == bank;
-        const uint64_t m = __builtin_amdgcn_ballot_w64(mine);
-        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        if (mine) rank[s] = (int)(base + below);
-        base += (uint32_t)__builtin_popcountll(m);
+      const bool v = s < spr && 64 * s + lane < K;
+      const int bk = row[s].column() & (kLdsBanks - 1);
+      live[s] = __builtin_amdgcn_ballot_w64(v);
+#pragma unroll
+      for (int i = 0; i < 5; ++i) bit[s][i] = __builtin_amdgcn_ballot_w64(v && ((bk >> i) & 1));
+    }
+    const uint64_t lanes_below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) {
+      const int bk = row[s].column() & (kLdsBanks - 1);
+      int r = 0;
+#pragma unroll
+      for (int s2 = 0; s2 < SPR; ++s2) {
+        uint64_t eq = live[s2], lt = 0;
+#pragma unroll
+        for (int i = 4; i >= 0; --i) {
+          const uint64_t m = 0ull - (uint64_t)((bk >> i) & 1);  // all ones where my bit i is set
+          lt |= eq & ~bit[s2][i] & m;
+          eq &= ~(bit[s2][i] ^ m);
+        }
+        r += __builtin_popcountll(lt);
+        if (s2 < s) r += __builtin_popcountll(eq);
+        if (s2 == s) r += __builtin_popcountll(eq & lanes_below);
+      }
+      rank[s] = r;
+    }
+  } else {
+    uint32_t base = 0;
+    for (int bank = 0; bank < kLdsBanks; ++bank) {
+#pragma unroll
+      for (int s = 0; s < SPR; ++s) {
+        if (s < spr) {
+          const bool mine = 64 * s + lane < K && (row[s].column() & (kLdsBanks - 1)) == bank;
+          const uint64_t m = __builtin_amdgcn_ballot_w64(mine);
+          const uint32_t below =
+              __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          if (mine) rank[s] = (int)(base + below);
+          base += (uint32_t)__builtin_popcountll(m);
+        }
       }
     }
   }
@@ -126,13 +164,26 @@ __device__ __forceinline__ void place_rows_bank_aware(P (&pr)[RW][SPR], int nr, 
   }
 }
 
+constexpr int kLoadAllPairs = 48;  // pairs per lane up to which a block's loads are issued together
+
 // Loads rows [R, RW) of a register-resident pair block and places each one
 // before the next row's loads are issued: with every row's loads in flight
 // at once the largest blocks would not fit the registers.
 template <int R, int RW, typename P, int SPR>
 __device__ __forceinline__ void load_place_rows(P (&pr)[RW][SPR], const int16_t* col, const void* val, int r0, int nr,
                                                 int spr, int K, int n, int lane, uint2* scratch) {
-  if constexpr (R < RW) {
+  if constexpr (R == 0 && RW * SPR <= kLoadAllPairs) {
+    // small blocks: every row's loads in flight at once, then the placements
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int s = 0; s < SPR; ++s) {
+        const int k = 64 * s + lane;
+        const bool live = r < nr && s < spr && k < K;
+        pr[r][s].load(col, val, live ? (size_t)(r0 + r) * K + k : 0, live, n);
+      }
+    place_rows_bank_aware<0, RW, P, SPR>(pr, nr, spr, K, n, lane, scratch);
+  } else if constexpr (R < RW) {
 #pragma unroll
     for (int s = 0; s < SPR; ++s) {
       const int k = 64 * s + lane;
