@@ -64,7 +64,12 @@ struct Pair<float> {
 // same word at once.  A gather whose 32 lanes hit b distinct words in one
 // bank takes b cycles for that half (measured on gfx950).
 constexpr int kLdsBanks = 32;
-constexpr int kBitSlicedSlots = 5;  // slot capacities up to which ranks come from bit-sliced ballots
+// Ranks from bit-sliced ballots for pair blocks of up to 4 slots and 32 pairs
+// per lane; larger blocks keep the per-bank loop, whose scalar registers the
+// bigger blocks can spare (the bit-sliced form made them spill).
+constexpr int kBitSlicedSlots = 4;
+constexpr int kBitSlicedPairs = 32;
+constexpr bool bit_sliced(int rw, int spr) { return spr <= kBitSlicedSlots && rw * spr <= kBitSlicedPairs; }
 
 // Bank-aware placement of one row's pairs (the pages' bank-aware layout,
 // our reading: every gather instruction should touch each LDS bank once).
@@ -76,7 +81,15 @@ constexpr int kBitSlicedSlots = 5;  // slot capacities up to which ranks come fr
 // summation order are deterministic) and dealt round-robin over the 2 * spr
 // groups.  The sum is order-free, so any placement computes the same row.
 // `scratch` is this wave's LDS area of SPR * 64 entries.
-template <typename P, int SPR>
+// A wave-uniform 64-bit value copied to vector registers (an empty asm the
+// compiler cannot see through).
+__device__ __forceinline__ uint64_t in_vgprs(uint64_t x) {
+  uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+  asm("" : "+v"(lo), "+v"(hi));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <typename P, int SPR, bool BIT_SLICED>
 __device__ __forceinline__ void place_row_bank_aware(P (&row)[SPR], int spr, int K, int n, int lane, uint2* scratch) {
   P pad;
   pad.load(nullptr, nullptr, 0, false, n);
@@ -87,39 +100,38 @@ __device__ __forceinline__ void place_row_bank_aware(P (&row)[SPR], int spr, int
     if (s < spr) scratch[64 * s + lane] = pad.raw();
   }
   // rank = number of pairs in lower banks + earlier pairs of the same bank
-  if constexpr (SPR <= kBitSlicedSlots) {
+  if constexpr (BIT_SLICED) {
     // Five ballots per slot hold its banks bit by bit.  Each lane then
-    // compares its own bank with every slot's lanes at once: a walk from the
-    // top bit down keeps the lanes still equal to it (eq) and collects those
-    // found lower (lt).  No scalar chain between banks, unlike the loop below.
-    uint64_t live[SPR], bit[SPR][5];
+    // compares its own bank with a whole slot at once: a walk from the top
+    // bit down keeps the lanes still equal to it (eq) and collects those
+    // found lower (lt).  No scalar chain between banks, unlike the loop below;
+    // one slot's masks are live at a time.
+    int bk[SPR];
 #pragma unroll
-    for (int s = 0; s < SPR; ++s) {
-      const bool v = s < spr && 64 * s + lane < K;
-      const int bk = row[s].column() & (kLdsBanks - 1);
-      live[s] = __builtin_amdgcn_ballot_w64(v);
-#pragma unroll
-      for (int i = 0; i < 5; ++i) bit[s][i] = __builtin_amdgcn_ballot_w64(v && ((bk >> i) & 1));
-    }
+    for (int s = 0; s < SPR; ++s) bk[s] = row[s].column() & (kLdsBanks - 1);
     const uint64_t lanes_below = (1ull << lane) - 1ull;
 #pragma unroll
-    for (int s = 0; s < SPR; ++s) {
-      const int bk = row[s].column() & (kLdsBanks - 1);
-      int r = 0;
+    for (int s2 = 0; s2 < SPR; ++s2) {
+      const bool v = s2 < spr && 64 * s2 + lane < K;
+      // The masks move to vector registers: held in scalar ones they pushed
+      // the kernel's own scalars out to spill slots that the time loop reloads.
+      const uint64_t live = in_vgprs(__builtin_amdgcn_ballot_w64(v));
+      uint64_t bit[5];
 #pragma unroll
-      for (int s2 = 0; s2 < SPR; ++s2) {
-        uint64_t eq = live[s2], lt = 0;
+      for (int i = 0; i < 5; ++i) bit[i] = in_vgprs(__builtin_amdgcn_ballot_w64(v && ((bk[s2] >> i) & 1)));
+#pragma unroll
+      for (int s = 0; s < SPR; ++s) {
+        uint64_t eq = live, lt = 0;
 #pragma unroll
         for (int i = 4; i >= 0; --i) {
-          const uint64_t m = 0ull - (uint64_t)((bk >> i) & 1);  // all ones where my bit i is set
-          lt |= eq & ~bit[s2][i] & m;
-          eq &= ~(bit[s2][i] ^ m);
+          const uint64_t m = 0ull - (uint64_t)((bk[s] >> i) & 1);  // all ones where my bit i is set
+          lt |= eq & ~bit[i] & m;
+          eq &= ~(bit[i] ^ m);
         }
-        r += __builtin_popcountll(lt);
-        if (s2 < s) r += __builtin_popcountll(eq);
-        if (s2 == s) r += __builtin_popcountll(eq & lanes_below);
+        rank[s] += __builtin_popcountll(lt);
+        if (s2 < s) rank[s] += __builtin_popcountll(eq);
+        if (s2 == s) rank[s] += __builtin_popcountll(eq & lanes_below);
       }
-      rank[s] = r;
     }
   } else {
     uint32_t base = 0;
@@ -159,7 +171,7 @@ template <int R, int RW, typename P, int SPR>
 __device__ __forceinline__ void place_rows_bank_aware(P (&pr)[RW][SPR], int nr, int spr, int K, int n, int lane,
                                                       uint2* scratch) {
   if constexpr (R < RW) {
-    if (R < nr) place_row_bank_aware<P, SPR>(pr[R], spr, K, n, lane, scratch);
+    if (R < nr) place_row_bank_aware<P, SPR, bit_sliced(RW, SPR)>(pr[R], spr, K, n, lane, scratch);
     place_rows_bank_aware<R + 1, RW, P, SPR>(pr, nr, spr, K, n, lane, scratch);
   }
 }
@@ -190,7 +202,7 @@ __device__ __forceinline__ void load_place_rows(P (&pr)[RW][SPR], const int16_t*
       const bool live = R < nr && s < spr && k < K;
       pr[R][s].load(col, val, live ? (size_t)(r0 + R) * K + k : 0, live, n);
     }
-    if (R < nr) place_row_bank_aware<P, SPR>(pr[R], spr, K, n, lane, scratch);
+    if (R < nr) place_row_bank_aware<P, SPR, bit_sliced(RW, SPR)>(pr[R], spr, K, n, lane, scratch);
     asm volatile("" ::: "memory");
     load_place_rows<R + 1, RW, P, SPR>(pr, col, val, r0, nr, spr, K, n, lane, scratch);
   }
@@ -210,7 +222,7 @@ __device__ __forceinline__ void load_place_rows_ragged(P (&pr)[RW][SPR], const i
       const bool live = k < lens[R];
       pr[R][s].load(col, val, live ? (size_t)rows[R] * K + k : 0, live, n);
     }
-    if (ns[R] > 0) place_row_bank_aware<P, SPR>(pr[R], ns[R], lens[R], n, lane, scratch);
+    if (ns[R] > 0) place_row_bank_aware<P, SPR, bit_sliced(RW, SPR)>(pr[R], ns[R], lens[R], n, lane, scratch);
     asm volatile("" ::: "memory");
     load_place_rows_ragged<R + 1, RW, P, SPR>(pr, col, val, rows, lens, ns, K, n, lane, scratch);
   }
