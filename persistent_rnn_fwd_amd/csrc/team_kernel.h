@@ -330,6 +330,11 @@ __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
           }
       }
     }
+    if constexpr (TRACE) {
+      // the products in asm blocks may otherwise sink past the clock read
+#pragma unroll
+      for (int r = 0; r < M; ++r) asm volatile("" : : "v"(acc[r]));
+    }
     clk.mark(kTrCompute);
     const float sum = RowReduce<M>::reduce(acc, p.lane);
     clk.mark(kTrReduce);
