@@ -379,7 +379,7 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
             else:
                 h.forward_sparse(g["col"], g["val"], g["X"][:t], g["h0"], out=o[:t])
         try:
-            full = timed(call)
+            full, half = timed(call, other=lambda: call(T // 2))
         except PrnnError as e:
             if e.status != _b.NOT_SUPPORTED:
                 raise
@@ -388,7 +388,6 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
             rows[name] = {"N": N, "K": w.K, "T": T, "w": w.w_dtype, "not_supported": True}
             del g, o
             continue
-        half = timed(lambda: call(T // 2))
         step_us = (full - half) * 1e3 / (T - T // 2)
         h.synchronize()
         plan = {k: v for k, v in h.last_plan().items() if k != "first_step"}
@@ -398,8 +397,8 @@ def per_config_table(torch, dev, Handle, WORKLOADS, generate, timed, no_check=Fa
         if plan["layout"] == _b.LAYOUT_TEAM:
             h.set_team_waves(plan["waves_per_wg"])
             h.set_xcds_per_row(plan["xcds_per_row"])
-        f_full = timed(lambda: h.sync_floor(N, B, T, out=fo))
-        f_half = timed(lambda: h.sync_floor(N, B, T // 2, out=fo[: T // 2]))
+        f_full, f_half = timed(lambda: h.sync_floor(N, B, T, out=fo),
+                               other=lambda: h.sync_floor(N, B, T // 2, out=fo[: T // 2]))
         h.set_team_waves(0)
         h.set_xcds_per_row(0)
         floor_us = (f_full - f_half) * 1e3 / (T - T // 2)
@@ -555,11 +554,10 @@ def large_dense_table(torch, dev, Handle, timed, no_check=False):
         W = torch.from_numpy(d["W"]).to(dev)
         X = torch.from_numpy(d["X"]).to(dev)
         o = torch.empty_like(X)
-        full = timed(lambda: h.forward_dense(W, X, out=o))
-        half = timed(lambda: h.forward_dense(W, X[:T // 2], out=o[:T // 2]))
+        full, half = timed(lambda: h.forward_dense(W, X, out=o), other=lambda: h.forward_dense(W, X[:T // 2], out=o[:T // 2]))
         plan = h.last_plan()
-        f_full = timed(lambda: h.sync_floor(N, B, T, out=o))
-        f_half = timed(lambda: h.sync_floor(N, B, T // 2, out=o[:T // 2]))
+        f_full, f_half = timed(lambda: h.sync_floor(N, B, T, out=o),
+                               other=lambda: h.sync_floor(N, B, T // 2, out=o[:T // 2]))
         step = (full - half) / (T // 2) * 1e3
         floor = (f_full - f_half) / (T // 2) * 1e3
         row = {"N": N, "B": B, "T": T, "xcds_per_row": plan["xcds_per_row"], "rows_per_wave": plan["rows_per_wave"],
@@ -703,16 +701,24 @@ def main():
     sparse_ms = float(np.mean(sparse_list))
     ms_per_step = wall * 1e3 / args.steps
 
-    def timed(fn, reps=20):
-        fn()
+    def timed(fn, reps=20, other=None):
+        """Median ms of fn over reps calls; with `other`, the two alternate
+        call by call and both medians are returned (a slope between them
+        then sees no drift of the clock between two blocks of calls)."""
+        fns = [fn] if other is None else [fn, other]
+        for f in fns:
+            f()
         torch.cuda.synchronize()
-        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for a, b in es:
-            a.record(stream)
-            fn()
-            b.record(stream)
+        es = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+              for _ in fns]
+        for r in range(reps):
+            for f, ev in zip(fns, es):
+                ev[r][0].record(stream)
+                f()
+                ev[r][1].record(stream)
         torch.cuda.synchronize()
-        return float(np.median([a.elapsed_time(b) for a, b in es]))
+        med = [float(np.median([a.elapsed_time(b) for a, b in ev])) for ev in es]
+        return med[0] if other is None else tuple(med)
 
     detail = {}
     if args.only_timed and args.profile_layers:
@@ -751,13 +757,12 @@ def main():
 
     # per-step time by the slope between T and T/2, and the sync floor
     floor_out = torch.empty((T, B, N), dtype=torch.float32, device=dev)
-    f_full = timed(lambda: h.sync_floor(N, B, T, out=floor_out))
-    f_half = timed(lambda: h.sync_floor(N, B, T // 2, out=floor_out[: T // 2]))
+    f_full, f_half = timed(lambda: h.sync_floor(N, B, T, out=floor_out),
+                           other=lambda: h.sync_floor(N, B, T // 2, out=floor_out[: T // 2]))
     floor_us = (f_full - f_half) * 1e3 / (T - T // 2)
     h.synchronize()
     for w in (wd, ws, w1):
-        full = timed(lambda: call(w.name))
-        half = timed(lambda: call(w.name, T // 2))
+        full, half = timed(lambda: call(w.name), other=lambda: call(w.name, T // 2))
         step_us = (full - half) * 1e3 / (T - T // 2)
         flop = w.flop_per_step
         detail[w.name] = {
@@ -789,11 +794,10 @@ def main():
         h.set_math(mode)
         fl = floor_us
         if w is not wd:
-            f_a = timed(lambda: h.sync_floor(w.N, w.B, w.T, out=out[w.name]))
-            f_b = timed(lambda: h.sync_floor(w.N, w.B, w.T // 2, out=out[w.name][: w.T // 2]))
+            f_a, f_b = timed(lambda: h.sync_floor(w.N, w.B, w.T, out=out[w.name]),
+                             other=lambda: h.sync_floor(w.N, w.B, w.T // 2, out=out[w.name][: w.T // 2]))
             fl = (f_a - f_b) * 1e3 / (w.T - w.T // 2)
-        full = timed(lambda: call(w.name, w.T))
-        half = timed(lambda: call(w.name, w.T // 2))
+        full, half = timed(lambda: call(w.name, w.T), other=lambda: call(w.name, w.T // 2))
         step_us = (full - half) * 1e3 / (w.T - w.T // 2)
         h.synchronize()
         alt = {"ms_per_call": round(full, 4), "timesteps_per_s": round(w.T / (full * 1e-3), 1),
