@@ -185,15 +185,24 @@ __global__ void __launch_bounds__(512) dense_split_kernel(StepArgs a) {
     float acc[M];
 #pragma unroll
     for (int r = 0; r < M; ++r) acc[r] = 0.f;
+    if constexpr (kPinnedWeights && PinnedFma<RW, J>::kAvailable && WR == RW) {
+      // the weights at fixed registers, as in the team kernel
+      float4 h[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const float4 h = *reinterpret_cast<const float4*>(hrow + 256 * j + 4 * p.lane);
+      for (int j = 0; j < J; ++j) h[j] = *reinterpret_cast<const float4*>(hrow + 256 * j + 4 * p.lane);
+      __builtin_amdgcn_sched_barrier(0);
+      PinnedFma<RW, J>::run(acc, ww, h);
+    } else {
 #pragma unroll
-      for (int r = 0; r < RW; ++r) {
-        if (r < WR)
-          ww[r < WR ? r : 0][j].fma4(acc[r], h);
-        else
-          wp[r < WR ? 0 : r - WR][j].fma4(acc[r], h);
+      for (int j = 0; j < J; ++j) {
+        const float4 h = *reinterpret_cast<const float4*>(hrow + 256 * j + 4 * p.lane);
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+          if (r < WR)
+            ww[r < WR ? r : 0][j].fma4(acc[r], h);
+          else
+            wp[r < WR ? 0 : r - WR][j].fma4(acc[r], h);
+        }
       }
     }
     const float sum = RowReduce<M>::reduce(acc, p.lane);
