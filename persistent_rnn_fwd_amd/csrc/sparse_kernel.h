@@ -69,6 +69,12 @@ constexpr int kLdsBanks = 32;
 // bigger blocks can spare (the bit-sliced form made them spill).
 constexpr int kBitSlicedSlots = 4;
 constexpr int kBitSlicedPairs = 32;
+// Small blocks of 3 slots or more: ranks from per-bank counts and a scan,
+// linear in the slots.  With 1 or 2 slots the scan costs more than it saves
+// (launch prologue, 1 % at N = 1792: 9.4 us bit-sliced, 11.3 with counts;
+// 10 % at N = 1792, 3 slots: 24.6 and 19.3; 10 % at N = 2304, 4 slots: 41
+// and 26).
+constexpr int kHistogramSlots = 3;
 constexpr bool bit_sliced(int rw, int spr) { return spr <= kBitSlicedSlots && rw * spr <= kBitSlicedPairs; }
 
 // Bank-aware placement of one row's pairs (the pages' bank-aware layout,
@@ -100,7 +106,55 @@ __device__ __forceinline__ void place_row_bank_aware(P (&row)[SPR], int spr, int
     if (s < spr) scratch[64 * s + lane] = pad.raw();
   }
   // rank = number of pairs in lower banks + earlier pairs of the same bank
-  if constexpr (BIT_SLICED) {
+  if constexpr (BIT_SLICED && SPR >= kHistogramSlots) {
+    // Five ballots per slot hold the slot's banks bit by bit; from them each
+    // lane tells which of a slot's lanes share any one bank (match).  Lane b
+    // (and b + 32) counts bank b in every slot; a scan over lanes 0-31 turns
+    // the counts into the pairs of lower banks; each pair then reads from
+    // lane `bank` the pairs before its slot and adds its slot's earlier lanes
+    // of the same bank.  Linear in the slots, no scalar chain.
+    int bk[SPR], cnt[SPR];
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) bk[s] = row[s].column() & (kLdsBanks - 1);
+    const uint64_t lanes_below = (1ull << lane) - 1ull;
+    const int lane_bank = lane & (kLdsBanks - 1);
+    auto masks = [&](int s, uint64_t& live, uint64_t (&bit)[5]) {
+      const bool v = s < spr && 64 * s + lane < K;
+      // in vector registers: held in scalar ones they pushed the kernel's own
+      // scalars out to spill slots that the time loop reloads
+      live = in_vgprs(__builtin_amdgcn_ballot_w64(v));
+#pragma unroll
+      for (int i = 0; i < 5; ++i) bit[i] = in_vgprs(__builtin_amdgcn_ballot_w64(v && ((bk[s] >> i) & 1)));
+    };
+    auto match = [](uint64_t live, const uint64_t (&bit)[5], int b) {
+      uint64_t eq = live;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) eq &= ~(bit[i] ^ (0ull - (uint64_t)((b >> i) & 1)));
+      return eq;
+    };
+    int total = 0;
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) {
+      uint64_t live, bit[5];
+      masks(s, live, bit);
+      cnt[s] = __builtin_popcountll(match(live, bit, lane_bank));
+      total += cnt[s];
+    }
+    int incl = total;  // inclusive scan of the bank totals over lanes 0-31 (and 32-63)
+#pragma unroll
+    for (int d = 1; d < kLdsBanks; d <<= 1) {
+      const int y = __shfl_up(incl, d, kLdsBanks);
+      if (lane_bank >= d) incl += y;
+    }
+    int off = incl - total;  // lane b: pairs in banks below b, then also in the slots done
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) {
+      uint64_t live, bit[5];
+      masks(s, live, bit);
+      rank[s] = __shfl(off, bk[s]) + __builtin_popcountll(match(live, bit, bk[s]) & lanes_below);
+      off += cnt[s];
+    }
+  } else if constexpr (BIT_SLICED) {
     // Five ballots per slot hold its banks bit by bit.  Each lane then
     // compares its own bank with a whole slot at once: a walk from the top
     // bit down keeps the lanes still equal to it (eq) and collects those
