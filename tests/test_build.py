@@ -10,6 +10,8 @@ of a 256-thread workgroup = 1 per SIMD).
 """
 import json
 import os
+import subprocess
+import sys
 
 import pytest
 
@@ -49,3 +51,12 @@ def test_remark_parser():
             "x.h:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]\n"
             "x.h:1:1: remark:     Dynamic Stack: False [-Rpass-analysis=kernel-resource-usage]\n")
     assert buildmod.parse_resource_remarks(text) == {"_Zk": {"VGPRs": 82, "ScratchSize": 0, "Dynamic Stack": "False"}}
+
+
+def test_pinned_weight_blocks_match_their_generator():
+    """team_pinned.h is the committed output of gen_team_pinned.py."""
+    csrc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "persistent_rnn_fwd_amd", "csrc")
+    out = subprocess.run([sys.executable, os.path.join(csrc, "gen_team_pinned.py")], capture_output=True, text=True,
+                         check=True).stdout
+    with open(os.path.join(csrc, "team_pinned.h")) as fh:
+        assert fh.read() == out
