@@ -32,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -44,15 +45,23 @@ HBM_PEAK = 8.0e12             # MI355X HBM3E, bytes/s
 COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_rnn_fwd_n1792.json")
 KERNEL_SOURCES = ["device_common.h", "kernels.h", "dense_kernel.h", "sparse_kernel.h", "team_kernel.h", "team_mfma.h",
                   "dense_f16.hip", "dense_f32.hip", "sparse_f16.hip", "sparse_f32.hip", "team_f16.hip", "team_f32.hip",
-                  "team_half.hip", "team_split.hip", "team_rows.hip", "team_pinned.h", "project_tile.h", "project.hip", "stack.hip", "noalloc.hip",
-                  "host_internal.h"]
+                  "team_half.hip", "team_split.hip", "team_rows.hip", "team_pinned.h", "project_tile.h", "project.hip",
+                  "stack.hip", "noalloc.hip", "host_internal.h"]
+
+
+def code_only(text: str) -> str:
+    """The source without its comments and with whitespace collapsed: what
+    the compiler sees, so that a comment edit keeps the counters valid."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "persistent_rnn_fwd_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "persistent_rnn_fwd_amd", "csrc", f)) as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

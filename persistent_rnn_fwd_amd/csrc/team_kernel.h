@@ -195,10 +195,6 @@ __device__ __forceinline__ void team_stamp_tail(const StepArgs& a, const TeamPos
   }
 }
 
-//
-// HALF (fp16 W only): the staged row holds h_{t-1} rounded to fp16 and every
-// instruction adds two exact fp16 x fp16 products to the fp32 sums (dot4);
-// a finite h outside the fp16 range raises kStatusRange.
 // Widened weights at fixed registers (team_pinned.h) for the instances that
 // have them.  Left to itself the register allocator scattered the widened
 // weights (two components of a chunk near v20-v100, the other two near
@@ -208,6 +204,10 @@ __device__ __forceinline__ void team_stamp_tail(const StepArgs& a, const TeamPos
 // SIMD).  The order of the products in each sum does not change.
 constexpr bool kPinnedWeights = true;
 
+//
+// HALF (fp16 W only): the staged row holds h_{t-1} rounded to fp16 and every
+// instruction adds two exact fp16 x fp16 products to the fp32 sums (dot4);
+// a finite h outside the fp16 range raises kStatusRange.
 template <typename WT, int RW, int J, bool WIDE = false, bool TRACE = false, bool HALF = false>
 __global__ void __launch_bounds__(512) dense_team_kernel(StepArgs a) {
   static_assert(!HALF || (std::is_same<WT, _Float16>::value && !WIDE), "half-h needs packed fp16 weights");
