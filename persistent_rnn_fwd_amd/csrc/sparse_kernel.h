@@ -101,10 +101,7 @@ __device__ __forceinline__ void place_row_bank_aware(P (&row)[SPR], int spr, int
   pad.load(nullptr, nullptr, 0, false, n);
   int rank[SPR];
 #pragma unroll
-  for (int s = 0; s < SPR; ++s) {
-    rank[s] = 0;
-    if (s < spr) scratch[64 * s + lane] = pad.raw();
-  }
+  for (int s = 0; s < SPR; ++s) rank[s] = 0;
   // rank = number of pairs in lower banks + earlier pairs of the same bank
   if constexpr (BIT_SLICED && SPR >= kHistogramSlots) {
     // Five ballots per slot hold the slot's banks bit by bit; from them each
@@ -188,21 +185,55 @@ __device__ __forceinline__ void place_row_bank_aware(P (&row)[SPR], int spr, int
       }
     }
   } else {
-    uint32_t base = 0;
-    for (int bank = 0; bank < kLdsBanks; ++bank) {
+    // Larger blocks: the same counts and scan, one slot at a time through
+    // this wave's scratch (.x the pair's bank, .y its bank's count in the
+    // slot, then its rank), so that no per-slot array but the ranks lives in
+    // registers; held there, the masks and counts made these blocks spill.
+    const uint64_t lanes_below = (1ull << lane) - 1ull;
+    const int lane_bank = lane & (kLdsBanks - 1);
 #pragma unroll
-      for (int s = 0; s < SPR; ++s) {
-        if (s < spr) {
-          const bool mine = 64 * s + lane < K && (row[s].column() & (kLdsBanks - 1)) == bank;
-          const uint64_t m = __builtin_amdgcn_ballot_w64(mine);
-          const uint32_t below =
-              __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-          if (mine) rank[s] = (int)(base + below);
-          base += (uint32_t)__builtin_popcountll(m);
-        }
+    for (int s = 0; s < SPR; ++s)
+      if (s < spr) scratch[64 * s + lane] = make_uint2((uint32_t)(row[s].column() & (kLdsBanks - 1)), 0u);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    auto match_in = [&](int s, int b) {  // the lanes of slot s whose pair is in bank b
+      const uint32_t bs = scratch[64 * s + lane].x;
+      const bool v = 64 * s + lane < K;
+      uint64_t eq = in_vgprs(__builtin_amdgcn_ballot_w64(v));
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const uint64_t bit = in_vgprs(__builtin_amdgcn_ballot_w64(v && ((bs >> i) & 1u)));
+        eq &= ~(bit ^ (0ull - (uint64_t)((b >> i) & 1)));
       }
+      return eq;
+    };
+    int total = 0;
+    for (int s = 0; s < spr; ++s) {
+      const int c = __builtin_popcountll(match_in(s, lane_bank));
+      scratch[64 * s + lane].y = (uint32_t)c;
+      total += c;
     }
+    int incl = total;  // inclusive scan of the bank totals over lanes 0-31 (and 32-63)
+#pragma unroll
+    for (int d = 1; d < kLdsBanks; d <<= 1) {
+      const int y = __shfl_up(incl, d, kLdsBanks);
+      if (lane_bank >= d) incl += y;
+    }
+    int off = incl - total;
+    for (int s = 0; s < spr; ++s) {
+      const uint2 e = scratch[64 * s + lane];
+      const int r = __shfl(off, (int)e.x) + __builtin_popcountll(match_in(s, (int)e.x) & lanes_below);
+      off += (int)e.y;
+      scratch[64 * s + lane].y = (uint32_t)r;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int s = 0; s < SPR; ++s)
+      if (s < spr) rank[s] = (int)scratch[64 * s + lane].y;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
+#pragma unroll
+  for (int s = 0; s < SPR; ++s)
+    if (s < spr) scratch[64 * s + lane] = pad.raw();
   const int groups = 2 * spr;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // padding written before the pairs
 #pragma unroll
