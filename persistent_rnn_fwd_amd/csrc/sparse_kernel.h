@@ -64,9 +64,9 @@ struct Pair<float> {
 // same word at once.  A gather whose 32 lanes hit b distinct words in one
 // bank takes b cycles for that half (measured on gfx950).
 constexpr int kLdsBanks = 32;
-// Ranks from bit-sliced ballots for pair blocks of up to 4 slots and 32 pairs
-// per lane; larger blocks keep the per-bank loop, whose scalar registers the
-// bigger blocks can spare (the bit-sliced form made them spill).
+// Ranks with every slot's masks and counts in registers for pair blocks of up
+// to 4 slots and 32 pairs per lane; larger blocks stage them in LDS, slot by
+// slot (held in registers they made those blocks spill).
 constexpr int kBitSlicedSlots = 4;
 constexpr int kBitSlicedPairs = 32;
 // Small blocks of 3 slots or more: ranks from per-bank counts and a scan,
@@ -155,8 +155,8 @@ __device__ __forceinline__ void place_row_bank_aware(P (&row)[SPR], int spr, int
     // Five ballots per slot hold its banks bit by bit.  Each lane then
     // compares its own bank with a whole slot at once: a walk from the top
     // bit down keeps the lanes still equal to it (eq) and collects those
-    // found lower (lt).  No scalar chain between banks, unlike the loop below;
-    // one slot's masks are live at a time.
+    // found lower (lt).  Cheaper than the counts above for 1 or 2 slots; one
+    // slot's masks are live at a time.
     int bk[SPR];
 #pragma unroll
     for (int s = 0; s < SPR; ++s) bk[s] = row[s].column() & (kLdsBanks - 1);
