@@ -82,3 +82,21 @@ def test_no_weight_load_inside_the_time_loop(key):
     assert not [l for l in ins if l.startswith("scratch_")]
     if quads:
         assert sum(l.startswith("global_load_dwordx2") for l in ins[:lo]) == quads
+
+
+def test_pinned_weights_need_no_copies_in_the_time_loop():
+    """The exact 7 x 7 instance keeps its widened weights at the registers its
+    multiply-add blocks name (v8 .. v203): the time loop holds all 196
+    multiply-adds, and nothing in it writes a weight register."""
+    inst, name, _ = INSTANCES["dense_exact_7x7"]
+    ins = kernel_asm(inst, name)
+    lo, hi = time_loop(ins)
+    body = ins[lo:hi + 1]
+    fmas = [l for l in body if l.startswith(("v_fmac_f32", "v_fma_f32"))]
+    assert len(fmas) == 196
+    weights = {f"v{r}" for r in range(8, 204)}
+    srcs = {l.replace(",", " ").split()[2] for l in fmas}
+    assert srcs <= weights, sorted(srcs - weights)[:5]
+    writes = [l for l in body if l.startswith("v_") and not l.startswith(("v_fmac_f32", "v_fma_f32"))
+              and l.replace(",", " ").split()[1] in weights]
+    assert not writes, writes[:5]
